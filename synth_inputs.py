@@ -1,0 +1,213 @@
+"""Seeded synthetic inputs for the layout-permuting tile copy.
+
+This module is shared by the tests, ``bench.py`` and the oracle checks.  It holds
+workload *data* only -- shapes, element strides, offsets, element types, value
+distributions and seeds -- and the random generators that fill source buffers.
+It contains no part of the copy, the layout algebra, the partition or the bank
+planning: both the product path and the oracle derive everything else on their
+own from these plain tuples.
+
+Layouts are given in elements as ``(shape, stride, offset)`` tuples over one
+storage buffer, the shape:stride form used by the TileLayout pages.  Values are
+generated on the host with NumPy's PCG64 (``numpy.random.default_rng(seed)``)
+and handled as raw bytes: floating point values are produced in their own type
+and then only ever moved as bit patterns.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+# element type name -> (bytes per element, numpy type used to make values)
+ELEMENT_TYPES = {
+    "int8": (1, np.int8),
+    "uint8": (1, np.uint8),
+    "float16": (2, np.float16),
+    "bfloat16": (2, None),  # made from float32 by round-to-nearest-even
+    "float32": (4, np.float32),
+    "int32": (4, np.int32),
+    "float64": (8, np.float64),
+    "int64": (8, np.int64),
+    "int4vec": (16, None),  # 16-byte struct of four int32 (a vector type, not 4-bit ints)
+}
+
+
+def elem_bytes(dtype: str) -> int:
+    return ELEMENT_TYPES[dtype][0]
+
+
+@dataclass(frozen=True)
+class Side:
+    shape: tuple
+    stride: tuple
+    offset: int = 0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    src: Side
+    dst: Side
+    dtype: str
+    values: str  # "uniform_pm1" | "uniform01" | "normal" | "bits"
+    seed: int
+    src_storage: Optional[int] = None  # storage elements; default = span of the layout
+    dst_storage: Optional[int] = None
+    notes: str = field(default="", compare=False)
+
+    @property
+    def eb(self) -> int:
+        return elem_bytes(self.dtype)
+
+
+def span(side: Side) -> int:
+    """Number of storage elements needed to hold every element the layout names
+    (non-negative strides only, which is all the workloads use)."""
+    if any(e == 0 for e in side.shape):
+        return side.offset
+    return side.offset + sum((e - 1) * s for e, s in zip(side.shape, side.stride)) + 1
+
+
+def storage_elems(w: Workload, which: str) -> int:
+    side = w.src if which == "src" else w.dst
+    given = w.src_storage if which == "src" else w.dst_storage
+    return given if given is not None else span(side)
+
+
+def _row_major(shape):
+    st, acc = [], 1
+    for e in reversed(shape):
+        st.append(acc)
+        acc *= e
+    return tuple(reversed(st))
+
+
+# --- the five workloads, at their full sizes ------------------------------------------------
+
+def tile32_roundtrip() -> Workload:
+    return Workload("tile32x32_f32_roundtrip",
+                    Side((32, 32), (32, 1)), Side((32, 32), (32, 1)),
+                    "float32", "uniform_pm1", seed=1,
+                    notes="one 32x32 fp32 tile, identity row-major layouts, one wave64")
+
+
+def sf_transpose(tiles: int = 65536) -> Workload:
+    shape = (tiles, 2, 1, 4, 32)
+    return Workload(f"sf_transpose_{tiles}x2x1x4x32_f32",
+                    Side(shape, (256, 128, 128, 32, 1)), Side(shape, (256, 128, 128, 1, 4)),
+                    "float32", "uniform_pm1", seed=2,
+                    notes="scale-factor tile transpose, tiles contiguous in HBM (tile t at 256*t)")
+
+
+def transpose2d(n: int = 16384, m: Optional[int] = None, dtype: str = "float32", seed: Optional[int] = None,
+                values: Optional[str] = None) -> Workload:
+    m = n if m is None else m
+    if seed is None:
+        seed = {"float32": 3, "bfloat16": 31}.get(dtype, 50)
+    if values is None:
+        values = "normal" if dtype in ("float32", "bfloat16") else "bits"
+    return Workload(f"transpose_{n}x{m}_{dtype}",
+                    Side((n, m), (m, 1)), Side((n, m), (1, n)), dtype, values, seed)
+
+
+def permute0213(b: int = 32, h: int = 32, s: int = 2048, d: int = 128, dtype: str = "bfloat16") -> Workload:
+    # logical index (b, h, s, d); source [B,H,S,D] row-major, destination [B,S,H,D] row-major
+    return Workload(f"permute0213_{b}x{h}x{s}x{d}_{dtype}",
+                    Side((b, h, s, d), (h * s * d, s * d, d, 1)),
+                    Side((b, h, s, d), (s * h * d, d, h * d, 1)),
+                    dtype, "normal", seed=4)
+
+
+SWEEP_DTYPES = ("int8", "float16", "float64", "int4vec")
+SWEEP_SEEDS = {"int8": 50, "float16": 51, "float64": 52, "int4vec": 53}
+
+
+def sweep_dense(dtype: str, n: int = 8192) -> Workload:
+    return Workload(f"transpose_{n}x{n}_{dtype}",
+                    Side((n, n), (n, 1)), Side((n, n), (1, n)), dtype, "bits", SWEEP_SEEDS[dtype])
+
+
+def sweep_slice(dtype: str, n: int = 8192) -> Workload:
+    # source view [1:n-1:1, 0:n-2:2] of an n x n row-major buffer; dense transposed destination
+    rows = n - 2          # range(1, n-1)
+    cols = (n - 2 + 1) // 2  # range(0, n-2, 2)
+    return Workload(f"slice_{n}x{n}[1:{n-1}:1,0:{n-2}:2]_{dtype}",
+                    Side((rows, cols), (n, 2), offset=n), Side((rows, cols), (1, rows)),
+                    dtype, "bits", seed=54, src_storage=n * n)
+
+
+def sweep_odd(dtype: str, rows: int = 8191, cols: int = 8190) -> Workload:
+    return Workload(f"transpose_{rows}x{cols}_{dtype}",
+                    Side((rows, cols), (cols, 1)), Side((rows, cols), (1, rows)),
+                    dtype, "bits", seed=55)
+
+
+def all_workloads():
+    ws = [tile32_roundtrip(), sf_transpose(), transpose2d(dtype="float32"), transpose2d(dtype="bfloat16"),
+          permute0213()]
+    for dt in SWEEP_DTYPES:
+        ws += [sweep_dense(dt), sweep_slice(dt), sweep_odd(dt)]
+    return ws
+
+
+# --- generators -----------------------------------------------------------------------------
+
+def _bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns of float32 values, rounded to nearest even (finite inputs)."""
+    u = x.astype(np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def make_values(dtype: str, values: str, count: int, seed: int) -> np.ndarray:
+    """``count`` elements of ``dtype`` as a flat uint8 array of count*eb bytes."""
+    rng = np.random.default_rng(seed)
+    eb = elem_bytes(dtype)
+    if values == "bits" or dtype == "int4vec":
+        return np.frombuffer(rng.bytes(count * eb), dtype=np.uint8).copy()
+    if dtype == "bfloat16":
+        f = (rng.standard_normal(count, dtype=np.float32) if values == "normal"
+             else _uniform(rng, values, count, np.float32))
+        return _bf16_bits_from_f32(f).view(np.uint8)
+    npt = ELEMENT_TYPES[dtype][1]
+    if values == "normal":
+        if npt in (np.float32, np.float64):
+            arr = rng.standard_normal(count, dtype=npt)
+        else:
+            arr = rng.standard_normal(count).astype(npt)
+    elif values in ("uniform_pm1", "uniform01"):
+        arr = _uniform(rng, values, count, npt)
+    else:
+        raise ValueError(values)
+    return np.ascontiguousarray(arr).view(np.uint8)
+
+
+def _uniform(rng, values, count, npt):
+    if npt in (np.float32, np.float64):
+        u = rng.random(count, dtype=npt)
+    else:
+        u = rng.random(count).astype(npt)
+    return (u * 2 - 1).astype(npt) if values == "uniform_pm1" else u
+
+
+def make_source(w: Workload) -> np.ndarray:
+    """The whole source storage buffer (uint8, storage_elems*eb bytes), seeded."""
+    return make_values(w.dtype, w.values, storage_elems(w, "src"), w.seed)
+
+
+def sentinel_dst(w: Workload, byte: int = 0xA5) -> np.ndarray:
+    """Destination storage prefilled with a sentinel byte, so writes outside the
+    destination image are visible."""
+    return np.full(storage_elems(w, "dst") * w.eb, byte, dtype=np.uint8)
+
+
+def scaled_2d(w: Workload, n: int, m: int) -> Workload:
+    """The same 2-D transpose family at another size (row-major source, transposed destination)."""
+    return Workload(f"{w.name}@{n}x{m}", Side((n, m), (m, 1)), Side((n, m), (1, n)), w.dtype, w.values, w.seed)
+
+
+__all__ = [n for n in dir() if not n.startswith("_")]
+_row_major = _row_major
