@@ -1,0 +1,197 @@
+/*
+ * tile_copy.h -- layout-permuting tile copy for AMD MI355X (gfx950), C ABI.
+ *
+ * The operation (TVM TIRx docs, "copy -> gmem_smem" intro and "What it accepts";
+ * "permute_layout" intro): a region described by a source shape:stride
+ * TileLayout is copied to a destination TileLayout.  A layout maps a logical
+ * index i = (i_0 .. i_{r-1}) to the element offset
+ *
+ *     offset + sum_k i_k * stride_k
+ *
+ * and the copy writes, for every logical index i of the common shape,
+ *
+ *     dst[dst_layout(i)] = src[src_layout(i)]
+ *
+ * as raw element bytes (no conversion; floating point payloads, NaNs and
+ * denormals are moved as bit patterns).  Extent-1 modes are ignored on both
+ * sides; the remaining extents must be equal and in the same order.  Bytes of
+ * the destination buffer that no logical index names are not written.
+ *
+ * The work runs on the GPU: global -> LDS -> global through a synthesized
+ * [outer, threads, vec] thread partition (TVM TIRx "copy -> gmem_smem",
+ * Algorithm; TileLang tutorial "loop_mapping.py", the partition formula) and an
+ * XOR-swizzled LDS stage chosen by simulating gfx950's LDS banks (TVM TIRx
+ * "permute_layout", Algorithm step 2).  The host part (layout algebra,
+ * partition planner, swizzle chooser) is exposed through tc_plan for
+ * inspection; it needs no GPU.
+ *
+ * Thread safety: all entry points may be called from several host threads;
+ * plans are cached in a library-owned, locked cache.  The error string is
+ * per host thread.
+ */
+#ifndef TILE_COPY_H
+#define TILE_COPY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TC_MAX_RANK 8
+
+/*
+ * A TileLayout, S[shape : stride] (TVM TIRx "copy -> gmem_smem", demonstration
+ * program).  All quantities are in elements of the copy's dtype.
+ *   rank    number of modes, 0..TC_MAX_RANK (rank 0 = one element)
+ *   offset  element offset of logical index (0, .., 0) from the base pointer;
+ *           region slices fold into it (see tc_layout_slice)
+ *   shape   extents, >= 0 (an extent of 0 makes the copy empty)
+ *   stride  element strides; a source stride may be 0 (broadcast read) or
+ *           negative; destination strides must make the layout injective
+ * Only the first `rank` entries of shape/stride are read.
+ */
+typedef struct tc_layout {
+  int32_t rank;
+  int32_t reserved;
+  int64_t offset;
+  int64_t shape[TC_MAX_RANK];
+  int64_t stride[TC_MAX_RANK];
+} tc_layout;
+
+/* Element types.  Only the width matters: 1, 2, 4, 8 or 16 bytes
+ * (TVM TIRx "permute_layout", "What it accepts": dtype byte width in
+ * {1, 2, 4, 8, 16}).  TC_B128 is a 16-byte struct such as four int32. */
+enum tc_dtype {
+  TC_U8 = 0, TC_I8 = 1, TC_F16 = 2, TC_BF16 = 3, TC_F32 = 4, TC_I32 = 5,
+  TC_F64 = 6, TC_I64 = 7, TC_B128 = 8
+};
+
+/* Return codes: 0 = success, negative = error (tc_last_error() has the reason). */
+enum tc_status {
+  TC_OK = 0,
+  TC_E_NULL = -1,          /* a required pointer is null */
+  TC_E_RANK = -2,          /* rank outside 0..TC_MAX_RANK */
+  TC_E_EXTENT = -3,        /* negative extent, or non-unit extents differ */
+  TC_E_DTYPE = -4,         /* unknown dtype */
+  TC_E_ALIGN = -5,         /* a base pointer is not aligned to the element size */
+  TC_E_NONINJECTIVE = -6,  /* two logical indices map to one destination element */
+  TC_E_ALIAS = -7,         /* the source and destination byte ranges overlap */
+  TC_E_DECLINED = -8,      /* strict mode: no integer [outer, threads, vec] partition,
+                              no vector of >= 4 bytes, or no conflict-free swizzle */
+  TC_E_HIP = -9,           /* a HIP runtime call failed (launch or device query) */
+  TC_E_RANGE = -10,        /* sizes beyond what the kernels index (e.g. > 2^31 vectors) */
+  TC_E_ARG = -11           /* other invalid argument (bad slice, unknown flag) */
+};
+
+/* Flags for tc_set_flags / tc_plan.  Unknown bits are rejected (TC_E_ARG). */
+#define TC_FLAG_STRICT        0x01 /* decline (TC_E_DECLINED) instead of falling back to the
+                                      guarded element-wise path */
+#define TC_FLAG_FORCE_GUARDED 0x02 /* always take the guarded element-wise path */
+#define TC_FLAG_FORCE_REGS    0x04 /* co-contiguous copies: stage through registers only */
+#define TC_FLAG_FORCE_LDS     0x08 /* co-contiguous copies: stage through LDS */
+#define TC_FLAG_NO_SWIZZLE    0x10 /* transposes: no XOR swizzle (k = 0), to measure its effect */
+#define TC_FLAG_ALL           0x1f
+
+/* Which kernel a plan runs. */
+enum tc_path {
+  TC_PATH_EMPTY = 0,       /* nothing to copy */
+  TC_PATH_TRANSPOSE = 1,   /* the source- and destination-contiguous modes differ:
+                              LDS tile, 16/8/4-byte vectors, XOR swizzle */
+  TC_PATH_ROWS = 2,        /* both sides contiguous along the same mode: vectors staged in
+                              registers (no LDS needed) */
+  TC_PATH_ROUNDTRIP = 3,   /* co-contiguous and small: one workgroup, global -> LDS ->
+                              global with the [outer, threads, vec] partition */
+  TC_PATH_GUARDED_TILE = 4,/* fallback: LDS tile with element-wide accesses and guards */
+  TC_PATH_GUARDED_ROWS = 5 /* fallback: element-wise, destination order, guarded */
+};
+
+/*
+ * What the planner decided, for inspection and tests (filled by tc_plan, and by
+ * tile_copy_ex).  Modes are the joint canonical modes (extent, src stride, dst
+ * stride), outermost first in destination-stride order.
+ */
+typedef struct tc_plan_info {
+  int32_t path;             /* enum tc_path */
+  int32_t elem_bytes;
+  int64_t count;            /* elements copied */
+  int32_t rank;             /* joint canonical rank */
+  int32_t declined;         /* 1 if the fast path was declined (reason below) */
+  int64_t extent[TC_MAX_RANK];
+  int64_t src_stride[TC_MAX_RANK];
+  int64_t dst_stride[TC_MAX_RANK];
+  int64_t src_offset, dst_offset;
+  /* partition: per workgroup, [outer, threads, vec] in each phase */
+  int32_t threads;          /* threads per workgroup (multiple of 64) */
+  int32_t vec_bytes;        /* bytes per global access (16, 8, 4, or the element size) */
+  int32_t load_outer;       /* accesses per thread in the load phase (global -> LDS/regs) */
+  int32_t store_outer;      /* accesses per thread in the store phase (LDS/regs -> global) */
+  /* tile (transpose paths): index of the modes and tile extents in elements */
+  int32_t mode_r, mode_c, mode_b; /* dst-contiguous mode, src-contiguous mode, batch mode (-1 none) */
+  int32_t tile_r, tile_c, tile_b;
+  int64_t workgroups;       /* workgroups launched */
+  int32_t lds_bytes;        /* LDS per workgroup */
+  /* XOR swizzle of the LDS tile's 16-byte (write-width) column chunks:
+   chunk' = chunk ^ (((row >> shift) & mask) << tbit) ^ ((chunk >> cshift) & cmask), k = log2(mask+1) */
+  int32_t xor_k, xor_shift, xor_mask, xor_tbit;
+  int32_t xor_cshift, xor_cmask;
+  int32_t lds_write_bytes, lds_read_bytes;       /* LDS instruction widths */
+  int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
+  char reason[192];         /* why the fast path was declined ("" if it was not) */
+} tc_plan_info;
+
+/*
+ * Copy `src` (device pointer, read through src_layout) into `dst` (device
+ * pointer, written through dst_layout), on `stream` (a hipStream_t; NULL = the
+ * null stream).  Asynchronous: returns after the launch; kernel faults surface
+ * at the caller's next synchronisation.  Layout structs are read during the
+ * call only.  The library allocates no device memory (LDS only).
+ * Errors: TC_E_NULL, TC_E_RANK, TC_E_EXTENT, TC_E_DTYPE, TC_E_ALIGN,
+ * TC_E_NONINJECTIVE, TC_E_ALIAS, TC_E_DECLINED (strict mode), TC_E_RANGE,
+ * TC_E_HIP; nothing is launched when an error is returned.
+ */
+int tile_copy(const void* src, const tc_layout* src_layout, void* dst, const tc_layout* dst_layout,
+              int dtype, void* stream);
+
+/* tile_copy with explicit flags (instead of the process-wide ones) and, when
+ * info is not NULL, the plan that ran. */
+int tile_copy_ex(const void* src, const tc_layout* src_layout, void* dst, const tc_layout* dst_layout,
+                 int dtype, void* stream, int flags, tc_plan_info* info);
+
+/*
+ * Host only: plan the copy without running it (no GPU needed).
+ * `ptr_align` is the byte alignment both base pointers will have (a power of
+ * two; 0 means 16).  Fills *out.  Returns the status tile_copy would return
+ * for the layouts (alias and pointer checks aside).
+ */
+int tc_plan(const tc_layout* src_layout, const tc_layout* dst_layout, int dtype, int flags,
+            int ptr_align, tc_plan_info* out);
+
+/* The reason for the last error on this host thread ("" after success). */
+const char* tc_last_error(void);
+
+/* Process-wide default flags for tile_copy.  Returns the previous flags, or
+ * TC_E_ARG for unknown bits. */
+int tc_set_flags(int flags);
+int tc_get_flags(void);
+
+/*
+ * Region slice of a layout (TVM TIRx "copy -> gmem_smem", demonstration
+ * program: A[fs] with fs a tuple of slices).  For every mode k, Python slice
+ * semantics with start/stop/step (step != 0; negative start/stop count from
+ * the end; out-of-range values are clipped): the new extent is the number of
+ * indices in range(start, stop, step), offset += start * stride,
+ * stride *= step.  `start`, `stop`, `step` have in->rank entries.
+ * Returns TC_OK or TC_E_NULL / TC_E_RANK / TC_E_ARG.
+ */
+int tc_layout_slice(const tc_layout* in, const int64_t* start, const int64_t* stop, const int64_t* step,
+                    tc_layout* out);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int tc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILE_COPY_H */

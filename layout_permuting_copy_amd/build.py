@@ -1,0 +1,62 @@
+"""Builds the tile-copy library for gfx950, in-tree: libtile_copy.so (C ABI declared in
+include/tile_copy.h) and the LDS bank probe (bin/lds_bank_probe)."""
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libtile_copy.so")
+PROBE = os.path.join(PKG, "bin", "lds_bank_probe")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "--offload-arch=gfx950"
+# packed fp32 ops are disabled for all device code
+NO_PK = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+SOURCES = ["layout.cpp", "bank.cpp", "plan.cpp", "abi.cpp", "kernels.hip"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{out}")
+    return out
+
+
+def _compile(src):
+    obj = os.path.join(BUILD, src + ".o")
+    path = os.path.join(CSRC, src)
+    if src.endswith(".hip"):
+        cmd = [HIPCC, ARCH, *NO_PK, *COMMON, "-c", path, "-o", obj]
+    else:
+        cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
+    out = _run(cmd)
+    if out.strip():
+        print(out, file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(os.path.dirname(PROBE), exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+        probe = ex.submit(_run, [HIPCC, ARCH, *NO_PK, "-O3", "-std=c++17",
+                                 os.path.join(CSRC, "probe", "lds_bank_probe.hip"), "-o", PROBE + ".tmp"])
+        tmp = LIB + ".tmp"
+        _run([HIPCC, ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
+        os.replace(tmp, LIB)
+        probe.result()
+        os.replace(PROBE + ".tmp", PROBE)
+    if verbose:
+        print(LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,347 @@
+// Partition planner and LDS swizzle chooser.
+//
+// Synthesizing the thread partition follows TVM TIRx docs, "copy -> gmem_smem", Algorithm:
+//  1. slice and canonicalize both layouts (the destination side drives the canonical order of
+//     the joint modes; each phase is then coalesced on its own global side);
+//  2. choose the vector width widest first -- here 16, 8 then 4 bytes -- accepting it when the
+//     contiguous tail divides it and every other stride and both base offsets are multiples of it;
+//  3. split into [outer, threads, vec] with the TileLang default mapping (tutorial
+//     "loop_mapping.py": access_idx = flat // vec, thread = access_idx % threads,
+//     local_idx = (access_idx // threads) * vec + flat % vec).
+// The copy declines ("What it accepts", divisibility) when the element count is not a multiple
+// of the thread count of a wavefront (64 on gfx950): there is no integer [outer, threads, vec]
+// split.  Strict mode reports that; otherwise a guarded element-wise path runs.
+//
+// When the source- and destination-contiguous modes differ, a workgroup stages a tile through
+// LDS.  The swizzle of that tile is chosen as in TVM TIRx docs, "permute_layout", Algorithm
+// step 2: simulate the banks for the write phase and the read phase and keep the smallest XOR
+// bit count k (then the smallest shift and target bit) that leaves both conflict-free.
+#include <algorithm>
+#include <cstdlib>
+
+#include "plan.hpp"
+
+namespace tc {
+
+int elem_bytes_of(int dtype) {
+  switch (dtype) {
+    case TC_U8: case TC_I8: return 1;
+    case TC_F16: case TC_BF16: return 2;
+    case TC_F32: case TC_I32: return 4;
+    case TC_F64: case TC_I64: return 8;
+    case TC_B128: return 16;
+    default: return -1;
+  }
+}
+
+static int ilog2i(int64_t x) {
+  int r = 0;
+  while ((int64_t(1) << r) < x) ++r;
+  return r;
+}
+
+static int64_t pow2ceil(int64_t x) { return int64_t(1) << ilog2i(std::max<int64_t>(1, x)); }
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Step 2 of the page: widest vector whose tail divides it and whose other strides/offsets are
+// multiples of it.  `inner_src`/`inner_dst` are the modes vectorized on each side.
+static int choose_vec(const Joint& j, int eb, int inner_src, int inner_dst, int ptr_align) {
+  for (int vb : {16, 8, 4}) {
+    if (vb < eb || vb % eb || vb > ptr_align) continue;
+    const int64_t ve = vb / eb;
+    bool ok = j.so % ve == 0 && j.dof % ve == 0;
+    ok = ok && j.m[inner_src].e % ve == 0 && j.m[inner_dst].e % ve == 0;
+    for (int k = 0; ok && k < j.rank; ++k) {
+      if (k != inner_src && j.m[k].s % ve) ok = false;
+      if (k != inner_dst && j.m[k].d % ve) ok = false;
+    }
+    if (ok) return vb;
+  }
+  return 0;
+}
+
+static void decline(Plan* p, int flags, const std::string& why) {
+  p->declined = true;
+  if (p->reason.empty()) p->reason = why;
+  if (flags & TC_FLAG_STRICT) p->status = TC_E_DECLINED;
+}
+
+// Tile geometry and swizzle of the transpose path.  Tile extents are powers of two filling
+// kTileBytes; candidates prefer 128-byte destination column segments, then 256 and 64.
+static bool plan_transpose_tile(Plan* p, int flags) {
+  const Joint& j = p->j;
+  const Mode& R = j.m[p->mode_r];
+  const Mode& C = j.m[p->mode_c];
+  const int64_t eB = p->mode_b >= 0 ? j.m[p->mode_b].e : 1;
+  bool have = false;
+  TileGeom best;
+  int64_t best_cost = -1, best_w = 0, best_r = 0;
+  int seen[16][3];
+  int nseen = 0;
+  // Without the swizzle only the first geometry is planned, so that TC_FLAG_NO_SWIZZLE measures
+  // the swizzle on the tile the default plan uses.
+  const bool first_only = flags & TC_FLAG_NO_SWIZZLE;
+  for (int trb : {128, 256, 64}) {
+    if (first_only && have) break;
+    TileGeom g;
+    g.eb = p->eb;
+    g.vb = p->vb;
+    const int ve = p->vb / p->eb;
+    int64_t TR = std::max<int64_t>(trb / p->eb, 1);
+    TR = std::max<int64_t>(std::min<int64_t>(TR, pow2ceil(R.e)), std::max(ve, p->eb < 4 ? 4 / p->eb : 1));
+    int64_t TC = std::max<int64_t>(kTileBytes / (TR * p->eb), 1);
+    TC = std::max<int64_t>(std::min<int64_t>(TC, pow2ceil(C.e)), ve);
+    int64_t NB = kTileBytes / (TR * TC * p->eb);
+    if (NB < 1) continue;
+    g.TR = int(TR);
+    g.TC = int(TC);
+    g.NB = int(NB);
+    bool dup = false;
+    for (int i = 0; i < nseen; ++i)
+      if (seen[i][0] == g.TR && seen[i][1] == g.TC && seen[i][2] == g.NB) dup = true;
+    if (dup) continue;
+    seen[nseen][0] = g.TR; seen[nseen][1] = g.TC; seen[nseen][2] = g.NB; ++nseen;
+    if (!finish_geom(&g)) continue;
+    const int chunk_bits = ilog2i(g.TC / g.CW());
+    const int row_bits = ilog2i(g.TRu());
+    const int kmax = (flags & TC_FLAG_NO_SWIZZLE) ? 0 : chunk_bits;
+    // column terms: none first, then (cshift, cmask) by increasing cshift and mask
+    int col_terms[32][2];
+    int ncol = 0;
+    col_terms[ncol][0] = 0; col_terms[ncol][1] = 0; ++ncol;
+    if (!(flags & TC_FLAG_NO_SWIZZLE))
+      for (int cs = 1; cs < chunk_bits && ncol < 32; ++cs)
+        for (int cm = 1; cm < (1 << cs) && cm <= 7 && ncol < 32; cm = 2 * cm + 1) {
+          col_terms[ncol][0] = cs; col_terms[ncol][1] = cm; ++ncol;
+        }
+    bool found = false;
+    for (int k = 0; k <= kmax && !found; ++k)
+      for (int shift = 0; shift <= (k ? std::max(0, row_bits - 1) : 0) && !found; ++shift)
+        for (int tbit = 0; tbit <= (k ? chunk_bits - k : 0) && !found; ++tbit)
+          for (int ct = 0; ct < ncol && !found; ++ct) {
+            TileGeom c = g;
+            c.k = k;
+            c.shift = shift;
+            c.tbit = tbit;
+            c.cshift = col_terms[ct][0];
+            c.cmask = col_terms[ct][1];
+            if (!finish_geom(&c)) continue;
+            int64_t wc, rc;
+            simulate_tile(c, &wc, &rc);
+            const int64_t cost = wc + rc;
+            if (best_cost < 0 || cost < best_cost) {
+              best_cost = cost;
+              best = c;
+              best_w = wc;
+              best_r = rc;
+              have = true;
+            }
+            if (cost == 0) found = true;
+          }
+    if (found) break;
+  }
+  (void)eB;
+  if (!have) return false;
+  p->g = best;
+  p->wconf = best_w;
+  p->rconf = best_r;
+  if (best_cost > 0)
+    decline(p, flags, "no XOR swizzle leaves both LDS phases conflict-free (best: " + std::to_string(best_w) +
+                          " write + " + std::to_string(best_r) + " read extra cycles per tile)");
+  return true;
+}
+
+Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags, int ptr_align) {
+  Plan p;
+  std::string err;
+  if (ptr_align <= 0) ptr_align = 16;
+  p.eb = elem_bytes_of(dtype);
+  if (p.eb < 0) {
+    p.status = TC_E_DTYPE;
+    p.reason = "unknown dtype " + std::to_string(dtype);
+    return p;
+  }
+  if (flags & ~TC_FLAG_ALL) {
+    p.status = TC_E_ARG;
+    p.reason = "unknown flag bits";
+    return p;
+  }
+  int st = make_joint(src, dst, &p.j, &err);
+  if (st != TC_OK) {
+    p.status = st;
+    p.reason = err;
+    return p;
+  }
+  if (p.j.count == 0) {
+    p.path = TC_PATH_EMPTY;
+    return p;
+  }
+  canonicalize(&p.j);
+  const int inj = dst_injective(p.j);
+  if (inj != 1) {
+    p.status = TC_E_NONINJECTIVE;
+    p.reason = inj == 0 ? "destination layout maps two logical indices to one element"
+                        : "destination layout could not be shown injective";
+    return p;
+  }
+  Joint& j = p.j;
+  // modes contiguous on each side
+  int r = -1, c = -1;
+  for (int k = 0; k < j.rank; ++k) {
+    if (j.m[k].d == 1 && r < 0) r = k;
+    if (j.m[k].s == 1 && c < 0) c = k;
+  }
+  const bool forced_guarded = flags & TC_FLAG_FORCE_GUARDED;
+  if (j.count % kWave != 0)
+    decline(&p, flags, "element count " + std::to_string(j.count) + " is not divisible by the thread count " +
+                           std::to_string(kWave) + ": the [outer, threads, vec] split has no integer solution");
+  if (p.status != TC_OK) return p;
+
+  bool fast = !p.declined && !forced_guarded && j.rank >= 1;
+  if (fast && (r < 0 || c < 0)) {
+    decline(&p, flags, std::string("no unit-stride mode on the ") + (r < 0 ? "destination" : "source") +
+                           " side: no vector of 4 bytes or more is contiguous there");
+    fast = false;
+  }
+  if (fast) {
+    p.vb = choose_vec(j, p.eb, c, r, ptr_align);
+    if (p.vb == 0) {
+      decline(&p, flags, "no vector of 16, 8 or 4 bytes is contiguous and aligned on both sides");
+      fast = false;
+    }
+  }
+  if (p.status != TC_OK) return p;
+
+  if (fast && r == c) {
+    // Both sides contiguous along one mode: no cross-lane exchange needed.
+    const bool small = j.count * p.eb <= kTileBytes;
+    const bool lds = (flags & TC_FLAG_FORCE_LDS) || (small && !(flags & TC_FLAG_FORCE_REGS));
+    p.path = lds ? TC_PATH_ROUNDTRIP : TC_PATH_ROWS;
+    p.threads = lds ? kWave : kTileThreads;
+    const int64_t nvec = j.count / (p.vb / p.eb);
+    const int64_t per_wg = int64_t(p.threads) * kRowRounds;
+    p.workgroups = ceil_div(nvec, per_wg);
+    p.load_outer = p.store_outer = int(std::min<int64_t>(kRowRounds, ceil_div(nvec, p.threads)));
+    p.lds_bytes = lds ? int(per_wg * p.vb) : 0;
+    if (nvec >= (int64_t(1) << 31)) {
+      p.status = TC_E_RANGE;
+      p.reason = "more than 2^31 vectors";
+    }
+    return p;
+  }
+  if (fast) {
+    p.path = TC_PATH_TRANSPOSE;
+    p.mode_r = r;
+    p.mode_c = c;
+    // batch mode folded into the tile: the remaining mode with the smallest strides
+    int b = -1;
+    for (int k = 0; k < j.rank; ++k) {
+      if (k == r || k == c) continue;
+      if (b < 0 || std::llabs(j.m[k].s) + std::llabs(j.m[k].d) < std::llabs(j.m[b].s) + std::llabs(j.m[b].d)) b = k;
+    }
+    p.mode_b = b;
+    if (!plan_transpose_tile(&p, flags)) {
+      p.path = TC_PATH_EMPTY;
+      p.status = TC_E_ARG;
+      p.reason = "internal: no tile geometry";
+      return p;
+    }
+    if (p.status != TC_OK) return p;
+    p.threads = p.g.NT;
+    p.load_outer = p.g.loads;
+    p.store_outer = p.g.stores;
+    p.lds_bytes = kTileBytes;
+    const int64_t eB = b >= 0 ? j.m[b].e : 1;
+    p.workgroups = ceil_div(j.m[r].e, p.g.TR) * ceil_div(j.m[c].e, p.g.TC) * ceil_div(eB, p.g.NB);
+    for (int k = 0; k < j.rank; ++k)
+      if (k != r && k != c && k != b) p.workgroups *= j.m[k].e;
+    if (p.workgroups >= (int64_t(1) << 31)) {
+      p.status = TC_E_RANGE;
+      p.reason = "more than 2^31 workgroups";
+    }
+    return p;
+  }
+
+  // Guarded fallback: an LDS tile over the two modes with the smallest strides on each side
+  // (element-wide accesses), or an element-wise copy in destination order.
+  p.vb = p.eb;
+  int gr = -1, gc = -1;
+  for (int k = 0; k < j.rank; ++k)
+    if (j.m[k].d != 0 && (gr < 0 || std::llabs(j.m[k].d) < std::llabs(j.m[gr].d))) gr = k;
+  for (int k = 0; k < j.rank; ++k)
+    if (k != gr && (gc < 0 || std::llabs(j.m[k].s) < std::llabs(j.m[gc].s))) gc = k;
+  const bool tile = gr >= 0 && gc >= 0 && std::llabs(j.m[gc].s) < std::llabs(j.m[gr].s);
+  if (tile) {
+    p.path = TC_PATH_GUARDED_TILE;
+    p.mode_r = gr;
+    p.mode_c = gc;
+    p.g = TileGeom();
+    p.g.eb = p.eb;
+    p.g.vb = p.eb;
+    p.g.TR = p.eb <= 4 ? 64 : 32;
+    p.g.TC = p.eb <= 4 ? 64 : (p.eb == 8 ? 64 : 32);
+    p.g.NB = 1;
+    p.threads = kTileThreads;
+    p.load_outer = p.store_outer = p.g.TR * p.g.TC / kTileThreads;
+    const int pad = std::max(1, 4 / p.eb);
+    p.lds_bytes = p.g.TR * (p.g.TC + pad) * p.eb;
+    p.workgroups = ceil_div(j.m[gr].e, p.g.TR) * ceil_div(j.m[gc].e, p.g.TC);
+    for (int k = 0; k < j.rank; ++k)
+      if (k != gr && k != gc) p.workgroups *= j.m[k].e;
+    if (p.workgroups >= (int64_t(1) << 31)) { p.status = TC_E_RANGE; p.reason = "more than 2^31 workgroups"; }
+  } else {
+    p.path = TC_PATH_GUARDED_ROWS;
+    p.threads = kTileThreads;
+    p.load_outer = p.store_outer = kRowRounds;
+    p.workgroups = ceil_div(j.count, int64_t(kTileThreads) * kRowRounds);
+    if (j.count >= (int64_t(1) << 31)) { p.status = TC_E_RANGE; p.reason = "more than 2^31 elements on the guarded path"; }
+  }
+  return p;
+}
+
+void plan_to_info(const Plan& p, tc_plan_info* info) {
+  *info = tc_plan_info{};
+  info->path = p.path;
+  info->elem_bytes = p.eb;
+  info->count = p.j.count;
+  info->rank = p.j.rank;
+  info->declined = p.declined ? 1 : 0;
+  for (int k = 0; k < p.j.rank; ++k) {
+    info->extent[k] = p.j.m[k].e;
+    info->src_stride[k] = p.j.m[k].s;
+    info->dst_stride[k] = p.j.m[k].d;
+  }
+  info->src_offset = p.j.so;
+  info->dst_offset = p.j.dof;
+  info->threads = p.threads;
+  info->vec_bytes = p.vb;
+  info->load_outer = p.load_outer;
+  info->store_outer = p.store_outer;
+  info->mode_r = p.mode_r;
+  info->mode_c = p.mode_c;
+  info->mode_b = p.mode_b;
+  const bool tiled = p.path == TC_PATH_TRANSPOSE || p.path == TC_PATH_GUARDED_TILE;
+  info->tile_r = tiled ? p.g.TR : 0;
+  info->tile_c = tiled ? p.g.TC : 0;
+  info->tile_b = tiled ? p.g.NB : 0;
+  info->workgroups = p.workgroups;
+  info->lds_bytes = p.lds_bytes;
+  if (p.path == TC_PATH_TRANSPOSE) {
+    info->xor_k = p.g.k;
+    info->xor_shift = p.g.shift;
+    info->xor_mask = (1 << p.g.k) - 1;
+    info->xor_tbit = p.g.tbit;
+    info->xor_cshift = p.g.cshift;
+    info->xor_cmask = p.g.cmask;
+    info->lds_write_bytes = p.g.ww;
+    info->lds_read_bytes = p.g.rw;
+    info->write_conflicts = p.wconf;
+    info->read_conflicts = p.rconf;
+  }
+  const size_t n = std::min(p.reason.size(), sizeof(info->reason) - 1);
+  p.reason.copy(info->reason, n);
+  info->reason[n] = 0;
+}
+
+}  // namespace tc

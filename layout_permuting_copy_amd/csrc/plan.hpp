@@ -1,0 +1,138 @@
+// Internal host-side types of the tile-copy library: layout algebra, partition
+// planner, LDS swizzle chooser, and the argument blocks the kernels take.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "tile_copy.h"
+
+namespace tc {
+
+constexpr int kMaxRank = TC_MAX_RANK;
+constexpr int kWave = 64;          // gfx950 wavefront
+constexpr int kTileThreads = 256;  // threads per workgroup on the tiled paths
+constexpr int kTileBytes = 16384;  // LDS tile per workgroup on the tiled paths
+constexpr int kRowRounds = 4;      // vectors per thread on the register-staged path
+
+// One joint mode: extent, source stride, destination stride (elements).
+struct Mode {
+  int64_t e, s, d;
+};
+
+// Both layouts over the common logical shape, after extent-1 modes are dropped.
+struct Joint {
+  int rank = 0;
+  Mode m[kMaxRank];
+  int64_t so = 0, dof = 0;  // element offsets
+  int64_t count = 1;
+};
+
+// ---- layout algebra (layout.cpp) -------------------------------------------------------------
+int make_joint(const tc_layout& src, const tc_layout& dst, Joint* out, std::string* err);
+// Sort by destination stride (descending |d|, stable) and merge adjacent modes that are
+// contiguous on both sides.
+void canonicalize(Joint* j);
+// 1 injective, 0 not, -1 undecided (too large to check by enumeration)
+int dst_injective(const Joint& j);
+// [lo, hi) element range a layout side touches (for the alias check)
+void side_range(const Joint& j, bool src_side, int64_t* lo, int64_t* hi);
+int slice_layout(const tc_layout& in, const int64_t* start, const int64_t* stop, const int64_t* step,
+                 tc_layout* out, std::string* err);
+
+// ---- LDS bank model (bank.cpp) ----------------------------------------------------------------
+// gfx950 LDS geometry per access: number of 4-byte banks and lanes served together.
+struct BankGeom {
+  int banks, group;
+};
+BankGeom gfx950_bank_geom(bool write, int width_bytes);
+// Extra cycles one LDS instruction costs: byte_addr[l] for lanes with active[l].
+int64_t lds_conflict_cycles(const int64_t* byte_addr, const bool* active, int lanes, int width_bytes,
+                            bool write);
+
+// ---- transpose tile geometry -------------------------------------------------------------------
+// The LDS tile is NB x TRu x TC units of U bytes.  For elements narrower than 4 bytes a unit is a
+// 4-byte column of B = 4/eb consecutive rows (made in registers by a BxB micro-transpose);
+// otherwise a unit is one element (B = 1).  The tile's column chunks of CW units (one LDS write
+// instruction) are XOR-swizzled by row:  chunk' = chunk ^ (((ru >> shift) & mask) << tbit).
+struct TileGeom {
+  int eb = 4, vb = 16;  // element bytes, global vector bytes
+  int U = 4, B = 1;     // LDS unit bytes, rows per unit
+  int VE = 4;           // elements per global vector
+  int TR = 32, TC = 128, NB = 1;  // tile extents: rows (dst-contiguous mode), cols (src-contiguous mode), batch
+  int NT = kTileThreads;
+  int loads = 4, stores = 4;  // accesses per thread per phase
+  int ww = 16, rw = 4;        // LDS write / read instruction bytes
+  int k = 0, shift = 0, tbit = 0;
+  int cshift = 0, cmask = 0;
+  int CW() const { return ww / U; }  // units per write chunk
+  int TRu() const { return TR / B; }
+  int RPV() const { return vb / U; }  // LDS unit reads per store vector
+  int64_t unit_addr(int nb, int ru, int c) const {
+    const int cw = CW();
+    const int ch = c / cw;
+    const int chs = ch ^ (((ru >> shift) & ((1 << k) - 1)) << tbit) ^ ((ch >> cshift) & cmask);
+    return (int64_t(nb) * TRu() + ru) * TC + int64_t(chs) * cw + (c % cw);
+  }
+};
+// Fill loads/stores/ww/rw/U/B/VE from eb, vb, TR, TC, NB.  False if the geometry is invalid.
+bool finish_geom(TileGeom* g);
+// Simulated extra LDS cycles of one interior tile: write phase and read phase.
+void simulate_tile(const TileGeom& g, int64_t* write_cycles, int64_t* read_cycles);
+
+// ---- plan -------------------------------------------------------------------------------------
+struct Plan {
+  int status = TC_OK;
+  int path = TC_PATH_EMPTY;
+  int eb = 4;
+  Joint j;
+  int vb = 0;                       // global vector bytes
+  int mode_r = -1, mode_c = -1, mode_b = -1;
+  TileGeom g;
+  int threads = 0, load_outer = 0, store_outer = 0;
+  int64_t workgroups = 0;
+  int lds_bytes = 0;
+  int64_t wconf = 0, rconf = 0;
+  bool declined = false;
+  std::string reason;
+};
+
+int elem_bytes_of(int dtype);
+// Plans a copy.  ptr_align: byte alignment of both base pointers (power of two, <= 16).
+Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags, int ptr_align);
+void plan_to_info(const Plan& p, tc_plan_info* info);
+
+// ---- kernel argument blocks (passed by value) ------------------------------------------------
+struct TransposeArgs {
+  const unsigned char* src;
+  unsigned char* dst;
+  int64_t src_off, dst_off;  // elements
+  int64_t eR, eC, eB;        // extents of the tile modes (eB = 1 without a batch mode)
+  int64_t sR, sC, sB;        // source strides of R, C, B
+  int64_t dR, dC, dB;        // destination strides of R, C, B
+  int64_t tilesR, tilesC, tilesB;
+  int32_t nbatch;            // further modes walked by the grid, innermost last
+  int32_t pad0;
+  int64_t bext[kMaxRank], bs[kMaxRank], bd[kMaxRank];
+  int32_t lTR, lTC, lNB;     // log2 of the tile extents
+  int32_t xshift, xmask, xtbit;
+  int32_t xcshift, xcmask;
+};
+
+struct RowArgs {
+  const unsigned char* src;
+  unsigned char* dst;
+  int64_t src_off, dst_off;  // elements
+  int32_t rank;              // modes of the vector grid, innermost last
+  int32_t pad0;
+  uint32_t ext[kMaxRank];    // extents; the innermost counts vectors
+  uint32_t mul[kMaxRank];    // fast division: q = (umulhi(n, mul) + n) >> shr
+  uint32_t shr[kMaxRank];
+  int64_t s[kMaxRank], d[kMaxRank];  // element strides per step of each grid mode
+  int64_t nvec;              // vectors in the whole copy
+};
+
+// ---- launch (kernels.hip) ------------------------------------------------------------------------
+int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::string* err);
+
+}  // namespace tc

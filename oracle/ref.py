@@ -445,3 +445,106 @@ def permute_layout_py(src: np.ndarray, src_lay: Layout, dst: np.ndarray, dst_lay
             _, do = permute_access(extent, ss, ds, lanes, k, shift, r, lane)
             do += db
             dst[do * elem_bytes:(do + 1) * elem_bytes] = regs[(lane, r)]
+
+
+# ----------------------------------------------------------------------------------------------
+# LDS tile of the global -> LDS -> global transpose on gfx950 (the library's kernel design; the
+# pages fix the method -- the [outer, threads, vec] partition of each phase and the smallest-k XOR
+# search over both phases -- but not this tile, so it is pinned by brute force, the measured bank
+# model and the hardware conflict counter, not by printed values).
+#
+# The tile holds NB x TR x TC elements (TR along the destination-contiguous mode, TC along the
+# source-contiguous mode).  In LDS it is a grid of units of U = max(eb, 4) bytes: for eb < 4 a
+# unit is one column of B = 4/eb consecutive rows, otherwise one element.  Unit (nb, ru, c) is
+# stored at byte ((nb*TRu + ru)*TC + chunk'*CW + c % CW) * U, where CW units form one LDS write
+# (WW = min(16, VE*U) bytes), chunk = c // CW and
+#     chunk' = chunk ^ (((ru >> shift) & (2^k - 1)) << tbit) ^ ((chunk >> cshift) & cmask).
+# Load phase: the TileLang partition of the unit grid (NB, TRu, TC) in source order, vector VE
+# units, NT threads; each write instruction stores CW consecutive units of a thread's vector.
+# Store phase: the TileLang partition of the unit grid (NB, TC, TRu) in destination order, vector
+# RPV = vb / U units; each read instruction loads one unit.
+# ----------------------------------------------------------------------------------------------
+
+def _tile_units(eb, vb, TR, TC, NB):
+    U = max(eb, 4)
+    B = 4 // eb if eb < 4 else 1
+    VE = vb // eb
+    WW = min(16, VE * U)
+    return U, B, VE, WW // U, vb // U, TR // B, WW
+
+
+def _tile_instructions(eb, vb, TR, TC, NB, NT):
+    """[(op, width, {thread: (nb, ru, c)})] for every LDS instruction of the tile, from the
+    TileLang partitions of both phases."""
+    U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB)
+    insts = {}
+    for (nb, ru, c), (t, slot) in loop_partition((NB, TRu, TC), NT, VE).items():
+        if slot % CW == 0:  # first unit of a write instruction
+            insts.setdefault(("write", slot // CW), {})[t] = (nb, ru, c)
+    for (nb, c, ru), (t, slot) in loop_partition((NB, TC, TRu), NT, RPV).items():
+        insts.setdefault(("read", slot), {})[t] = (nb, ru, c)
+    out = []
+    for (op, _), lanes in sorted(insts.items()):
+        out.append((op, WW if op == "write" else U, lanes))
+    return out
+
+
+_TILE_CACHE = {}
+
+
+def lds_tile_conflicts(eb, vb, TR, TC, NB, NT=256, k=0, shift=0, tbit=0, cshift=0, cmask=0,
+                       model=None, stop_at_first=False):
+    """(write-phase, read-phase) extra LDS cycles of one tile under the gfx950 model."""
+    model = model or gfx950_model()
+    key = (eb, vb, TR, TC, NB, NT)
+    if key not in _TILE_CACHE:
+        _TILE_CACHE[key] = _tile_instructions(eb, vb, TR, TC, NB, NT)
+    U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB)
+    mask = (1 << k) - 1
+
+    def addr(nb, ru, c):
+        ch = c // CW
+        chs = ch ^ (((ru >> shift) & mask) << tbit) ^ ((ch >> cshift) & cmask)
+        return ((nb * TRu + ru) * TC + chs * CW + c % CW) * U
+
+    wc = rc = 0
+    for op, width, lanes in _TILE_CACHE[key]:
+        for w0 in range(0, NT, model.lanes):
+            wave = [lanes.get(t) for t in range(w0, w0 + model.lanes)]
+            if all(x is None for x in wave):
+                continue
+            addrs = [addr(*x) if x is not None else 0 for x in wave]
+            cyc = conflict_cycles(addrs, width, op, model, active=[x is not None for x in wave])
+            if op == "write":
+                wc += cyc
+            else:
+                rc += cyc
+            if stop_at_first and cyc:
+                return wc, rc
+    return wc, rc
+
+
+def lds_tile_swizzle(eb, vb, TR, TC, NB, NT=256, model=None):
+    """Smallest-k XOR swizzle of the tile that leaves both phases conflict-free (the permute
+    page's search, Algorithm step 2, on the tile above).  Candidates in order: k ascending, then
+    shift, then tbit, then the column term -- none, then (cshift, cmask) by increasing cshift and
+    cmask in (1, 3, 7).  Returns a dict, or None when no candidate is conflict-free."""
+    U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB)
+    chunks = TC // CW
+    chunk_bits = chunks.bit_length() - 1
+    row_bits = TRu.bit_length() - 1
+    cols = [(0, 0)] + [(cs, cm) for cs in range(1, chunk_bits) for cm in (1, 3, 7) if cm < (1 << cs)]
+    for k in range(0, chunk_bits + 1):
+        for shift in (range(0, max(0, row_bits - 1) + 1) if k else [0]):
+            for tbit in (range(0, chunk_bits - k + 1) if k else [0]):
+                if k and (1 << (k + tbit)) > chunks:
+                    continue
+                for cs, cm in cols:
+                    if cm and (1 << cs) >= chunks:
+                        continue
+                    w, r = lds_tile_conflicts(eb, vb, TR, TC, NB, NT, k, shift, tbit, cs, cm, model,
+                                              stop_at_first=True)
+                    if w == 0 and r == 0:
+                        return {"k": k, "shift": shift, "tbit": tbit, "cshift": cs, "cmask": cm,
+                                "mask": (1 << k) - 1}
+    return None

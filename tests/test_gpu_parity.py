@@ -1,0 +1,230 @@
+"""Bit-exact parity of the HIP path (through the C ABI) with the oracle, on seeded inputs.
+Every destination is prefilled with a sentinel, so writes outside the destination image fail
+the comparison too."""
+
+import itertools
+
+import numpy as np
+import pytest
+
+import layout_permuting_copy_amd as L
+import synth_inputs as SI
+from gpu_util import assert_same, check_workload, dtype_code, oracle_copy, run_copy, say
+
+pytestmark = pytest.mark.gpu
+
+DT_BY_EB = {1: "int8", 2: "bfloat16", 4: "float32", 8: "float64", 16: "int4vec"}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _bits(n_bytes, seed):
+    return np.frombuffer(np.random.default_rng(seed).bytes(n_bytes), dtype=np.uint8).copy()
+
+
+def _check(shape, s_stride, d_stride, eb, s_off=0, d_off=0, src_elems=None, dst_elems=None, flags=0, seed=0,
+           expect=None):
+    sl = (shape, s_stride, s_off)
+    dl = (shape, d_stride, d_off)
+
+    def span(st, off):
+        if any(e == 0 for e in shape):
+            return off + 1
+        return off + sum((e - 1) * s for e, s in zip(shape, st) if s > 0) + 1
+
+    n_src = src_elems or span(s_stride, s_off)
+    n_dst = dst_elems or span(d_stride, d_off)
+    src = _bits(n_src * eb, seed)
+    say(f"[gpu] shape={shape} src={s_stride}+{s_off} dst={d_stride}+{d_off} eb={eb} flags={flags}")
+    got, plan = run_copy(src, sl, n_dst, dl, eb, dtype_code(DT_BY_EB[eb]), flags)
+    want = oracle_copy(src, sl, n_dst, dl, eb)
+    assert_same(got, want, eb, f"{shape}/{eb}")
+    if expect is not None:
+        assert plan["path_name"] == expect, plan
+    return plan
+
+
+# --- the five workloads -----------------------------------------------------------------------
+
+def test_cfg1_tile32_roundtrip_one_wave():
+    plan = check_workload(SI.tile32_roundtrip(), expect_path="roundtrip")
+    assert (plan["threads"], plan["load_outer"], plan["vec_bytes"], plan["workgroups"]) == (64, 4, 16, 1)
+
+
+def test_cfg2_sf_transpose_full():
+    plan = check_workload(SI.sf_transpose(), expect_path="transpose")
+    assert plan["write_conflicts"] == 0 and plan["read_conflicts"] == 0
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+def test_cfg3_transpose_16384(dtype):
+    plan = check_workload(SI.transpose2d(dtype=dtype), expect_path="transpose")
+    assert plan["write_conflicts"] == 0 and plan["read_conflicts"] == 0
+
+
+def test_cfg4_permute0213_full():
+    check_workload(SI.permute0213(), expect_path="rows")
+
+
+@pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
+def test_cfg5_dense_8192(dtype):
+    check_workload(SI.sweep_dense(dtype), expect_path="transpose")
+
+
+@pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
+def test_cfg5_slice_8192(dtype):
+    plan = check_workload(SI.sweep_slice(dtype))
+    assert plan["declined"] == 1 and plan["path_name"].startswith("guarded")
+
+
+@pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
+def test_cfg5_odd_8191x8190(dtype):
+    plan = check_workload(SI.sweep_odd(dtype))
+    assert plan["declined"] == 1 and plan["path_name"].startswith("guarded")
+
+
+def test_cfg5_odd_strict_declines():
+    import torch
+    w = SI.sweep_odd("float32", 191, 190)
+    src = torch.zeros(191 * 190, dtype=torch.float32, device="cuda")
+    dst = torch.zeros_like(src)
+    with pytest.raises(L.TileCopyError) as e:
+        L.tile_copy_ex(src, (w.src.shape, w.src.stride), dst, (w.dst.shape, w.dst.stride), L.TC_F32,
+                       flags=L.TC_FLAG_STRICT)
+    assert e.value.code == L.TC_E_DECLINED and "not divisible" in e.value.reason
+
+
+# --- several tiles, ragged tails, every element width ----------------------------------------
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("n,m", [(64, 64), (96, 272), (272, 48), (16, 1040), (1024, 16), (528, 400)])
+def test_transpose_small_ragged(eb, n, m):
+    _check((n, m), (m, 1), (1, n), eb, seed=n * 7 + m + eb, expect="transpose")
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("n", [72, 68, 66, 65])
+def test_transpose_vector_widths(eb, n):
+    """n x 64 tiles: the row extent admits 16-, 8- or 4-byte vectors only, or none."""
+    plan = _check((n, 64), (64, 1), (1, n), eb, seed=n + eb)
+    if plan["path_name"] == "transpose":
+        ve = plan["vec_bytes"] // eb
+        assert n % ve == 0 and all(n % (v // eb) for v in (16, 8) if v > plan["vec_bytes"] and v >= eb)
+    else:
+        assert plan["path_name"] == "guarded_tile"
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+def test_transpose_with_offsets_and_pitches(eb):
+    # source rows of pitch 80 starting at element 16, destination columns of pitch 40 at 8
+    _check((32, 64), (80, 1), (1, 40), eb, s_off=16, d_off=8, src_elems=80 * 33, dst_elems=40 * 65,
+           seed=eb)
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+def test_sf_tiles_small(eb):
+    w = SI.sf_transpose(tiles=37)
+    _check(w.src.shape, w.src.stride, w.dst.stride, eb, seed=37 + eb)
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+def test_permute0213_small(eb):
+    w = SI.permute0213(b=3, h=5, s=24, d=16)
+    _check(w.src.shape, w.src.stride, w.dst.stride, eb, seed=5 + eb)
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+def test_identity_rows_and_roundtrip(eb):
+    _check((8, 256), (256, 1), (256, 1), eb, seed=eb, expect="roundtrip" if 8 * 256 * eb <= 16384 else "rows")
+    _check((300, 512), (512, 1), (512, 1), eb, seed=eb + 1, expect="rows")
+    _check((300, 512), (512, 1), (512, 1), eb, seed=eb + 2, flags=L.TC_FLAG_FORCE_LDS, expect="roundtrip")
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+def test_guarded_paths(eb):
+    _check((67, 45), (45, 1), (1, 67), eb, seed=eb)                       # odd: guarded tile
+    _check((40, 30), (60, 2), (1, 40), eb, src_elems=60 * 40, seed=eb)   # strided source
+    _check((7, 9), (9, 1), (9, 1), eb, seed=eb)                           # 63 elements: guarded rows
+    _check((64, 64), (64, 1), (1, 64), eb, flags=L.TC_FLAG_FORCE_GUARDED, seed=eb, expect="guarded_tile")
+
+
+def test_no_swizzle_flag_same_result():
+    plan = _check((256, 256), (256, 1), (1, 256), 4, flags=L.TC_FLAG_NO_SWIZZLE, seed=3)
+    assert plan["xor_k"] == 0 and plan["xor_cmask"] == 0
+
+
+def test_edge_cases():
+    import torch
+    # empty copies launch nothing and touch nothing
+    _check((0, 5), (5, 1), (1, 0), 4, src_elems=1, dst_elems=4, expect="empty")
+    # one element (rank 0 and a 1x1 tile)
+    _check((), (), (), 4, src_elems=1, dst_elems=1)
+    _check((1, 1), (1, 1), (1, 1), 8, src_elems=1, dst_elems=1)
+    # negative source stride (row-flipped view) and a broadcast source (stride 0)
+    _check((64, 32), (-32, 1), (1, 64), 4, s_off=63 * 32, src_elems=64 * 32, seed=9)
+    _check((64, 32), (0, 1), (32, 1), 2, src_elems=32, seed=10)
+    # maximum rank, permuted
+    shape = (2, 3, 2, 4, 2, 3, 2, 4)
+    st = np.cumprod((1,) + shape[:0:-1])[::-1]
+    perm = (7, 0, 3, 1, 6, 2, 5, 4)
+    dst_st = [0] * 8
+    acc = 1
+    for k in reversed(perm):
+        dst_st[k] = acc
+        acc *= shape[k]
+    _check(shape, tuple(int(x) for x in st), tuple(dst_st), 4, seed=11)
+    # errors: non-injective destination and overlapping buffers
+    t = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    u = torch.zeros(1024, dtype=torch.float32, device="cuda")
+    with pytest.raises(L.TileCopyError) as e:
+        L.tile_copy(t, ((32, 32), (32, 1)), u, ((32, 32), (1, 1)), L.TC_F32)
+    assert e.value.code == L.TC_E_NONINJECTIVE
+    with pytest.raises(L.TileCopyError) as e:
+        L.tile_copy(t, ((32, 32), (32, 1)), t.data_ptr() + 64, ((32, 32), (1, 32)), L.TC_F32)
+    assert e.value.code == L.TC_E_ALIAS
+
+
+def test_random_layouts():
+    rng = np.random.default_rng(1234)
+    for case in range(60):
+        rank = int(rng.integers(1, 6))
+        shape = tuple(int(x) for x in rng.integers(1, 9, size=rank) * rng.choice([1, 2, 4], size=rank))
+        eb = int(rng.choice([1, 2, 4, 8, 16]))
+        # source: a permuted row-major buffer, optionally sliced with steps
+        perm_s = rng.permutation(rank)
+        perm_d = rng.permutation(rank)
+        steps = rng.choice([1, 1, 1, 2], size=rank)
+        full = [shape[k] * steps[k] for k in range(rank)]
+        st_full = [0] * rank
+        acc = 1
+        for k in reversed(perm_s):
+            st_full[k] = acc
+            acc *= full[k]
+        s_stride = tuple(int(st_full[k] * steps[k]) for k in range(rank))
+        d_stride = [0] * rank
+        acc = 1
+        for k in reversed(perm_d):
+            d_stride[k] = acc
+            acc *= shape[k]
+        _check(shape, s_stride, tuple(d_stride), eb, src_elems=acc * int(np.prod(steps)) + 1, seed=case)
+
+
+def test_stream_ordering_on_side_stream():
+    import torch
+    s = torch.cuda.Stream()
+    src_h = _bits(512 * 512 * 4, 77)
+    src = torch.from_numpy(src_h).cuda()
+    dst = torch.full_like(src, 0xA5)
+    with torch.cuda.stream(s):
+        L.tile_copy(src, ((512, 512), (512, 1)), dst, ((512, 512), (1, 512)), L.TC_F32, stream=s)
+    s.synchronize()
+    want = oracle_copy(src_h, ((512, 512), (512, 1), 0), 512 * 512, ((512, 512), (1, 512), 0), 4)
+    assert_same(dst.cpu().numpy(), want, 4, "side stream")

@@ -1,0 +1,208 @@
+"""Host-side tests of the library (no GPU): the C ABI loads and exports what the header declares,
+the layout algebra and planner decide as the pages prescribe, and the planner's partition and
+LDS swizzle agree with the oracle's independent re-derivation."""
+
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import layout_permuting_copy_amd as L
+import synth_inputs as SI
+from conftest import ROOT
+
+
+def _plan(w, flags=0, align=16):
+    return L.tc_plan((w.src.shape, w.src.stride, w.src.offset), (w.dst.shape, w.dst.stride, w.dst.offset),
+                     L.DTYPE_BY_NAME[w.dtype], flags=flags, ptr_align=align, raise_on_error=False)
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "tile_copy.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|const char\*)\s+(\w+)\s*\(", header, re.M))
+    assert {"tile_copy", "tile_copy_ex", "tc_plan", "tc_last_error", "tc_set_flags", "tc_get_flags",
+            "tc_layout_slice", "tc_version"} <= declared
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert declared <= exported, declared - exported
+    lib = L.load_library()
+    for name in declared:
+        assert hasattr(lib, name)
+    assert L.tc_version() >= 100
+
+
+def test_abi_struct_sizes_match_header():
+    """Compile a tiny C program against the header and compare struct layouts with ctypes."""
+    import ctypes
+    import tempfile
+    src = ('#include <stdio.h>\n#include <stddef.h>\n#include "tile_copy.h"\n'
+           'int main(){printf("%zu %zu %zu %zu\\n", sizeof(tc_layout), sizeof(tc_plan_info),'
+           ' offsetof(tc_plan_info, reason), offsetof(tc_plan_info, xor_cmask));return 0;}\n')
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "s.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "s")
+        subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe])
+        sizes = [int(x) for x in subprocess.check_output([exe]).split()]
+    assert sizes == [ctypes.sizeof(L.TcLayout), ctypes.sizeof(L.TcPlanInfo), L.TcPlanInfo.reason.offset,
+                     L.TcPlanInfo.xor_cmask.offset]
+
+
+def test_workload_paths_and_declines():
+    expect = {"tile32x32_f32_roundtrip": "roundtrip", "sf_transpose": "transpose", "transpose_16384": "transpose",
+              "permute0213": "rows", "transpose_8192x8192": "transpose", "slice_": "guarded_tile",
+              "transpose_8191x8190": "guarded_tile"}
+    for w in SI.all_workloads():
+        p = _plan(w)
+        assert p["status"] == 0, (w.name, p["error"])
+        key = next(k for k in expect if w.name.startswith(k))
+        assert p["path_name"] == expect[key], (w.name, p["path_name"])
+        if p["path_name"] == "transpose":
+            assert p["write_conflicts"] == 0 and p["read_conflicts"] == 0, w.name
+        declined = w.name.startswith(("slice_", "transpose_8191x8190"))
+        assert p["declined"] == int(declined), w.name
+        if declined:
+            assert "not divisible by the thread count 64" in p["reason"]
+            s = _plan(w, flags=L.TC_FLAG_STRICT)
+            assert s["status"] == L.TC_E_DECLINED and "no integer solution" in s["error"]
+
+
+def test_canonical_modes_of_the_workloads():
+    p = _plan(SI.sf_transpose())
+    # (65536, 2) merge into one batch mode of stride 128 on both sides; the 4x32 block stays
+    assert p["extent"] == (131072, 32, 4)
+    assert p["src_stride"] == (128, 1, 32) and p["dst_stride"] == (128, 4, 1)
+    p = _plan(SI.permute0213())
+    assert p["extent"] == (32, 2048, 32, 128) and p["dst_stride"] == (8388608, 4096, 128, 1)
+    p = _plan(SI.tile32_roundtrip())
+    assert p["extent"] == (1024,) and p["src_stride"] == (1,)
+
+
+def test_roundtrip_partition_matches_oracle_gmem_smem():
+    """The 32x32 fp32 round trip on one wave64: the oracle's [outer, threads, vec] split of the
+    same copy (global side = source, shared side = an identical LDS tile) gives the plan."""
+    from oracle import ref as R
+    w = SI.tile32_roundtrip()
+    p = _plan(w)
+    o = R.gmem_smem_partition(R.layout(w.src.shape, w.src.stride), R.layout((32, 32)), 64, 4)
+    assert (p["threads"], p["load_outer"], p["vec_bytes"]) == (o["threads"], o["outer"], o["copy_bytes"])
+    assert o["g_lin"][1][:3] == [256, 260, 264]  # f*256 + tid*4 on a wave64
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+def test_vector_width_rule(eb):
+    dt = {1: L.TC_I8, 2: L.TC_BF16, 4: L.TC_F32, 8: L.TC_F64, 16: L.TC_B128}[eb]
+    for n in (72, 68, 66, 65, 64):
+        p = L.tc_plan(((n, 64), (64, 1)), ((n, 64), (1, n)), dt, raise_on_error=False)
+        widths = [v for v in (16, 8, 4) if v >= eb and n % (v // eb) == 0 and 64 % (v // eb) == 0]
+        if widths:
+            assert p["path_name"] == "transpose" and p["vec_bytes"] == widths[0], (eb, n, p["vec_bytes"])
+        else:
+            assert p["path_name"] == "guarded_tile" and "no vector" in p["reason"]
+    # pointer alignment limits the vector
+    p = L.tc_plan(((64, 64), (64, 1)), ((64, 64), (1, 64)), dt, ptr_align=max(eb, 4))
+    assert p["vec_bytes"] == max(eb, 4) or p["path_name"] != "transpose"
+
+
+def test_errors():
+    f32 = L.TC_F32
+    p = L.tc_plan(((4, 32), (32, 1)), ((32, 4), (4, 1)), f32, raise_on_error=False)
+    assert p["status"] == L.TC_E_EXTENT and "extent mismatch" in p["error"]
+    p = L.tc_plan(((4, 32), (32, 1)), ((4, 32), (1, 1)), f32, raise_on_error=False)
+    assert p["status"] == L.TC_E_NONINJECTIVE
+    p = L.tc_plan(((4, 32), (32, 1)), ((4, 32), (32, 1)), 99, raise_on_error=False)
+    assert p["status"] == L.TC_E_DTYPE
+    p = L.tc_plan(((4, 32), (32, 1)), ((4, 32), (32, 1)), f32, flags=0x100, raise_on_error=False)
+    assert p["status"] == L.TC_E_ARG
+    bad = L.make_layout((4, 32), (32, 1))
+    bad.rank = 9
+    p = L.tc_plan(bad, ((4, 32), (32, 1)), f32, raise_on_error=False)
+    assert p["status"] == L.TC_E_RANK
+    p = L.tc_plan(((-1, 32), (32, 1)), ((4, 32), (32, 1)), f32, raise_on_error=False)
+    assert p["status"] == L.TC_E_EXTENT
+    # unit modes are ignored on both sides (TIRx: equal non-unit extents)
+    p = L.tc_plan(((1, 4, 1, 32), (7, 32, 9, 1)), ((4, 32), (1, 4)), f32)
+    assert p["extent"] == (32, 4)
+    with pytest.raises(L.TileCopyError):
+        L.tc_set_flags(0x400)
+    old = L.tc_set_flags(L.TC_FLAG_STRICT)
+    assert L.tc_get_flags() == L.TC_FLAG_STRICT
+    L.tc_set_flags(old)
+
+
+def test_null_pointers_rejected_without_gpu():
+    import ctypes
+    lib = L.load_library()
+    lay = L.make_layout((4, 32))
+    assert lib.tile_copy(None, ctypes.byref(lay), None, ctypes.byref(lay), L.TC_F32, None) == L.TC_E_NULL
+    assert "null" in L.tc_last_error()
+    # misaligned base pointer (a fake address; nothing is launched when the check fails)
+    assert lib.tile_copy(ctypes.c_void_p(0x1002), ctypes.byref(lay), ctypes.c_void_p(0x10000),
+                         ctypes.byref(lay), L.TC_F32, None) == L.TC_E_ALIGN
+
+
+@pytest.mark.parametrize("n", [5, 8, 13])
+def test_layout_slice_matches_python_slicing(n):
+    rng = np.random.default_rng(n)
+    base = np.arange(n * (n + 3)).reshape(n, n + 3)
+    for _ in range(200):
+        sl = []
+        for ext in base.shape:
+            step = int(rng.choice([-3, -2, -1, 1, 2, 3]))
+            a, b = (int(x) for x in rng.integers(-ext - 2, ext + 3, size=2))
+            sl.append((a, b, step))
+        view = base[tuple(slice(*s) for s in sl)]
+        out = L.tc_layout_slice(((n, n + 3), (n + 3, 1), 0), [s[0] for s in sl], [s[1] for s in sl],
+                                [s[2] for s in sl])
+        shape, stride, off = out.as_tuple()
+        assert shape == view.shape
+        if view.size:
+            idx = np.indices(shape).reshape(2, -1)
+            flat = off + (np.array(stride)[:, None] * idx).sum(0)
+            assert np.array_equal(base.reshape(-1)[flat], view.reshape(-1))
+    with pytest.raises(L.TileCopyError):
+        L.tc_layout_slice(((4,), (1,), 0), [0], [4], [0])
+
+
+def test_config5_slice_through_tc_layout_slice():
+    w = SI.sweep_slice("int8")
+    full = L.make_layout((8192, 8192), (8192, 1))
+    out = L.tc_layout_slice(full, [1, 0], [8191, 8190], [1, 2])
+    assert out.as_tuple() == (w.src.shape, w.src.stride, w.src.offset)
+
+
+def _transposing(dtypes=("int8", "float16", "bfloat16", "float32", "float64", "int4vec")):
+    ws = [SI.sf_transpose()]
+    for dt in dtypes:
+        ws.append(SI.transpose2d(4096, 8192, dtype=dt, seed=1, values="bits"))
+    return ws
+
+
+@pytest.mark.parametrize("w", _transposing(), ids=lambda w: w.name)
+def test_swizzle_matches_oracle_rederivation(w):
+    """The oracle re-derives the LDS swizzle for the planner's tile geometry by brute force
+    (TileLang partition of each phase, gfx950 bank model, same search order): the planner's
+    choice must be the oracle's, and conflict-free under the oracle's own counting."""
+    from oracle import ref as R
+    p = _plan(w)
+    assert p["path_name"] == "transpose"
+    geo = dict(eb=p["elem_bytes"], vb=p["vec_bytes"], TR=p["tile_r"], TC=p["tile_c"], NB=p["tile_b"])
+    o = R.lds_tile_swizzle(**geo)
+    assert o is not None
+    assert (o["k"], o["shift"], o["tbit"], o["cshift"], o["cmask"]) == (
+        p["xor_k"], p["xor_shift"], p["xor_tbit"], p["xor_cshift"], p["xor_cmask"])
+    assert R.lds_tile_conflicts(**geo, k=p["xor_k"], shift=p["xor_shift"], tbit=p["xor_tbit"],
+                                cshift=p["xor_cshift"], cmask=p["xor_cmask"]) == (0, 0)
+
+
+def test_no_swizzle_has_conflicts_for_transposes():
+    """Without the swizzle the 2-D transposes pay bank conflicts (which the swizzle removes):
+    the planner's simulation and the oracle's agree on the count."""
+    from oracle import ref as R
+    w = SI.transpose2d(4096, 4096, dtype="float32", seed=1)
+    p = _plan(w, flags=L.TC_FLAG_NO_SWIZZLE)
+    assert p["xor_k"] == 0 and p["read_conflicts"] > 0
+    geo = dict(eb=4, vb=16, TR=p["tile_r"], TC=p["tile_c"], NB=p["tile_b"])
+    assert R.lds_tile_conflicts(**geo) == (p["write_conflicts"], p["read_conflicts"])
