@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark of the layout-permuting tile copy on one MI355X.
+
+A step is one tile_copy of the scale-factor transpose workload: 65536 tiles of shape
+(2, 1, 4, 32) float32, source strides (256, 128, 128, 32, 1) -> destination strides
+(256, 128, 128, 1, 4), tiles contiguous in HBM -- every step runs the whole hot path (layout
+algebra and plan lookup, [outer, threads, vec] partition, swizzled LDS tile kernel).  The
+inputs are resident in HBM before timing starts; successive steps rotate over several
+source/destination pairs so that more than 512 MiB is touched between reuses of a pair and
+the 256 MB MALL cannot serve them.
+
+Prints one JSON line: throughput as achieved HBM GB/s (algorithmic bytes read + written per
+second), the roofline of the kernel (HIP-event time per launch on the launch stream, against
+8 TB/s), the oracle's CPU throughput on a bounded sample of the same workload, and a sweep of
+the other workloads (same metric, context only).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth_inputs as SI  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD specification
+METRIC = "achieved HBM GB/s (read+write) and % of peak for layout-permuting tile copy"
+MALL_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "plan.cpp", "bank.cpp"):
+        with open(os.path.join(ROOT, "layout_permuting_copy_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, launches_bytes: int):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    entry = doc.get("workloads", {}).get(workload)
+    if not entry or doc.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def device_tensors(torch, w: SI.Workload, pairs: int, host_src: np.ndarray | None, seed: int):
+    n_src = SI.storage_elems(w, "src") * w.eb
+    n_dst = SI.storage_elems(w, "dst") * w.eb
+    srcs, dsts = [], []
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    for i in range(pairs):
+        if host_src is not None:
+            s = torch.from_numpy(host_src).to("cuda")
+        else:  # bench-only inputs for the sweep: random bits made on the device
+            s = torch.empty(n_src, dtype=torch.uint8, device="cuda")
+            s.random_(0, 256, generator=g)
+        srcs.append(s)
+        dsts.append(torch.empty(n_dst, dtype=torch.uint8, device="cuda"))
+    return srcs, dsts
+
+
+def time_workload(torch, L, w: SI.Workload, steps: int, warmup: int, host_src=None, seed=0):
+    """Returns dict with wall ms/step and mean per-launch event ms."""
+    bytes_step = 2 * int(np.prod(w.src.shape)) * w.eb
+    pair_bytes = (SI.storage_elems(w, "src") + SI.storage_elems(w, "dst")) * w.eb
+    # rotate so that more than 2x the MALL is touched between reuses of a pair (cap: 8 GiB)
+    pairs = max(2, -(-2 * MALL_BYTES // pair_bytes) + 1)
+    pairs = max(1, min(pairs, (8 << 30) // pair_bytes))
+    srcs, dsts = device_tensors(torch, w, pairs, host_src, seed)
+    sl = (w.src.shape, w.src.stride, w.src.offset)
+    dl = (w.dst.shape, w.dst.stride, w.dst.offset)
+    code = L.DTYPE_BY_NAME[w.dtype]
+    stream = torch.cuda.current_stream()
+    plan = L.tile_copy_ex(srcs[0], sl, dsts[0], dl, code)
+    for i in range(warmup):
+        L.tile_copy(srcs[i % pairs], sl, dsts[i % pairs], dl, code, stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        L.tile_copy(srcs[i % pairs], sl, dsts[i % pairs], dl, code, stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kms = [a.elapsed_time(b) for a, b in ev]
+    out = {"workload": w.name, "path": plan["path_name"], "elem_bytes": w.eb, "elements": int(np.prod(w.src.shape)),
+           "bytes_per_step": bytes_step, "ms_per_step": wall * 1e3 / steps,
+           "kernel_ms_mean": float(np.mean(kms)), "kernel_ms_median": float(np.median(kms)),
+           "kernel_ms_min": float(np.min(kms)), "rotating_pairs": pairs,
+           "tile": [plan["tile_r"], plan["tile_c"], plan["tile_b"]], "vec_bytes": plan["vec_bytes"],
+           "xor": [plan["xor_k"], plan["xor_shift"], plan["xor_tbit"], plan["xor_cshift"], plan["xor_cmask"]],
+           "workgroups": plan["workgroups"]}
+    out["gbs_wall"] = bytes_step / (out["ms_per_step"] * 1e-3) / 1e9
+    out["gbs_kernel"] = bytes_step / (out["kernel_ms_mean"] * 1e-3) / 1e9
+    out["gbs_kernel_median"] = bytes_step / (out["kernel_ms_median"] * 1e-3) / 1e9
+    out["pct_peak_kernel"] = 100 * out["gbs_kernel"] / PEAK_HBM_GBS
+    # sampled parity of the last destination written against the oracle's offsets
+    out["_last"] = (srcs[(steps - 1) % pairs], dsts[(steps - 1) % pairs])
+    del srcs, dsts
+    return out
+
+
+def sampled_parity(torch, w: SI.Workload, src_d, dst_d, n: int = 1 << 16) -> bool:
+    from oracle import ref as R
+    count = int(np.prod(w.src.shape))
+    rng = np.random.default_rng(7)
+    flat = np.unique(np.concatenate([rng.integers(0, count, n), [0, count - 1]]))
+    so, do = R.sample_offsets((w.src.shape, w.src.stride, w.src.offset), (w.dst.shape, w.dst.stride, w.dst.offset),
+                              flat)
+    eb = w.eb
+    s = src_d.view(-1, eb) if eb > 1 else src_d.view(-1, 1)
+    d = dst_d.view(-1, eb) if eb > 1 else dst_d.view(-1, 1)
+    a = s[torch.from_numpy(so).to("cuda")].cpu().numpy()
+    b = d[torch.from_numpy(do).to("cuda")].cpu().numpy()
+    return bool(np.array_equal(a, b))
+
+
+def cpu_baseline(w: SI.Workload, host_src: np.ndarray, budget_s: float = 12.0):
+    """The oracle (C, OpenMP) on a bounded sample of the workload: the first `tiles` tiles of
+    the outermost mode, repeated for about budget_s seconds."""
+    from oracle import ref as R
+    outer = w.src.shape[0]
+    tiles = max(1, outer // 8)
+    shape = (tiles,) + tuple(w.src.shape[1:])
+    sl = (shape, w.src.stride, w.src.offset)
+    dl = (shape, w.dst.stride, w.dst.offset)
+    n_dst = SI.span(SI.Side(shape, w.dst.stride, w.dst.offset))
+    dst = np.empty(n_dst * w.eb, dtype=np.uint8)
+    src = host_src[: SI.span(SI.Side(shape, w.src.stride, w.src.offset)) * w.eb].copy()
+    R.copy(src, sl, dst, dl, w.eb)  # warm-up
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        R.copy(src, sl, dst, dl, w.eb)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > budget_s:
+            break
+    bytes_rep = 2 * int(np.prod(shape)) * w.eb
+    return {"value": bytes_rep * reps / el / 1e9, "unit": "GB/s", "cores": R.max_threads(), "kind": "oracle",
+            "sample": f"{tiles} of {outer} outer tiles ({bytes_rep / 2**20:.1f} MiB moved per copy), "
+                      f"{reps} copies in {el:.1f} s"}
+
+
+def time_memcpy(torch, nbytes: int = 1 << 30, steps: int = 30):
+    """Context row: device-to-device hipMemcpy (torch copy_ of contiguous bytes), 2 buffer pairs."""
+    a = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    b = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    for i in range(3):
+        b[i % 2].copy_(a[i % 2])
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        b[i % 2].copy_(a[i % 2])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([x.elapsed_time(y) for x, y in ev]))
+    del a, b
+    return {"workload": f"memcpy_dtod_{nbytes >> 20}MiB", "path": "hipMemcpy (context)", "bytes_per_step": 2 * nbytes,
+            "kernel_ms_mean": ms, "gbs_kernel": 2 * nbytes / (ms * 1e-3) / 1e9,
+            "pct_peak_kernel": 100 * 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def identity_workload(n: int = 1 << 28) -> SI.Workload:
+    return SI.Workload(f"identity_{n}_float32", SI.Side((n,), (1,)), SI.Side((n,), (1,)), "float32", "bits", 12)
+
+
+def sweep_workloads():
+    ws = [SI.transpose2d(dtype="float32"), SI.transpose2d(dtype="bfloat16"), SI.permute0213()]
+    ws += [SI.sweep_dense(dt) for dt in SI.SWEEP_DTYPES]
+    ws += [SI.sweep_slice("float16"), SI.sweep_odd("float16")]
+    return ws
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the per-workload context sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only", default=None, help="time only the named sweep workload (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the copy has no multi-GPU path "
+                                   "in this build (--gpus must be 1)"}))
+        return 2
+    for k in ("RANK", "WORLD_SIZE"):
+        if int(os.environ.get(k, "0" if k == "RANK" else "1")) != (0 if k == "RANK" else 1):
+            print(json.dumps({"error": "run on one GPU without torch.distributed"}))
+            return 2
+    import torch
+    import layout_permuting_copy_amd as L
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        return 2
+    L.load_library()
+    if args.only:
+        w = next(w for w in [SI.sf_transpose(), identity_workload()] + sweep_workloads() if w.name == args.only)
+        r = time_workload(torch, L, w, args.steps, args.warmup)
+        r.pop("_last")
+        print(json.dumps(r))
+        return 0
+
+    w = SI.sf_transpose()
+    host_src = SI.make_source(w)
+    r = time_workload(torch, L, w, args.steps, args.warmup, host_src=host_src)
+    src_d, dst_d = r.pop("_last")
+    parity = sampled_parity(torch, w, src_d, dst_d)
+    del src_d, dst_d
+    torch.cuda.empty_cache()
+    sweep = []
+    if not args.no_sweep:
+        sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in time_memcpy(torch).items()})
+        torch.cuda.empty_cache()
+        for sw in [identity_workload()] + sweep_workloads():
+            s = time_workload(torch, L, sw, 30, 3, seed=11)
+            s_src, s_dst = s.pop("_last")
+            s["sampled_parity"] = sampled_parity(torch, sw, s_src, s_dst, 1 << 14)
+            del s_src, s_dst
+            torch.cuda.empty_cache()
+            sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
+    traffic = traffic_from_profiles(w.name, r["bytes_per_step"])
+    achieved = r["gbs_kernel"]
+    line = {
+        "metric": METRIC,
+        "value": round(r["gbs_wall"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "shape": list(w.src.shape), "src_stride": list(w.src.stride),
+                   "dst_stride": list(w.dst.stride), "element": "float32 moved as raw 32-bit words",
+                   "bytes_per_step": r["bytes_per_step"], "path": r["path"], "tile": r["tile"],
+                   "vec_bytes": r["vec_bytes"], "xor": r["xor"], "workgroups": r["workgroups"],
+                   "rotating_buffer_pairs": r["rotating_pairs"], "sampled_parity": parity,
+                   "pct_of_peak_wall": round(100 * r["gbs_wall"] / PEAK_HBM_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 3),
+                     "kernel_us_median": round(r["kernel_ms_median"] * 1e3, 3),
+                     "algorithmic_bytes_per_launch": r["bytes_per_step"]},
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, host_src)
+        line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 3)
+    if sweep:
+        line["sweep"] = sweep
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -135,6 +135,8 @@ typedef struct tc_plan_info {
    chunk' = chunk ^ (((row >> shift) & mask) << tbit) ^ ((chunk >> cshift) & cmask), k = log2(mask+1) */
   int32_t xor_k, xor_shift, xor_mask, xor_tbit;
   int32_t xor_cshift, xor_cmask;
+  int32_t grid_order;       /* transpose grid: 0 column tiles fastest, 1 row tiles fastest */
+  int32_t nontemporal;      /* nontemporal global accesses: bit 0 loads, bit 1 stores */
   int32_t lds_write_bytes, lds_read_bytes;       /* LDS instruction widths */
   int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
   char reason[192];         /* why the fast path was declined ("" if it was not) */

@@ -52,18 +52,19 @@ int64_t lds_conflict_cycles(const int64_t* byte_addr, const bool* active, int la
 
 bool finish_geom(TileGeom* g) {
   if (g->eb <= 0 || g->vb < g->eb || g->vb % g->eb) return false;
-  g->U = g->eb < 4 ? 4 : g->eb;
-  g->B = g->eb < 4 ? 4 / g->eb : 1;
+  if (g->U == 0) g->U = g->eb < 4 ? 4 : g->eb;
+  if ((g->U != 4 && g->U != 8 && g->U != 16) || g->U < g->eb) return false;
+  g->B = g->U / g->eb;
   g->VE = g->vb / g->eb;
   if (g->vb < g->U) return false;  // a store vector covers whole units
   for (int v : {g->TR, g->TC, g->NB})
     if (v <= 0 || (v & (v - 1))) return false;
   if (g->TR % g->VE || g->TC % g->VE || g->TR % g->B) return false;
-  if (int64_t(g->TR) * g->TC * g->NB * g->eb != kTileBytes) return false;
+  if (int64_t(g->TR) * g->TC * g->NB * g->eb != g->tile_bytes) return false;
   const int per_load = g->NT * g->vb * g->B, per_store = g->NT * g->vb;
-  if (kTileBytes % per_load || kTileBytes % per_store) return false;
-  g->loads = kTileBytes / per_load;
-  g->stores = kTileBytes / per_store;
+  if (g->tile_bytes % per_load || g->tile_bytes % per_store) return false;
+  g->loads = g->tile_bytes / per_load;
+  g->stores = g->tile_bytes / per_store;
   g->ww = std::min(16, g->VE * g->U);
   g->rw = g->U;
   if (g->TRu() < g->RPV()) return false;

@@ -1,0 +1,152 @@
+// Device helpers shared by the tile-copy kernels (gfx950): raw word moves, global accesses with
+// an optional nontemporal hint, byte permutes and 32-bit division by a runtime constant.
+// All data moves as unsigned integers: floating point payloads are never touched.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "plan.hpp"
+
+namespace tc {
+namespace dev {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int N>
+struct Bytes;
+template <>
+struct Bytes<1> { typedef uint8_t T; };
+template <>
+struct Bytes<2> { typedef uint16_t T; };
+template <>
+struct Bytes<4> { typedef uint32_t T; };
+template <>
+struct Bytes<8> { typedef u32x2 T; };
+template <>
+struct Bytes<16> { typedef u32x4 T; };
+
+constexpr int clog2(int x) { return x <= 1 ? 0 : 1 + clog2(x / 2); }
+
+// N bytes (N = 4, 8, 16) between memory (LDS or global) and N/4 dwords.
+template <int N>
+__device__ __forceinline__ void load_words(const unsigned char* p, uint32_t* w) {
+  if constexpr (N == 16) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (N == 8) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void store_words(unsigned char* p, const uint32_t* w) {
+  if constexpr (N == 16) {
+    *reinterpret_cast<u32x4*>(p) = u32x4{w[0], w[1], w[2], w[3]};
+  } else if constexpr (N == 8) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{w[0], w[1]};
+  } else {
+    *reinterpret_cast<uint32_t*>(p) = w[0];
+  }
+}
+
+// Global accesses of N bytes (N = 4, 8, 16).  NTM bit 0: nontemporal loads, bit 1: nontemporal
+// stores (streaming data that is read or written once).
+template <int N, int NTM>
+__device__ __forceinline__ void gload(const unsigned char* p, uint32_t* w) {
+  if constexpr (!(NTM & 1)) {
+    load_words<N>(p, w);
+  } else if constexpr (N == 16) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (N == 8) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  }
+}
+
+template <int N, int NTM>
+__device__ __forceinline__ void gstore(unsigned char* p, const uint32_t* w) {
+  if constexpr (!(NTM & 2)) {
+    store_words<N>(p, w);
+  } else if constexpr (N == 16) {
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4*>(p));
+  } else if constexpr (N == 8) {
+    __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(p));
+  } else {
+    __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p));
+  }
+}
+
+template <typename V, int NTM>
+__device__ __forceinline__ V gload_v(const V* p) {
+  if constexpr (NTM & 1) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <typename V, int NTM>
+__device__ __forceinline__ void gstore_v(V* p, V v) {
+  if constexpr (NTM & 2) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+// v_perm_b32: byte i of the result is byte sel.i of {hi:lo} (0-3 from lo, 4-7 from hi).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+__device__ __forceinline__ uint32_t udiv(uint32_t n, const Div32& d) {
+  return uint32_t((uint64_t(__umulhi(n, d.mul)) + n) >> d.shr);
+}
+
+// Tile `tile` of the grid: column tiles fastest, then row tiles (or the other way round when
+// a.order is 1), then batch tiles, then the remaining grid modes (innermost last).  Returns the
+// tile's first element on both sides and how much of each tile extent lies inside the copy.
+struct TileAt {
+  int64_t sbase, dbase;
+  int64_t remR, remC, remB;
+};
+
+__device__ __forceinline__ TileAt tile_at(const TransposeArgs& a, uint32_t tile) {
+  uint32_t idx = tile;
+  const Div32& first = a.order ? a.tilesR : a.tilesC;
+  const Div32& second = a.order ? a.tilesC : a.tilesR;
+  uint32_t q = udiv(idx, first);
+  const uint32_t i0 = idx - q * first.d;
+  idx = q;
+  q = udiv(idx, second);
+  const uint32_t i1 = idx - q * second.d;
+  const uint32_t tcI = a.order ? i1 : i0, trI = a.order ? i0 : i1;
+  idx = q;
+  q = udiv(idx, a.tilesB);
+  const uint32_t tbI = idx - q * a.tilesB.d;
+  idx = q;
+  int64_t s = a.src_off, d = a.dst_off;
+  for (int k = a.nbatch - 1; k >= 0; --k) {
+    q = udiv(idx, a.bdiv[k]);
+    const uint32_t i = idx - q * a.bdiv[k].d;
+    idx = q;
+    s += int64_t(i) * a.bs[k];
+    d += int64_t(i) * a.bd[k];
+  }
+  const int64_t r0 = int64_t(trI) << a.lTR, c0 = int64_t(tcI) << a.lTC, b0 = int64_t(tbI) << a.lNB;
+  TileAt t;
+  t.sbase = s + r0 * a.sR + c0 * a.sC + b0 * a.sB;
+  t.dbase = d + r0 * a.dR + c0 * a.dC + b0 * a.dB;
+  t.remR = a.eR - r0;
+  t.remC = a.eC - c0;
+  t.remB = a.eB - b0;
+  return t;
+}
+
+__device__ __forceinline__ bool tile_full(const TransposeArgs& a, const TileAt& t) {
+  return t.remR >= (int64_t(1) << a.lTR) && t.remC >= (int64_t(1) << a.lTC) && t.remB >= (int64_t(1) << a.lNB);
+}
+
+}  // namespace dev
+}  // namespace tc

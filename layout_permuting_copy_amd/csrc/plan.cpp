@@ -18,6 +18,7 @@
 // bit count k (then the smallest shift and target bit) that leaves both conflict-free.
 #include <algorithm>
 #include <cstdlib>
+#include <string>
 
 #include "plan.hpp"
 
@@ -46,8 +47,9 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Step 2 of the page: widest vector whose tail divides it and whose other strides/offsets are
 // multiples of it.  `inner_src`/`inner_dst` are the modes vectorized on each side.
-static int choose_vec(const Joint& j, int eb, int inner_src, int inner_dst, int ptr_align) {
+static int choose_vec(const Joint& j, int eb, int inner_src, int inner_dst, int ptr_align, int max_vb = 16) {
   for (int vb : {16, 8, 4}) {
+    if (vb > max_vb) continue;
     if (vb < eb || vb % eb || vb > ptr_align) continue;
     const int64_t ve = vb / eb;
     bool ok = j.so % ve == 0 && j.dof % ve == 0;
@@ -67,81 +69,168 @@ static void decline(Plan* p, int flags, const std::string& why) {
   if (flags & TC_FLAG_STRICT) p->status = TC_E_DECLINED;
 }
 
-// Tile geometry and swizzle of the transpose path.  Tile extents are powers of two filling
-// kTileBytes; candidates prefer 128-byte destination column segments, then 256 and 64.
+// Tile geometry and swizzle of the transpose path.  Tile extents are powers of two filling the
+// tile.  Candidates are tried in a fixed order of destination run length (bytes of one column
+// segment, TR * eb) and LDS unit size; the first one with a conflict-free swizzle wins.
+//
+// Tile bytes, threads per workgroup and the nontemporal hint are chosen per element width from
+// measurements on MI355X (16384x16384 / 8192x8192 transposes and the batched 4x32 scale-factor
+// tiles, HIP-event timed, HBM-resident inputs).  TC_TUNE (environment, read once) overrides
+// them for tuning sweeps: "tile=32768,threads=512,nt=3,order=0,trb=128,unit=4".
+struct TuneCfg {
+  int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0;
+};
+
+static TuneCfg tune_override() {
+  static const TuneCfg cfg = [] {
+    TuneCfg c;
+    const char* env = std::getenv("TC_TUNE");
+    if (!env) return c;
+    std::string s(env);
+    size_t pos = 0;
+    while (pos < s.size()) {
+      size_t end = s.find(',', pos);
+      if (end == std::string::npos) end = s.size();
+      const std::string kv = s.substr(pos, end - pos);
+      const size_t eq = kv.find('=');
+      if (eq != std::string::npos) {
+        const std::string k = kv.substr(0, eq);
+        const int v = std::atoi(kv.c_str() + eq + 1);
+        if (k == "tile") c.tile = v;
+        else if (k == "threads") c.threads = v;
+        else if (k == "nt") c.nt = v;
+        else if (k == "order") c.order = v;
+        else if (k == "trb") c.trb = v;
+        else if (k == "unit") c.unit = v;
+      }
+      pos = end + 1;
+    }
+    return c;
+  }();
+  return cfg;
+}
+
+// Defaults per element width: {tile bytes, threads, nontemporal mode, grid order}.  `batched` =
+// the destination-contiguous extent is shorter than one 128-byte run, so the tile is filled from
+// a batch mode (the scale-factor case).
+static TuneCfg default_cfg(int eb, bool batched) {
+  TuneCfg c;
+  if (batched) { c.tile = 8192; c.threads = 256; c.nt = 3; c.order = 0; return c; }
+  switch (eb) {
+    case 1: c.tile = 65536; c.threads = 512; c.nt = 3; c.order = 1; break;
+    case 2: c.tile = 65536; c.threads = 512; c.nt = 3; c.order = 0; break;
+    case 4: c.tile = 32768; c.threads = 256; c.nt = 3; c.order = 0; break;
+    case 8: c.tile = 65536; c.threads = 256; c.nt = 3; c.order = 0; break;
+    default: c.tile = 16384; c.threads = 512; c.nt = 3; c.order = 0; break;
+  }
+  return c;
+}
+
 static bool plan_transpose_tile(Plan* p, int flags) {
   const Joint& j = p->j;
   const Mode& R = j.m[p->mode_r];
   const Mode& C = j.m[p->mode_c];
-  const int64_t eB = p->mode_b >= 0 ? j.m[p->mode_b].e : 1;
+  const bool batched = pow2ceil(R.e) * p->eb < 128;
+  TuneCfg cfg = default_cfg(p->eb, batched);
+  const TuneCfg ov = tune_override();
+  if (ov.tile) cfg.tile = ov.tile;
+  if (ov.threads) cfg.threads = ov.threads;
+  if (ov.nt >= 0) cfg.nt = ov.nt;
+  if (ov.order >= 0) cfg.order = ov.order;
+  const int unit_min = p->eb < 4 ? 4 : p->eb;
+  // configurations with kernel instances: 16-byte vectors in every tile size, narrower vectors
+  // in 16 KiB tiles of 256 threads; a tile must give every thread whole loads
+  const int b_min = (ov.unit ? ov.unit : unit_min) / p->eb;
+  if (p->vb < 16 || cfg.tile < cfg.threads * p->vb * b_min) {
+    cfg.tile = 16384;
+    cfg.threads = 256;
+  }
+  const int trb_list[] = {ov.trb ? ov.trb : 128, 256, 64};
+  const int unit_list[] = {ov.unit ? ov.unit : unit_min};
   bool have = false;
   TileGeom best;
   int64_t best_cost = -1, best_w = 0, best_r = 0;
-  int seen[16][3];
+  int seen[64][4];
   int nseen = 0;
   // Without the swizzle only the first geometry is planned, so that TC_FLAG_NO_SWIZZLE measures
   // the swizzle on the tile the default plan uses.
   const bool first_only = flags & TC_FLAG_NO_SWIZZLE;
-  for (int trb : {128, 256, 64}) {
+  for (int trb : trb_list) {
     if (first_only && have) break;
-    TileGeom g;
-    g.eb = p->eb;
-    g.vb = p->vb;
-    const int ve = p->vb / p->eb;
-    int64_t TR = std::max<int64_t>(trb / p->eb, 1);
-    TR = std::max<int64_t>(std::min<int64_t>(TR, pow2ceil(R.e)), std::max(ve, p->eb < 4 ? 4 / p->eb : 1));
-    int64_t TC = std::max<int64_t>(kTileBytes / (TR * p->eb), 1);
-    TC = std::max<int64_t>(std::min<int64_t>(TC, pow2ceil(C.e)), ve);
-    int64_t NB = kTileBytes / (TR * TC * p->eb);
-    if (NB < 1) continue;
-    g.TR = int(TR);
-    g.TC = int(TC);
-    g.NB = int(NB);
-    bool dup = false;
-    for (int i = 0; i < nseen; ++i)
-      if (seen[i][0] == g.TR && seen[i][1] == g.TC && seen[i][2] == g.NB) dup = true;
-    if (dup) continue;
-    seen[nseen][0] = g.TR; seen[nseen][1] = g.TC; seen[nseen][2] = g.NB; ++nseen;
-    if (!finish_geom(&g)) continue;
-    const int chunk_bits = ilog2i(g.TC / g.CW());
-    const int row_bits = ilog2i(g.TRu());
-    const int kmax = (flags & TC_FLAG_NO_SWIZZLE) ? 0 : chunk_bits;
-    // column terms: none first, then (cshift, cmask) by increasing cshift and mask
-    int col_terms[32][2];
-    int ncol = 0;
-    col_terms[ncol][0] = 0; col_terms[ncol][1] = 0; ++ncol;
-    if (!(flags & TC_FLAG_NO_SWIZZLE))
-      for (int cs = 1; cs < chunk_bits && ncol < 32; ++cs)
-        for (int cm = 1; cm < (1 << cs) && cm <= 7 && ncol < 32; cm = 2 * cm + 1) {
-          col_terms[ncol][0] = cs; col_terms[ncol][1] = cm; ++ncol;
-        }
-    bool found = false;
-    for (int k = 0; k <= kmax && !found; ++k)
-      for (int shift = 0; shift <= (k ? std::max(0, row_bits - 1) : 0) && !found; ++shift)
-        for (int tbit = 0; tbit <= (k ? chunk_bits - k : 0) && !found; ++tbit)
-          for (int ct = 0; ct < ncol && !found; ++ct) {
-            TileGeom c = g;
-            c.k = k;
-            c.shift = shift;
-            c.tbit = tbit;
-            c.cshift = col_terms[ct][0];
-            c.cmask = col_terms[ct][1];
-            if (!finish_geom(&c)) continue;
-            int64_t wc, rc;
-            simulate_tile(c, &wc, &rc);
-            const int64_t cost = wc + rc;
-            if (best_cost < 0 || cost < best_cost) {
-              best_cost = cost;
-              best = c;
-              best_w = wc;
-              best_r = rc;
-              have = true;
-            }
-            if (cost == 0) found = true;
+    for (int unit : unit_list) {
+      if (first_only && have) break;
+      TileGeom g;
+      g.eb = p->eb;
+      g.vb = p->vb;
+      g.U = unit;
+      g.NT = cfg.threads;
+      g.tile_bytes = cfg.tile;
+      g.ntm = cfg.nt;
+      g.order = cfg.order;
+      if (unit < p->eb || unit < 4 || unit > p->vb) continue;
+      const int ve = p->vb / p->eb;
+      const int bmin = unit / p->eb;
+      int64_t TR = std::max<int64_t>(trb / p->eb, 1);
+      TR = std::max<int64_t>(std::min<int64_t>(TR, pow2ceil(R.e)), std::max(ve, bmin));
+      int64_t TC = std::max<int64_t>(cfg.tile / (TR * p->eb), 1);
+      TC = std::max<int64_t>(std::min<int64_t>(TC, pow2ceil(C.e)), ve);
+      // source runs of at least one 128-byte cache line where the extent has them
+      if (TC * p->eb < 128 && TC < pow2ceil(C.e)) continue;
+      int64_t NB = cfg.tile / (TR * TC * p->eb);
+      if (NB < 1) continue;
+      g.TR = int(TR);
+      g.TC = int(TC);
+      g.NB = int(NB);
+      bool dup = false;
+      for (int i = 0; i < nseen; ++i)
+        if (seen[i][0] == g.TR && seen[i][1] == g.TC && seen[i][2] == g.NB && seen[i][3] == g.U) dup = true;
+      if (dup || nseen >= 64) continue;
+      seen[nseen][0] = g.TR; seen[nseen][1] = g.TC; seen[nseen][2] = g.NB; seen[nseen][3] = g.U; ++nseen;
+      if (!finish_geom(&g)) continue;
+      const int chunk_bits = ilog2i(g.TC / g.CW());
+      const int row_bits = ilog2i(g.TRu());
+      const int kmax = (flags & TC_FLAG_NO_SWIZZLE) ? 0 : chunk_bits;
+      // column terms: none first, then (cshift, cmask) by increasing cshift and mask
+      int col_terms[32][2];
+      int ncol = 0;
+      col_terms[ncol][0] = 0; col_terms[ncol][1] = 0; ++ncol;
+      if (!(flags & TC_FLAG_NO_SWIZZLE))
+        for (int cs = 1; cs < chunk_bits && ncol < 32; ++cs)
+          for (int cm = 1; cm < (1 << cs) && cm <= 7 && ncol < 32; cm = 2 * cm + 1) {
+            col_terms[ncol][0] = cs; col_terms[ncol][1] = cm; ++ncol;
           }
-    if (found) break;
+      bool found = false;
+      for (int k = 0; k <= kmax && !found; ++k)
+        for (int shift = 0; shift <= (k ? std::max(0, row_bits - 1) : 0) && !found; ++shift)
+          for (int tbit = 0; tbit <= (k ? chunk_bits - k : 0) && !found; ++tbit)
+            for (int ct = 0; ct < ncol && !found; ++ct) {
+              TileGeom c = g;
+              c.k = k;
+              c.shift = shift;
+              c.tbit = tbit;
+              c.cshift = col_terms[ct][0];
+              c.cmask = col_terms[ct][1];
+              if (!finish_geom(&c)) continue;
+              int64_t wc, rc;
+              simulate_tile(c, &wc, &rc);
+              const int64_t cost = wc + rc;
+              if (best_cost < 0 || cost < best_cost) {
+                best_cost = cost;
+                best = c;
+                best_w = wc;
+                best_r = rc;
+                have = true;
+              }
+              if (cost == 0) found = true;
+            }
+      if (found) {
+        p->g = best;
+        p->wconf = 0;
+        p->rconf = 0;
+        return true;
+      }
+    }
   }
-  (void)eB;
   if (!have) return false;
   p->g = best;
   p->wconf = best_w;
@@ -215,10 +304,11 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
 
   if (fast && r == c) {
     // Both sides contiguous along one mode: no cross-lane exchange needed.
-    const bool small = j.count * p.eb <= kTileBytes;
+    const bool small = j.count * p.eb <= kSmallCopyBytes;
     const bool lds = (flags & TC_FLAG_FORCE_LDS) || (small && !(flags & TC_FLAG_FORCE_REGS));
     p.path = lds ? TC_PATH_ROUNDTRIP : TC_PATH_ROWS;
-    p.threads = lds ? kWave : kTileThreads;
+    p.ntm = lds ? 0 : 3;  // streaming copies: nontemporal loads and stores (measured faster)
+    p.threads = lds ? kWave : kRowThreads;
     const int64_t nvec = j.count / (p.vb / p.eb);
     const int64_t per_wg = int64_t(p.threads) * kRowRounds;
     p.workgroups = ceil_div(nvec, per_wg);
@@ -241,17 +331,21 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
       if (b < 0 || std::llabs(j.m[k].s) + std::llabs(j.m[k].d) < std::llabs(j.m[b].s) + std::llabs(j.m[b].d)) b = k;
     }
     p.mode_b = b;
-    if (!plan_transpose_tile(&p, flags)) {
-      p.path = TC_PATH_EMPTY;
-      p.status = TC_E_ARG;
-      p.reason = "internal: no tile geometry";
-      return p;
+    // the widest vector whose tile gives every thread whole loads and stores
+    while (!plan_transpose_tile(&p, flags)) {
+      p.vb = p.vb > 4 ? choose_vec(j, p.eb, c, r, ptr_align, p.vb / 2) : 0;
+      if (p.vb == 0) {
+        p.path = TC_PATH_EMPTY;
+        p.status = TC_E_ARG;
+        p.reason = "internal: no tile geometry";
+        return p;
+      }
     }
     if (p.status != TC_OK) return p;
     p.threads = p.g.NT;
     p.load_outer = p.g.loads;
     p.store_outer = p.g.stores;
-    p.lds_bytes = kTileBytes;
+    p.lds_bytes = p.g.tile_bytes;
     const int64_t eB = b >= 0 ? j.m[b].e : 1;
     p.workgroups = ceil_div(j.m[r].e, p.g.TR) * ceil_div(j.m[c].e, p.g.TC) * ceil_div(eB, p.g.NB);
     for (int k = 0; k < j.rank; ++k)
@@ -282,8 +376,8 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     p.g.TR = p.eb <= 4 ? 64 : 32;
     p.g.TC = p.eb <= 4 ? 64 : (p.eb == 8 ? 64 : 32);
     p.g.NB = 1;
-    p.threads = kTileThreads;
-    p.load_outer = p.store_outer = p.g.TR * p.g.TC / kTileThreads;
+    p.threads = kGuardThreads;
+    p.load_outer = p.store_outer = p.g.TR * p.g.TC / kGuardThreads;
     const int pad = std::max(1, 4 / p.eb);
     p.lds_bytes = p.g.TR * (p.g.TC + pad) * p.eb;
     p.workgroups = ceil_div(j.m[gr].e, p.g.TR) * ceil_div(j.m[gc].e, p.g.TC);
@@ -292,9 +386,9 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     if (p.workgroups >= (int64_t(1) << 31)) { p.status = TC_E_RANGE; p.reason = "more than 2^31 workgroups"; }
   } else {
     p.path = TC_PATH_GUARDED_ROWS;
-    p.threads = kTileThreads;
+    p.threads = kGuardThreads;
     p.load_outer = p.store_outer = kRowRounds;
-    p.workgroups = ceil_div(j.count, int64_t(kTileThreads) * kRowRounds);
+    p.workgroups = ceil_div(j.count, int64_t(kGuardThreads) * kRowRounds);
     if (j.count >= (int64_t(1) << 31)) { p.status = TC_E_RANGE; p.reason = "more than 2^31 elements on the guarded path"; }
   }
   return p;
@@ -327,6 +421,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
   info->tile_b = tiled ? p.g.NB : 0;
   info->workgroups = p.workgroups;
   info->lds_bytes = p.lds_bytes;
+  if (p.path == TC_PATH_ROWS) info->nontemporal = p.ntm;
   if (p.path == TC_PATH_TRANSPOSE) {
     info->xor_k = p.g.k;
     info->xor_shift = p.g.shift;
@@ -334,6 +429,8 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
     info->xor_tbit = p.g.tbit;
     info->xor_cshift = p.g.cshift;
     info->xor_cmask = p.g.cmask;
+    info->grid_order = p.g.order;
+    info->nontemporal = p.g.ntm;
     info->lds_write_bytes = p.g.ww;
     info->lds_read_bytes = p.g.rw;
     info->write_conflicts = p.wconf;

@@ -9,11 +9,20 @@
 
 namespace tc {
 
+// Build-time constants of the rows path (measured choices on MI355X).
+#ifndef TC_ROW_THREADS
+#define TC_ROW_THREADS 256   // threads per workgroup of the register-staged rows path
+#endif
+#ifndef TC_ROW_ROUNDS
+#define TC_ROW_ROUNDS 4      // vectors per thread of the rows path
+#endif
+
 constexpr int kMaxRank = TC_MAX_RANK;
-constexpr int kWave = 64;          // gfx950 wavefront
-constexpr int kTileThreads = 256;  // threads per workgroup on the tiled paths
-constexpr int kTileBytes = 16384;  // LDS tile per workgroup on the tiled paths
-constexpr int kRowRounds = 4;      // vectors per thread on the register-staged path
+constexpr int kWave = 64;                      // gfx950 wavefront
+constexpr int kSmallCopyBytes = 16384;         // co-contiguous copies up to this size: one LDS round trip
+constexpr int kRowThreads = TC_ROW_THREADS;    // threads per workgroup on the rows path
+constexpr int kRowRounds = TC_ROW_ROUNDS;      // vectors per thread on the rows path
+constexpr int kGuardThreads = 256;             // threads per workgroup on the guarded paths
 
 // One joint mode: extent, source stride, destination stride (elements).
 struct Mode {
@@ -51,16 +60,25 @@ int64_t lds_conflict_cycles(const int64_t* byte_addr, const bool* active, int la
                             bool write);
 
 // ---- transpose tile geometry -------------------------------------------------------------------
-// The LDS tile is NB x TRu x TC units of U bytes.  For elements narrower than 4 bytes a unit is a
-// 4-byte column of B = 4/eb consecutive rows (made in registers by a BxB micro-transpose);
-// otherwise a unit is one element (B = 1).  The tile's column chunks of CW units (one LDS write
-// instruction) are XOR-swizzled by row:  chunk' = chunk ^ (((ru >> shift) & mask) << tbit).
+// The LDS tile is NB x TRu x TC units of U bytes (U in {4, 8, 16}, U >= eb).  A unit is one
+// column of B = U/eb consecutive rows, assembled in registers from B loaded row vectors (a
+// register regrouping for 4-byte and wider elements, a BxB byte/halfword micro-transpose with
+// v_perm_b32 for narrower ones).  One store vector (VE consecutive rows of one column) is then
+// RPV = vb/U whole units, so the store phase reads it with RPV LDS reads of U bytes.  The tile's
+// column chunks of CW units (one 16-byte LDS write, or less) are XOR-swizzled by row and by
+// their own higher bits:  chunk' = chunk ^ (((ru >> shift) & mask) << tbit) ^ ((chunk >> cshift) & cmask).
+// The row term spreads the lanes of one read instruction (same column, different rows) over the
+// banks; the column term spreads the chunks one write instruction stores when a lane writes
+// several adjacent chunks.  Both are bijections of a row's chunks.
 struct TileGeom {
   int eb = 4, vb = 16;  // element bytes, global vector bytes
-  int U = 4, B = 1;     // LDS unit bytes, rows per unit
+  int U = 0, B = 1;     // LDS unit bytes (0: the smallest allowed), rows per unit
   int VE = 4;           // elements per global vector
   int TR = 32, TC = 128, NB = 1;  // tile extents: rows (dst-contiguous mode), cols (src-contiguous mode), batch
-  int NT = kTileThreads;
+  int NT = 256;                   // threads per workgroup
+  int tile_bytes = 16384;         // LDS tile per workgroup
+  int ntm = 0;                    // nontemporal global accesses: bit 0 loads, bit 1 stores
+  int order = 0;                  // grid order: 0 column tiles fastest, 1 row tiles fastest
   int loads = 4, stores = 4;  // accesses per thread per phase
   int ww = 16, rw = 4;        // LDS write / read instruction bytes
   int k = 0, shift = 0, tbit = 0;
@@ -87,6 +105,7 @@ struct Plan {
   int eb = 4;
   Joint j;
   int vb = 0;                       // global vector bytes
+  int ntm = 0;                      // rows path: nontemporal global accesses (bit 0 loads, bit 1 stores)
   int mode_r = -1, mode_c = -1, mode_b = -1;
   TileGeom g;
   int threads = 0, load_outer = 0, store_outer = 0;
@@ -103,6 +122,12 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
 void plan_to_info(const Plan& p, tc_plan_info* info);
 
 // ---- kernel argument blocks (passed by value) ------------------------------------------------
+// 32-bit division by a runtime constant d: q = (umulhi(n, mul) + n) >> shr, exact for n < 2^32.
+struct Div32 {
+  uint32_t d, mul, shr;
+};
+Div32 make_div32(uint32_t d);
+
 struct TransposeArgs {
   const unsigned char* src;
   unsigned char* dst;
@@ -110,13 +135,14 @@ struct TransposeArgs {
   int64_t eR, eC, eB;        // extents of the tile modes (eB = 1 without a batch mode)
   int64_t sR, sC, sB;        // source strides of R, C, B
   int64_t dR, dC, dB;        // destination strides of R, C, B
-  int64_t tilesR, tilesC, tilesB;
+  Div32 tilesR, tilesC, tilesB;
   int32_t nbatch;            // further modes walked by the grid, innermost last
-  int32_t pad0;
-  int64_t bext[kMaxRank], bs[kMaxRank], bd[kMaxRank];
+  Div32 bdiv[kMaxRank];      // their extents
+  int64_t bs[kMaxRank], bd[kMaxRank];
   int32_t lTR, lTC, lNB;     // log2 of the tile extents
   int32_t xshift, xmask, xtbit;
   int32_t xcshift, xcmask;
+  int32_t order;             // 0: column tiles fastest, 1: row tiles fastest
 };
 
 struct RowArgs {

@@ -1,0 +1,224 @@
+// The LDS-tiled transpose kernel (gfx950, wave64): one tile of TILE bytes per workgroup of NT
+// lanes, global -> registers -> LDS -> registers -> global.
+//
+// Load phase: the tile in source order, split [outer, threads, vec] with the TileLang default
+// mapping (tutorial "loop_mapping.py": access_idx = flat // vec, thread = access_idx % threads,
+// local_idx = (access_idx // threads) * vec + flat % vec), vectors of VB bytes along the
+// source-contiguous mode, every load of a thread issued back to back.  Store phase: the same
+// split of the tile in destination order, vectors of VB bytes along the destination-contiguous
+// mode.  Between them the LDS exchange, whose XOR swizzle is chosen on the host by simulating
+// gfx950's banks for both phases (TVM TIRx docs, "permute_layout", Algorithm step 2) and an
+// s_barrier (TVM TIRx docs, "copy -> gmem_smem", demonstration program: cta_sync between the
+// two copies).  Elements narrower than 4 bytes are grouped into 4-byte units in registers first
+// (v_perm_b32 micro-transposes), so the LDS stage moves whole dwords.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace tc {
+namespace dev {
+
+// Geometry of the tile for element width EB, vector width VB, LDS unit U, tile bytes TILE and
+// NT threads.  A unit is one column of B = U/EB consecutive rows.
+template <int EB, int VB, int U, int TILE, int NT>
+struct Geo {
+  static constexpr int B = U / EB;               // rows per unit
+  static constexpr int VE = VB / EB;             // elements per global vector
+  static constexpr int LOADS = TILE / (NT * VB * B);
+  static constexpr int STORES = TILE / (NT * VB);
+  static constexpr int RPV = VB / U;             // units per store vector
+  static constexpr int UB = VE * U;              // LDS bytes written per load access
+  static constexpr int WW = UB < 16 ? UB : 16;   // LDS write instruction bytes
+  static constexpr int CW = WW / U;              // units per write chunk
+  static constexpr int LB = clog2(B), LVE = clog2(VE), LRPV = clog2(RPV), LCW = clog2(CW);
+  static constexpr int VW = VB / 4;              // dwords per global vector
+  static constexpr bool valid = U >= 4 && U >= EB && U <= VB && TILE % (NT * VB * B) == 0 &&
+                                TILE / (NT * VB * B) >= 1 && TILE % (NT * VB) == 0;
+};
+
+template <typename G>
+struct TileRegs {
+  uint32_t w[G::LOADS][G::B][G::VW];
+};
+
+// Load phase of one tile: global -> registers.  GUARD (tile reaches past an extent): positions
+// outside the copy load the tile's first vector instead -- always inside the copy, and never
+// stored -- so no load waits on a branch.
+template <int EB, int VB, typename G, int NT, int NTM, bool GUARD>
+__device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& t, TileRegs<G>& r) {
+  const int lTRu = a.lTR - G::LB;
+  const int lnCV = a.lTC - G::LVE;  // load vectors per unit-row
+  const int TRu = 1 << lTRu, NB = 1 << a.lNB;
+  const int64_t sR = a.sR;
+#pragma unroll
+  for (int f = 0; f < G::LOADS; ++f) {
+    const int acc = f * NT + threadIdx.x;
+    const int cv = acc & ((1 << lnCV) - 1);
+    const int ru = (acc >> lnCV) & (TRu - 1);
+    const int nb = acc >> (lnCV + lTRu);
+    int64_t off = t.sbase + nb * a.sB + (int64_t(ru) << G::LB) * sR + (cv << G::LVE);
+    if constexpr (GUARD) {
+      const bool ok = nb < NB && nb < t.remB && (int64_t(ru) << G::LB) < t.remR && (int64_t(cv) << G::LVE) < t.remC;
+      off = ok ? off : t.sbase;
+    }
+    const unsigned char* p = a.src + off * EB;
+#pragma unroll
+    for (int i = 0; i < G::B; ++i) gload<VB, NTM>(p + i * sR * EB, r.w[f][i]);
+  }
+}
+
+// Registers -> LDS: the VE units (columns) of each access, U/4 dwords each, into swizzled chunks.
+// Unit j, dword m holds rows m*4/EB .. of column j (EB < 4: packed with v_perm_b32) or part
+// m % (EB/4) of row m / (EB/4) (EB >= 4: a plain register regrouping).
+template <int EB, int VB, int U, typename G, int NT>
+__device__ __forceinline__ void write_lds(const TransposeArgs& a, unsigned char* __restrict__ lds,
+                                          const TileRegs<G>& r) {
+  constexpr int UW = U / 4;  // dwords per unit
+  const int lTRu = a.lTR - G::LB;
+  const int lnCV = a.lTC - G::LVE;
+  const int TRu = 1 << lTRu;
+  const int xmask = a.xmask, xshift = a.xshift, xtbit = a.xtbit, xcshift = a.xcshift, xcmask = a.xcmask;
+#pragma unroll
+  for (int f = 0; f < G::LOADS; ++f) {
+    const int acc = f * NT + threadIdx.x;
+    const int cv = acc & ((1 << lnCV) - 1);
+    const int ru = (acc >> lnCV) & (TRu - 1);
+    const int nb = acc >> (lnCV + lTRu);
+    uint32_t unit[G::UB / 4];
+    if constexpr (EB >= 4) {
+      constexpr int DPE = EB / 4;  // dwords per element
+#pragma unroll
+      for (int j = 0; j < G::VE; ++j)
+#pragma unroll
+        for (int m = 0; m < UW; ++m) unit[j * UW + m] = r.w[f][m / DPE][j * DPE + m % DPE];
+    } else if constexpr (EB == 2) {
+#pragma unroll
+      for (int m = 0; m < UW; ++m)
+#pragma unroll
+        for (int d = 0; d < VB / 4; ++d) {
+          unit[(2 * d) * UW + m] = perm(r.w[f][2 * m + 1][d], r.w[f][2 * m][d], 0x05040100u);
+          unit[(2 * d + 1) * UW + m] = perm(r.w[f][2 * m + 1][d], r.w[f][2 * m][d], 0x07060302u);
+        }
+    } else {
+#pragma unroll
+      for (int m = 0; m < UW; ++m)
+#pragma unroll
+        for (int d = 0; d < VB / 4; ++d) {
+          const uint32_t p01 = perm(r.w[f][4 * m + 1][d], r.w[f][4 * m][d], 0x05010400u);
+          const uint32_t q01 = perm(r.w[f][4 * m + 1][d], r.w[f][4 * m][d], 0x07030602u);
+          const uint32_t p23 = perm(r.w[f][4 * m + 3][d], r.w[f][4 * m + 2][d], 0x05010400u);
+          const uint32_t q23 = perm(r.w[f][4 * m + 3][d], r.w[f][4 * m + 2][d], 0x07030602u);
+          unit[(4 * d) * UW + m] = perm(p23, p01, 0x05040100u);
+          unit[(4 * d + 1) * UW + m] = perm(p23, p01, 0x07060302u);
+          unit[(4 * d + 2) * UW + m] = perm(q23, q01, 0x05040100u);
+          unit[(4 * d + 3) * UW + m] = perm(q23, q01, 0x07060302u);
+        }
+    }
+    const int xr = ((ru >> xshift) & xmask) << xtbit;
+    const int row = (nb << lTRu) + ru;
+#pragma unroll
+    for (int q = 0; q < G::UB / G::WW; ++q) {
+      const int ch = ((cv << G::LVE) >> G::LCW) + q;
+      const int chs = ch ^ xr ^ ((ch >> xcshift) & xcmask);
+      store_words<G::WW>(lds + ((row << a.lTC) + (chs << G::LCW)) * U, unit + q * (G::WW / 4));
+    }
+  }
+}
+
+// LDS -> registers (all reads first), then registers -> global.  GUARD skips stores of
+// positions outside the copy.
+template <int EB, int VB, int U, typename G, int NT, int NTM, bool GUARD>
+__device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt& t,
+                                           const unsigned char* __restrict__ lds) {
+  const int lTRu = a.lTR - G::LB;
+  const int lnRV = lTRu - G::LRPV;  // store vectors per column
+  const int TC = 1 << a.lTC, NB = 1 << a.lNB;
+  const int xmask = a.xmask, xshift = a.xshift, xtbit = a.xtbit, xcshift = a.xcshift, xcmask = a.xcmask;
+  uint32_t out[G::STORES][VB / 4];
+#pragma unroll
+  for (int f = 0; f < G::STORES; ++f) {
+    const int acc = f * NT + threadIdx.x;
+    const int rv = acc & ((1 << lnRV) - 1);
+    const int c = (acc >> lnRV) & (TC - 1);
+    const int nb = acc >> (lnRV + a.lTC);
+    const int ch = c >> G::LCW, cin = c & (G::CW - 1);
+#pragma unroll
+    for (int v = 0; v < G::RPV; ++v) {
+      const int ru = (rv << G::LRPV) + v;
+      const int xr = ((ru >> xshift) & xmask) << xtbit;
+      const int chs = ch ^ xr ^ ((ch >> xcshift) & xcmask);
+      load_words<U>(lds + ((((nb << lTRu) + ru) << a.lTC) + (chs << G::LCW) + cin) * U, out[f] + v * (U / 4));
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < G::STORES; ++f) {
+    const int acc = f * NT + threadIdx.x;
+    const int rv = acc & ((1 << lnRV) - 1);
+    const int c = (acc >> lnRV) & (TC - 1);
+    const int nb = acc >> (lnRV + a.lTC);
+    unsigned char* p = a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB))) * EB;
+    if constexpr (GUARD) {
+      const bool ok = nb < NB && nb < t.remB && (int64_t(rv) << (G::LRPV + G::LB)) < t.remR && c < t.remC;
+      if (ok) gstore<VB, NTM>(p, out[f]);
+    } else {
+      gstore<VB, NTM>(p, out[f]);
+    }
+  }
+}
+
+// One tile per workgroup.  Interior tiles (the common case) take the unguarded path, which has
+// no per-lane conditions at all.
+template <int EB, int VB, int U, int TILE, int NT, int NTM>
+__global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
+  typedef Geo<EB, VB, U, TILE, NT> G;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[TILE];
+  const TileAt t = tile_at(a, blockIdx.x);
+  TileRegs<G> r;
+  const bool full = tile_full(a, t);
+  if (full) load_tile<EB, VB, G, NT, NTM, false>(a, t, r);
+  else load_tile<EB, VB, G, NT, NTM, true>(a, t, r);
+  write_lds<EB, VB, U, G, NT>(a, lds, r);
+  __syncthreads();
+  if (full) read_store<EB, VB, U, G, NT, NTM, false>(a, t, lds);
+  else read_store<EB, VB, U, G, NT, NTM, true>(a, t, lds);
+}
+
+template <int EB, int VB, int U, int TILE, int NT, int NTM>
+bool launch_transpose_cfg(const TransposeArgs& ta, int64_t wgs, hipStream_t s) {
+  if constexpr (Geo<EB, VB, U, TILE, NT>::valid) {
+    hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM>), dim3(uint32_t(wgs)), dim3(NT), 0, s, ta);
+    return true;
+  }
+  return false;
+}
+
+}  // namespace dev
+
+// One compilation unit per element width instantiates the configurations it supports.
+bool launch_transpose_eb1(const Plan& p, const TransposeArgs& ta, hipStream_t s);
+bool launch_transpose_eb2(const Plan& p, const TransposeArgs& ta, hipStream_t s);
+bool launch_transpose_eb4(const Plan& p, const TransposeArgs& ta, hipStream_t s);
+bool launch_transpose_eb8(const Plan& p, const TransposeArgs& ta, hipStream_t s);
+bool launch_transpose_eb16(const Plan& p, const TransposeArgs& ta, hipStream_t s);
+
+}  // namespace tc
+
+// Instantiation list of one element width: every (vector bytes, tile bytes, threads,
+// nontemporal mode) the planner can choose, with the smallest LDS unit.
+#define TC_TRANSPOSE_DISPATCH(EB)                                                                           \
+  bool launch_transpose_eb##EB(const Plan& p, const TransposeArgs& ta, hipStream_t s) {                      \
+    const int vb = p.vb, tile = p.g.tile_bytes, nt = p.g.NT, ntm = p.g.ntm;                                  \
+    constexpr int U = EB < 4 ? 4 : EB;                                                                       \
+    if (p.g.U != U) return false;                                                                            \
+    TC_CFG(EB, 16, U, 8192, 256) TC_CFG(EB, 16, U, 16384, 256) TC_CFG(EB, 16, U, 16384, 512)                  \
+    TC_CFG(EB, 16, U, 32768, 256) TC_CFG(EB, 16, U, 32768, 512) TC_CFG(EB, 16, U, 65536, 256)                 \
+    TC_CFG(EB, 16, U, 65536, 512)                                                                            \
+    TC_CFG(EB, 8, U, 16384, 256) TC_CFG(EB, 4, U, 16384, 256)                                                \
+    return false;                                                                                            \
+  }
+
+#define TC_CFG(EB, VB, U, TILE, NT)                                                                          \
+  if (vb == VB && tile == TILE && nt == NT) {                                                                \
+    if (ntm == 3) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 3>(ta, p.workgroups, s);             \
+    if (ntm == 0) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 0>(ta, p.workgroups, s);             \
+  }

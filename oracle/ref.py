@@ -454,8 +454,8 @@ def permute_layout_py(src: np.ndarray, src_lay: Layout, dst: np.ndarray, dst_lay
 # model and the hardware conflict counter, not by printed values).
 #
 # The tile holds NB x TR x TC elements (TR along the destination-contiguous mode, TC along the
-# source-contiguous mode).  In LDS it is a grid of units of U = max(eb, 4) bytes: for eb < 4 a
-# unit is one column of B = 4/eb consecutive rows, otherwise one element.  Unit (nb, ru, c) is
+# source-contiguous mode).  In LDS it is a grid of units of U bytes (U in {4, 8, 16}, U >= eb,
+# default max(eb, 4)): a unit is one column of B = U/eb consecutive rows.  Unit (nb, ru, c) is
 # stored at byte ((nb*TRu + ru)*TC + chunk'*CW + c % CW) * U, where CW units form one LDS write
 # (WW = min(16, VE*U) bytes), chunk = c // CW and
 #     chunk' = chunk ^ (((ru >> shift) & (2^k - 1)) << tbit) ^ ((chunk >> cshift) & cmask).
@@ -465,18 +465,18 @@ def permute_layout_py(src: np.ndarray, src_lay: Layout, dst: np.ndarray, dst_lay
 # RPV = vb / U units; each read instruction loads one unit.
 # ----------------------------------------------------------------------------------------------
 
-def _tile_units(eb, vb, TR, TC, NB):
-    U = max(eb, 4)
-    B = 4 // eb if eb < 4 else 1
+def _tile_units(eb, vb, TR, TC, NB, U=None):
+    U = U or max(eb, 4)
+    B = U // eb
     VE = vb // eb
     WW = min(16, VE * U)
     return U, B, VE, WW // U, vb // U, TR // B, WW
 
 
-def _tile_instructions(eb, vb, TR, TC, NB, NT):
+def _tile_instructions(eb, vb, TR, TC, NB, NT, U=None):
     """[(op, width, {thread: (nb, ru, c)})] for every LDS instruction of the tile, from the
     TileLang partitions of both phases."""
-    U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB)
+    U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB, U)
     insts = {}
     for (nb, ru, c), (t, slot) in loop_partition((NB, TRu, TC), NT, VE).items():
         if slot % CW == 0:  # first unit of a write instruction
@@ -493,13 +493,13 @@ _TILE_CACHE = {}
 
 
 def lds_tile_conflicts(eb, vb, TR, TC, NB, NT=256, k=0, shift=0, tbit=0, cshift=0, cmask=0,
-                       model=None, stop_at_first=False):
+                       model=None, stop_at_first=False, U=None):
     """(write-phase, read-phase) extra LDS cycles of one tile under the gfx950 model."""
     model = model or gfx950_model()
-    key = (eb, vb, TR, TC, NB, NT)
+    key = (eb, vb, TR, TC, NB, NT, U)
     if key not in _TILE_CACHE:
-        _TILE_CACHE[key] = _tile_instructions(eb, vb, TR, TC, NB, NT)
-    U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB)
+        _TILE_CACHE[key] = _tile_instructions(eb, vb, TR, TC, NB, NT, U)
+    U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB, U)
     mask = (1 << k) - 1
 
     def addr(nb, ru, c):
@@ -524,12 +524,12 @@ def lds_tile_conflicts(eb, vb, TR, TC, NB, NT=256, k=0, shift=0, tbit=0, cshift=
     return wc, rc
 
 
-def lds_tile_swizzle(eb, vb, TR, TC, NB, NT=256, model=None):
+def lds_tile_swizzle(eb, vb, TR, TC, NB, NT=256, model=None, U=None):
     """Smallest-k XOR swizzle of the tile that leaves both phases conflict-free (the permute
     page's search, Algorithm step 2, on the tile above).  Candidates in order: k ascending, then
     shift, then tbit, then the column term -- none, then (cshift, cmask) by increasing cshift and
     cmask in (1, 3, 7).  Returns a dict, or None when no candidate is conflict-free."""
-    U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB)
+    U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB, U)
     chunks = TC // CW
     chunk_bits = chunks.bit_length() - 1
     row_bits = TRu.bit_length() - 1
@@ -543,7 +543,7 @@ def lds_tile_swizzle(eb, vb, TR, TC, NB, NT=256, model=None):
                     if cm and (1 << cs) >= chunks:
                         continue
                     w, r = lds_tile_conflicts(eb, vb, TR, TC, NB, NT, k, shift, tbit, cs, cm, model,
-                                              stop_at_first=True)
+                                              stop_at_first=True, U=U)
                     if w == 0 and r == 0:
                         return {"k": k, "shift": shift, "tbit": tbit, "cshift": cs, "cmask": cm,
                                 "mask": (1 << k) - 1}

@@ -188,7 +188,8 @@ def test_swizzle_matches_oracle_rederivation(w):
     from oracle import ref as R
     p = _plan(w)
     assert p["path_name"] == "transpose"
-    geo = dict(eb=p["elem_bytes"], vb=p["vec_bytes"], TR=p["tile_r"], TC=p["tile_c"], NB=p["tile_b"])
+    geo = dict(eb=p["elem_bytes"], vb=p["vec_bytes"], TR=p["tile_r"], TC=p["tile_c"], NB=p["tile_b"],
+               U=p["lds_read_bytes"], NT=p["threads"])
     o = R.lds_tile_swizzle(**geo)
     assert o is not None
     assert (o["k"], o["shift"], o["tbit"], o["cshift"], o["cmask"]) == (
@@ -204,5 +205,5 @@ def test_no_swizzle_has_conflicts_for_transposes():
     w = SI.transpose2d(4096, 4096, dtype="float32", seed=1)
     p = _plan(w, flags=L.TC_FLAG_NO_SWIZZLE)
     assert p["xor_k"] == 0 and p["read_conflicts"] > 0
-    geo = dict(eb=4, vb=16, TR=p["tile_r"], TC=p["tile_c"], NB=p["tile_b"])
+    geo = dict(eb=4, vb=16, TR=p["tile_r"], TC=p["tile_c"], NB=p["tile_b"], U=p["lds_read_bytes"], NT=p["threads"])
     assert R.lds_tile_conflicts(**geo) == (p["write_conflicts"], p["read_conflicts"])
