@@ -44,7 +44,8 @@ def _compile(src, build_dir, extra):
 
 def build(verbose: bool = False, extra=(), lib_path: str = LIB, with_probe: bool = True) -> str:
     """Compiles every source (in parallel) and links lib_path.  `extra` adds compiler flags,
-    e.g. -DTC_TILE_BYTES=8192 to build a tuning variant (see csrc/plan.hpp)."""
+    e.g. -DTC_ROW_ROUNDS=1 to build a tuning variant (see csrc/plan.hpp; the transpose's tile
+    configuration is a plan parameter, overridable at run time with TC_TUNE)."""
     extra = list(extra)
     build_dir = BUILD if lib_path == LIB else os.path.join(os.path.dirname(os.path.abspath(lib_path)), "_build")
     os.makedirs(build_dir, exist_ok=True)
