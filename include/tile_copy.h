@@ -85,8 +85,8 @@ enum tc_status {
 };
 
 /* Flags for tc_set_flags / tc_plan.  Unknown bits are rejected (TC_E_ARG). */
-#define TC_FLAG_STRICT        0x01 /* decline (TC_E_DECLINED) instead of falling back to the
-                                      guarded element-wise path */
+#define TC_FLAG_STRICT        0x01 /* decline (TC_E_DECLINED) instead of falling back (to the
+                                      transpose with unaligned vectors, or the guarded paths) */
 #define TC_FLAG_FORCE_GUARDED 0x02 /* always take the guarded element-wise path */
 #define TC_FLAG_FORCE_REGS    0x04 /* co-contiguous copies: stage through registers only */
 #define TC_FLAG_FORCE_LDS     0x08 /* co-contiguous copies: stage through LDS */
@@ -116,7 +116,7 @@ typedef struct tc_plan_info {
   int32_t elem_bytes;
   int64_t count;            /* elements copied */
   int32_t rank;             /* joint canonical rank */
-  int32_t declined;         /* 1 if the fast path was declined (reason below) */
+  int32_t declined;         /* 1 if the aligned [outer, threads, vec] split was declined (reason below) */
   int64_t extent[TC_MAX_RANK];
   int64_t src_stride[TC_MAX_RANK];
   int64_t dst_stride[TC_MAX_RANK];
@@ -137,6 +137,8 @@ typedef struct tc_plan_info {
   int32_t xor_cshift, xor_cmask;
   int32_t grid_order;       /* transpose grid: 0 column tiles fastest, 1 row tiles fastest */
   int32_t nontemporal;      /* nontemporal global accesses: bit 0 loads, bit 1 stores */
+  int32_t unaligned;        /* 1: declined split run by the transpose kernel with 16-byte vectors at
+                               element alignment and element accesses at the edges of the copy */
   int32_t lds_write_bytes, lds_read_bytes;       /* LDS instruction widths */
   int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
   char reason[192];         /* why the fast path was declined ("" if it was not) */

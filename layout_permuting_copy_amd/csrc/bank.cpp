@@ -24,26 +24,25 @@ BankGeom gfx950_bank_geom(bool write, int width) {
 int64_t lds_conflict_cycles(const int64_t* byte_addr, const bool* active, int lanes, int width, bool write) {
   const BankGeom g = gfx950_bank_geom(write, width);
   int64_t total = 0;
-  // (bank, dword) keys of one lane group: at most 32 lanes x 4 dwords
-  int64_t key[kWave * 4];
+  // Distinct dwords per bank within one lane group.  A lane's dwords are consecutive, so it adds
+  // at most one dword to a bank: a bank holds at most `group` (<= 32) entries.
+  int64_t seen[64][32];
+  int cnt[64];
   for (int g0 = 0; g0 < lanes; g0 += g.group) {
-    int n = 0;
+    std::fill(cnt, cnt + g.banks, 0);
+    int worst = 0;
     for (int l = g0; l < std::min(lanes, g0 + g.group); ++l) {
       if (active && !active[l]) continue;
       const int64_t first = byte_addr[l] / 4, last = (byte_addr[l] + width - 1) / 4;
       for (int64_t wd = first; wd <= last; ++wd) {
-        const int64_t bank = ((wd % g.banks) + g.banks) % g.banks;
-        key[n++] = bank * (int64_t(1) << 40) + wd;  // sorts by bank, then dword
+        const int bank = int(((wd % g.banks) + g.banks) % g.banks);
+        int i = 0;
+        while (i < cnt[bank] && seen[bank][i] != wd) ++i;
+        if (i == cnt[bank]) {
+          seen[bank][cnt[bank]++] = wd;
+          worst = std::max(worst, cnt[bank]);
+        }
       }
-    }
-    std::sort(key, key + n);
-    int64_t worst = n ? 1 : 0, run = 0, prev_bank = -1, prev = -1;
-    for (int i = 0; i < n; ++i) {
-      const int64_t bank = key[i] >> 40;
-      if (bank != prev_bank) { run = 1; prev_bank = bank; }
-      else if (key[i] != prev) ++run;
-      prev = key[i];
-      worst = std::max(worst, run);
     }
     total += worst > 0 ? worst - 1 : 0;
   }
@@ -81,7 +80,7 @@ bool finish_geom(TileGeom* g) {
 // it writes the VE units of columns cv*VE.. of unit-row ru, in instructions of ww bytes.
 // Store phase: access a = f*NT + t in destination order (nb, c, rv) with rv fastest; it reads
 // the RPV units ru = rv*RPV + v of column c, one rw-byte instruction each.
-void simulate_tile(const TileGeom& g, int64_t* write_cycles, int64_t* read_cycles) {
+void simulate_tile(const TileGeom& g, int64_t* write_cycles, int64_t* read_cycles, int64_t limit) {
   const int nCV = g.TC / g.VE;
   const int TRu = g.TRu();
   const int RPV = g.RPV();
@@ -99,6 +98,7 @@ void simulate_tile(const TileGeom& g, int64_t* write_cycles, int64_t* read_cycle
           addr[l] = g.unit_addr(nb, ru, cv * g.VE + q * CW) * g.U;
         }
         wc += lds_conflict_cycles(addr, nullptr, kWave, g.ww, true);
+        if (limit >= 0 && wc + rc >= limit) goto done;
       }
     for (int f = 0; f < g.stores; ++f)
       for (int v = 0; v < RPV; ++v) {
@@ -108,8 +108,10 @@ void simulate_tile(const TileGeom& g, int64_t* write_cycles, int64_t* read_cycle
           addr[l] = g.unit_addr(nb, rv * RPV + v, c) * g.U;
         }
         rc += lds_conflict_cycles(addr, nullptr, kWave, g.rw, false);
+        if (limit >= 0 && wc + rc >= limit) goto done;
       }
   }
+done:
   *write_cycles = wc;
   *read_cycles = rc;
 }

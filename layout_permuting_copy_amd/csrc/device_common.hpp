@@ -83,6 +83,44 @@ __device__ __forceinline__ void gstore(unsigned char* p, const uint32_t* w) {
   }
 }
 
+// The first n (0 < n <= VB/EB) elements of a VB-byte vector, one element access each (the
+// vector reaches past an extent of the copy); the other bytes of w are zero.
+template <int EB, int VB>
+__device__ __forceinline__ void gload_partial(const unsigned char* p, int n, uint32_t* w) {
+#pragma unroll
+  for (int k = 0; k < VB / 4; ++k) w[k] = 0;
+#pragma unroll
+  for (int e = 0; e < VB / EB; ++e) {
+    if (e < n) {
+      if constexpr (EB >= 4) {
+#pragma unroll
+        for (int m = 0; m < EB / 4; ++m) w[e * (EB / 4) + m] = reinterpret_cast<const uint32_t*>(p + e * EB)[m];
+      } else if constexpr (EB == 2) {
+        w[e / 2] |= uint32_t(*reinterpret_cast<const uint16_t*>(p + 2 * e)) << (16 * (e & 1));
+      } else {
+        w[e / 4] |= uint32_t(p[e]) << (8 * (e & 3));
+      }
+    }
+  }
+}
+
+template <int EB, int VB>
+__device__ __forceinline__ void gstore_partial(unsigned char* p, int n, const uint32_t* w) {
+#pragma unroll
+  for (int e = 0; e < VB / EB; ++e) {
+    if (e < n) {
+      if constexpr (EB >= 4) {
+#pragma unroll
+        for (int m = 0; m < EB / 4; ++m) reinterpret_cast<uint32_t*>(p + e * EB)[m] = w[e * (EB / 4) + m];
+      } else if constexpr (EB == 2) {
+        *reinterpret_cast<uint16_t*>(p + 2 * e) = uint16_t(w[e / 2] >> (16 * (e & 1)));
+      } else {
+        p[e] = uint8_t(w[e / 4] >> (8 * (e & 3)));
+      }
+    }
+  }
+}
+
 template <typename V, int NTM>
 __device__ __forceinline__ V gload_v(const V* p) {
   if constexpr (NTM & 1) return __builtin_nontemporal_load(p);

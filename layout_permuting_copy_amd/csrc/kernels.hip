@@ -136,6 +136,17 @@ Div32 make_div32(uint32_t d) {
   return v;
 }
 
+bool launch_transpose(int eb, const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream) {
+  switch (eb) {
+    case 1: return launch_transpose_eb1(c, ta, wgs, stream);
+    case 2: return launch_transpose_eb2(c, ta, wgs, stream);
+    case 4: return launch_transpose_eb4(c, ta, wgs, stream);
+    case 8: return launch_transpose_eb8(c, ta, wgs, stream);
+    case 16: return launch_transpose_eb16(c, ta, wgs, stream);
+    default: return false;
+  }
+}
+
 int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::string* err) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.path == TC_PATH_EMPTY) return TC_OK;
@@ -172,16 +183,8 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
       ta.xcmask = p.g.cmask;
       ta.order = p.g.order;
       fill_batch(p, &ta, p.mode_r, p.mode_c, p.mode_b);
-      bool ok = false;
-      switch (p.eb) {
-        case 1: ok = launch_transpose_eb1(p, ta, s); break;
-        case 2: ok = launch_transpose_eb2(p, ta, s); break;
-        case 4: ok = launch_transpose_eb4(p, ta, s); break;
-        case 8: ok = launch_transpose_eb8(p, ta, s); break;
-        case 16: ok = launch_transpose_eb16(p, ta, s); break;
-        default: break;
-      }
-      if (!ok) {
+      const TransposeCfg cfg{p.vb, p.g.U, p.g.tile_bytes, p.g.NT, p.g.ntm};
+      if (!launch_transpose(p.eb, cfg, &ta, p.workgroups, stream)) {
         *err = "no transpose kernel instance for this element width, vector width, tile size and thread count";
         return TC_E_ARG;
       }

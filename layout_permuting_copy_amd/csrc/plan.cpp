@@ -17,6 +17,9 @@
 // step 2: simulate the banks for the write phase and the read phase and keep the smallest XOR
 // bit count k (then the smallest shift and target bit) that leaves both conflict-free.
 #include <algorithm>
+#include <array>
+#include <map>
+#include <mutex>
 #include <cstdlib>
 #include <string>
 
@@ -126,6 +129,88 @@ static TuneCfg default_cfg(int eb, bool batched) {
   return c;
 }
 
+// The XOR swizzle of one tile geometry: the first candidate, in search order, with the fewest
+// simulated extra LDS cycles (search order: k ascending, then the row shift, the target bit and
+// the column term).  A candidate's simulation stops once it can no longer beat the best so far.
+// The result depends on the geometry alone, so it is kept for the life of the process.
+static bool search_swizzle_pass(const TileGeom& g, bool no_swizzle, bool zero_only, TileGeom* out, int64_t* out_w,
+                                int64_t* out_r) {
+  const int chunk_bits = ilog2i(g.TC / g.CW());
+  const int row_bits = ilog2i(g.TRu());
+  const int kmax = no_swizzle ? 0 : chunk_bits;
+  // column terms: none first, then (cshift, cmask) by increasing cshift and mask
+  int col_terms[32][2];
+  int ncol = 0;
+  col_terms[ncol][0] = 0; col_terms[ncol][1] = 0; ++ncol;
+  if (!no_swizzle)
+    for (int cs = 1; cs < chunk_bits && ncol < 32; ++cs)
+      for (int cm = 1; cm < (1 << cs) && cm <= 7 && ncol < 32; cm = 2 * cm + 1) {
+        col_terms[ncol][0] = cs; col_terms[ncol][1] = cm; ++ncol;
+      }
+  int64_t best_cost = -1;
+  for (int k = 0; k <= kmax; ++k)
+    for (int shift = 0; shift <= (k ? std::max(0, row_bits - 1) : 0); ++shift)
+      for (int tbit = 0; tbit <= (k ? chunk_bits - k : 0); ++tbit)
+        for (int ct = 0; ct < ncol; ++ct) {
+          TileGeom c = g;
+          c.k = k;
+          c.shift = shift;
+          c.tbit = tbit;
+          c.cshift = col_terms[ct][0];
+          c.cmask = col_terms[ct][1];
+          if (!finish_geom(&c)) continue;
+          int64_t wc, rc;
+          simulate_tile(c, &wc, &rc, zero_only ? 1 : best_cost);
+          if (zero_only && wc + rc > 0) continue;
+          if (best_cost < 0 || wc + rc < best_cost) {
+            best_cost = wc + rc;
+            *out = c;
+            *out_w = wc;
+            *out_r = rc;
+            if (best_cost == 0) return true;
+          }
+        }
+  return best_cost >= 0;
+}
+
+// First a pass that only looks for a conflict-free candidate (each simulation stops at the first
+// extra cycle), then, if there is none, the full search for the fewest extra cycles.
+static bool search_swizzle_uncached(const TileGeom& g, bool no_swizzle, TileGeom* out, int64_t* out_w,
+                                    int64_t* out_r) {
+  if (search_swizzle_pass(g, no_swizzle, true, out, out_w, out_r)) return true;
+  return search_swizzle_pass(g, no_swizzle, false, out, out_w, out_r);
+}
+
+static bool search_swizzle(const TileGeom& g, bool no_swizzle, TileGeom* out, int64_t* out_w, int64_t* out_r) {
+  struct Found {
+    bool any;
+    TileGeom g;
+    int64_t w, r;
+  };
+  static std::mutex mu;
+  static std::map<std::array<int, 10>, Found> memo;
+  const std::array<int, 10> key{g.eb, g.vb, g.U, g.TR, g.TC, g.NB, g.NT, g.tile_bytes, g.ntm * 8 + g.order,
+                                no_swizzle ? 1 : 0};
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = memo.find(key);
+    if (it != memo.end()) {
+      *out = it->second.g;
+      *out_w = it->second.w;
+      *out_r = it->second.r;
+      return it->second.any;
+    }
+  }
+  Found f{false, g, 0, 0};
+  f.any = search_swizzle_uncached(g, no_swizzle, &f.g, &f.w, &f.r);
+  std::lock_guard<std::mutex> lock(mu);
+  memo.emplace(key, f);
+  *out = f.g;
+  *out_w = f.w;
+  *out_r = f.r;
+  return f.any;
+}
+
 static bool plan_transpose_tile(Plan* p, int flags) {
   const Joint& j = p->j;
   const Mode& R = j.m[p->mode_r];
@@ -138,12 +223,24 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   if (ov.nt >= 0) cfg.nt = ov.nt;
   if (ov.order >= 0) cfg.order = ov.order;
   const int unit_min = p->eb < 4 ? 4 : p->eb;
-  // configurations with kernel instances: 16-byte vectors in every tile size, narrower vectors
-  // in 16 KiB tiles of 256 threads; a tile must give every thread whole loads
-  const int b_min = (ov.unit ? ov.unit : unit_min) / p->eb;
-  if (p->vb < 16 || cfg.tile < cfg.threads * p->vb * b_min) {
-    cfg.tile = 16384;
-    cfg.threads = 256;
+  // no bigger than the copy needs: shrink small copies' tiles (instances exist for 8, 16, 32 and
+  // 64 KiB), rather than filling them with positions outside the copy
+  const int64_t eB = p->mode_b >= 0 ? j.m[p->mode_b].e : 1;
+  const int64_t useful = pow2ceil(R.e) * pow2ceil(C.e) * pow2ceil(eB) * p->eb;
+  while (!ov.tile && cfg.tile > 8192 && cfg.tile / 2 >= useful) cfg.tile /= 2;
+  // only configurations the library holds a kernel for (each gives every thread whole loads):
+  // the same tile with 256 threads, else 16 KiB tiles of 256 threads (every vector width)
+  const int unit0 = ov.unit ? ov.unit : unit_min;
+  auto instance = [&](int tile, int threads) {
+    return launch_transpose(p->eb, TransposeCfg{p->vb, unit0, tile, threads, cfg.nt}, nullptr, 0, nullptr);
+  };
+  if (!instance(cfg.tile, cfg.threads)) {
+    if (instance(cfg.tile, 256)) {
+      cfg.threads = 256;
+    } else {
+      cfg.tile = 16384;
+      cfg.threads = 256;
+    }
   }
   const int trb_list[] = {ov.trb ? ov.trb : 128, 256, 64};
   const int unit_list[] = {ov.unit ? ov.unit : unit_min};
@@ -187,43 +284,18 @@ static bool plan_transpose_tile(Plan* p, int flags) {
       if (dup || nseen >= 64) continue;
       seen[nseen][0] = g.TR; seen[nseen][1] = g.TC; seen[nseen][2] = g.NB; seen[nseen][3] = g.U; ++nseen;
       if (!finish_geom(&g)) continue;
-      const int chunk_bits = ilog2i(g.TC / g.CW());
-      const int row_bits = ilog2i(g.TRu());
-      const int kmax = (flags & TC_FLAG_NO_SWIZZLE) ? 0 : chunk_bits;
-      // column terms: none first, then (cshift, cmask) by increasing cshift and mask
-      int col_terms[32][2];
-      int ncol = 0;
-      col_terms[ncol][0] = 0; col_terms[ncol][1] = 0; ++ncol;
-      if (!(flags & TC_FLAG_NO_SWIZZLE))
-        for (int cs = 1; cs < chunk_bits && ncol < 32; ++cs)
-          for (int cm = 1; cm < (1 << cs) && cm <= 7 && ncol < 32; cm = 2 * cm + 1) {
-            col_terms[ncol][0] = cs; col_terms[ncol][1] = cm; ++ncol;
-          }
-      bool found = false;
-      for (int k = 0; k <= kmax && !found; ++k)
-        for (int shift = 0; shift <= (k ? std::max(0, row_bits - 1) : 0) && !found; ++shift)
-          for (int tbit = 0; tbit <= (k ? chunk_bits - k : 0) && !found; ++tbit)
-            for (int ct = 0; ct < ncol && !found; ++ct) {
-              TileGeom c = g;
-              c.k = k;
-              c.shift = shift;
-              c.tbit = tbit;
-              c.cshift = col_terms[ct][0];
-              c.cmask = col_terms[ct][1];
-              if (!finish_geom(&c)) continue;
-              int64_t wc, rc;
-              simulate_tile(c, &wc, &rc);
-              const int64_t cost = wc + rc;
-              if (best_cost < 0 || cost < best_cost) {
-                best_cost = cost;
-                best = c;
-                best_w = wc;
-                best_r = rc;
-                have = true;
-              }
-              if (cost == 0) found = true;
-            }
-      if (found) {
+      if (!launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm}, nullptr, 0, nullptr)) continue;
+      TileGeom c;
+      int64_t wc, rc;
+      if (!search_swizzle(g, flags & TC_FLAG_NO_SWIZZLE, &c, &wc, &rc)) continue;
+      if (best_cost < 0 || wc + rc < best_cost) {
+        best_cost = wc + rc;
+        best = c;
+        best_w = wc;
+        best_r = rc;
+        have = true;
+      }
+      if (wc + rc == 0) {
         p->g = best;
         p->wconf = 0;
         p->rconf = 0;
@@ -357,6 +429,46 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     return p;
   }
 
+  // Declined by the aligned-vector rule, but both sides have a distinct unit-stride mode: the
+  // transpose kernel with 16-byte vectors at element alignment (gfx950 global memory takes
+  // unaligned vector accesses), whole vectors where the extents allow and element accesses at
+  // the edges of the copy.
+  if (!forced_guarded && r >= 0 && c >= 0 && r != c) {
+    p.vb = 16;
+    p.unaligned = true;
+    p.path = TC_PATH_TRANSPOSE;
+    p.mode_r = r;
+    p.mode_c = c;
+    int b = -1;
+    for (int k = 0; k < j.rank; ++k) {
+      if (k == r || k == c) continue;
+      if (b < 0 || std::llabs(j.m[k].s) + std::llabs(j.m[k].d) < std::llabs(j.m[b].s) + std::llabs(j.m[b].d)) b = k;
+    }
+    p.mode_b = b;
+    const std::string reason = p.reason;
+    const bool declined = p.declined;
+    if (plan_transpose_tile(&p, flags & ~TC_FLAG_STRICT)) {
+      p.reason = reason;
+      p.declined = declined;
+      p.threads = p.g.NT;
+      p.load_outer = p.g.loads;
+      p.store_outer = p.g.stores;
+      p.lds_bytes = p.g.tile_bytes;
+      const int64_t eB = b >= 0 ? j.m[b].e : 1;
+      p.workgroups = ceil_div(j.m[r].e, p.g.TR) * ceil_div(j.m[c].e, p.g.TC) * ceil_div(eB, p.g.NB);
+      for (int k = 0; k < j.rank; ++k)
+        if (k != r && k != c && k != b) p.workgroups *= j.m[k].e;
+      if (p.workgroups >= (int64_t(1) << 31)) {
+        p.status = TC_E_RANGE;
+        p.reason = "more than 2^31 workgroups";
+      }
+      return p;
+    }
+    p.unaligned = false;
+    p.reason = reason;
+    p.declined = declined;
+  }
+
   // Guarded fallback: an LDS tile over the two modes with the smallest strides on each side
   // (element-wide accesses), or an element-wise copy in destination order.
   p.vb = p.eb;
@@ -401,6 +513,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
   info->count = p.j.count;
   info->rank = p.j.rank;
   info->declined = p.declined ? 1 : 0;
+  info->unaligned = p.unaligned ? 1 : 0;
   for (int k = 0; k < p.j.rank; ++k) {
     info->extent[k] = p.j.m[k].e;
     info->src_stride[k] = p.j.m[k].s;

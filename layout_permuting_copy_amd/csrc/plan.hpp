@@ -95,8 +95,9 @@ struct TileGeom {
 };
 // Fill loads/stores/ww/rw/U/B/VE from eb, vb, TR, TC, NB.  False if the geometry is invalid.
 bool finish_geom(TileGeom* g);
-// Simulated extra LDS cycles of one interior tile: write phase and read phase.
-void simulate_tile(const TileGeom& g, int64_t* write_cycles, int64_t* read_cycles);
+// Simulated extra LDS cycles of one interior tile: write phase and read phase.  With limit >= 0
+// the simulation stops once write + read cycles reach the limit (the counts are then partial).
+void simulate_tile(const TileGeom& g, int64_t* write_cycles, int64_t* read_cycles, int64_t limit = -1);
 
 // ---- plan -------------------------------------------------------------------------------------
 struct Plan {
@@ -106,6 +107,8 @@ struct Plan {
   Joint j;
   int vb = 0;                       // global vector bytes
   int ntm = 0;                      // rows path: nontemporal global accesses (bit 0 loads, bit 1 stores)
+  bool unaligned = false;           // transpose with vectors at element alignment (extents or strides
+                                    // not multiples of the vector; edges element by element)
   int mode_r = -1, mode_c = -1, mode_b = -1;
   TileGeom g;
   int threads = 0, load_outer = 0, store_outer = 0;
@@ -160,5 +163,18 @@ struct RowArgs {
 
 // ---- launch (kernels.hip) ------------------------------------------------------------------------
 int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::string* err);
+
+// A transpose kernel configuration: vector bytes, LDS unit bytes, tile bytes, threads and
+// nontemporal mode.  One launcher per element width holds the instances it was built with: it
+// launches `ta` on `stream`, or with ta == nullptr only reports whether the instance exists.
+struct TransposeCfg {
+  int vb, unit, tile, threads, ntm;
+};
+bool launch_transpose_eb1(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
+bool launch_transpose_eb2(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
+bool launch_transpose_eb4(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
+bool launch_transpose_eb8(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
+bool launch_transpose_eb16(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
+bool launch_transpose(int eb, const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
 
 }  // namespace tc

@@ -41,9 +41,8 @@ struct TileRegs {
   uint32_t w[G::LOADS][G::B][G::VW];
 };
 
-// Load phase of one tile: global -> registers.  GUARD (tile reaches past an extent): positions
-// outside the copy load the tile's first vector instead -- always inside the copy, and never
-// stored -- so no load waits on a branch.
+// Load phase of one tile: global -> registers.  GUARD (tile reaches past an extent): only
+// positions inside the copy are loaded; the registers of the others are never stored.
 template <int EB, int VB, typename G, int NT, int NTM, bool GUARD>
 __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& t, TileRegs<G>& r) {
   const int lTRu = a.lTR - G::LB;
@@ -56,14 +55,25 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
     const int cv = acc & ((1 << lnCV) - 1);
     const int ru = (acc >> lnCV) & (TRu - 1);
     const int nb = acc >> (lnCV + lTRu);
-    int64_t off = t.sbase + nb * a.sB + (int64_t(ru) << G::LB) * sR + (cv << G::LVE);
-    if constexpr (GUARD) {
-      const bool ok = nb < NB && nb < t.remB && (int64_t(ru) << G::LB) < t.remR && (int64_t(cv) << G::LVE) < t.remC;
-      off = ok ? off : t.sbase;
-    }
+    const int64_t off = t.sbase + nb * a.sB + (int64_t(ru) << G::LB) * sR + (cv << G::LVE);
     const unsigned char* p = a.src + off * EB;
+    if constexpr (GUARD) {
+      // whole vectors inside the copy load as one access (alignment is only the element's:
+      // gfx950 global memory takes unaligned 16-byte accesses); vectors reaching past the
+      // column extent load their valid elements one by one; the rest are not loaded (their
+      // LDS contents are never stored)
+      const bool in_b = nb < NB && nb < t.remB;
+      const int64_t cols = t.remC - (int64_t(cv) << G::LVE);
 #pragma unroll
-    for (int i = 0; i < G::B; ++i) gload<VB, NTM>(p + i * sR * EB, r.w[f][i]);
+      for (int i = 0; i < G::B; ++i) {
+        const bool in_row = in_b && (int64_t(ru) << G::LB) + i < t.remR && cols > 0;
+        if (in_row && cols >= G::VE) gload<VB, NTM>(p + i * sR * EB, r.w[f][i]);
+        else if (in_row) gload_partial<EB, VB>(p + i * sR * EB, int(cols), r.w[f][i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < G::B; ++i) gload<VB, NTM>(p + i * sR * EB, r.w[f][i]);
+    }
   }
 }
 
@@ -158,8 +168,11 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
     const int nb = acc >> (lnRV + a.lTC);
     unsigned char* p = a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB))) * EB;
     if constexpr (GUARD) {
-      const bool ok = nb < NB && nb < t.remB && (int64_t(rv) << (G::LRPV + G::LB)) < t.remR && c < t.remC;
-      if (ok) gstore<VB, NTM>(p, out[f]);
+      // whole vectors as one store, vectors reaching past the row extent element by element
+      const int64_t rows = t.remR - (int64_t(rv) << (G::LRPV + G::LB));
+      const bool ok = nb < NB && nb < t.remB && c < t.remC && rows > 0;
+      if (ok && rows >= G::VE) gstore<VB, NTM>(p, out[f]);
+      else if (ok) gstore_partial<EB, VB>(p, int(rows), out[f]);
     } else {
       gstore<VB, NTM>(p, out[f]);
     }
@@ -167,7 +180,7 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
 }
 
 // One tile per workgroup.  Interior tiles (the common case) take the unguarded path, which has
-// no per-lane conditions at all.
+// no per-lane conditions at all; tiles at the edges of the copy take the guarded one.
 template <int EB, int VB, int U, int TILE, int NT, int NTM>
 __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   typedef Geo<EB, VB, U, TILE, NT> G;
@@ -183,33 +196,27 @@ __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   else read_store<EB, VB, U, G, NT, NTM, true>(a, t, lds);
 }
 
+// Launches the instance (ta != nullptr) or only reports whether it exists (ta == nullptr).
 template <int EB, int VB, int U, int TILE, int NT, int NTM>
-bool launch_transpose_cfg(const TransposeArgs& ta, int64_t wgs, hipStream_t s) {
+bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
   if constexpr (Geo<EB, VB, U, TILE, NT>::valid) {
-    hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM>), dim3(uint32_t(wgs)), dim3(NT), 0, s, ta);
+    if (ta) hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM>), dim3(uint32_t(wgs)), dim3(NT), 0, s, *ta);
     return true;
   }
   return false;
 }
 
 }  // namespace dev
-
-// One compilation unit per element width instantiates the configurations it supports.
-bool launch_transpose_eb1(const Plan& p, const TransposeArgs& ta, hipStream_t s);
-bool launch_transpose_eb2(const Plan& p, const TransposeArgs& ta, hipStream_t s);
-bool launch_transpose_eb4(const Plan& p, const TransposeArgs& ta, hipStream_t s);
-bool launch_transpose_eb8(const Plan& p, const TransposeArgs& ta, hipStream_t s);
-bool launch_transpose_eb16(const Plan& p, const TransposeArgs& ta, hipStream_t s);
-
 }  // namespace tc
 
 // Instantiation list of one element width: every (vector bytes, tile bytes, threads,
 // nontemporal mode) the planner can choose, with the smallest LDS unit.
 #define TC_TRANSPOSE_DISPATCH(EB)                                                                           \
-  bool launch_transpose_eb##EB(const Plan& p, const TransposeArgs& ta, hipStream_t s) {                      \
-    const int vb = p.vb, tile = p.g.tile_bytes, nt = p.g.NT, ntm = p.g.ntm;                                  \
+  bool launch_transpose_eb##EB(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream) {   \
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);                                             \
+    const int vb = c.vb, tile = c.tile, nt = c.threads, ntm = c.ntm;                                         \
     constexpr int U = EB < 4 ? 4 : EB;                                                                       \
-    if (p.g.U != U) return false;                                                                            \
+    if (c.unit != U) return false;                                                                           \
     TC_CFG(EB, 16, U, 8192, 256) TC_CFG(EB, 16, U, 16384, 256) TC_CFG(EB, 16, U, 16384, 512)                  \
     TC_CFG(EB, 16, U, 32768, 256) TC_CFG(EB, 16, U, 32768, 512) TC_CFG(EB, 16, U, 65536, 256)                 \
     TC_CFG(EB, 16, U, 65536, 512)                                                                            \
@@ -219,6 +226,6 @@ bool launch_transpose_eb16(const Plan& p, const TransposeArgs& ta, hipStream_t s
 
 #define TC_CFG(EB, VB, U, TILE, NT)                                                                          \
   if (vb == VB && tile == TILE && nt == NT) {                                                                \
-    if (ntm == 3) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 3>(ta, p.workgroups, s);             \
-    if (ntm == 0) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 0>(ta, p.workgroups, s);             \
+    if (ntm == 3) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 3>(ta, wgs, s);                      \
+    if (ntm == 0) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 0>(ta, wgs, s);                      \
   }

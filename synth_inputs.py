@@ -211,3 +211,30 @@ def scaled_2d(w: Workload, n: int, m: int) -> Workload:
 
 __all__ = [n for n in dir() if not n.startswith("_")]
 _row_major = _row_major
+
+
+def random_layouts(seed: int = 1234, count: int = 60):
+    """Random layout pairs: a permuted row-major source buffer, optionally sliced with steps of
+    2, into a destination that is row-major in another mode order.  Yields
+    (shape, src_stride, dst_stride, elem_bytes, src_elems)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(count):
+        rank = int(rng.integers(1, 6))
+        shape = tuple(int(x) for x in rng.integers(1, 9, size=rank) * rng.choice([1, 2, 4], size=rank))
+        eb = int(rng.choice([1, 2, 4, 8, 16]))
+        perm_s = rng.permutation(rank)
+        perm_d = rng.permutation(rank)
+        steps = rng.choice([1, 1, 1, 2], size=rank)
+        full = [shape[k] * steps[k] for k in range(rank)]
+        st_full = [0] * rank
+        acc = 1
+        for k in reversed(perm_s):
+            st_full[k] = acc
+            acc *= full[k]
+        s_stride = tuple(int(st_full[k] * steps[k]) for k in range(rank))
+        d_stride = [0] * rank
+        acc = 1
+        for k in reversed(perm_d):
+            d_stride[k] = acc
+            acc *= shape[k]
+        yield shape, s_stride, tuple(d_stride), eb, acc * int(np.prod(steps)) + 1

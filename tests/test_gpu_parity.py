@@ -88,7 +88,7 @@ def test_cfg5_slice_8192(dtype):
 @pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
 def test_cfg5_odd_8191x8190(dtype):
     plan = check_workload(SI.sweep_odd(dtype))
-    assert plan["declined"] == 1 and plan["path_name"].startswith("guarded")
+    assert plan["declined"] == 1 and plan["path_name"] == "transpose" and plan["unaligned"] == 1
 
 
 def test_cfg5_odd_strict_declines():
@@ -105,6 +105,25 @@ def test_cfg5_odd_strict_declines():
 # --- several tiles, ragged tails, every element width ----------------------------------------
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("n,m,soff,doff,batch", [(67, 45, 0, 0, 1), (65, 64, 0, 0, 1), (64, 65, 0, 0, 1),
+                                                 (131, 257, 0, 0, 1), (7, 3, 0, 0, 1), (300, 129, 0, 0, 1),
+                                                 (67, 45, 3, 5, 1), (67, 45, 0, 0, 3)])
+def test_transpose_unaligned(eb, n, m, soff, doff, batch):
+    """Extents with no aligned vector (or counts not divisible by 64): the transpose runs with
+    vectors at element alignment, element accesses where a vector would leave the copy."""
+    if batch == 1:
+        shape, ss, ds = (n, m), (m, 1), (1, n)
+    else:
+        shape, ss, ds = (batch, n, m), (n * m, m, 1), (n * m, 1, n)
+    p = L.tc_plan((shape, ss, soff), (shape, ds, doff), {1: L.TC_I8, 2: L.TC_BF16, 4: L.TC_F32, 8: L.TC_F64,
+                                                          16: L.TC_B128}[eb])
+    assert p["path_name"] == "transpose"
+    # 65 x 64 and 64 x 65 have an aligned 4-byte vector from 4-byte elements up
+    assert p["unaligned"] == (eb < 4 or (n, m) not in ((65, 64), (64, 65)))
+    _check(shape, ss, ds, eb, s_off=soff, d_off=doff, seed=n + m + eb, expect="transpose")
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("n,m", [(64, 64), (96, 272), (272, 48), (16, 1040), (1024, 16), (528, 400)])
 def test_transpose_small_ragged(eb, n, m):
     _check((n, m), (m, 1), (1, n), eb, seed=n * 7 + m + eb, expect="transpose")
@@ -115,11 +134,10 @@ def test_transpose_small_ragged(eb, n, m):
 def test_transpose_vector_widths(eb, n):
     """n x 64 tiles: the row extent admits 16-, 8- or 4-byte vectors only, or none."""
     plan = _check((n, 64), (64, 1), (1, n), eb, seed=n + eb)
-    if plan["path_name"] == "transpose":
+    assert plan["path_name"] == "transpose"
+    if not plan["unaligned"]:
         ve = plan["vec_bytes"] // eb
         assert n % ve == 0 and all(n % (v // eb) for v in (16, 8) if v > plan["vec_bytes"] and v >= eb)
-    else:
-        assert plan["path_name"] == "guarded_tile"
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
@@ -150,7 +168,8 @@ def test_identity_rows_and_roundtrip(eb):
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
 def test_guarded_paths(eb):
-    _check((67, 45), (45, 1), (1, 67), eb, seed=eb)                       # odd: guarded tile
+    _check((67, 45), (45, 1), (1, 67), eb, seed=eb, expect="transpose")  # odd: unaligned vectors
+    _check((67, 45), (45, 1), (1, 67), eb, seed=eb, flags=L.TC_FLAG_FORCE_GUARDED, expect="guarded_tile")
     _check((40, 30), (60, 2), (1, 40), eb, src_elems=60 * 40, seed=eb)   # strided source
     _check((7, 9), (9, 1), (9, 1), eb, seed=eb)                           # 63 elements: guarded rows
     _check((64, 64), (64, 1), (1, 64), eb, flags=L.TC_FLAG_FORCE_GUARDED, seed=eb, expect="guarded_tile")
@@ -193,28 +212,8 @@ def test_edge_cases():
 
 
 def test_random_layouts():
-    rng = np.random.default_rng(1234)
-    for case in range(60):
-        rank = int(rng.integers(1, 6))
-        shape = tuple(int(x) for x in rng.integers(1, 9, size=rank) * rng.choice([1, 2, 4], size=rank))
-        eb = int(rng.choice([1, 2, 4, 8, 16]))
-        # source: a permuted row-major buffer, optionally sliced with steps
-        perm_s = rng.permutation(rank)
-        perm_d = rng.permutation(rank)
-        steps = rng.choice([1, 1, 1, 2], size=rank)
-        full = [shape[k] * steps[k] for k in range(rank)]
-        st_full = [0] * rank
-        acc = 1
-        for k in reversed(perm_s):
-            st_full[k] = acc
-            acc *= full[k]
-        s_stride = tuple(int(st_full[k] * steps[k]) for k in range(rank))
-        d_stride = [0] * rank
-        acc = 1
-        for k in reversed(perm_d):
-            d_stride[k] = acc
-            acc *= shape[k]
-        _check(shape, s_stride, tuple(d_stride), eb, src_elems=acc * int(np.prod(steps)) + 1, seed=case)
+    for case, (shape, s_stride, d_stride, eb, src_elems) in enumerate(SI.random_layouts(1234, 60)):
+        _check(shape, s_stride, d_stride, eb, src_elems=src_elems, seed=case)
 
 
 def test_stream_ordering_on_side_stream():
@@ -228,3 +227,39 @@ def test_stream_ordering_on_side_stream():
     s.synchronize()
     want = oracle_copy(src_h, ((512, 512), (512, 1), 0), 512 * 512, ((512, 512), (1, 512), 0), 4)
     assert_same(dst.cpu().numpy(), want, 4, "side stream")
+
+
+def test_hip_graph_capture_and_replays():
+    """tile_copy can be captured in a graph (it allocates nothing and records no memset): the
+    captured transpose, permute and guarded copies replay correctly several times, with eager
+    work in between and new source values each time."""
+    import torch
+    w1 = SI.transpose2d(512, 768, dtype="float32")
+    w2 = SI.permute0213(b=2, h=4, s=64, d=32)
+    w3 = SI.sweep_odd("float16", 67, 45)
+    ws = [w1, w2, w3]
+    srcs = [torch.from_numpy(SI.make_source(w)).cuda() for w in ws]
+    dsts = [torch.full((SI.storage_elems(w, "dst") * w.eb,), 0xA5, dtype=torch.uint8, device="cuda") for w in ws]
+    lays = [(L.make_layout(w.src.shape, w.src.stride, w.src.offset), L.make_layout(w.dst.shape, w.dst.stride, w.dst.offset))
+            for w in ws]
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):  # plans are made (and cached) before capture
+        for w, a, b, (sl, dl) in zip(ws, srcs, dsts, lays):
+            L.tile_copy(a, sl, b, dl, L.DTYPE_BY_NAME[w.dtype], stream=s)
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for w, a, b, (sl, dl) in zip(ws, srcs, dsts, lays):
+            L.tile_copy(a, sl, b, dl, L.DTYPE_BY_NAME[w.dtype], stream=s)
+    for rep in range(4):
+        for i, w in enumerate(ws):  # new inputs and a fresh sentinel through eager work
+            srcs[i].copy_(torch.from_numpy(SI.make_values(w.dtype, "bits", srcs[i].numel() // w.eb, 100 + rep)).cuda())
+            dsts[i].fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for w, a, b in zip(ws, srcs, dsts):
+            want = oracle_copy(a.cpu().numpy(), (w.src.shape, w.src.stride, w.src.offset), SI.storage_elems(w, "dst"),
+                               (w.dst.shape, w.dst.stride, w.dst.offset), w.eb)
+            assert_same(b.cpu().numpy(), want, w.eb, f"graph replay {rep} {w.name}")
