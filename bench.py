@@ -194,7 +194,8 @@ def identity_workload(n: int = 1 << 28) -> SI.Workload:
 def sweep_workloads():
     ws = [SI.transpose2d(dtype="float32"), SI.transpose2d(dtype="bfloat16"), SI.permute0213()]
     ws += [SI.sweep_dense(dt) for dt in SI.SWEEP_DTYPES]
-    ws += [SI.sweep_slice("float16"), SI.sweep_odd("float16")]
+    ws += [SI.sweep_odd(dt) for dt in SI.SWEEP_DTYPES]
+    ws += [SI.sweep_slice("float16")]
     return ws
 
 

@@ -115,9 +115,18 @@ static TuneCfg tune_override() {
 
 // Defaults per element width: {tile bytes, threads, nontemporal mode, grid order}.  `batched` =
 // the destination-contiguous extent is shorter than one 128-byte run, so the tile is filled from
-// a batch mode (the scale-factor case).
-static TuneCfg default_cfg(int eb, bool batched) {
+// a batch mode (the scale-factor case).  `unaligned` = vectors at element alignment: there a
+// destination cache line is shared by two tiles, and nontemporal stores of such partial lines
+// were measured 1.5-2x slower than plain ones, as were large tiles.
+static TuneCfg default_cfg(int eb, bool batched, bool unaligned) {
   TuneCfg c;
+  if (unaligned) {
+    c.tile = eb == 2 ? 8192 : 16384;
+    c.threads = eb == 2 ? 256 : 512;
+    c.nt = 0;
+    c.order = 0;
+    return c;
+  }
   if (batched) { c.tile = 8192; c.threads = 256; c.nt = 3; c.order = 0; return c; }
   switch (eb) {
     case 1: c.tile = 65536; c.threads = 512; c.nt = 3; c.order = 1; break;
@@ -216,7 +225,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   const Mode& R = j.m[p->mode_r];
   const Mode& C = j.m[p->mode_c];
   const bool batched = pow2ceil(R.e) * p->eb < 128;
-  TuneCfg cfg = default_cfg(p->eb, batched);
+  TuneCfg cfg = default_cfg(p->eb, batched, p->unaligned);
   const TuneCfg ov = tune_override();
   if (ov.tile) cfg.tile = ov.tile;
   if (ov.threads) cfg.threads = ov.threads;
