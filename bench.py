@@ -195,7 +195,7 @@ def sweep_workloads():
     ws = [SI.transpose2d(dtype="float32"), SI.transpose2d(dtype="bfloat16"), SI.permute0213()]
     ws += [SI.sweep_dense(dt) for dt in SI.SWEEP_DTYPES]
     ws += [SI.sweep_odd(dt) for dt in SI.SWEEP_DTYPES]
-    ws += [SI.sweep_slice("float16")]
+    ws += [SI.sweep_slice(dt) for dt in SI.SWEEP_DTYPES]
     return ws
 
 

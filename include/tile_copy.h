@@ -127,7 +127,8 @@ typedef struct tc_plan_info {
   int32_t load_outer;       /* accesses per thread in the load phase (global -> LDS/regs) */
   int32_t store_outer;      /* accesses per thread in the store phase (LDS/regs -> global) */
   /* tile (transpose paths): index of the modes and tile extents in elements */
-  int32_t mode_r, mode_c, mode_b; /* dst-contiguous mode, src-contiguous mode, batch mode (-1 none) */
+  int32_t mode_r, mode_c, mode_b; /* dst-contiguous mode, src-contiguous (or stride-2) mode, batch
+                                     mode (-1 none) */
   int32_t tile_r, tile_c, tile_b;
   int64_t workgroups;       /* workgroups launched */
   int32_t lds_bytes;        /* LDS per workgroup */
@@ -139,6 +140,8 @@ typedef struct tc_plan_info {
   int32_t nontemporal;      /* nontemporal global accesses: bit 0 loads, bit 1 stores */
   int32_t unaligned;        /* 1: declined split run by the transpose kernel with 16-byte vectors at
                                element alignment and element accesses at the edges of the copy */
+  int32_t src_step;         /* transpose: source stride of mode_c, 1 or 2 (2: each vector read as two
+                               contiguous ones and compacted); 0 on the other paths */
   int32_t lds_write_bytes, lds_read_bytes;       /* LDS instruction widths */
   int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
   char reason[192];         /* why the fast path was declined ("" if it was not) */

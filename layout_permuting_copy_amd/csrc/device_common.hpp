@@ -53,6 +53,11 @@ __device__ __forceinline__ void store_words(unsigned char* p, const uint32_t* w)
   }
 }
 
+// v_perm_b32: byte i of the result is byte sel.i of {hi:lo} (0-3 from lo, 4-7 from hi).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
 // Global accesses of N bytes (N = 4, 8, 16).  NTM bit 0: nontemporal loads, bit 1: nontemporal
 // stores (streaming data that is read or written once).
 template <int N, int NTM>
@@ -83,23 +88,49 @@ __device__ __forceinline__ void gstore(unsigned char* p, const uint32_t* w) {
   }
 }
 
-// The first n (0 < n <= VB/EB) elements of a VB-byte vector, one element access each (the
-// vector reaches past an extent of the copy); the other bytes of w are zero.
-template <int EB, int VB>
+// The first n (0 < n <= VB/EB) elements of a VB-byte vector whose elements lie S elements apart
+// in memory, one element access each (the vector reaches past an extent of the copy, or is the
+// last of a strided row); the other bytes of w are zero.
+template <int EB, int VB, int S = 1>
 __device__ __forceinline__ void gload_partial(const unsigned char* p, int n, uint32_t* w) {
 #pragma unroll
   for (int k = 0; k < VB / 4; ++k) w[k] = 0;
 #pragma unroll
   for (int e = 0; e < VB / EB; ++e) {
     if (e < n) {
+      const unsigned char* q = p + e * S * EB;
       if constexpr (EB >= 4) {
 #pragma unroll
-        for (int m = 0; m < EB / 4; ++m) w[e * (EB / 4) + m] = reinterpret_cast<const uint32_t*>(p + e * EB)[m];
+        for (int m = 0; m < EB / 4; ++m) w[e * (EB / 4) + m] = reinterpret_cast<const uint32_t*>(q)[m];
       } else if constexpr (EB == 2) {
-        w[e / 2] |= uint32_t(*reinterpret_cast<const uint16_t*>(p + 2 * e)) << (16 * (e & 1));
+        w[e / 2] |= uint32_t(*reinterpret_cast<const uint16_t*>(q)) << (16 * (e & 1));
       } else {
-        w[e / 4] |= uint32_t(p[e]) << (8 * (e & 3));
+        w[e / 4] |= uint32_t(*q) << (8 * (e & 3));
       }
+    }
+  }
+}
+
+// A VB-byte vector of elements S apart in memory (S = 1 or 2).  S = 2: the 2*VB contiguous bytes
+// from p are loaded as two vectors and every other element kept (v_perm_b32 for 1- and 2-byte
+// elements, dword selection for wider ones); the caller guarantees that those bytes lie inside
+// the source allocation (they end before the row's next element).  A one-element vector is a
+// single load at any S.
+template <int EB, int VB, int S, int NTM>
+__device__ __forceinline__ void gload_step(const unsigned char* p, uint32_t* w) {
+  if constexpr (S == 1 || VB == EB) {
+    gload<VB, NTM>(p, w);
+  } else {
+    static_assert(S == 2, "source step 1 or 2");
+    uint32_t a[2 * (VB / 4)];
+    gload<VB, NTM>(p, a);
+    gload<VB, NTM>(p + VB, a + VB / 4);
+#pragma unroll
+    for (int k = 0; k < VB / 4; ++k) {
+      if constexpr (EB == 1) w[k] = perm(a[2 * k + 1], a[2 * k], 0x06040200u);
+      else if constexpr (EB == 2) w[k] = perm(a[2 * k + 1], a[2 * k], 0x05040100u);
+      else if constexpr (EB == 4) w[k] = a[2 * k];
+      else w[k] = a[4 * (k / 2) + (k & 1)];  // EB == 8: dwords 0, 1 of every 16 bytes
     }
   }
 }
@@ -131,11 +162,6 @@ template <typename V, int NTM>
 __device__ __forceinline__ void gstore_v(V* p, V v) {
   if constexpr (NTM & 2) __builtin_nontemporal_store(v, p);
   else *p = v;
-}
-
-// v_perm_b32: byte i of the result is byte sel.i of {hi:lo} (0-3 from lo, 4-7 from hi).
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
 __device__ __forceinline__ uint32_t udiv(uint32_t n, const Div32& d) {

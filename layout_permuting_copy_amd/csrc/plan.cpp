@@ -200,24 +200,28 @@ static bool search_swizzle(const TileGeom& g, bool no_swizzle, TileGeom* out, in
   static std::map<std::array<int, 10>, Found> memo;
   const std::array<int, 10> key{g.eb, g.vb, g.U, g.TR, g.TC, g.NB, g.NT, g.tile_bytes, g.ntm * 8 + g.order,
                                 no_swizzle ? 1 : 0};
+  // the swizzle fields only: the rest of the geometry is the caller's
+  auto apply = [&](const Found& f) {
+    *out = g;
+    out->k = f.g.k;
+    out->shift = f.g.shift;
+    out->tbit = f.g.tbit;
+    out->cshift = f.g.cshift;
+    out->cmask = f.g.cmask;
+    *out_w = f.w;
+    *out_r = f.r;
+    return f.any;
+  };
   {
     std::lock_guard<std::mutex> lock(mu);
     auto it = memo.find(key);
-    if (it != memo.end()) {
-      *out = it->second.g;
-      *out_w = it->second.w;
-      *out_r = it->second.r;
-      return it->second.any;
-    }
+    if (it != memo.end()) return apply(it->second);
   }
   Found f{false, g, 0, 0};
   f.any = search_swizzle_uncached(g, no_swizzle, &f.g, &f.w, &f.r);
   std::lock_guard<std::mutex> lock(mu);
   memo.emplace(key, f);
-  *out = f.g;
-  *out_w = f.w;
-  *out_r = f.r;
-  return f.any;
+  return apply(f);
 }
 
 static bool plan_transpose_tile(Plan* p, int flags) {
@@ -241,7 +245,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   // the same tile with 256 threads, else 16 KiB tiles of 256 threads (every vector width)
   const int unit0 = ov.unit ? ov.unit : unit_min;
   auto instance = [&](int tile, int threads) {
-    return launch_transpose(p->eb, TransposeCfg{p->vb, unit0, tile, threads, cfg.nt}, nullptr, 0, nullptr);
+    return launch_transpose(p->eb, TransposeCfg{p->vb, unit0, tile, threads, cfg.nt, p->step}, nullptr, 0, nullptr);
   };
   if (!instance(cfg.tile, cfg.threads)) {
     if (instance(cfg.tile, 256)) {
@@ -273,6 +277,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
       g.tile_bytes = cfg.tile;
       g.ntm = cfg.nt;
       g.order = cfg.order;
+      g.step = p->step;
       if (unit < p->eb || unit < 4 || unit > p->vb) continue;
       const int ve = p->vb / p->eb;
       const int bmin = unit / p->eb;
@@ -293,7 +298,8 @@ static bool plan_transpose_tile(Plan* p, int flags) {
       if (dup || nseen >= 64) continue;
       seen[nseen][0] = g.TR; seen[nseen][1] = g.TC; seen[nseen][2] = g.NB; seen[nseen][3] = g.U; ++nseen;
       if (!finish_geom(&g)) continue;
-      if (!launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm}, nullptr, 0, nullptr)) continue;
+      if (!launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step}, nullptr, 0, nullptr))
+        continue;
       TileGeom c;
       int64_t wc, rc;
       if (!search_swizzle(g, flags & TC_FLAG_NO_SWIZZLE, &c, &wc, &rc)) continue;
@@ -438,13 +444,20 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     return p;
   }
 
-  // Declined by the aligned-vector rule, but both sides have a distinct unit-stride mode: the
-  // transpose kernel with 16-byte vectors at element alignment (gfx950 global memory takes
-  // unaligned vector accesses), whole vectors where the extents allow and element accesses at
-  // the edges of the copy.
-  if (!forced_guarded && r >= 0 && c >= 0 && r != c) {
+  // Declined by the aligned-vector rule, but the destination has a unit-stride mode and the
+  // source a distinct mode of stride 1 or 2: the transpose kernel with 16-byte vectors at element
+  // alignment (gfx950 global memory takes unaligned vector accesses), whole vectors where the
+  // extents allow and element accesses at the edges of the copy.  Along a stride-2 mode every
+  // vector is read as two contiguous ones (the elements in between are fetched and dropped).
+  int c2 = c;
+  if (c2 < 0 || c2 == r)
+    for (int k = 0; k < j.rank && (c2 < 0 || c2 == r); ++k)
+      if (k != r && j.m[k].s == 2) c2 = k;
+  if (!forced_guarded && r >= 0 && c2 >= 0 && r != c2) {
+    c = c2;
     p.vb = 16;
     p.unaligned = true;
+    p.step = int(j.m[c].s);
     p.path = TC_PATH_TRANSPOSE;
     p.mode_r = r;
     p.mode_c = c;
@@ -474,6 +487,7 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
       return p;
     }
     p.unaligned = false;
+    p.step = 1;
     p.reason = reason;
     p.declined = declined;
   }
@@ -523,6 +537,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
   info->rank = p.j.rank;
   info->declined = p.declined ? 1 : 0;
   info->unaligned = p.unaligned ? 1 : 0;
+  info->src_step = p.path == TC_PATH_TRANSPOSE ? p.step : 0;
   for (int k = 0; k < p.j.rank; ++k) {
     info->extent[k] = p.j.m[k].e;
     info->src_stride[k] = p.j.m[k].s;

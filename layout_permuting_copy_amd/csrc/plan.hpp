@@ -79,6 +79,8 @@ struct TileGeom {
   int tile_bytes = 16384;         // LDS tile per workgroup
   int ntm = 0;                    // nontemporal global accesses: bit 0 loads, bit 1 stores
   int order = 0;                  // grid order: 0 column tiles fastest, 1 row tiles fastest
+  int step = 1;                   // source element stride along the column mode (1, or 2: every
+                                  // vector read as two contiguous ones and compacted in registers)
   int loads = 4, stores = 4;  // accesses per thread per phase
   int ww = 16, rw = 4;        // LDS write / read instruction bytes
   int k = 0, shift = 0, tbit = 0;
@@ -109,6 +111,7 @@ struct Plan {
   int ntm = 0;                      // rows path: nontemporal global accesses (bit 0 loads, bit 1 stores)
   bool unaligned = false;           // transpose with vectors at element alignment (extents or strides
                                     // not multiples of the vector; edges element by element)
+  int step = 1;                     // source stride of the transpose's column mode (1 or 2)
   int mode_r = -1, mode_c = -1, mode_b = -1;
   TileGeom g;
   int threads = 0, load_outer = 0, store_outer = 0;
@@ -164,11 +167,11 @@ struct RowArgs {
 // ---- launch (kernels.hip) ------------------------------------------------------------------------
 int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::string* err);
 
-// A transpose kernel configuration: vector bytes, LDS unit bytes, tile bytes, threads and
-// nontemporal mode.  One launcher per element width holds the instances it was built with: it
+// A transpose kernel configuration: vector bytes, LDS unit bytes, tile bytes, threads,
+// nontemporal mode and source step.  One launcher per element width holds the instances it was built with: it
 // launches `ta` on `stream`, or with ta == nullptr only reports whether the instance exists.
 struct TransposeCfg {
-  int vb, unit, tile, threads, ntm;
+  int vb, unit, tile, threads, ntm, step;
 };
 bool launch_transpose_eb1(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
 bool launch_transpose_eb2(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);

@@ -42,8 +42,11 @@ struct TileRegs {
 };
 
 // Load phase of one tile: global -> registers.  GUARD (tile reaches past an extent): only
-// positions inside the copy are loaded; the registers of the others are never stored.
-template <int EB, int VB, typename G, int NT, int NTM, bool GUARD>
+// positions inside the copy are loaded; the registers of the others are never stored.  S: source
+// stride of the column mode (1, or 2: each vector is read as two contiguous ones, which stay
+// inside the allocation as long as the row's next element exists; the vector holding a row's
+// last element is loaded element by element).
+template <int EB, int VB, typename G, int NT, int NTM, int S, bool GUARD>
 __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& t, TileRegs<G>& r) {
   const int lTRu = a.lTR - G::LB;
   const int lnCV = a.lTC - G::LVE;  // load vectors per unit-row
@@ -55,7 +58,7 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
     const int cv = acc & ((1 << lnCV) - 1);
     const int ru = (acc >> lnCV) & (TRu - 1);
     const int nb = acc >> (lnCV + lTRu);
-    const int64_t off = t.sbase + nb * a.sB + (int64_t(ru) << G::LB) * sR + (cv << G::LVE);
+    const int64_t off = t.sbase + nb * a.sB + (int64_t(ru) << G::LB) * sR + (cv << G::LVE) * S;
     const unsigned char* p = a.src + off * EB;
     if constexpr (GUARD) {
       // whole vectors inside the copy load as one access (alignment is only the element's:
@@ -67,12 +70,13 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
 #pragma unroll
       for (int i = 0; i < G::B; ++i) {
         const bool in_row = in_b && (int64_t(ru) << G::LB) + i < t.remR && cols > 0;
-        if (in_row && cols >= G::VE) gload<VB, NTM>(p + i * sR * EB, r.w[f][i]);
-        else if (in_row) gload_partial<EB, VB>(p + i * sR * EB, int(cols), r.w[f][i]);
+        const bool whole = S == 1 ? cols >= G::VE : cols > G::VE;
+        if (in_row && whole) gload_step<EB, VB, S, NTM>(p + i * sR * EB, r.w[f][i]);
+        else if (in_row) gload_partial<EB, VB, S>(p + i * sR * EB, int(cols < G::VE ? cols : G::VE), r.w[f][i]);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < G::B; ++i) gload<VB, NTM>(p + i * sR * EB, r.w[f][i]);
+      for (int i = 0; i < G::B; ++i) gload_step<EB, VB, S, NTM>(p + i * sR * EB, r.w[f][i]);
     }
   }
 }
@@ -180,16 +184,17 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
 }
 
 // One tile per workgroup.  Interior tiles (the common case) take the unguarded path, which has
-// no per-lane conditions at all; tiles at the edges of the copy take the guarded one.
-template <int EB, int VB, int U, int TILE, int NT, int NTM>
+// no per-lane conditions at all; tiles at the edges of the copy take the guarded one (with S = 2
+// also the tiles holding a row's last element).
+template <int EB, int VB, int U, int TILE, int NT, int NTM, int S>
 __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   typedef Geo<EB, VB, U, TILE, NT> G;
   __shared__ __attribute__((aligned(16))) unsigned char lds[TILE];
   const TileAt t = tile_at(a, blockIdx.x);
   TileRegs<G> r;
-  const bool full = tile_full(a, t);
-  if (full) load_tile<EB, VB, G, NT, NTM, false>(a, t, r);
-  else load_tile<EB, VB, G, NT, NTM, true>(a, t, r);
+  const bool full = tile_full(a, t) && (S == 1 || t.remC > (int64_t(1) << a.lTC));
+  if (full) load_tile<EB, VB, G, NT, NTM, S, false>(a, t, r);
+  else load_tile<EB, VB, G, NT, NTM, S, true>(a, t, r);
   write_lds<EB, VB, U, G, NT>(a, lds, r);
   __syncthreads();
   if (full) read_store<EB, VB, U, G, NT, NTM, false>(a, t, lds);
@@ -197,10 +202,10 @@ __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
 }
 
 // Launches the instance (ta != nullptr) or only reports whether it exists (ta == nullptr).
-template <int EB, int VB, int U, int TILE, int NT, int NTM>
+template <int EB, int VB, int U, int TILE, int NT, int NTM, int S>
 bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
   if constexpr (Geo<EB, VB, U, TILE, NT>::valid) {
-    if (ta) hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM>), dim3(uint32_t(wgs)), dim3(NT), 0, s, *ta);
+    if (ta) hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM, S>), dim3(uint32_t(wgs)), dim3(NT), 0, s, *ta);
     return true;
   }
   return false;
@@ -210,7 +215,8 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 }  // namespace tc
 
 // Instantiation list of one element width: every (vector bytes, tile bytes, threads,
-// nontemporal mode) the planner can choose, with the smallest LDS unit.
+// nontemporal mode, source step) the planner can choose, with the smallest LDS unit.  Step 2
+// (strided sources) only in the configurations of the element-aligned plans.
 #define TC_TRANSPOSE_DISPATCH(EB)                                                                           \
   bool launch_transpose_eb##EB(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream) {   \
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);                                             \
@@ -221,11 +227,16 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
     TC_CFG(EB, 16, U, 32768, 256) TC_CFG(EB, 16, U, 32768, 512) TC_CFG(EB, 16, U, 65536, 256)                 \
     TC_CFG(EB, 16, U, 65536, 512)                                                                            \
     TC_CFG(EB, 8, U, 16384, 256) TC_CFG(EB, 4, U, 16384, 256)                                                \
+    TC_CFG_STEP2(EB, U, 8192, 256) TC_CFG_STEP2(EB, U, 16384, 256) TC_CFG_STEP2(EB, U, 16384, 512)             \
     return false;                                                                                            \
   }
 
 #define TC_CFG(EB, VB, U, TILE, NT)                                                                          \
-  if (vb == VB && tile == TILE && nt == NT) {                                                                \
-    if (ntm == 3) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 3>(ta, wgs, s);                      \
-    if (ntm == 0) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 0>(ta, wgs, s);                      \
+  if (vb == VB && tile == TILE && nt == NT && c.step == 1) {                                                 \
+    if (ntm == 3) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 3, 1>(ta, wgs, s);                   \
+    if (ntm == 0) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 0, 1>(ta, wgs, s);                   \
   }
+
+#define TC_CFG_STEP2(EB, U, TILE, NT)                                                                        \
+  if (vb == 16 && tile == TILE && nt == NT && c.step == 2 && ntm == 0)                                       \
+    return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, 2>(ta, wgs, s);

@@ -40,6 +40,7 @@ GROUPS = {"fetch": ["FETCH_SIZE"], "write": ["WRITE_SIZE"], "lds": ["SQ_LDS_BANK
 WORKLOADS = ["sf_transpose_65536x2x1x4x32_f32", "transpose_16384x16384_float32", "transpose_16384x16384_bfloat16",
              "transpose_8192x8192_int8", "transpose_8192x8192_float16", "transpose_8192x8192_float64",
              "transpose_8192x8192_int4vec", "transpose_8191x8190_float16", "transpose_8191x8190_int8",
+             "slice_8192x8192[1:8191:1,0:8190:2]_float16",
              "permute0213_32x32x2048x128_bfloat16", CALIBRATION]
 
 

@@ -82,7 +82,7 @@ def test_cfg5_dense_8192(dtype):
 @pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
 def test_cfg5_slice_8192(dtype):
     plan = check_workload(SI.sweep_slice(dtype))
-    assert plan["declined"] == 1 and plan["path_name"].startswith("guarded")
+    assert plan["declined"] == 1 and plan["path_name"] == "transpose" and plan["src_step"] == 2
 
 
 @pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
@@ -121,6 +121,22 @@ def test_transpose_unaligned(eb, n, m, soff, doff, batch):
     # 65 x 64 and 64 x 65 have an aligned 4-byte vector from 4-byte elements up
     assert p["unaligned"] == (eb < 4 or (n, m) not in ((65, 64), (64, 65)))
     _check(shape, ss, ds, eb, s_off=soff, d_off=doff, seed=n + m + eb, expect="transpose")
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("n,m,pitch,soff", [(40, 30, 60, 0), (129, 67, 140, 3), (64, 64, 128, 0), (33, 300, 601, 1),
+                                            (7, 5, 11, 0), (300, 257, 515, 2)])
+def test_transpose_stride2_source(eb, n, m, pitch, soff):
+    """Source columns two elements apart (a [.., ::2] slice): each vector is read as two
+    contiguous ones and compacted; a row's last vector element by element."""
+    p = _check((n, m), (pitch, 2), (1, n), eb, s_off=soff, seed=n * m + eb, expect="transpose")
+    assert p["src_step"] == 2
+
+
+def test_transpose_stride2_batched():
+    for eb in (1, 2, 4, 8, 16):
+        p = _check((3, 37, 45), (37 * 100, 100, 2), (37 * 45, 1, 37), eb, seed=eb, expect="transpose")
+        assert p["src_step"] == 2
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])

@@ -55,7 +55,7 @@ def test_abi_struct_layout_matches_header():
 
 def test_workload_paths_and_declines():
     expect = {"tile32x32_f32_roundtrip": "roundtrip", "sf_transpose": "transpose", "transpose_16384": "transpose",
-              "permute0213": "rows", "transpose_8192x8192": "transpose", "slice_": "guarded_tile",
+              "permute0213": "rows", "transpose_8192x8192": "transpose", "slice_": "transpose",
               "transpose_8191x8190": "transpose"}
     for w in SI.all_workloads():
         p = _plan(w)
@@ -66,7 +66,9 @@ def test_workload_paths_and_declines():
             assert p["write_conflicts"] == 0 and p["read_conflicts"] == 0, w.name
         declined = w.name.startswith(("slice_", "transpose_8191x8190"))
         assert p["declined"] == int(declined), w.name
-        assert p["unaligned"] == int(w.name.startswith("transpose_8191x8190")), w.name
+        assert p["unaligned"] == int(declined), w.name
+        # the stride-2 slice reads every vector as two contiguous ones
+        assert p["src_step"] == (2 if w.name.startswith("slice_") else 1 if p["path_name"] == "transpose" else 0)
         if declined:
             assert "not divisible by the thread count 64" in p["reason"]
             s = _plan(w, flags=L.TC_FLAG_STRICT)
