@@ -142,6 +142,8 @@ typedef struct tc_plan_info {
                                element alignment and element accesses at the edges of the copy */
   int32_t src_step;         /* transpose: source stride of mode_c, 1 or 2 (2: each vector read as two
                                contiguous ones and compacted); 0 on the other paths */
+  int32_t wave_local;       /* transpose: 1 if every wave reads back only LDS data it wrote itself,
+                               so the phases are ordered per wave instead of by a workgroup barrier */
   int32_t lds_write_bytes, lds_read_bytes;       /* LDS instruction widths */
   int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
   char reason[192];         /* why the fast path was declined ("" if it was not) */

@@ -10,6 +10,7 @@
 // Inside one such lane group a bank that must deliver n different dwords costs n - 1 extra
 // cycles; lanes asking for the same dword share it.
 #include <algorithm>
+#include <vector>
 
 #include "plan.hpp"
 
@@ -114,6 +115,26 @@ void simulate_tile(const TileGeom& g, int64_t* write_cycles, int64_t* read_cycle
 done:
   *write_cycles = wc;
   *read_cycles = rc;
+}
+
+bool tile_wave_local(const TileGeom& g) {
+  // owner wave of every LDS unit (by its unswizzled position: the swizzle is a bijection)
+  const int nCV = g.TC / g.VE, TRu = g.TRu(), RPV = g.RPV(), nRV = TRu / RPV;
+  std::vector<int> owner(size_t(g.NB) * TRu * g.TC, -1);
+  for (int f = 0; f < g.loads; ++f)
+    for (int t = 0; t < g.NT; ++t) {
+      const int a = f * g.NT + t;
+      const int cv = a % nCV, ru = (a / nCV) % TRu, nb = a / (nCV * TRu);
+      for (int j = 0; j < g.VE; ++j) owner[(size_t(nb) * TRu + ru) * g.TC + cv * g.VE + j] = t / kWave;
+    }
+  for (int f = 0; f < g.stores; ++f)
+    for (int t = 0; t < g.NT; ++t) {
+      const int a = f * g.NT + t;
+      const int rv = a % nRV, c = (a / nRV) % g.TC, nb = a / (nRV * g.TC);
+      for (int v = 0; v < RPV; ++v)
+        if (owner[(size_t(nb) * TRu + rv * RPV + v) * g.TC + c] != t / kWave) return false;
+    }
+  return true;
 }
 
 }  // namespace tc

@@ -164,6 +164,15 @@ __device__ __forceinline__ void gstore_v(V* p, V v) {
   else *p = v;
 }
 
+// Orders one wave's LDS writes before its later LDS reads (other lanes' data included): a wave's
+// LDS operations execute in issue order, so a wave-scope release/acquire pair around a wave
+// barrier (which keeps the compiler from moving accesses across it) is enough; no s_barrier.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ uint32_t udiv(uint32_t n, const Div32& d) {
   return uint32_t((uint64_t(__umulhi(n, d.mul)) + n) >> d.shr);
 }

@@ -79,9 +79,10 @@ static void decline(Plan* p, int flags, const std::string& why) {
 // Tile bytes, threads per workgroup and the nontemporal hint are chosen per element width from
 // measurements on MI355X (16384x16384 / 8192x8192 transposes and the batched 4x32 scale-factor
 // tiles, HIP-event timed, HBM-resident inputs).  TC_TUNE (environment, read once) overrides
-// them for tuning sweeps: "tile=32768,threads=512,nt=3,order=0,trb=128,unit=4".
+// them for tuning sweeps: "tile=32768,threads=512,nt=3,order=0,trb=128,unit=4,wl=0" (wl=0: keep the
+// workgroup barrier even where the phases are wave-local).
 struct TuneCfg {
-  int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0;
+  int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1;
 };
 
 static TuneCfg tune_override() {
@@ -105,6 +106,7 @@ static TuneCfg tune_override() {
         else if (k == "order") c.order = v;
         else if (k == "trb") c.trb = v;
         else if (k == "unit") c.unit = v;
+        else if (k == "wl") c.wl = v;
       }
       pos = end + 1;
     }
@@ -245,7 +247,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   // the same tile with 256 threads, else 16 KiB tiles of 256 threads (every vector width)
   const int unit0 = ov.unit ? ov.unit : unit_min;
   auto instance = [&](int tile, int threads) {
-    return launch_transpose(p->eb, TransposeCfg{p->vb, unit0, tile, threads, cfg.nt, p->step}, nullptr, 0, nullptr);
+    return launch_transpose(p->eb, TransposeCfg{p->vb, unit0, tile, threads, cfg.nt, p->step, false}, nullptr, 0, nullptr);
   };
   if (!instance(cfg.tile, cfg.threads)) {
     if (instance(cfg.tile, 256)) {
@@ -257,6 +259,13 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   }
   const int trb_list[] = {ov.trb ? ov.trb : 128, 256, 64};
   const int unit_list[] = {ov.unit ? ov.unit : unit_min};
+  // wave-local phases drop the workgroup barrier where the library holds such an instance
+  auto with_phase_order = [&](TileGeom g) {
+    g.wave_local = ov.wl != 0 && tile_wave_local(g) &&
+                   launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, true}, nullptr,
+                                    0, nullptr);
+    return g;
+  };
   bool have = false;
   TileGeom best;
   int64_t best_cost = -1, best_w = 0, best_r = 0;
@@ -298,7 +307,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
       if (dup || nseen >= 64) continue;
       seen[nseen][0] = g.TR; seen[nseen][1] = g.TC; seen[nseen][2] = g.NB; seen[nseen][3] = g.U; ++nseen;
       if (!finish_geom(&g)) continue;
-      if (!launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step}, nullptr, 0, nullptr))
+      if (!launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, false}, nullptr, 0, nullptr))
         continue;
       TileGeom c;
       int64_t wc, rc;
@@ -311,7 +320,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
         have = true;
       }
       if (wc + rc == 0) {
-        p->g = best;
+        p->g = with_phase_order(best);
         p->wconf = 0;
         p->rconf = 0;
         return true;
@@ -319,7 +328,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     }
   }
   if (!have) return false;
-  p->g = best;
+  p->g = with_phase_order(best);
   p->wconf = best_w;
   p->rconf = best_r;
   if (best_cost > 0)
@@ -538,6 +547,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
   info->declined = p.declined ? 1 : 0;
   info->unaligned = p.unaligned ? 1 : 0;
   info->src_step = p.path == TC_PATH_TRANSPOSE ? p.step : 0;
+  info->wave_local = p.path == TC_PATH_TRANSPOSE && p.g.wave_local ? 1 : 0;
   for (int k = 0; k < p.j.rank; ++k) {
     info->extent[k] = p.j.m[k].e;
     info->src_stride[k] = p.j.m[k].s;

@@ -81,6 +81,8 @@ struct TileGeom {
   int order = 0;                  // grid order: 0 column tiles fastest, 1 row tiles fastest
   int step = 1;                   // source element stride along the column mode (1, or 2: every
                                   // vector read as two contiguous ones and compacted in registers)
+  bool wave_local = false;        // every wave reads back only LDS units it wrote itself: the
+                                  // phases are ordered per wave, without a workgroup barrier
   int loads = 4, stores = 4;  // accesses per thread per phase
   int ww = 16, rw = 4;        // LDS write / read instruction bytes
   int k = 0, shift = 0, tbit = 0;
@@ -97,6 +99,9 @@ struct TileGeom {
 };
 // Fill loads/stores/ww/rw/U/B/VE from eb, vb, TR, TC, NB.  False if the geometry is invalid.
 bool finish_geom(TileGeom* g);
+// Whether every LDS unit a wave reads in the store phase was written by the same wave in the
+// load phase (then no workgroup barrier is needed between the phases).
+bool tile_wave_local(const TileGeom& g);
 // Simulated extra LDS cycles of one interior tile: write phase and read phase.  With limit >= 0
 // the simulation stops once write + read cycles reach the limit (the counts are then partial).
 void simulate_tile(const TileGeom& g, int64_t* write_cycles, int64_t* read_cycles, int64_t limit = -1);
@@ -168,10 +173,11 @@ struct RowArgs {
 int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::string* err);
 
 // A transpose kernel configuration: vector bytes, LDS unit bytes, tile bytes, threads,
-// nontemporal mode and source step.  One launcher per element width holds the instances it was built with: it
+// nontemporal mode, source step and wave-local phase ordering.  One launcher per element width holds the instances it was built with: it
 // launches `ta` on `stream`, or with ta == nullptr only reports whether the instance exists.
 struct TransposeCfg {
   int vb, unit, tile, threads, ntm, step;
+  bool wave_local;
 };
 bool launch_transpose_eb1(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
 bool launch_transpose_eb2(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);

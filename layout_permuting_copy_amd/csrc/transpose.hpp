@@ -185,8 +185,10 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
 
 // One tile per workgroup.  Interior tiles (the common case) take the unguarded path, which has
 // no per-lane conditions at all; tiles at the edges of the copy take the guarded one (with S = 2
-// also the tiles holding a row's last element).
-template <int EB, int VB, int U, int TILE, int NT, int NTM, int S>
+// also the tiles holding a row's last element).  WL: the planner has shown that every wave reads
+// back only LDS units it wrote itself, so the phases are ordered per wave and the waves of the
+// workgroup never wait for each other.
+template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL>
 __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   typedef Geo<EB, VB, U, TILE, NT> G;
   __shared__ __attribute__((aligned(16))) unsigned char lds[TILE];
@@ -196,16 +198,18 @@ __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   if (full) load_tile<EB, VB, G, NT, NTM, S, false>(a, t, r);
   else load_tile<EB, VB, G, NT, NTM, S, true>(a, t, r);
   write_lds<EB, VB, U, G, NT>(a, lds, r);
-  __syncthreads();
+  if constexpr (WL) wave_lds_sync();
+  else __syncthreads();
   if (full) read_store<EB, VB, U, G, NT, NTM, false>(a, t, lds);
   else read_store<EB, VB, U, G, NT, NTM, true>(a, t, lds);
 }
 
 // Launches the instance (ta != nullptr) or only reports whether it exists (ta == nullptr).
-template <int EB, int VB, int U, int TILE, int NT, int NTM, int S>
+template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL = false>
 bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
   if constexpr (Geo<EB, VB, U, TILE, NT>::valid) {
-    if (ta) hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM, S>), dim3(uint32_t(wgs)), dim3(NT), 0, s, *ta);
+    if (ta)
+      hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM, S, WL>), dim3(uint32_t(wgs)), dim3(NT), 0, s, *ta);
     return true;
   }
   return false;
@@ -215,8 +219,9 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 }  // namespace tc
 
 // Instantiation list of one element width: every (vector bytes, tile bytes, threads,
-// nontemporal mode, source step) the planner can choose, with the smallest LDS unit.  Step 2
-// (strided sources) only in the configurations of the element-aligned plans.
+// nontemporal mode, source step, phase ordering) the planner can choose, with the smallest LDS
+// unit.  Step 2 (strided sources) only in the configurations of the element-aligned plans;
+// wave-local ordering in the small batched tiles, where it occurs.
 #define TC_TRANSPOSE_DISPATCH(EB)                                                                           \
   bool launch_transpose_eb##EB(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream) {   \
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);                                             \
@@ -228,15 +233,20 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
     TC_CFG(EB, 16, U, 65536, 512)                                                                            \
     TC_CFG(EB, 8, U, 16384, 256) TC_CFG(EB, 4, U, 16384, 256)                                                \
     TC_CFG_STEP2(EB, U, 8192, 256) TC_CFG_STEP2(EB, U, 16384, 256) TC_CFG_STEP2(EB, U, 16384, 512)             \
+    TC_CFG_WL(EB, U, 8192, 256) TC_CFG_WL(EB, U, 16384, 256)                                                 \
     return false;                                                                                            \
   }
 
 #define TC_CFG(EB, VB, U, TILE, NT)                                                                          \
-  if (vb == VB && tile == TILE && nt == NT && c.step == 1) {                                                 \
+  if (vb == VB && tile == TILE && nt == NT && c.step == 1 && !c.wave_local) {                                \
     if (ntm == 3) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 3, 1>(ta, wgs, s);                   \
     if (ntm == 0) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 0, 1>(ta, wgs, s);                   \
   }
 
 #define TC_CFG_STEP2(EB, U, TILE, NT)                                                                        \
-  if (vb == 16 && tile == TILE && nt == NT && c.step == 2 && ntm == 0)                                       \
+  if (vb == 16 && tile == TILE && nt == NT && c.step == 2 && ntm == 0 && !c.wave_local)                      \
     return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, 2>(ta, wgs, s);
+
+#define TC_CFG_WL(EB, U, TILE, NT)                                                                           \
+  if (vb == 16 && tile == TILE && nt == NT && c.step == 1 && ntm == 3 && c.wave_local)                       \
+    return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 3, 1, true>(ta, wgs, s);

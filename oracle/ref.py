@@ -489,6 +489,26 @@ def _tile_instructions(eb, vb, TR, TC, NB, NT, U=None):
     return out
 
 
+def tile_wave_local(eb, vb, TR, TC, NB, NT, U=None, wave=64):
+    """Whether every LDS unit a wave reads in the store phase was written by that same wave in the
+    load phase, under the two TileLang partitions of the tile (then the phases need no
+    workgroup-wide barrier, only ordering within each wave).  Positions are logical (nb, row
+    unit, column): an XOR swizzle permutes addresses one to one and does not change the answer."""
+    U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB, U)
+    owner = {}
+    for op, width, lanes in _tile_instructions(eb, vb, TR, TC, NB, NT, U):
+        if op == "write":
+            for t, (nb, ru, c) in lanes.items():
+                for u in range(CW):
+                    owner[(nb, ru, c + u)] = t // wave
+    for op, width, lanes in _tile_instructions(eb, vb, TR, TC, NB, NT, U):
+        if op == "read":
+            for t, pos in lanes.items():
+                if owner.get(pos) != t // wave:
+                    return False
+    return True
+
+
 _TILE_CACHE = {}
 
 

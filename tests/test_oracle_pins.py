@@ -372,6 +372,27 @@ def test_gfx950_model_matches_probe_measurements(oracle_lib):
     assert n == 84
 
 
+def test_tile_wave_locality_pins():
+    """Which waves own which LDS units follows from the two loop partitions by hand:
+    * the scale-factor 4x32 fp32 block: 8 loads of 16 bytes per row x 4 rows = 32 loads, and
+      32 columns x 1 store vector each = 32 stores, both in block-major order, so lanes 0-31
+      and 32-63 of every wave load and store the same two whole blocks -> wave-local;
+    * a 32x256 fp32 tile of 256 lanes: a wave loads one row per round (64 x 16 bytes), but its
+      first store round reads 8 columns x all 32 rows, rows loaded by all four waves -> not;
+    * one wave per workgroup is wave-local whatever the tile."""
+    from oracle import ref as R
+    assert R.tile_wave_local(4, 16, 4, 32, 16, 256)
+    assert not R.tile_wave_local(4, 16, 32, 256, 1, 256)
+    assert R.tile_wave_local(4, 16, 32, 256, 1, 64) and R.tile_wave_local(1, 16, 128, 128, 1, 64)
+    # 8-byte elements: a 4x32 block is 16 loads per row x 4 rows = 64 loads and 32 columns x 2
+    # store vectors = 64 stores, one whole block per wave and round -> wave-local; with 16
+    # columns per block it is 32 loads but 16 x 2 = 32 stores -> still whole blocks
+    assert R.tile_wave_local(8, 16, 4, 32, 8, 256) and R.tile_wave_local(8, 16, 4, 16, 16, 256)
+    # a 16x64 fp32 tile: 16 loads per row -> a wave loads 4 rows; a store vector covers 4 rows
+    # of a column, 4 vectors per column -> a wave stores 16 columns x all 16 rows -> not
+    assert not R.tile_wave_local(4, 16, 16, 64, 1, 256)
+
+
 def test_synthetic_inputs_are_seeded_and_shaped():
     w = SI.transpose2d(n=64, dtype="bfloat16")
     a, b = SI.make_source(w), SI.make_source(w)
