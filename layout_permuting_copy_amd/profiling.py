@@ -25,6 +25,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import subprocess
 import sys
 from collections import defaultdict
@@ -73,7 +74,7 @@ def _csv(path_glob):
 
 def counters_per_kernel(raw_dir):
     """{kernel name: {counter: mean over dispatches}} for the library's kernels (tc:: names)."""
-    rows = _csv(os.path.join(raw_dir, "**", "*counter_collection.csv"))
+    rows = _csv(os.path.join(glob.escape(raw_dir), "**", "*counter_collection.csv"))
     per = defaultdict(lambda: defaultdict(float))
     name = {}
     for r in rows:
@@ -88,6 +89,11 @@ def counters_per_kernel(raw_dir):
             out[name[d]][c].append(v)
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} | {"dispatches": len(next(iter(cs.values())))}
             for k, cs in out.items()}
+
+
+def file_stem(workload: str) -> str:
+    """A workload name as a portable file name (slice brackets, colons and commas become _)."""
+    return re.sub(r"[^A-Za-z0-9.-]+", "_", workload).strip("_")
 
 
 def short_kernel(name: str) -> str:
@@ -105,7 +111,7 @@ def collect(raw: str, out: str, quick: bool = False) -> None:
     log = _run(cmd, os.path.join(raw, "trace.log"), 600)
     line = next(l for l in log.splitlines() if l.startswith('{"metric"'))
     bench = json.loads(line)
-    stats = _csv(os.path.join(tdir, "**", "*kernel_stats.csv"))
+    stats = _csv(os.path.join(glob.escape(tdir), "**", "*kernel_stats.csv"))
     wl = bench["config"]["workload"]
     md = [f"# Kernel trace: {wl} (benchmark command)", "",
           "Command (repo root, library built):", "```", " ".join(cmd).replace(tdir, "<raw>/trace"), "```", "",
@@ -125,7 +131,7 @@ def collect(raw: str, out: str, quick: bool = False) -> None:
                    f"({alg / (avg * 1e-6) / 1e9 / 80:.1f}% of 8 TB/s); the benchmark's HIP-event figure also "
                    f"counts the dispatch gap between back-to-back launches "
                    f"({bench['roofline']['kernel_us_mean'] - avg:.2f} us per launch here)."]
-    with open(os.path.join(out, f"kernel_trace_{wl}.md"), "w") as f:
+    with open(os.path.join(out, f"kernel_trace_{file_stem(wl)}.md"), "w") as f:
         f.write("\n".join(md) + "\n")
     # 2. counter passes
     workloads = [wl, CALIBRATION] if quick else WORKLOADS
@@ -167,7 +173,7 @@ def collect(raw: str, out: str, quick: bool = False) -> None:
         hits, miss = r.get("TCC_HIT_sum"), r.get("TCC_MISS_sum")
         if hits is not None and miss:
             md.append(f"TCC hit rate: {100 * hits / (hits + miss):.1f}%.")
-        with open(os.path.join(out, f"counters_{w}.md"), "w") as f:
+        with open(os.path.join(out, f"counters_{file_stem(w)}.md"), "w") as f:
             f.write("\n".join(md) + "\n")
     with open(os.path.join(out, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
