@@ -227,6 +227,11 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);                                             \
     const int vb = c.vb, tile = c.tile, nt = c.threads, ntm = c.ntm;                                         \
     constexpr int U = EB < 4 ? 4 : EB;                                                                       \
+    if (c.unit == 16 && U != 16) {                                                                           \
+      TC_CFG_U16(EB, 16384, 256) TC_CFG_U16(EB, 32768, 256) TC_CFG_U16(EB, 65536, 256)                        \
+      TC_CFG_U16(EB, 32768, 512) TC_CFG_U16(EB, 65536, 512)                                                  \
+      return false;                                                                                          \
+    }                                                                                                        \
     if (c.unit != U) return false;                                                                           \
     TC_CFG(EB, 16, U, 8192, 256) TC_CFG(EB, 16, U, 16384, 256) TC_CFG(EB, 16, U, 16384, 512)                  \
     TC_CFG(EB, 16, U, 32768, 256) TC_CFG(EB, 16, U, 32768, 512) TC_CFG(EB, 16, U, 65536, 256)                 \
@@ -246,6 +251,13 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 #define TC_CFG_STEP2(EB, U, TILE, NT)                                                                        \
   if (vb == 16 && tile == TILE && nt == NT && c.step == 2 && ntm == 0 && !c.wave_local)                      \
     return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, 2>(ta, wgs, s);
+
+// 16-byte LDS units (16/EB rows of one column): tall tiles whose store lanes run down a column
+#define TC_CFG_U16(EB, TILE, NT)                                                                             \
+  if (vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local) {                                \
+    if (ntm == 3) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1>(ta, wgs, s);                  \
+    if (ntm == 0) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 0, 1>(ta, wgs, s);                  \
+  }
 
 #define TC_CFG_WL(EB, U, TILE, NT)                                                                           \
   if (vb == 16 && tile == TILE && nt == NT && c.step == 1 && ntm == 3 && c.wave_local)                       \
