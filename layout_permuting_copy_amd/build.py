@@ -1,6 +1,8 @@
 """Builds the tile-copy library for gfx950, in-tree: libtile_copy.so (C ABI declared in
 include/tile_copy.h) and the LDS bank probe (bin/lds_bank_probe)."""
+import json
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -17,6 +19,9 @@ ARCH = "--offload-arch=gfx950"
 # packed fp32 ops are disabled for all device code
 NO_PK = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# per-kernel register, scratch and occupancy figures, from the compiler's resource-usage remarks
+RESOURCES = os.path.join(BUILD, "kernel_resources.json")
+REMARK = ["-Rpass-analysis=kernel-resource-usage"]
 SOURCES = ["layout.cpp", "bank.cpp", "plan.cpp", "abi.cpp", "kernels.hip", "transpose_eb1.hip", "transpose_eb2.hip",
            "transpose_eb4.hip", "transpose_eb8.hip", "transpose_eb16.hip"]
 
@@ -29,17 +34,38 @@ def _run(cmd):
     return out
 
 
+def _resources(remarks: str) -> dict:
+    """{kernel: {"vgprs", "scratch_bytes", "occupancy"}} from kernel-resource-usage remarks."""
+    out, name = {}, None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            out[name] = {}
+            continue
+        m = re.search(r"remark:\s+(VGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]): (\d+)", line)
+        if m and name:
+            key = {"VGPRs": "vgprs", "ScratchSize [bytes/lane]": "scratch_bytes", "Occupancy [waves/SIMD]": "occupancy"}
+            out[name][key[m.group(1)]] = int(m.group(2))
+    return out
+
+
 def _compile(src, build_dir, extra):
     obj = os.path.join(build_dir, src + ".o")
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
-        cmd = [HIPCC, ARCH, *NO_PK, *COMMON, *extra, "-c", path, "-o", obj]
+        cmd = [HIPCC, ARCH, *NO_PK, *COMMON, *REMARK, *extra, "-c", path, "-o", obj]
     else:
         cmd = [HIPCC, *COMMON, *extra, "-c", path, "-o", obj]
     out = _run(cmd)
-    if out.strip():
-        print(out, file=sys.stderr)
-    return obj
+    res = _resources(out)
+    # drop the remarks and the source excerpts printed under them
+    rest = "\n".join(l for l in out.splitlines()
+                     if "kernel-resource-usage" not in l and not l.startswith("In file included from")
+                     and not re.match(r"\s*(\d+\s*)?\|", l))
+    if rest.strip():
+        print(rest, file=sys.stderr)
+    return obj, res
 
 
 def build(verbose: bool = False, extra=(), lib_path: str = LIB, with_probe: bool = True) -> str:
@@ -51,7 +77,13 @@ def build(verbose: bool = False, extra=(), lib_path: str = LIB, with_probe: bool
     os.makedirs(build_dir, exist_ok=True)
     os.makedirs(os.path.dirname(PROBE), exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
-        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
+        done = list(ex.map(lambda src: _compile(src, build_dir, extra), SOURCES))
+        objs = [o for o, _ in done]
+        resources = {}
+        for _, r in done:
+            resources.update(r)
+        with open(os.path.join(build_dir, "kernel_resources.json"), "w") as f:
+            json.dump(resources, f, indent=1, sort_keys=True)
         probe = None
         if with_probe:
             probe = ex.submit(_run, [HIPCC, ARCH, *NO_PK, "-O3", "-std=c++17",

@@ -227,28 +227,40 @@ static bool search_swizzle(const TileGeom& g, bool no_swizzle, TileGeom* out, in
 }
 
 // Tall tiles in row-tile-first grid order, where measured faster than the default shape: runs of
-// 1 KiB along the destination-contiguous mode and 128 bytes along the source-contiguous mode,
-// 16-byte LDS units (a store vector is one ds_read_b128), so that the workgroups running together
-// write whole destination columns.  On MI355X this beat the default tiles by 6-11% for 2-byte
-// elements (bf16 16384^2, fp16 8192^2) and by 9% for 16-byte elements (8192^2), and was no
-// better or worse for 1-, 4- and 8-byte ones.  `tiles64` = workgroups a 64 KiB tile would give.
-static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t tiles64_2b, TuneCfg* c) {
+// 1-2 KiB along the destination-contiguous mode and 128-256 bytes along the source-contiguous
+// mode, 16-byte LDS units (a store vector is one ds_read_b128), so that the workgroups running
+// together write whole destination columns.  On MI355X, against the default tiles: fp32 16384^2
+// 5700 -> 6250 GB/s, bf16 16384^2 5370 -> 5720, fp16 8192^2 4780 -> 5310, fp64 8192^2 5370 ->
+// 5780, 16-byte elements 8192^2 5520 -> 5950; no better for 1-byte elements.  64 KiB tiles where
+// they still give 8192 workgroups (`tiles64` counts them for the 64 KiB shape), else smaller.
+static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c) {
   c->nt = 3;
   c->order = 1;
   c->unit = 16;
-  if (eb == 16 && eR >= 64 && eC >= 8) {
-    c->tile = 8192; c->threads = 256; c->trb = 1024;  // 64 x 8 elements
-    return true;
+  auto tiles = [&](int64_t tr, int64_t tc) { return ceil_div(eR, tr) * ceil_div(eC, tc) * others; };
+  switch (eb) {
+    case 16:
+      if (eR < 64 || eC < 8) return false;
+      c->tile = 8192; c->threads = 256; c->trb = 1024;  // 64 x 8 elements
+      return true;
+    case 8:
+      if (eR < 128 || eC < 16) return false;
+      if (tiles(256, 32) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 2048; }  // 256 x 32
+      else { c->tile = 16384; c->threads = 256; c->trb = 1024; }                          // 128 x 16
+      return true;
+    case 4:
+      if (eR < 256 || eC < 32) return false;
+      if (tiles(256, 64) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 1024; }  // 256 x 64
+      else { c->tile = 32768; c->threads = 512; c->trb = 1024; }                         // 256 x 32
+      return true;
+    case 2:
+      if (eR < 256 || eC < 64) return false;
+      if (tiles(512, 64) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 1024; }  // 512 x 64
+      else { c->tile = 32768; c->threads = 256; c->trb = 512; }                          // 256 x 64
+      return true;
+    default:
+      return false;
   }
-  if (eb == 2 && eR >= 256 && eC >= 64) {
-    if (tiles64_2b >= 8192) {
-      c->tile = 65536; c->threads = 512; c->trb = 1024;  // 512 x 64 elements
-    } else {
-      c->tile = 32768; c->threads = 256; c->trb = 512;  // 256 x 64 elements
-    }
-    return true;
-  }
-  return false;
 }
 
 // The tile geometries of one configuration, in the candidate order of destination run length
@@ -355,8 +367,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   int ncand = 0;
   TuneCfg tall;
   const int64_t others = j.count / (R.e * C.e);
-  const int64_t tiles64_2b = ceil_div(R.e, 512) * ceil_div(C.e, 64) * others;
-  if (!pinned && !batched && !p->unaligned && p->vb == 16 && p->step == 1 && tall_cfg(p->eb, R.e, C.e, tiles64_2b, &tall))
+  if (!pinned && !batched && !p->unaligned && p->vb == 16 && p->step == 1 && tall_cfg(p->eb, R.e, C.e, others, &tall))
     cands[ncand++] = tall;
   cands[ncand++] = base;
   if (flags & TC_FLAG_NO_SWIZZLE) ncand = 1;  // the swizzle is measured on the default plan's tile

@@ -98,14 +98,26 @@ __device__ __forceinline__ void write_lds(const TransposeArgs& a, unsigned char*
     const int cv = acc & ((1 << lnCV) - 1);
     const int ru = (acc >> lnCV) & (TRu - 1);
     const int nb = acc >> (lnCV + lTRu);
-    uint32_t unit[G::UB / 4];
+    const int xr = ((ru >> xshift) & xmask) << xtbit;
+    const int row = (nb << lTRu) + ru;
     if constexpr (EB >= 4) {
+      // each write chunk straight from the loaded rows (a staging array here was kept in scratch)
       constexpr int DPE = EB / 4;  // dwords per element
 #pragma unroll
-      for (int j = 0; j < G::VE; ++j)
+      for (int q = 0; q < G::UB / G::WW; ++q) {
+        uint32_t chunk[G::WW / 4];
 #pragma unroll
-        for (int m = 0; m < UW; ++m) unit[j * UW + m] = r.w[f][m / DPE][j * DPE + m % DPE];
-    } else if constexpr (EB == 2) {
+        for (int uu = 0; uu < G::CW; ++uu)
+#pragma unroll
+          for (int m = 0; m < UW; ++m) chunk[uu * UW + m] = r.w[f][m / DPE][(q * G::CW + uu) * DPE + m % DPE];
+        const int ch = ((cv << G::LVE) >> G::LCW) + q;
+        const int chs = ch ^ xr ^ ((ch >> xcshift) & xcmask);
+        store_words<G::WW>(lds + ((row << a.lTC) + (chs << G::LCW)) * U, chunk);
+      }
+      continue;
+    }
+    uint32_t unit[G::UB / 4];
+    if constexpr (EB == 2) {
 #pragma unroll
       for (int m = 0; m < UW; ++m)
 #pragma unroll
@@ -128,8 +140,6 @@ __device__ __forceinline__ void write_lds(const TransposeArgs& a, unsigned char*
           unit[(4 * d + 3) * UW + m] = perm(q23, q01, 0x07060302u);
         }
     }
-    const int xr = ((ru >> xshift) & xmask) << xtbit;
-    const int row = (nb << lTRu) + ru;
 #pragma unroll
     for (int q = 0; q < G::UB / G::WW; ++q) {
       const int ch = ((cv << G::LVE) >> G::LCW) + q;
@@ -228,8 +238,13 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
     const int vb = c.vb, tile = c.tile, nt = c.threads, ntm = c.ntm;                                         \
     constexpr int U = EB < 4 ? 4 : EB;                                                                       \
     if (c.unit == 16 && U != 16) {                                                                           \
-      TC_CFG_U16(EB, 16384, 256) TC_CFG_U16(EB, 32768, 256) TC_CFG_U16(EB, 65536, 256)                        \
-      TC_CFG_U16(EB, 32768, 512) TC_CFG_U16(EB, 65536, 512)                                                  \
+      TC_CFG_UNIT(EB, 16, 16384, 256) TC_CFG_UNIT(EB, 16, 32768, 256) TC_CFG_UNIT(EB, 16, 65536, 256)         \
+      TC_CFG_UNIT(EB, 16, 32768, 512) TC_CFG_UNIT(EB, 16, 65536, 512)                                        \
+      return false;                                                                                          \
+    }                                                                                                        \
+    if (c.unit == 8 && U < 8) {                                                                              \
+      TC_CFG_UNIT(EB, 8, 16384, 256) TC_CFG_UNIT(EB, 8, 32768, 256) TC_CFG_UNIT(EB, 8, 65536, 256)            \
+      TC_CFG_UNIT(EB, 8, 32768, 512) TC_CFG_UNIT(EB, 8, 65536, 512)                                          \
       return false;                                                                                          \
     }                                                                                                        \
     if (c.unit != U) return false;                                                                           \
@@ -252,11 +267,11 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
   if (vb == 16 && tile == TILE && nt == NT && c.step == 2 && ntm == 0 && !c.wave_local)                      \
     return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, 2>(ta, wgs, s);
 
-// 16-byte LDS units (16/EB rows of one column): tall tiles whose store lanes run down a column
-#define TC_CFG_U16(EB, TILE, NT)                                                                             \
+// Wider LDS units (UNIT/EB rows of one column): tall tiles whose store lanes run down a column
+#define TC_CFG_UNIT(EB, UNIT, TILE, NT)                                                                      \
   if (vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local) {                                \
-    if (ntm == 3) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1>(ta, wgs, s);                  \
-    if (ntm == 0) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 0, 1>(ta, wgs, s);                  \
+    if (ntm == 3) return dev::launch_transpose_cfg<EB, 16, UNIT, TILE, NT, 3, 1>(ta, wgs, s);                \
+    if (ntm == 0) return dev::launch_transpose_cfg<EB, 16, UNIT, TILE, NT, 0, 1>(ta, wgs, s);                \
   }
 
 #define TC_CFG_WL(EB, U, TILE, NT)                                                                           \

@@ -139,12 +139,13 @@ def test_transpose_stride2_batched():
         assert p["src_step"] == 2
 
 
-@pytest.mark.parametrize("eb", [2, 16])
+@pytest.mark.parametrize("eb", [2, 4, 8, 16])
 @pytest.mark.parametrize("n,m", [(512, 128), (256, 64), (1024, 320), (768, 136), (64, 8)])
 def test_transpose_tall_tiles(eb, n, m):
-    """Tall tiles with 16-byte LDS units and row-tile-first order (2- and 16-byte elements)."""
-    if eb == 2 and m < 64:
-        pytest.skip("tall tiles start at 64 columns for 2-byte elements")
+    """Tall tiles with 16-byte LDS units and row-tile-first order (2- to 16-byte elements)."""
+    min_rows, min_cols = {2: (256, 64), 4: (256, 32), 8: (128, 16), 16: (64, 8)}[eb]
+    if n < min_rows or m < min_cols:
+        pytest.skip("below the extents where tall tiles are planned")
     p = _check((n, m), (m, 1), (1, n), eb, seed=n + 3 * m + eb, expect="transpose")
     assert p["lds_read_bytes"] == 16 and p["grid_order"] == 1
 

@@ -269,3 +269,16 @@ def test_every_plan_has_a_kernel_instance():
             assert cfg in TRANSPOSE_INSTANCES, (shape, ss, ds, eb, cfg)
             seen.add(cfg)
     assert len(seen) >= 5
+
+
+def test_no_kernel_uses_scratch_memory():
+    """Every kernel keeps its per-lane data in registers: the compiler reports no scratch (a
+    private array it cannot promote would turn into extra memory instructions per tile)."""
+    import json
+    path = os.path.join(ROOT, "layout_permuting_copy_amd", "_build", "kernel_resources.json")
+    if not os.path.exists(path):
+        pytest.skip("library not built by layout_permuting_copy_amd/build.py")
+    res = json.load(open(path))
+    kernels = {k: v for k, v in res.items() if "tc3dev" in k}
+    assert sum("transpose_kernel" in k for k in kernels) >= 50
+    assert not {k: v for k, v in kernels.items() if v.get("scratch_bytes", 0) != 0}
