@@ -367,7 +367,9 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   int ncand = 0;
   TuneCfg tall;
   const int64_t others = j.count / (R.e * C.e);
-  if (!pinned && !batched && !p->unaligned && p->vb == 16 && p->step == 1 && tall_cfg(p->eb, R.e, C.e, others, &tall))
+  // (element-aligned plans: only 16-byte elements gained, 4870 -> 5140 GB/s on 8191 x 8190)
+  if (!pinned && !batched && (!p->unaligned || p->eb == 16) && p->vb == 16 && p->step == 1 &&
+      tall_cfg(p->eb, R.e, C.e, others, &tall))
     cands[ncand++] = tall;
   cands[ncand++] = base;
   if (flags & TC_FLAG_NO_SWIZZLE) ncand = 1;  // the swizzle is measured on the default plan's tile
