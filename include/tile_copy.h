@@ -196,6 +196,38 @@ int tc_get_flags(void);
 int tc_layout_slice(const tc_layout* in, const int64_t* start, const int64_t* stop, const int64_t* step,
                     tc_layout* out);
 
+/*
+ * The bank plan of a wave-scope register-staged permute of an LDS tile (the device primitive
+ * tcd::wave_permute in tile_copy_dev.hpp), TVM TIRx docs, "permute_layout":
+ *   step 1 -- both layouts keep their logical mode order with unit modes dropped; neighbouring
+ *             modes merge where they are contiguous on both sides (the source is regrouped onto
+ *             the destination's shard); P = element count / 64 elements per lane;
+ *   step 2 -- for k = 0 .. log2 P (k = 0 only when P is not a power of two) and, for k > 0,
+ *             shift = 0 .. 6 - k ascending: lane l's element at step r is flat index
+ *             l + 64 * (r ^ ((l >> shift) & (2^k - 1))); the LDS accesses of all P steps are
+ *             simulated under gfx950's bank model (read phase through the source layout, write
+ *             phase through the destination layout, element-wide accesses) and the first
+ *             (k, shift) with no extra cycle in either phase is taken.
+ * Host only: no GPU is touched.  `out` (caller-owned) receives the canonical shard and the
+ * result.  On TC_E_DECLINED (the page's "fails if none") it still holds the first candidate with
+ * the fewest extra cycles, its counts and the reason, for callers that accept conflicts.
+ * Errors: TC_E_NULL, TC_E_RANK, TC_E_EXTENT, TC_E_DTYPE; TC_E_DECLINED when the count is not a
+ * multiple of 64 (no integer P) or no k is conflict-free in both phases; TC_E_RANGE when an
+ * offset needs more than 31 bits.
+ */
+typedef struct tc_permute_info {
+  int32_t rank;             /* canonical shard modes */
+  int32_t elements_per_lane;/* P */
+  int64_t extent[TC_MAX_RANK], src_stride[TC_MAX_RANK], dst_stride[TC_MAX_RANK];
+  int32_t k, shift, mask;   /* chosen swizzle (when declined: the cheapest candidate) */
+  int32_t reserved;
+  int64_t read_conflicts, write_conflicts; /* simulated extra cycles over the P steps */
+  char reason[192];         /* why it declined ("" otherwise) */
+} tc_permute_info;
+
+int tc_wave_permute_plan(const tc_layout* src_layout, const tc_layout* dst_layout, int dtype,
+                         tc_permute_info* out);
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int tc_version(void);
 

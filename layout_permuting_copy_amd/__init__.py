@@ -84,6 +84,25 @@ class TcPlanInfo(ctypes.Structure):
         return d
 
 
+class TcPermuteInfo(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("elements_per_lane", ctypes.c_int32),
+                ("extent", ctypes.c_int64 * TC_MAX_RANK), ("src_stride", ctypes.c_int64 * TC_MAX_RANK),
+                ("dst_stride", ctypes.c_int64 * TC_MAX_RANK), ("k", ctypes.c_int32), ("shift", ctypes.c_int32),
+                ("mask", ctypes.c_int32), ("reserved", ctypes.c_int32), ("read_conflicts", ctypes.c_int64),
+                ("write_conflicts", ctypes.c_int64), ("reason", ctypes.c_char * 192)]
+
+    def to_dict(self) -> dict:
+        d = {}
+        for name, _ in self._fields_:
+            v = getattr(self, name)
+            if name == "reason":
+                v = v.decode()
+            elif name in ("extent", "src_stride", "dst_stride"):
+                v = tuple(v[: self.rank])
+            d[name] = v
+        return d
+
+
 class TileCopyError(RuntimeError):
     def __init__(self, code: int, reason: str):
         super().__init__(f"{STATUS_NAMES.get(code, code)}: {reason}")
@@ -122,6 +141,8 @@ def load_library(path: str = LIB_PATH):
     lib.tc_layout_slice.restype = ctypes.c_int
     lib.tc_version.argtypes = []
     lib.tc_version.restype = ctypes.c_int
+    lib.tc_wave_permute_plan.argtypes = [P(TcLayout), P(TcLayout), ctypes.c_int, P(TcPermuteInfo)]
+    lib.tc_wave_permute_plan.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -247,6 +268,21 @@ def tc_layout_slice(layout: LayoutLike, start: Sequence[int], stop: Sequence[int
 
 def tc_version() -> int:
     return load_library().tc_version()
+
+
+def tc_wave_permute_plan(src_layout: LayoutLike, dst_layout: LayoutLike, dtype: int,
+                         raise_on_error: bool = True) -> dict:
+    """Host-only bank plan (k, shift, mask) of the wave-scope permute tcd::wave_permute."""
+    lib = load_library()
+    s, d = _as_layout(src_layout), _as_layout(dst_layout)
+    info = TcPermuteInfo()
+    rc = lib.tc_wave_permute_plan(ctypes.byref(s), ctypes.byref(d), int(dtype), ctypes.byref(info))
+    out = info.to_dict()
+    out["status"] = rc
+    out["error"] = tc_last_error() if rc != TC_OK else ""
+    if rc != TC_OK and raise_on_error:
+        raise TileCopyError(rc, out["error"])
+    return out
 
 
 def torch_dtype_code(torch_dtype) -> int:

@@ -13,6 +13,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtile_copy.so")
 PROBE = os.path.join(PKG, "bin", "lds_bank_probe")
+# example kernels of the device primitives (include/tile_copy_dev.hpp), with their own C ABI
+DEV_LIB = os.path.join(PKG, "libtile_copy_dev.so")
+DEV_SOURCES = ["dev_examples.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "--offload-arch=gfx950"
@@ -22,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "inclu
 # per-kernel register, scratch and occupancy figures, from the compiler's resource-usage remarks
 RESOURCES = os.path.join(BUILD, "kernel_resources.json")
 REMARK = ["-Rpass-analysis=kernel-resource-usage"]
-SOURCES = ["layout.cpp", "bank.cpp", "plan.cpp", "abi.cpp", "kernels.hip", "transpose_eb1.hip", "transpose_eb2.hip",
+SOURCES = ["layout.cpp", "bank.cpp", "plan.cpp", "permute.cpp", "abi.cpp", "kernels.hip", "transpose_eb1.hip", "transpose_eb2.hip",
            "transpose_eb4.hip", "transpose_eb8.hip", "transpose_eb16.hip"]
 
 
@@ -88,9 +91,18 @@ def build(verbose: bool = False, extra=(), lib_path: str = LIB, with_probe: bool
         if with_probe:
             probe = ex.submit(_run, [HIPCC, ARCH, *NO_PK, "-O3", "-std=c++17",
                                      os.path.join(CSRC, "probe", "lds_bank_probe.hip"), "-o", PROBE + ".tmp"])
+        dev = [ex.submit(_compile, src, build_dir, extra) for src in DEV_SOURCES] if lib_path == LIB else []
         tmp = lib_path + ".tmp"
         _run([HIPCC, ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
         os.replace(tmp, lib_path)
+        if dev:
+            dev_done = [f.result() for f in dev]
+            for _, r in dev_done:
+                resources.update(r)
+            with open(os.path.join(build_dir, "kernel_resources.json"), "w") as f:
+                json.dump(resources, f, indent=1, sort_keys=True)
+            _run([HIPCC, ARCH, "-shared", "-fPIC", *[o for o, _ in dev_done], "-o", DEV_LIB + ".tmp"])
+            os.replace(DEV_LIB + ".tmp", DEV_LIB)
         if probe is not None:
             probe.result()
             os.replace(PROBE + ".tmp", PROBE)

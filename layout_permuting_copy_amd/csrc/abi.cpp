@@ -55,6 +55,13 @@ int ptr_alignment(uintptr_t a, uintptr_t b) {
 
 }  // namespace
 
+namespace tc {
+int set_last_error(int code, const std::string& why) {
+  g_err = why;
+  return code;
+}
+}  // namespace tc
+
 extern "C" {
 
 int tile_copy_ex(const void* src, const tc_layout* src_layout, void* dst, const tc_layout* dst_layout, int dtype,

@@ -172,6 +172,11 @@ struct RowArgs {
 // ---- launch (kernels.hip) ------------------------------------------------------------------------
 int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::string* err);
 
+// Sets the calling thread's tc_last_error() text; returns `code`.
+int set_last_error(int code, const std::string& why);
+// The wave-scope permute's bank plan (tc_wave_permute_plan).
+int wave_permute_plan(const tc_layout& src, const tc_layout& dst, int dtype, tc_permute_info* out, std::string* err);
+
 // A transpose kernel configuration: vector bytes, LDS unit bytes, tile bytes, threads,
 // nontemporal mode, source step and wave-local phase ordering.  One launcher per element width holds the instances it was built with: it
 // launches `ta` on `stream`, or with ta == nullptr only reports whether the instance exists.

@@ -1,0 +1,65 @@
+"""ctypes binding of libtile_copy_dev.so: example kernels built on the device primitives of
+include/tile_copy_dev.hpp (argument marshalling only; every step runs in the HIP kernels)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import _ptr, _stream
+
+DEV_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtile_copy_dev.so")
+_dev = None
+
+
+def load_dev_library(path: str = DEV_LIB_PATH):
+    """Loads libtile_copy_dev.so; raises if it has not been built."""
+    global _dev
+    if _dev is not None:
+        return _dev
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python layout_permuting_copy_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    for name, args in [("tcd_ex_roundtrip32", [vp, vp, vp]), ("tcd_ex_permute_tiles", [vp, vp, i, i, i, i, vp]),
+                       ("tcd_ex_swizzled_transpose", [vp, vp, vp, i, i, vp]), ("tcd_ex_lane_copy", [vp, vp, vp]),
+                       ("tcd_ex_waves2_copy", [vp, vp, vp]), ("tcd_ex_plan", [i, ctypes.POINTER(ctypes.c_int)])]:
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = ctypes.c_int
+    _dev = lib
+    return lib
+
+
+def _ok(rc: int, what: str) -> None:
+    if rc != 0:
+        raise RuntimeError(f"{what}: HIP error {rc}")
+
+
+def roundtrip32(src, dst, stream=None) -> None:
+    _ok(load_dev_library().tcd_ex_roundtrip32(_ptr(src), _ptr(dst), _stream(stream)), "tcd_ex_roundtrip32")
+
+
+def permute_tiles(src, dst, ntiles: int, which: int, k: int, shift: int, stream=None) -> None:
+    _ok(load_dev_library().tcd_ex_permute_tiles(_ptr(src), _ptr(dst), int(ntiles), int(which), int(k), int(shift),
+                                                _stream(stream)), "tcd_ex_permute_tiles")
+
+
+def swizzled_transpose(src, dst, lds_dump, tiles_r: int, tiles_c: int, stream=None) -> None:
+    _ok(load_dev_library().tcd_ex_swizzled_transpose(_ptr(src), _ptr(dst), _ptr(lds_dump), int(tiles_r), int(tiles_c),
+                                                     _stream(stream)), "tcd_ex_swizzled_transpose")
+
+
+def lane_copy(src, dst, stream=None) -> None:
+    _ok(load_dev_library().tcd_ex_lane_copy(_ptr(src), _ptr(dst), _stream(stream)), "tcd_ex_lane_copy")
+
+
+def waves2_copy(src, dst, stream=None) -> None:
+    _ok(load_dev_library().tcd_ex_waves2_copy(_ptr(src), _ptr(dst), _stream(stream)), "tcd_ex_waves2_copy")
+
+
+def example_plan(which: int) -> dict:
+    """(vec, outer, exact) the example's copy compiled to (see tcd_ex_plan)."""
+    out = (ctypes.c_int * 3)()
+    if load_dev_library().tcd_ex_plan(int(which), out) != 0:
+        raise ValueError(f"no example plan {which}")
+    return {"vec": out[0], "outer": out[1], "exact": bool(out[2])}

@@ -366,6 +366,17 @@ def permute_shard(src_lay: Layout, dst_lay: Layout):
     return extent, tuple(s for _, s, _ in modes), tuple(d for _, _, d in modes), src_lay[2], dst_lay[2]
 
 
+def xor_swizzle(off: int, bits: int, base: int, shift: int) -> int:
+    """Element offset inside an XOR-swizzled shared layout (TVM TIRx "copy -> gmem_smem", closing
+    remarks: a swizzle wraps the shared side's layout and a vector never spans more than one
+    swizzle chunk).  The page does not print the function; the reading taken is the usual bit-field
+    XOR: a chunk is 2**base consecutive elements, and the chunk-index bits [base, base + bits) are
+    XORed with bits [base + shift, base + shift + bits) of the same offset (for a row of 2**shift
+    chunks, the chunk index within a row XOR the row index modulo 2**bits)."""
+    field = (off >> (base + shift)) & ((1 << bits) - 1)
+    return off ^ (field << base)
+
+
 def project(idx, st):
     return sum(i * s for i, s in zip(idx, st))
 

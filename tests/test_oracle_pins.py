@@ -402,3 +402,30 @@ def test_synthetic_inputs_are_seeded_and_shaped():
     # bfloat16 values are round-to-nearest-even of float32 normals
     f = np.array([1.0, 1.00390625, 1.01171875, -2.5], dtype=np.float32)
     assert list(SI._bf16_bits_from_f32(f)) == [0x3F80, 0x3F80, 0x3F82, 0xC020]
+
+
+def test_xor_swizzle_offsets_pins():
+    """The swizzled shared layout's offset function, checked by hand and by its properties:
+    64 x 64 elements, 8-element chunks (base 3), chunk index XOR row mod 8 (bits 3, shift 3)."""
+    from oracle import ref as R
+    # row 0 is unchanged; row 1 chunk 0 -> chunk 1; row 5 chunk 2 -> chunk 7; row 9 == row 1
+    assert [R.xor_swizzle(o, 3, 3, 3) for o in (0, 7, 64, 64 + 8 * 2 + 5, 5 * 64 + 2 * 8 + 3, 9 * 64)] == \
+        [0, 7, 72, 64 + 8 * 3 + 5, 5 * 64 + 7 * 8 + 3, 9 * 64 + 8]
+    image = [R.xor_swizzle(o, 3, 3, 3) for o in range(4096)]
+    assert sorted(image) == list(range(4096))  # a permutation of the tile
+    for o in range(0, 4096, 8):  # chunks stay whole and in their row
+        assert image[o] % 8 == 0 and image[o + 7] == image[o] + 7 and image[o] // 64 == o // 64
+    assert all(R.xor_swizzle(o, 0, 3, 3) == o for o in range(256))  # no bits: identity
+
+
+def test_wave64_permute_reproduces_page_result_on_4x64():
+    """At 64 lanes the page's printed plan (k, shift, mask) = (2, 3, 3) is the answer for the
+    4 x 64 fp32 tile, the wave64 counterpart of its 4 x 32 demo at 32 lanes; the 4 x 32 demo tile
+    itself has no conflict-free k on gfx950 (32-lane bank groups see only even rows of it)."""
+    from oracle import ref as R
+    m = R.gfx950_model()
+    ext, ss, ds, _, _ = R.permute_shard(R.layout((4, 64), (64, 1)), R.layout((4, 64), (1, 4)))
+    assert R.choose_xor_k(ext, ss, ds, 4, m) == (2, 3, 3)
+    ext, ss, ds, _, _ = R.permute_shard(R.layout((2, 1, 4, 32), (128, 128, 32, 1)), R.layout((2, 1, 4, 32), (128, 128, 1, 4)))
+    assert R.choose_xor_k(ext, ss, ds, 4, m) is None
+    assert R.permute_conflicts(ext, ss, ds, 4, 0, 0, m) == (0, 24)
