@@ -187,6 +187,48 @@ def time_memcpy(torch, nbytes: int = 1 << 30, steps: int = 30):
             "pct_peak_kernel": 100 * 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
+def time_device_permute(torch, tiles: int = 65536, steps: int = 30, seed: int = 21):
+    """Context row: the SF transpose done with the device primitives instead (tcd::g2s,
+    tcd::wave_permute in place, tcd::s2g; one wave per 4x32 block pair), rotating buffer pairs;
+    a sample of its tiles is checked against the oracle."""
+    import layout_permuting_copy_amd as L
+    import layout_permuting_copy_amd.dev as D
+    from oracle import ref as R
+    sl, dl = ((2, 1, 4, 32), (128, 128, 32, 1)), ((2, 1, 4, 32), (128, 128, 1, 4))
+    plan = L.tc_wave_permute_plan(sl, dl, L.TC_F32, raise_on_error=False)  # declines: the cheapest (k, shift)
+    k, shift = plan["k"], plan["shift"]
+    nbytes = tiles * 1024
+    pairs = max(2, -(-2 * MALL_BYTES // (2 * nbytes)) + 1)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    srcs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 256, generator=g) for _ in range(pairs)]
+    dsts = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(pairs)]
+    stream = torch.cuda.current_stream()
+    for i in range(3):
+        D.permute_tiles(srcs[i % pairs], dsts[i % pairs], tiles, 0, k, shift, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        D.permute_tiles(srcs[i % pairs], dsts[i % pairs], tiles, 0, k, shift, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    last = (steps - 1) % pairs
+    rng = np.random.default_rng(seed)
+    ok = True
+    for t in sorted(set(int(x) for x in rng.integers(0, tiles, 64)) | {0, tiles - 1}):
+        src_t = srcs[last][t * 1024:(t + 1) * 1024].cpu().numpy()
+        want = src_t.copy()
+        R.copy(src_t, R.layout(*sl), want, R.layout(*dl), 4)
+        ok = ok and bool(np.array_equal(dsts[last][t * 1024:(t + 1) * 1024].cpu().numpy(), want))
+    del srcs, dsts
+    return {"workload": "sf_transpose_65536x2x1x4x32_f32 via device primitives", "path": "tcd::wave_permute (context)",
+            "k": k, "shift": shift, "bytes_per_step": 2 * nbytes, "kernel_ms_mean": ms,
+            "gbs_kernel": 2 * nbytes / (ms * 1e-3) / 1e9, "pct_peak_kernel": 100 * 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "sampled_parity": ok}
+
+
 def identity_workload(n: int = 1 << 28) -> SI.Workload:
     return SI.Workload(f"identity_{n}_float32", SI.Side((n,), (1,)), SI.Side((n,), (1,)), "float32", "bits", 12)
 
@@ -239,6 +281,8 @@ def main() -> int:
     sweep = []
     if not args.no_sweep:
         sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in time_memcpy(torch).items()})
+        torch.cuda.empty_cache()
+        sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in time_device_permute(torch).items()})
         torch.cuda.empty_cache()
         for sw in [identity_workload()] + sweep_workloads():
             s = time_workload(torch, L, sw, 30, 3, seed=11)

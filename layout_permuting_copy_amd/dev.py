@@ -63,3 +63,55 @@ def example_plan(which: int) -> dict:
     if load_dev_library().tcd_ex_plan(int(which), out) != 0:
         raise ValueError(f"no example plan {which}")
     return {"vec": out[0], "outer": out[1], "exact": bool(out[2])}
+
+
+def _main(argv=None) -> int:
+    """python -m layout_permuting_copy_amd.dev permute --which W --k K --shift S --tiles N --reps R
+
+    Runs the in-place wave permute example R times on N tiles of random bits (rotating buffer
+    pairs, so that the MALL does not serve them) and prints one JSON line with the mean kernel time
+    (HIP events on the launch stream around the back-to-back launches) and the global bytes moved."""
+    import argparse
+    import json
+
+    import torch
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("what", choices=["permute"])
+    ap.add_argument("--which", type=int, default=1)
+    ap.add_argument("--k", type=int, default=0)
+    ap.add_argument("--shift", type=int, default=0)
+    ap.add_argument("--tiles", type=int, default=65536)
+    ap.add_argument("--reps", type=int, default=20)
+    a = ap.parse_args(argv)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        return 2
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    # rotate buffer pairs so that more than twice the 256 MB MALL is touched between reuses
+    pair = 2 * a.tiles * 1024
+    pairs = max(2, -(-(2 * (256 << 20)) // pair) + 1)
+    srcs, dsts = [], []
+    for _ in range(pairs):
+        srcs.append(torch.empty(a.tiles * 1024, dtype=torch.uint8, device="cuda"))
+        srcs[-1].random_(0, 256, generator=g)
+        dsts.append(torch.empty_like(srcs[-1]))
+    stream = torch.cuda.current_stream()
+    permute_tiles(srcs[0], dsts[0], a.tiles, a.which, a.k, a.shift, stream)  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(a.reps):
+        permute_tiles(srcs[i % pairs], dsts[i % pairs], a.tiles, a.which, a.k, a.shift, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / a.reps
+    moved = 2 * a.tiles * 1024
+    print(json.dumps({"what": "wave_permute", "which": a.which, "k": a.k, "shift": a.shift, "tiles": a.tiles,
+                      "kernel_us_mean": round(us, 3), "global_bytes": moved, "gbs": round(moved / (us * 1e-6) / 1e9, 1)}))
+    return 0
+
+
+if __name__ == "__main__":
+    import sys
+    sys.exit(_main())

@@ -45,12 +45,16 @@ WORKLOADS = ["sf_transpose_65536x2x1x4x32_f32", "transpose_16384x16384_float32",
              "permute0213_32x32x2048x128_bfloat16", CALIBRATION]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(paths=None) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
+    for path in paths or [os.path.join(CSRC, name) for name in KERNEL_SOURCES]:
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+# the device primitives and their example kernels (the wave permute's counters)
+DEV_SOURCES = (os.path.join(ROOT, "include", "tile_copy_dev.hpp"), os.path.join(CSRC, "dev_examples.hip"))
 
 
 def _run(cmd, log, timeout):
@@ -72,8 +76,9 @@ def _csv(path_glob):
         return list(csv.DictReader(f))
 
 
-def counters_per_kernel(raw_dir):
-    """{kernel name: {counter: mean over dispatches}} for the library's kernels (tc:: names)."""
+def counters_per_kernel(raw_dir, match="tc::"):
+    """{kernel name: {counter: mean over dispatches}} for the kernels whose name contains `match`
+    (default: the library's tc:: kernels)."""
     rows = _csv(os.path.join(glob.escape(raw_dir), "**", "*counter_collection.csv"))
     per = defaultdict(lambda: defaultdict(float))
     name = {}
@@ -83,7 +88,7 @@ def counters_per_kernel(raw_dir):
         name[d] = r["Kernel_Name"]
     out = defaultdict(lambda: defaultdict(list))
     for d, cs in per.items():
-        if "tc::" not in name[d]:
+        if match not in name[d]:
             continue
         for c, v in cs.items():
             out[name[d]][c].append(v)
@@ -180,13 +185,64 @@ def collect(raw: str, out: str, quick: bool = False) -> None:
     print(json.dumps({w: {k: v for k, v in d.items() if k != "kernel"} for w, d in traffic["workloads"].items()}))
 
 
+# (which tile, k, shift) of the wave permute example: 0 = the scale-factor tile (2,1,4,32),
+# 1 = the 4 x 64 transpose; the library's chooser takes (2, 3) for tile 1 and declines tile 0
+WAVE_PERMUTE_CASES = [(1, 0, 0), (1, 2, 3), (1, 1, 3), (0, 0, 0), (0, 1, 3), (0, 2, 3)]
+WAVE_PERMUTE_TILES = 65536
+
+
+def collect_wave_permute(raw: str, out: str) -> None:
+    """SQ_LDS_BANK_CONFLICT and SQ_INSTS_LDS per dispatch of the device wave permute example
+    (tcd::wave_permute in place on LDS tiles, one wave per tile), one counter pass per
+    (tile, k, shift), and its kernel time -> counters_wave_permute.md and wave_permute.json."""
+    os.makedirs(raw, exist_ok=True)
+    os.makedirs(out, exist_ok=True)
+    py = sys.executable or "python3"
+    rows, cmds = [], []
+    for which, k, shift in WAVE_PERMUTE_CASES:
+        d = os.path.join(raw, f"wp_{which}_{k}_{shift}")
+        args = ["-m", "layout_permuting_copy_amd.dev", "permute", "--which", str(which), "--k", str(k), "--shift",
+                str(shift), "--tiles", str(WAVE_PERMUTE_TILES)]
+        cmd = ["rocprofv3", "--pmc", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "--kernel-trace", "--output-format", "csv",
+               "-d", d, "-o", "run", "--", py, *args, "--reps", "3"]
+        _run(cmd, d + ".log", 120)
+        cmds.append(" ".join(cmd).replace(d, f"<raw>/wp_{which}_{k}_{shift}"))
+        cnt = next(iter(counters_per_kernel(d, match="permute_tiles").values()))
+        timing = _run([py, *args, "--reps", "20"], d + "_time.log", 120)
+        t = json.loads(next(l for l in timing.splitlines() if l.startswith("{")))
+        rows.append({"which": which, "k": k, "shift": shift, "tiles": WAVE_PERMUTE_TILES,
+                     "SQ_LDS_BANK_CONFLICT": cnt["SQ_LDS_BANK_CONFLICT"], "SQ_INSTS_LDS": cnt["SQ_INSTS_LDS"],
+                     "kernel_us_mean": t["kernel_us_mean"], "gbs": t["gbs"]})
+    with open(os.path.join(out, "wave_permute.json"), "w") as f:
+        json.dump({"device_source_hash": kernel_source_hash(DEV_SOURCES), "cases": rows}, f, indent=1)
+    md = ["# Counters: device wave permute (tcd::wave_permute, in place in LDS)", "",
+          f"{WAVE_PERMUTE_TILES} tiles of 256 fp32 per dispatch, one wave per tile, four waves per workgroup; "
+          "each tile is loaded (16-byte vectors), permuted in LDS, stored. Tile 0: the scale-factor tile "
+          "(2,1,4,32) strides (128,128,32,1) -> (128,128,1,4); tile 1: (4,64) strides (64,1) -> (1,4).", "",
+          "Commands (repo root, one pass each; the timing runs drop the rocprofv3 prefix and use --reps 20):",
+          "```", *cmds, "```", "",
+          "| tile | k | shift | SQ_LDS_BANK_CONFLICT / dispatch | per tile | SQ_INSTS_LDS / dispatch | kernel (us) | GB/s |",
+          "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        md.append(f"| {r['which']} | {r['k']} | {r['shift']} | {r['SQ_LDS_BANK_CONFLICT']:.0f} | "
+                  f"{r['SQ_LDS_BANK_CONFLICT'] / r['tiles']:.2f} | {r['SQ_INSTS_LDS']:.0f} | {r['kernel_us_mean']} | "
+                  f"{r['gbs']} |")
+    with open(os.path.join(out, "counters_wave_permute.md"), "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(rows))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof"))
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--quick", action="store_true", help="counters for the benchmark workload and calibration only")
+    ap.add_argument("--wave-permute", action="store_true", help="only the device wave permute's counters")
     args = ap.parse_args()
-    collect(args.raw, args.out, args.quick)
+    if args.wave_permute:
+        collect_wave_permute(args.raw, args.out)
+    else:
+        collect(args.raw, args.out, args.quick)
     return 0
 
 

@@ -185,3 +185,22 @@ def test_two_wave_guarded_copy():
     want = np.full(45 * 40 * 2 + 64, 0xA5, dtype=np.uint8)
     R.copy(src, R.layout((45, 40), (56, 1)), want, R.layout((45, 40), (40, 1)), 2)
     assert np.array_equal(d.cpu().numpy(), want)  # nothing written past the 1800 elements
+
+
+def test_wave_permute_hardware_counts_match_bank_model():
+    """The committed rocprofv3 counts of the device wave permute (SQ_LDS_BANK_CONFLICT per
+    dispatch, profiles/wave_permute.json) equal the oracle's simulated extra cycles per tile
+    times the tiles, for every (tile, k, shift) measured: the chooser's (2, 3) on the 4 x 64 tile
+    is conflict-free on the hardware, the others cost what the model predicts."""
+    import json
+    path = os.path.join(ROOT, "profiles", "wave_permute.json")
+    doc = json.load(open(path))
+    m = R.gfx950_model()
+    layouts = {0: (R.layout((2, 1, 4, 32), (128, 128, 32, 1)), R.layout((2, 1, 4, 32), (128, 128, 1, 4))),
+               1: (R.layout((4, 64), (64, 1)), R.layout((4, 64), (1, 4)))}
+    assert len(doc["cases"]) >= 6
+    for c in doc["cases"]:
+        ext, ss, ds, _, _ = R.permute_shard(*layouts[c["which"]])
+        per_tile = sum(R.permute_conflicts(ext, ss, ds, 4, c["k"], c["shift"], m))
+        assert c["SQ_LDS_BANK_CONFLICT"] == per_tile * c["tiles"], c
+    assert any(c["which"] == 1 and (c["k"], c["shift"]) == (2, 3) and c["SQ_LDS_BANK_CONFLICT"] == 0 for c in doc["cases"])
