@@ -91,7 +91,9 @@ enum tc_status {
 #define TC_FLAG_FORCE_REGS    0x04 /* co-contiguous copies: stage through registers only */
 #define TC_FLAG_FORCE_LDS     0x08 /* co-contiguous copies: stage through LDS */
 #define TC_FLAG_NO_SWIZZLE    0x10 /* transposes: no XOR swizzle (k = 0), to measure its effect */
-#define TC_FLAG_ALL           0x1f
+#define TC_FLAG_NO_SHUFFLE    0x20 /* small batched 4-row transposes: the LDS tile kernel instead
+                                      of the in-register butterfly, to measure its effect */
+#define TC_FLAG_ALL           0x3f
 
 /* Which kernel a plan runs. */
 enum tc_path {
@@ -103,7 +105,11 @@ enum tc_path {
   TC_PATH_ROUNDTRIP = 3,   /* co-contiguous and small: one workgroup, global -> LDS ->
                               global with the [outer, threads, vec] partition */
   TC_PATH_GUARDED_TILE = 4,/* fallback: LDS tile with element-wide accesses and guards */
-  TC_PATH_GUARDED_ROWS = 5 /* fallback: element-wise, destination order, guarded */
+  TC_PATH_GUARDED_ROWS = 5,/* fallback: element-wise, destination order, guarded */
+  TC_PATH_SHUFFLE = 6      /* batches of 4 x C blocks of 4-byte elements (C = 8, 16, 32), each
+                              block contiguous on both sides (e.g. the scale-factor tiles):
+                              16-byte vectors exchanged between lanes by a two-stage butterfly
+                              (ds_swizzle), no LDS */
 };
 
 /*

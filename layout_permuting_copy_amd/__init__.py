@@ -41,11 +41,13 @@ TC_FLAG_FORCE_GUARDED = 0x02
 TC_FLAG_FORCE_REGS = 0x04
 TC_FLAG_FORCE_LDS = 0x08
 TC_FLAG_NO_SWIZZLE = 0x10
+TC_FLAG_NO_SHUFFLE = 0x20
 
 # paths (enum tc_path)
 TC_PATH_EMPTY, TC_PATH_TRANSPOSE, TC_PATH_ROWS, TC_PATH_ROUNDTRIP, TC_PATH_GUARDED_TILE, \
-    TC_PATH_GUARDED_ROWS = range(6)
-PATH_NAMES = {0: "empty", 1: "transpose", 2: "rows", 3: "roundtrip", 4: "guarded_tile", 5: "guarded_rows"}
+    TC_PATH_GUARDED_ROWS, TC_PATH_SHUFFLE = range(7)
+PATH_NAMES = {0: "empty", 1: "transpose", 2: "rows", 3: "roundtrip", 4: "guarded_tile", 5: "guarded_rows",
+              6: "shuffle"}
 
 
 class TcLayout(ctypes.Structure):

@@ -98,6 +98,69 @@ __global__ void __launch_bounds__(kGuardThreads) guarded_tile_kernel(TransposeAr
 }
 
 
+// Batches of 4 x C blocks of 4-byte elements: each lane loads 16-byte vectors (row i = l / (C/4),
+// columns 4q.. of block row i, l the lane's index within the block), then two exchanges with the
+// partner lane move register bit 1 against lane bit log2(C/2) and register bit 0 against lane bit
+// log2(C/4) -- afterwards lane l = a (C/4) + q holds column 4q + a, rows 0..3: one 16-byte vector
+// of the column-major destination.  ds_swizzle (bit mode, xor within 32 lanes) does the
+// exchanges; every lane takes part (lanes past the end load and store nothing, and whole blocks
+// are past the end together).  The permute page's register-staged exchange, with the staging
+// done by cross-lane moves instead of shared memory (TVM TIRx docs, "permute_layout", Algorithm
+// step 3).
+template <int DIST>
+__device__ __forceinline__ uint32_t xor_lanes(uint32_t v) {
+  static_assert(DIST >= 1 && DIST <= 16, "ds_swizzle bit mode exchanges within 32 lanes");
+  return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x1F | (DIST << 10)));
+}
+
+template <int LC, int NTM, bool GUARD>
+__device__ __forceinline__ void shuffle_rounds(const ShuffleArgs& a) {
+  constexpr int LQ = LC - 2;  // log2 of the vectors per block row
+  constexpr int R = kShuffleRounds, NT = kShuffleThreads;
+  const int lane = int(threadIdx.x) & 63;
+  const bool hi1 = (lane >> (LQ + 1)) & 1, hi0 = (lane >> LQ) & 1;
+  const int row = (lane >> LQ) & 3, q = lane & ((1 << LQ) - 1);
+  const int col = 4 * q + row;  // destination column after the exchanges
+  const int64_t g0 = int64_t(blockIdx.x) * R * NT + threadIdx.x;
+  u32x4 v[R];
+#pragma unroll
+  for (int f = 0; f < R; ++f) {
+    const int64_t g = g0 + int64_t(f) * NT;  // g % 64 == lane
+    const int64_t blk = g >> LC;
+    const u32x4* p = reinterpret_cast<const u32x4*>(a.src) + ((a.so + blk * a.sB) >> 2) + row * (1 << LQ) + q;
+    if constexpr (GUARD) {
+      v[f] = u32x4{0, 0, 0, 0};
+      if (g < a.nvec) v[f] = gload_v<u32x4, NTM>(p);
+    } else {
+      v[f] = gload_v<u32x4, NTM>(p);
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < R; ++f) {
+    uint32_t w0 = v[f].x, w1 = v[f].y, w2 = v[f].z, w3 = v[f].w;
+    uint32_t t = xor_lanes<(2 << LQ)>(hi1 ? w0 : w2);
+    if (hi1) w0 = t; else w2 = t;
+    t = xor_lanes<(2 << LQ)>(hi1 ? w1 : w3);
+    if (hi1) w1 = t; else w3 = t;
+    t = xor_lanes<(1 << LQ)>(hi0 ? w0 : w1);
+    if (hi0) w0 = t; else w1 = t;
+    t = xor_lanes<(1 << LQ)>(hi0 ? w2 : w3);
+    if (hi0) w2 = t; else w3 = t;
+    const int64_t g = g0 + int64_t(f) * NT;
+    const int64_t blk = g >> LC;
+    u32x4* p = reinterpret_cast<u32x4*>(a.dst) + ((a.dof + blk * a.dB) >> 2) + col;
+    if (!GUARD || g < a.nvec) gstore_v<u32x4, NTM>(p, u32x4{w0, w1, w2, w3});
+  }
+}
+
+// Workgroups wholly inside the copy run with no per-lane condition (all loads in flight); the
+// last one, if ragged, is guarded.
+template <int LC, int NTM>
+__global__ void __launch_bounds__(kShuffleThreads) shuffle_kernel(ShuffleArgs a) {
+  if ((int64_t(blockIdx.x) + 1) * kShuffleRounds * kShuffleThreads <= a.nvec) shuffle_rounds<LC, NTM, false>(a);
+  else shuffle_rounds<LC, NTM, true>(a);
+}
+
 }  // namespace dev
 
 namespace {
@@ -151,7 +214,25 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.path == TC_PATH_EMPTY) return TC_OK;
   const Joint& j = p.j;
-  if (p.path == TC_PATH_TRANSPOSE || p.path == TC_PATH_GUARDED_TILE) {
+  if (p.path == TC_PATH_SHUFFLE) {
+    ShuffleArgs sa{};
+    sa.src = static_cast<const unsigned char*>(src);
+    sa.dst = static_cast<unsigned char*>(dst);
+    sa.so = j.so;
+    sa.dof = j.dof;
+    sa.sB = p.mode_b >= 0 ? j.m[p.mode_b].s : 0;
+    sa.dB = p.mode_b >= 0 ? j.m[p.mode_b].d : 0;
+    sa.nvec = j.count / 4;
+    const dim3 grid(uint32_t(p.workgroups)), block(kShuffleThreads);
+    switch (p.shuffle_c) {
+      case 8: hipLaunchKernelGGL((dev::shuffle_kernel<3, 3>), grid, block, 0, s, sa); break;
+      case 16: hipLaunchKernelGGL((dev::shuffle_kernel<4, 3>), grid, block, 0, s, sa); break;
+      case 32: hipLaunchKernelGGL((dev::shuffle_kernel<5, 3>), grid, block, 0, s, sa); break;
+      default:
+        *err = "no shuffle kernel for this block width";
+        return TC_E_ARG;
+    }
+  } else if (p.path == TC_PATH_TRANSPOSE || p.path == TC_PATH_GUARDED_TILE) {
     TransposeArgs ta{};
     ta.src = static_cast<const unsigned char*>(src);
     ta.dst = static_cast<unsigned char*>(dst);

@@ -488,6 +488,34 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     }
     return p;
   }
+  if (fast && !(flags & TC_FLAG_NO_SHUFFLE) && p.eb == 4 && p.vb == 16 && j.rank <= 3) {
+    // 4 x C blocks, row-major in the source and column-major in the destination, one batch mode:
+    // the lanes' 16-byte vectors are exchanged in registers (a two-stage butterfly), no LDS
+    const Mode& R = j.m[r];
+    const Mode& C = j.m[c];
+    int b = -1;
+    for (int k = 0; k < j.rank; ++k)
+      if (k != r && k != c) b = k;
+    const bool block = R.e == 4 && (C.e == 8 || C.e == 16 || C.e == 32) && r != c && R.s == C.e && C.s == 1 &&
+                       R.d == 1 && C.d == 4;
+    if (block) {
+      p.path = TC_PATH_SHUFFLE;
+      p.mode_r = r;
+      p.mode_c = c;
+      p.mode_b = b;
+      p.shuffle_c = int(C.e);
+      p.threads = kShuffleThreads;
+      p.load_outer = p.store_outer = kShuffleRounds;
+      p.ntm = 3;
+      const int64_t nvec = j.count / 4;
+      p.workgroups = ceil_div(nvec, int64_t(kShuffleThreads) * kShuffleRounds);
+      if (nvec >= (int64_t(1) << 31)) {
+        p.status = TC_E_RANGE;
+        p.reason = "more than 2^31 vectors";
+      }
+      return p;
+    }
+  }
   if (fast) {
     p.path = TC_PATH_TRANSPOSE;
     p.mode_r = r;
@@ -640,7 +668,12 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
   info->tile_b = tiled ? p.g.NB : 0;
   info->workgroups = p.workgroups;
   info->lds_bytes = p.lds_bytes;
-  if (p.path == TC_PATH_ROWS) info->nontemporal = p.ntm;
+  if (p.path == TC_PATH_ROWS || p.path == TC_PATH_SHUFFLE) info->nontemporal = p.ntm;
+  if (p.path == TC_PATH_SHUFFLE) {
+    info->tile_r = 4;
+    info->tile_c = p.shuffle_c;
+    info->tile_b = 1;
+  }
   if (p.path == TC_PATH_TRANSPOSE) {
     info->xor_k = p.g.k;
     info->xor_shift = p.g.shift;

@@ -117,6 +117,7 @@ struct Plan {
   bool unaligned = false;           // transpose with vectors at element alignment (extents or strides
                                     // not multiples of the vector; edges element by element)
   int step = 1;                     // source stride of the transpose's column mode (1 or 2)
+  int shuffle_c = 0;                // shuffle path: block columns C (8, 16 or 32; 4 rows)
   int mode_r = -1, mode_c = -1, mode_b = -1;
   TileGeom g;
   int threads = 0, load_outer = 0, store_outer = 0;
@@ -154,6 +155,17 @@ struct TransposeArgs {
   int32_t xshift, xmask, xtbit;
   int32_t xcshift, xcmask;
   int32_t order;             // 0: column tiles fastest, 1: row tiles fastest
+};
+
+// The shuffle path: nvec 16-byte vectors, C/4 per block row; block b starts at element
+// so + b * sB (source, row-major 4 x C) and dof + b * dB (destination, column-major).
+constexpr int kShuffleThreads = 256;  // lanes per workgroup
+constexpr int kShuffleRounds = 8;     // vectors per lane
+struct ShuffleArgs {
+  const unsigned char* src;
+  unsigned char* dst;
+  int64_t so, dof, sB, dB;
+  int64_t nvec;
 };
 
 struct RowArgs {

@@ -60,8 +60,26 @@ def test_cfg1_tile32_roundtrip_one_wave():
 
 
 def test_cfg2_sf_transpose_full():
-    plan = check_workload(SI.sf_transpose(), expect_path="transpose")
-    assert plan["write_conflicts"] == 0 and plan["read_conflicts"] == 0
+    plan = check_workload(SI.sf_transpose(), expect_path="shuffle")
+    assert (plan["tile_r"], plan["tile_c"]) == (4, 32)
+
+
+def test_cfg2_sf_transpose_full_lds_tile():
+    plan = check_workload(SI.sf_transpose(), flags=L.TC_FLAG_NO_SHUFFLE, expect_path="transpose")
+    assert plan["write_conflicts"] == 0 and plan["read_conflicts"] == 0 and plan["wave_local"] == 1
+
+
+@pytest.mark.parametrize("C", [8, 16, 32])
+@pytest.mark.parametrize("nb,pad_s,pad_d,soff,doff", [(1000, 0, 0, 0, 0), (16, 0, 0, 4, 8), (37, 8, 4, 0, 0),
+                                                      (515, 4, 12, 8, 4), (3, 0, 0, 0, 0)])
+def test_shuffle_blocks(C, nb, pad_s, pad_d, soff, doff):
+    """Batches of 4 x C fp32 blocks through the register butterfly (padded pitches, offsets,
+    a ragged last workgroup)."""
+    shape, ss, ds = (nb, 4, C), (4 * C + pad_s, C, 1), (4 * C + pad_d, 1, 4)
+    if (nb * 4 * C) % 64:
+        pytest.skip("count not a multiple of 64: another path")
+    p = _check(shape, ss, ds, 4, s_off=soff, d_off=doff, seed=nb + C)
+    assert p["path_name"] == "shuffle"
 
 
 @pytest.mark.parametrize("dtype", ["float32", "bfloat16"])

@@ -54,7 +54,7 @@ def test_abi_struct_layout_matches_header():
 
 
 def test_workload_paths_and_declines():
-    expect = {"tile32x32_f32_roundtrip": "roundtrip", "sf_transpose": "transpose", "transpose_16384": "transpose",
+    expect = {"tile32x32_f32_roundtrip": "roundtrip", "sf_transpose": "shuffle", "transpose_16384": "transpose",
               "permute0213": "rows", "transpose_8192x8192": "transpose", "slice_": "transpose",
               "transpose_8191x8190": "transpose"}
     for w in SI.all_workloads():
@@ -198,7 +198,7 @@ def test_swizzle_matches_oracle_rederivation(w):
     (TileLang partition of each phase, gfx950 bank model, same search order): the planner's
     choice must be the oracle's, and conflict-free under the oracle's own counting."""
     from oracle import ref as R
-    p = _plan(w)
+    p = _plan(w, flags=L.TC_FLAG_NO_SHUFFLE)  # the SF tiles' LDS plan, not their register butterfly
     assert p["path_name"] == "transpose"
     geo = dict(eb=p["elem_bytes"], vb=p["vec_bytes"], TR=p["tile_r"], TC=p["tile_c"], NB=p["tile_b"],
                U=p["lds_read_bytes"], NT=p["threads"])
@@ -222,7 +222,7 @@ def test_wave_locality_matches_oracle():
     cases += [(sh, ss, 0, ds, 0, dts[eb]) for sh, ss, ds, eb, _ in SI.random_layouts(5, 120)]
     seen = {True: 0, False: 0}
     for shape, ss, so, ds, do, dt in cases:
-        p = L.tc_plan((shape, ss, so), (shape, ds, do), dt, raise_on_error=False)
+        p = L.tc_plan((shape, ss, so), (shape, ds, do), dt, flags=L.TC_FLAG_NO_SHUFFLE, raise_on_error=False)
         if p["path_name"] != "transpose":
             continue
         o = R.tile_wave_local(p["elem_bytes"], p["vec_bytes"], p["tile_r"], p["tile_c"], p["tile_b"], p["threads"],
@@ -231,7 +231,7 @@ def test_wave_locality_matches_oracle():
         assert p["wave_local"] <= int(o), (shape, ss, ds, dt)
         seen[bool(p["wave_local"])] += 1
     assert seen[True] >= 2 and seen[False] >= 5
-    sf = _plan(SI.sf_transpose())
+    sf = _plan(SI.sf_transpose(), flags=L.TC_FLAG_NO_SHUFFLE)
     assert sf["wave_local"] == 1
 
 
@@ -282,3 +282,23 @@ def test_no_kernel_uses_scratch_memory():
     kernels = {k: v for k, v in res.items() if "tc3dev" in k}
     assert sum("transpose_kernel" in k for k in kernels) >= 50
     assert not {k: v for k, v in kernels.items() if v.get("scratch_bytes", 0) != 0}
+
+
+def test_shuffle_path_selection():
+    """4 x C blocks of 4-byte elements, contiguous on both sides, take the register butterfly;
+    anything else (other widths, C = 64, blocks not contiguous, the flag) does not."""
+    f32 = L.TC_F32
+    for C in (8, 16, 32):
+        p = L.tc_plan(((64, 4, C), (4 * C, C, 1)), ((64, 4, C), (4 * C, 1, 4)), f32)
+        assert p["path_name"] == "shuffle" and (p["tile_r"], p["tile_c"]) == (4, C)
+        # padded block pitch on either side is fine
+        p = L.tc_plan(((64, 4, C), (4 * C + 8, C, 1)), ((64, 4, C), (4 * C + 16, 1, 4)), f32)
+        assert p["path_name"] == "shuffle"
+    for shape, ss, ds, dt in [((64, 4, 64), (256, 64, 1), (256, 1, 4), f32),      # C = 64
+                              ((64, 4, 32), (128, 32, 1), (128, 1, 4), L.TC_BF16),  # 2-byte elements
+                              ((64, 4, 32), (256, 64, 1), (128, 1, 4), f32),      # source rows apart
+                              ((64, 8, 32), (256, 32, 1), (256, 1, 8), f32)]:     # 8 rows
+        assert L.tc_plan((shape, ss), (shape, ds), dt)["path_name"] != "shuffle", (shape, ss, ds)
+    sf = SI.sf_transpose()
+    assert _plan(sf)["path_name"] == "shuffle"
+    assert _plan(sf, flags=L.TC_FLAG_NO_SHUFFLE)["path_name"] == "transpose"
