@@ -68,8 +68,20 @@ def device_tensors(torch, w: SI.Workload, pairs: int, host_src: np.ndarray | Non
     return srcs, dsts
 
 
-def time_workload(torch, L, w: SI.Workload, steps: int, warmup: int, host_src=None, seed=0):
-    """Returns dict with wall ms/step and mean per-launch event ms."""
+def time_workload(torch, L, w: SI.Workload, steps: int, warmup: int, host_src=None, seed=0, flags: int = 0):
+    """Returns dict with wall ms/step and mean per-launch event ms.  `flags` (TC_FLAG_*) apply to
+    every launch of the measurement."""
+    prev = L.tc_set_flags(flags)
+    try:
+        out = _time_workload(torch, L, w, steps, warmup, host_src, seed, flags)
+    finally:
+        L.tc_set_flags(prev)
+    if flags:
+        out["flags"] = flags
+    return out
+
+
+def _time_workload(torch, L, w: SI.Workload, steps: int, warmup: int, host_src, seed, flags):
     bytes_step = 2 * int(np.prod(w.src.shape)) * w.eb
     pair_bytes = (SI.storage_elems(w, "src") + SI.storage_elems(w, "dst")) * w.eb
     # rotate so that more than 2x the MALL is touched between reuses of a pair (cap: 8 GiB)
@@ -84,7 +96,7 @@ def time_workload(torch, L, w: SI.Workload, steps: int, warmup: int, host_src=No
     code = L.DTYPE_BY_NAME[w.dtype]
     stream = torch.cuda.current_stream()
     sh = int(stream.cuda_stream)
-    plan = L.tile_copy_ex(sp[0], sl, dp[0], dl, code, sh)
+    plan = L.tile_copy_ex(sp[0], sl, dp[0], dl, code, sh, flags=flags)
     for i in range(warmup):
         L.tile_copy(sp[i % pairs], sl, dp[i % pairs], dl, code, sh)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -284,8 +296,12 @@ def main() -> int:
         torch.cuda.empty_cache()
         sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in time_device_permute(torch).items()})
         torch.cuda.empty_cache()
-        for sw in [identity_workload()] + sweep_workloads():
-            s = time_workload(torch, L, sw, 30, 3, seed=11)
+        # the alternatives the planner does not pick, for comparison: the SF tiles on the LDS tile
+        # kernel, the (0,2,1,3) permute staged through LDS
+        runs = [(sw, 0) for sw in [identity_workload()] + sweep_workloads()]
+        runs += [(SI.sf_transpose(), L.TC_FLAG_NO_SHUFFLE), (SI.permute0213(), L.TC_FLAG_FORCE_LDS)]
+        for sw, fl in runs:
+            s = time_workload(torch, L, sw, 30, 3, seed=11, flags=fl)
             s_src, s_dst = s.pop("_last")
             s["sampled_parity"] = sampled_parity(torch, sw, s_src, s_dst, 1 << 14)
             del s_src, s_dst
