@@ -33,23 +33,34 @@ __device__ __forceinline__ void row_offsets(const RowArgs& a, uint32_t n, int64_
 
 // [outer, threads, vec] copy: access v = blockIdx * NT*ROUNDS + f*NT + t.  With USE_LDS the
 // vectors make the round trip global -> LDS -> global of the gmem_smem demonstration.
-template <int VB, int NT, int ROUNDS, bool USE_LDS, int NTM>
-__global__ void __launch_bounds__(NT) rows_kernel(RowArgs a) {
+template <int VB, int NT, int ROUNDS, bool USE_LDS, int NTM, bool GUARD, bool BURST>
+__device__ __forceinline__ void rows_body(const RowArgs& a, typename Bytes<VB>::T* lds) {
   typedef typename Bytes<VB>::T V;
-  __shared__ __attribute__((aligned(16))) V lds[USE_LDS ? NT * ROUNDS : 1];
   const int t = threadIdx.x;
   const int64_t base = int64_t(blockIdx.x) * NT * ROUNDS;
   V reg[ROUNDS];
-  int64_t doff[ROUNDS];
+  int64_t soff[ROUNDS], doff[ROUNDS];
+  if constexpr (BURST) {
+    // all offsets first (the decode loop has a run-time trip count), then every load back to back
 #pragma unroll
-  for (int f = 0; f < ROUNDS; ++f) {
-    const int64_t v = base + f * NT + t;
-    doff[f] = -1;
-    if (v < a.nvec) {
-      int64_t so, dof;
-      row_offsets(a, uint32_t(v), &so, &dof);
-      reg[f] = gload_v<V, NTM>(reinterpret_cast<const V*>(a.src + so));
-      doff[f] = dof;
+    for (int f = 0; f < ROUNDS; ++f) {
+      const int64_t v = base + f * NT + t;
+      soff[f] = doff[f] = -1;
+      if (!GUARD || v < a.nvec) row_offsets(a, uint32_t(v), &soff[f], &doff[f]);
+    }
+#pragma unroll
+    for (int f = 0; f < ROUNDS; ++f)
+      if (!GUARD || doff[f] >= 0) reg[f] = gload_v<V, NTM>(reinterpret_cast<const V*>(a.src + soff[f]));
+  } else {
+    // each load right after its offsets: the decode loop between them leaves one load in flight
+#pragma unroll
+    for (int f = 0; f < ROUNDS; ++f) {
+      const int64_t v = base + f * NT + t;
+      doff[f] = -1;
+      if (!GUARD || v < a.nvec) {
+        row_offsets(a, uint32_t(v), &soff[f], &doff[f]);
+        reg[f] = gload_v<V, NTM>(reinterpret_cast<const V*>(a.src + soff[f]));
+      }
     }
   }
   if constexpr (USE_LDS) {
@@ -61,7 +72,17 @@ __global__ void __launch_bounds__(NT) rows_kernel(RowArgs a) {
   }
 #pragma unroll
   for (int f = 0; f < ROUNDS; ++f)
-    if (doff[f] >= 0) gstore_v<V, NTM>(reinterpret_cast<V*>(a.dst + doff[f]), reg[f]);
+    if (!GUARD || doff[f] >= 0) gstore_v<V, NTM>(reinterpret_cast<V*>(a.dst + doff[f]), reg[f]);
+}
+
+// BURST: workgroups wholly inside the copy take the unguarded body, all loads in flight.  Else
+// every workgroup takes the guarded body, whose per-vector branch paces the loads one at a time.
+template <int VB, int NT, int ROUNDS, bool USE_LDS, int NTM, bool BURST = false>
+__global__ void __launch_bounds__(NT) rows_kernel(RowArgs a) {
+  typedef typename Bytes<VB>::T V;
+  __shared__ __attribute__((aligned(16))) V lds[USE_LDS ? NT * ROUNDS : 1];
+  if (BURST && (int64_t(blockIdx.x) + 1) * NT * ROUNDS <= a.nvec) rows_body<VB, NT, ROUNDS, USE_LDS, NTM, false, BURST>(a, lds);
+  else rows_body<VB, NT, ROUNDS, USE_LDS, NTM, true, BURST>(a, lds);
 }
 
 // Fallback tile: element-wide accesses, padded LDS rows, guards on every element.
@@ -182,9 +203,9 @@ int lg(int64_t x) {
   return r;
 }
 
-template <int VB, int NT, bool LDS, int NTM>
+template <int VB, int NT, bool LDS, int NTM, bool BURST = false>
 void launch_rows_t(const RowArgs& ra, int64_t wgs, hipStream_t s) {
-  hipLaunchKernelGGL((dev::rows_kernel<VB, NT, kRowRounds, LDS, NTM>), dim3(uint32_t(wgs)), dim3(NT), 0, s, ra);
+  hipLaunchKernelGGL((dev::rows_kernel<VB, NT, kRowRounds, LDS, NTM, BURST>), dim3(uint32_t(wgs)), dim3(NT), 0, s, ra);
 }
 
 }  // namespace
@@ -304,6 +325,10 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
       if (p.vb == 16) launch_rows_t<16, kWave, true, 0>(ra, wgs, s);
       if (p.vb == 8) launch_rows_t<8, kWave, true, 0>(ra, wgs, s);
       if (p.vb == 4) launch_rows_t<4, kWave, true, 0>(ra, wgs, s);
+    } else if (p.path == TC_PATH_ROWS && p.row_burst) {
+      if (p.vb == 16) launch_rows_t<16, kRowThreads, false, 3, true>(ra, wgs, s);
+      if (p.vb == 8) launch_rows_t<8, kRowThreads, false, 3, true>(ra, wgs, s);
+      if (p.vb == 4) launch_rows_t<4, kRowThreads, false, 3, true>(ra, wgs, s);
     } else if (p.path == TC_PATH_ROWS) {
       if (p.vb == 16) launch_rows_t<16, kRowThreads, false, 3>(ra, wgs, s);
       if (p.vb == 8) launch_rows_t<8, kRowThreads, false, 3>(ra, wgs, s);

@@ -22,6 +22,7 @@ constexpr int kWave = 64;                      // gfx950 wavefront
 constexpr int kSmallCopyBytes = 16384;         // co-contiguous copies up to this size: one LDS round trip
 constexpr int kRowThreads = TC_ROW_THREADS;    // threads per workgroup on the rows path
 constexpr int kRowRounds = TC_ROW_ROUNDS;      // vectors per thread on the rows path
+constexpr int64_t kRowSmallBytes = int64_t(256) << 20;  // rows path: "small" contiguous copies
 constexpr int kGuardThreads = 256;             // threads per workgroup on the guarded paths
 
 // One joint mode: extent, source stride, destination stride (elements).
@@ -118,6 +119,8 @@ struct Plan {
                                     // not multiples of the vector; edges element by element)
   int step = 1;                     // source stride of the transpose's column mode (1 or 2)
   int shuffle_c = 0;                // shuffle path: block columns C (8, 16 or 32; 4 rows)
+  bool row_burst = false;           // rows path: every load of a thread issued at once (else one at
+                                    // a time, each after its offsets are decoded)
   int mode_r = -1, mode_c = -1, mode_b = -1;
   TileGeom g;
   int threads = 0, load_outer = 0, store_outer = 0;
