@@ -302,3 +302,18 @@ def test_shuffle_path_selection():
     sf = SI.sf_transpose()
     assert _plan(sf)["path_name"] == "shuffle"
     assert _plan(sf, flags=L.TC_FLAG_NO_SHUFFLE)["path_name"] == "transpose"
+
+
+def test_alias_check_covers_the_last_element():
+    """Overlap is judged on whole elements: a destination starting at the source's last element
+    shares its bytes and is rejected before anything is launched (host-only: the addresses are
+    never dereferenced)."""
+    lay = ((4,), (1,))
+    src = 0x10000
+    for dst in (src + 12, src + 8, src - 12):  # last element / inside / first element of dst = src
+        with pytest.raises(L.TileCopyError) as e:
+            L.tile_copy_ex(src, lay, dst, lay, L.TC_F32)
+        assert e.value.code == L.TC_E_ALIAS, hex(dst)
+    for dst in (src + 16, src - 16):  # adjacent, no shared byte: planned (not launched here)
+        p = L.tc_plan(lay, lay, L.TC_F32)
+        assert p["status"] == 0
