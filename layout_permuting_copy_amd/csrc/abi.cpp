@@ -80,13 +80,13 @@ int tile_copy_ex(const void* src, const tc_layout* src_layout, void* dst, const 
   if (info) tc::plan_to_info(*plan, info);
   if (plan->status != TC_OK) return fail(plan->status, plan->reason);
   if (plan->path == TC_PATH_EMPTY) return TC_OK;
-  // the byte images of source and destination must not overlap: [first element, last element
-  // + its bytes) on each side
+  // the byte images of source and destination must not overlap (side_range gives [lo, hi) in
+  // elements: hi is one past the last element)
   int64_t slo, shi, dlo, dhi;
   tc::side_range(plan->j, true, &slo, &shi);
   tc::side_range(plan->j, false, &dlo, &dhi);
-  const __int128 s0 = __int128(ps) + __int128(slo) * eb, s1 = __int128(ps) + (__int128(shi) + 1) * eb;
-  const __int128 d0 = __int128(pd) + __int128(dlo) * eb, d1 = __int128(pd) + (__int128(dhi) + 1) * eb;
+  const __int128 s0 = __int128(ps) + __int128(slo) * eb, s1 = __int128(ps) + __int128(shi) * eb;
+  const __int128 d0 = __int128(pd) + __int128(dlo) * eb, d1 = __int128(pd) + __int128(dhi) * eb;
   if (s0 < d1 && d0 < s1) return fail(TC_E_ALIAS, "source and destination byte ranges overlap");
   std::string err;
   const int rc = tc::launch_plan(*plan, src, dst, stream, &err);

@@ -46,6 +46,7 @@ void canonicalize(Joint* j);
 // 1 injective, 0 not, -1 undecided (too large to check by enumeration)
 int dst_injective(const Joint& j);
 // [lo, hi) element range a layout side touches (for the alias check)
+// Element offsets a side touches: [lo, hi), hi one past the last element.
 void side_range(const Joint& j, bool src_side, int64_t* lo, int64_t* hi);
 int slice_layout(const tc_layout& in, const int64_t* start, const int64_t* stop, const int64_t* step,
                  tc_layout* out, std::string* err);

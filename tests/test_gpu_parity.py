@@ -261,6 +261,21 @@ def test_random_layouts():
         _check(shape, s_stride, d_stride, eb, src_elems=src_elems, seed=case)
 
 
+def test_adjacent_buffers_are_not_aliases():
+    """A destination that starts right after the source's last byte (or ends right before its
+    first) shares no byte: the copy runs."""
+    import torch
+    buf = torch.from_numpy(_bits(3 * 4096, 31)).cuda()
+    want = buf[4096:8192].cpu().numpy()
+    base = buf.data_ptr()
+    lay = ((1024,), (1,))
+    L.tile_copy(base + 4096, lay, base + 8192, lay, L.TC_F32)   # dst right after src
+    L.tile_copy(base + 4096, lay, base, lay, L.TC_F32)          # dst right before src
+    torch.cuda.synchronize()
+    out = buf.cpu().numpy()
+    assert np.array_equal(out[8192:], want) and np.array_equal(out[:4096], want)
+
+
 def test_stream_ordering_on_side_stream():
     import torch
     s = torch.cuda.Stream()
