@@ -238,3 +238,38 @@ def random_layouts(seed: int = 1234, count: int = 60):
             d_stride[k] = acc
             acc *= shape[k]
         yield shape, s_stride, tuple(d_stride), eb, acc * int(np.prod(steps)) + 1
+
+
+def random_layouts_wide(seed: int = 4321, count: int = 120):
+    """Like random_layouts, plus negative source strides, broadcast (stride-0) source modes,
+    inserted extent-1 modes with arbitrary strides, and element offsets on both sides.  Yields
+    (src_shape, src_stride, src_offset, dst_shape, dst_stride, dst_offset, elem_bytes,
+    src_elems, dst_elems); every offset a layout reaches lies in [0, *_elems)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(count):
+        rank = int(rng.integers(1, 5))
+        shape = [int(x) for x in rng.integers(1, 9, size=rank) * rng.choice([1, 2, 4, 8], size=rank)]
+        eb = int(rng.choice([1, 2, 4, 8, 16]))
+        perm_s, perm_d = rng.permutation(rank), rng.permutation(rank)
+        steps = rng.choice([1, 1, 1, 2, -1], size=rank)
+        ss, acc = [0] * rank, 1
+        for k in reversed(perm_s):
+            ss[k] = int(acc * steps[k])
+            acc *= shape[k] * abs(int(steps[k]))
+        if rank > 1 and rng.integers(0, 6) == 0:
+            ss[int(rng.integers(0, rank))] = 0
+        ds, dacc = [0] * rank, 1
+        for k in reversed(perm_d):
+            ds[k] = dacc
+            dacc *= shape[k]
+        neg = -sum((e - 1) * s for e, s in zip(shape, ss) if s < 0)
+        so = neg + int(rng.integers(0, 5))
+        do = int(rng.integers(0, 5))
+        src_shape, src_stride = list(shape), list(ss)
+        if rng.integers(0, 3) == 0:
+            pos = int(rng.integers(0, rank + 1))
+            src_shape.insert(pos, 1)
+            src_stride.insert(pos, int(rng.integers(-100, 100)))
+        span_s = so + sum((e - 1) * s for e, s in zip(shape, ss) if s > 0) + 1
+        span_d = do + sum((e - 1) * d for e, d in zip(shape, ds)) + 1
+        yield (tuple(src_shape), tuple(src_stride), so, tuple(shape), tuple(ds), do, eb, span_s, span_d)

@@ -261,6 +261,19 @@ def test_random_layouts():
         _check(shape, s_stride, d_stride, eb, src_elems=src_elems, seed=case)
 
 
+def test_random_layouts_wide():
+    """Negative and zero source strides, unit modes with arbitrary strides, offsets, all widths."""
+    paths = set()
+    for case, (sshape, ss, so, dshape, ds, do, eb, ns, nd) in enumerate(SI.random_layouts_wide(4321, 120)):
+        src = _bits(ns * eb, 1000 + case)
+        sl, dl = (sshape, ss, so), (dshape, ds, do)
+        say(f"[gpu] wide case {case}: src={sl} dst={dl} eb={eb}")
+        got, plan = run_copy(src, sl, nd, dl, eb, dtype_code(DT_BY_EB[eb]))
+        assert_same(got, oracle_copy(src, sl, nd, dl, eb), eb, f"wide {case}")
+        paths.add(plan["path_name"])
+    assert len(paths) >= 3, paths
+
+
 def test_adjacent_buffers_are_not_aliases():
     """A destination that starts right after the source's last byte (or ends right before its
     first) shares no byte: the copy runs."""
