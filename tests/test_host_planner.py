@@ -314,3 +314,43 @@ def test_alias_check_covers_the_last_element():
         with pytest.raises(L.TileCopyError) as e:
             L.tile_copy_ex(src, lay, dst, lay, L.TC_F32)
         assert e.value.code == L.TC_E_ALIAS, hex(dst)
+
+
+def test_planning_is_thread_safe():
+    """Plans made concurrently from many threads (shared plan cache and swizzle memo) equal the
+    plans made one at a time."""
+    from concurrent.futures import ThreadPoolExecutor
+    dts = {1: L.TC_I8, 2: L.TC_BF16, 4: L.TC_F32, 8: L.TC_F64, 16: L.TC_B128}
+    cases = [((sh, ss), (sh, ds), dts[eb]) for sh, ss, ds, eb, _ in SI.random_layouts(2024, 150)]
+    cases += [(((n, m), (m, 1)), ((n, m), (1, n)), dts[eb]) for eb in dts for n, m in [(512, 256), (300, 129), (1024, 64)]]
+    keys = ("status", "path_name", "vec_bytes", "tile_r", "tile_c", "tile_b", "threads", "xor_k", "xor_shift",
+            "xor_tbit", "xor_cshift", "xor_cmask", "workgroups", "wave_local", "unaligned")
+
+    def plan(c):
+        p = L.tc_plan(*c, raise_on_error=False)
+        return tuple(p[k] for k in keys)
+
+    serial = [plan(c) for c in cases]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        for _ in range(3):
+            assert list(ex.map(plan, cases)) == serial
+
+    # the launch entry point's plan cache: overlapping (fake, never dereferenced) addresses make
+    # tile_copy_ex plan through the cache, fill the plan info and stop at the alias check
+    import ctypes
+    lib = L.load_library()
+
+    def cached(c):
+        info = L.TcPlanInfo()
+        s, d = L._as_layout(c[0]), L._as_layout(c[1])
+        rc = lib.tile_copy_ex(0x100000, ctypes.byref(s), 0x100000, ctypes.byref(d), int(c[2]), None, 0,
+                              ctypes.byref(info))
+        p = info.to_dict()
+        p["status"] = 0 if rc == L.TC_E_ALIAS else rc
+        return tuple(p[k] for k in keys)
+
+    ok = [i for i, c in enumerate(cases) if serial[i][0] == 0 and serial[i][1] != "empty"]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        for _ in range(3):
+            got = list(ex.map(cached, [cases[i] for i in ok]))
+            assert got == [serial[i] for i in ok]
