@@ -231,21 +231,29 @@ static bool search_swizzle(const TileGeom& g, bool no_swizzle, TileGeom* out, in
 // mode, 16-byte LDS units (a store vector is one ds_read_b128), so that the workgroups running
 // together write whole destination columns.  On MI355X, against the default tiles: fp32 16384^2
 // 5700 -> 6250 GB/s, bf16 16384^2 5370 -> 5720, fp16 8192^2 4780 -> 5310, fp64 8192^2 5370 ->
-// 5780, 16-byte elements 8192^2 5520 -> 5950; no better for 1-byte elements.  64 KiB tiles where
-// they still give 8192 workgroups (`tiles64` counts them for the 64 KiB shape), else smaller.
+// 5780, 16-byte elements 8192^2 5520 -> 5950.  64 KiB tiles where they still give 8192
+// workgroups, else smaller.  128 KiB tiles (one workgroup per CU) where the copy is large enough
+// to give every CU many of them: bf16 16384^2 as 1024 x 64 on 1024 lanes 5730 -> 5830, fp64 8192^2
+// as 256 x 64 5750 -> 5980, int8 8192^2 as 512 x 256 5000 -> 5190 (the default tile for 1-byte
+// elements otherwise); fp32 and smaller fp16 copies are faster on 64 KiB tiles.
 static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c) {
   c->nt = 3;
   c->order = 1;
   c->unit = 16;
   auto tiles = [&](int64_t tr, int64_t tc) { return ceil_div(eR, tr) * ceil_div(eC, tc) * others; };
   switch (eb) {
+    case 1:
+      if (eR < 512 || eC < 256 || tiles(512, 256) < 512) return false;
+      c->tile = 131072; c->threads = 512; c->trb = 512;  // 512 x 256
+      return true;
     case 16:
       if (eR < 64 || eC < 8) return false;
       c->tile = 8192; c->threads = 256; c->trb = 1024;  // 64 x 8 elements
       return true;
     case 8:
       if (eR < 128 || eC < 16) return false;
-      if (tiles(256, 32) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 2048; }  // 256 x 32
+      if (tiles(256, 64) >= 4096) { c->tile = 131072; c->threads = 512; c->trb = 2048; }  // 256 x 64
+      else if (tiles(256, 32) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 2048; }  // 256 x 32
       else { c->tile = 16384; c->threads = 256; c->trb = 1024; }                          // 128 x 16
       return true;
     case 4:
@@ -255,7 +263,8 @@ static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c)
       return true;
     case 2:
       if (eR < 256 || eC < 64) return false;
-      if (tiles(512, 64) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 1024; }  // 512 x 64
+      if (tiles(1024, 64) >= 4096) { c->tile = 131072; c->threads = 1024; c->trb = 2048; }  // 1024 x 64
+      else if (tiles(512, 64) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 1024; }  // 512 x 64
       else { c->tile = 32768; c->threads = 256; c->trb = 512; }                          // 256 x 64
       return true;
     default:

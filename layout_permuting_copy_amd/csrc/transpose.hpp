@@ -239,7 +239,8 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
     constexpr int U = EB < 4 ? 4 : EB;                                                                       \
     if (c.unit == 16 && U != 16) {                                                                           \
       TC_CFG_UNIT(EB, 16, 16384, 256) TC_CFG_UNIT(EB, 16, 32768, 256) TC_CFG_UNIT(EB, 16, 65536, 256)         \
-      TC_CFG_UNIT(EB, 16, 32768, 512) TC_CFG_UNIT(EB, 16, 65536, 512)                                        \
+      TC_CFG_UNIT(EB, 16, 32768, 512) TC_CFG_UNIT(EB, 16, 65536, 512) TC_CFG_UNIT(EB, 16, 65536, 1024)       \
+      TC_CFG_UNIT(EB, 16, 131072, 512) TC_CFG_UNIT(EB, 16, 131072, 1024)                                      \
       return false;                                                                                          \
     }                                                                                                        \
     if (c.unit == 8 && U < 8) {                                                                              \
