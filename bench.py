@@ -164,18 +164,25 @@ def cpu_baseline(w: SI.Workload, host_src: np.ndarray, budget_s: float = 12.0):
     n_dst = SI.span(SI.Side(shape, w.dst.stride, w.dst.offset))
     dst = np.empty(n_dst * w.eb, dtype=np.uint8)
     src = host_src[: SI.span(SI.Side(shape, w.src.stride, w.src.offset)) * w.eb].copy()
-    R.copy(src, sl, dst, dl, w.eb)  # warm-up
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        R.copy(src, sl, dst, dl, w.eb)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el > budget_s:
-            break
     bytes_rep = 2 * int(np.prod(shape)) * w.eb
-    return {"value": bytes_rep * reps / el / 1e9, "unit": "GB/s", "cores": R.max_threads(), "kind": "oracle",
+
+    def rate(nthreads, seconds):
+        R.copy(src, sl, dst, dl, w.eb, nthreads=nthreads)  # warm-up
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            R.copy(src, sl, dst, dl, w.eb, nthreads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > seconds:
+                return bytes_rep * reps / el / 1e9, reps, el
+
+    cores = R.max_threads()
+    value, reps, el = rate(cores, budget_s)
+    one, reps1, el1 = rate(1, budget_s / 3)
+    return {"value": value, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "value_1core": round(one, 3),
             "sample": f"{tiles} of {outer} outer tiles ({bytes_rep / 2**20:.1f} MiB moved per copy), "
-                      f"{reps} copies in {el:.1f} s"}
+                      f"{reps} copies in {el:.1f} s on {cores} threads, {reps1} in {el1:.1f} s on 1"}
 
 
 def time_memcpy(torch, nbytes: int = 1 << 30, steps: int = 30):

@@ -69,13 +69,14 @@ int oracle_copy(const unsigned char* src, int src_rank, const int64_t* src_shape
     return 0;
   }
 #ifdef _OPENMP
-  if (nthreads > 0) omp_set_num_threads(nthreads);
+  /* a per-call thread count: it does not change the default of later calls */
+  const int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
 #else
   (void)nthreads;
 #endif
   const int64_t outer = ss[0];
   /* One outermost index per iteration; an odometer walks the inner modes. */
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) num_threads(nt)
   for (int64_t i0 = 0; i0 < outer; ++i0) {
     int64_t idx[ORACLE_MAX_RANK];
     for (int k = 0; k < r; ++k) idx[k] = 0;
