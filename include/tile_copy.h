@@ -151,6 +151,10 @@ typedef struct tc_plan_info {
   int32_t wave_local;       /* transpose: 1 if every wave reads back only LDS data it wrote itself,
                                so the phases are ordered per wave instead of by a workgroup barrier */
   int32_t lds_write_bytes, lds_read_bytes;       /* LDS instruction widths */
+  int32_t edge_tiles;       /* transpose: 1 if the kernel carries its guarded code for tiles that
+                               reach past an extent; 0 if every tile lies inside the copy and the
+                               interior-only kernel runs */
+  int32_t reserved0;
   int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
   char reason[192];         /* why the fast path was declined ("" if it was not) */
 } tc_plan_info;

@@ -285,7 +285,7 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
       ta.xcmask = p.g.cmask;
       ta.order = p.g.order;
       fill_batch(p, &ta, p.mode_r, p.mode_c, p.mode_b);
-      const TransposeCfg cfg{p.vb, p.g.U, p.g.tile_bytes, p.g.NT, p.g.ntm, p.g.step, p.g.wave_local};
+      const TransposeCfg cfg{p.vb, p.g.U, p.g.tile_bytes, p.g.NT, p.g.ntm, p.g.step, p.g.wave_local, p.g.edges};
       if (!launch_transpose(p.eb, cfg, &ta, p.workgroups, stream)) {
         *err = "no transpose kernel instance for this element width, vector width, tile size and thread count";
         return TC_E_ARG;

@@ -85,6 +85,7 @@ struct TileGeom {
                                   // vector read as two contiguous ones and compacted in registers)
   bool wave_local = false;        // every wave reads back only LDS units it wrote itself: the
                                   // phases are ordered per wave, without a workgroup barrier
+  bool edges = true;              // some tile reaches past an extent (the kernel needs its guards)
   int loads = 4, stores = 4;  // accesses per thread per phase
   int ww = 16, rw = 4;        // LDS write / read instruction bytes
   int k = 0, shift = 0, tbit = 0;
@@ -199,6 +200,7 @@ int wave_permute_plan(const tc_layout& src, const tc_layout& dst, int dtype, tc_
 struct TransposeCfg {
   int vb, unit, tile, threads, ntm, step;
   bool wave_local;
+  bool edges = true;  // false: every tile lies wholly inside the copy (the interior-only kernel)
 };
 bool launch_transpose_eb1(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
 bool launch_transpose_eb2(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);

@@ -198,28 +198,35 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
 // also the tiles holding a row's last element).  WL: the planner has shown that every wave reads
 // back only LDS units it wrote itself, so the phases are ordered per wave and the waves of the
 // workgroup never wait for each other.
-template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL>
+//
+// EDGE = false: the host has shown that every tile lies wholly inside the copy, and the guarded
+// code is not compiled in (it needs more registers than the interior code, which can then
+// lower the number of workgroups per CU).
+template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL, bool EDGE = true>
 __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   typedef Geo<EB, VB, U, TILE, NT> G;
   __shared__ __attribute__((aligned(16))) unsigned char lds[TILE];
   const TileAt t = tile_at(a, blockIdx.x);
   TileRegs<G> r;
-  const bool full = tile_full(a, t) && (S == 1 || t.remC > (int64_t(1) << a.lTC));
-  if (full) load_tile<EB, VB, G, NT, NTM, S, false>(a, t, r);
+  const bool full = !EDGE || (tile_full(a, t) && (S == 1 || t.remC > (int64_t(1) << a.lTC)));
+  if constexpr (!EDGE) load_tile<EB, VB, G, NT, NTM, S, false>(a, t, r);
+  else if (full) load_tile<EB, VB, G, NT, NTM, S, false>(a, t, r);
   else load_tile<EB, VB, G, NT, NTM, S, true>(a, t, r);
   write_lds<EB, VB, U, G, NT>(a, lds, r);
   if constexpr (WL) wave_lds_sync();
   else __syncthreads();
-  if (full) read_store<EB, VB, U, G, NT, NTM, false>(a, t, lds);
+  if constexpr (!EDGE) read_store<EB, VB, U, G, NT, NTM, false>(a, t, lds);
+  else if (full) read_store<EB, VB, U, G, NT, NTM, false>(a, t, lds);
   else read_store<EB, VB, U, G, NT, NTM, true>(a, t, lds);
 }
 
 // Launches the instance (ta != nullptr) or only reports whether it exists (ta == nullptr).
-template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL = false>
+template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL = false, bool EDGE = true>
 bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
   if constexpr (Geo<EB, VB, U, TILE, NT>::valid) {
     if (ta)
-      hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM, S, WL>), dim3(uint32_t(wgs)), dim3(NT), 0, s, *ta);
+      hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM, S, WL, EDGE>), dim3(uint32_t(wgs)), dim3(NT), 0, s,
+                         *ta);
     return true;
   }
   return false;
@@ -260,6 +267,7 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 
 #define TC_CFG(EB, VB, U, TILE, NT)                                                                          \
   if (vb == VB && tile == TILE && nt == NT && c.step == 1 && !c.wave_local) {                                \
+    if (ntm == 3 && !c.edges) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 3, 1, false, false>(ta, wgs, s);    \
     if (ntm == 3) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 3, 1>(ta, wgs, s);                   \
     if (ntm == 0) return dev::launch_transpose_cfg<EB, VB, U, TILE, NT, 0, 1>(ta, wgs, s);                   \
   }
@@ -271,6 +279,7 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 // Wider LDS units (UNIT/EB rows of one column): tall tiles whose store lanes run down a column
 #define TC_CFG_UNIT(EB, UNIT, TILE, NT)                                                                      \
   if (vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local) {                                \
+    if (ntm == 3 && !c.edges) return dev::launch_transpose_cfg<EB, 16, UNIT, TILE, NT, 3, 1, false, false>(ta, wgs, s);    \
     if (ntm == 3) return dev::launch_transpose_cfg<EB, 16, UNIT, TILE, NT, 3, 1>(ta, wgs, s);                \
     if (ntm == 0) return dev::launch_transpose_cfg<EB, 16, UNIT, TILE, NT, 0, 1>(ta, wgs, s);                \
   }

@@ -248,7 +248,8 @@ def test_no_swizzle_has_conflicts_for_transposes():
 
 # (vector bytes, tile bytes, threads) of the transpose kernel instances the library is built with
 TRANSPOSE_INSTANCES = {(16, t, n) for t, n in [(8192, 256), (16384, 256), (16384, 512), (32768, 256), (32768, 512),
-                                                (65536, 256), (65536, 512)]} | {(8, 16384, 256), (4, 16384, 256)}
+                                                (65536, 256), (65536, 512), (65536, 1024), (131072, 512),
+                                                (131072, 1024)]} | {(8, 16384, 256), (4, 16384, 256)}
 
 
 def test_every_plan_has_a_kernel_instance():
@@ -260,6 +261,8 @@ def test_every_plan_has_a_kernel_instance():
         for n in (1, 3, 4, 16, 31, 64, 65, 100, 128, 129, 256, 1000, 4096):
             for m in (1, 2, 5, 16, 64, 67, 256, 300, 2048):
                 cases.append(((n, m), (m, 1), (1, n), eb))
+    cases += [((16384, 16384), (16384, 1), (1, 16384), 2), ((8192, 8192), (8192, 1), (1, 8192), 1),
+              ((8192, 8192), (8192, 1), (1, 8192), 8)]
     seen = set()
     for shape, ss, ds, eb in cases:
         p = L.tc_plan((shape, ss), (shape, ds), dts[eb], raise_on_error=False)
@@ -269,6 +272,24 @@ def test_every_plan_has_a_kernel_instance():
             assert cfg in TRANSPOSE_INSTANCES, (shape, ss, ds, eb, cfg)
             seen.add(cfg)
     assert len(seen) >= 5
+
+
+def test_interior_kernel_only_for_exact_tilings():
+    """The kernel without guarded code runs only where every tile lies inside the copy (and not
+    for 16-byte elements, which measured faster with the guarded kernel)."""
+    def edge(shape, ss, ds, dt, soff=0):
+        p = L.tc_plan((shape, ss, soff), (shape, ds), dt)
+        assert p["path_name"] == "transpose", p
+        return p["edge_tiles"]
+    assert edge((16384, 16384), (16384, 1), (1, 16384), L.TC_BF16) == 0
+    assert edge((16384, 16384), (16384, 1), (1, 16384), L.TC_F32) == 0
+    assert edge((8192, 8192), (8192, 1), (1, 8192), L.TC_I8) == 0
+    assert edge((4096, 1024), (1024, 1), (1, 4096), L.TC_F64) == 0
+    assert edge((16392, 16392), (16392, 1), (1, 16392), L.TC_BF16) == 1   # partial tiles
+    assert edge((1000, 600), (600, 1), (1, 1000), L.TC_F32) == 1
+    assert edge((8192, 8192), (8192, 1), (1, 8192), L.TC_B128) == 1        # 16-byte elements
+    assert edge((8191, 8190), (8190, 1), (1, 8191), L.TC_F16) == 1         # element-aligned vectors
+    assert edge((8190, 4095), (8192, 2), (1, 8190), L.TC_F16, 8192) == 1   # stride-2 source
 
 
 def test_no_kernel_uses_scratch_memory():
