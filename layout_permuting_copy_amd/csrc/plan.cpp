@@ -364,7 +364,16 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   const bool batched = pow2ceil(R.e) * p->eb < 128;
   const TuneCfg ov = tune_override();
   const bool pinned = ov.tile || ov.threads || ov.nt >= 0 || ov.order >= 0 || ov.trb || ov.unit;
-  TuneCfg base = default_cfg(p->eb, batched, p->unaligned);
+  // 8-byte elements whose destination columns do not start on 128-byte lines (a line-aligned base
+  // pointer assumed): the configuration of the element-aligned plans (plain stores, 16 KiB
+  // tiles, column tiles first) measured faster than the tall tiles with nontemporal stores, fp64
+  // 8190 x 8192 3.63 -> 5.24 TB/s and 8184 x 8184 3.71 -> 4.97.  (fp32, bf16 and fp16 copies of
+  // such pitches measured no better with it.)
+  bool dst_lines = (j.dof * p->eb) % 128 == 0;
+  for (int k = 0; k < j.rank; ++k)
+    if (k != p->mode_r && (std::llabs(j.m[k].d) * p->eb) % 128 != 0) dst_lines = false;
+  const bool line_cfg = p->unaligned || (p->eb == 8 && !dst_lines);
+  TuneCfg base = default_cfg(p->eb, batched, line_cfg);
   if (ov.tile) base.tile = ov.tile;
   if (ov.threads) base.threads = ov.threads;
   if (ov.nt >= 0) base.nt = ov.nt;
@@ -377,7 +386,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   TuneCfg tall;
   const int64_t others = j.count / (R.e * C.e);
   // (element-aligned plans: only 16-byte elements gained, 4870 -> 5140 GB/s on 8191 x 8190)
-  if (!pinned && !batched && (!p->unaligned || p->eb == 16) && p->vb == 16 && p->step == 1 &&
+  if (!pinned && !batched && (!line_cfg || (p->unaligned && p->eb == 16)) && p->vb == 16 && p->step == 1 &&
       tall_cfg(p->eb, R.e, C.e, others, &tall))
     cands[ncand++] = tall;
   cands[ncand++] = base;
@@ -478,6 +487,16 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     }
   }
   if (p.status != TC_OK) return p;
+  // The page's rule can leave a transpose 8- or 4-byte vectors (pitches that are multiples of
+  // them but not of 16 bytes).  Outside strict mode such a transpose takes 16-byte vectors at
+  // element alignment instead, which measured 1.1-2.8x faster on MI355X (8192 x 8192 copies with
+  // pitch 8188 or 8190: int8 1960 -> ~3600 GB/s, fp16 1440-1720 -> ~4000).  Strict mode keeps the
+  // page's plan.
+  if (fast && r != c && p.vb < 16 && !(flags & TC_FLAG_STRICT)) {
+    p.reason = "the aligned split allows only " + std::to_string(p.vb) +
+               "-byte vectors: 16-byte vectors at element alignment instead";
+    fast = false;
+  }
 
   if (fast && r == c) {
     // Both sides contiguous along one mode: no cross-lane exchange needed.

@@ -136,9 +136,15 @@ def test_transpose_unaligned(eb, n, m, soff, doff, batch):
     p = L.tc_plan((shape, ss, soff), (shape, ds, doff), {1: L.TC_I8, 2: L.TC_BF16, 4: L.TC_F32, 8: L.TC_F64,
                                                           16: L.TC_B128}[eb])
     assert p["path_name"] == "transpose"
-    # 65 x 64 and 64 x 65 have an aligned 4-byte vector from 4-byte elements up
-    assert p["unaligned"] == (eb < 4 or (n, m) not in ((65, 64), (64, 65)))
+    # 65 x 64 and 64 x 65 have an aligned vector of one element from 4-byte elements up: the
+    # page's plan (strict mode) takes it; by default only 16-byte elements keep it (narrower
+    # vectors give way to 16-byte ones at element alignment)
+    page_vec = eb >= 4 and (n, m) in ((65, 64), (64, 65)) and batch == 1 and soff == doff == 0
+    assert p["unaligned"] == (eb < 16 or not page_vec)
     _check(shape, ss, ds, eb, s_off=soff, d_off=doff, seed=n + m + eb, expect="transpose")
+    if page_vec and eb < 16:
+        sp = _check(shape, ss, ds, eb, seed=n + m + eb, flags=L.TC_FLAG_STRICT, expect="transpose")
+        assert sp["vec_bytes"] == max(eb, 4) and not sp["unaligned"], sp
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
@@ -169,7 +175,7 @@ def test_transpose_tall_tiles(eb, n, m):
 
 
 @pytest.mark.parametrize("eb,n,m,tile", [(1, 8208, 8224, (512, 256)), (2, 16392, 16392, (1024, 64)),
-                                          (8, 8200, 8200, (256, 64))])
+                                          (8, 8208, 8208, (256, 64))])
 def test_transpose_128k_tiles_ragged(eb, n, m, tile):
     """128 KiB tiles (one workgroup per CU), with partial tiles along both tile modes."""
     p = _check((n, m), (m, 1), (1, n), eb, seed=n + m + eb, expect="transpose")
@@ -188,9 +194,14 @@ def test_transpose_vector_widths(eb, n):
     """n x 64 tiles: the row extent admits 16-, 8- or 4-byte vectors only, or none."""
     plan = _check((n, 64), (64, 1), (1, n), eb, seed=n + eb)
     assert plan["path_name"] == "transpose"
-    if not plan["unaligned"]:
-        ve = plan["vec_bytes"] // eb
-        assert n % ve == 0 and all(n % (v // eb) for v in (16, 8) if v > plan["vec_bytes"] and v >= eb)
+    # the page's plan (strict mode): the widest aligned vector, 16, 8 or 4 bytes
+    dt = {1: L.TC_I8, 2: L.TC_BF16, 4: L.TC_F32, 8: L.TC_F64, 16: L.TC_B128}[eb]
+    sp = L.tc_plan(((n, 64), (64, 1)), ((n, 64), (1, n)), dt, flags=L.TC_FLAG_STRICT, raise_on_error=False)
+    if sp["status"] == L.TC_OK:
+        sp = _check((n, 64), (64, 1), (1, n), eb, seed=n + eb, flags=L.TC_FLAG_STRICT, expect="transpose")
+        ve = sp["vec_bytes"] // eb
+        assert not sp["unaligned"]
+        assert n % ve == 0 and all(n % (v // eb) for v in (16, 8) if v > sp["vec_bytes"] and v >= eb)
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])

@@ -104,17 +104,27 @@ def test_vector_width_rule(eb):
         p = L.tc_plan(((n, 64), (64, 1)), ((n, 64), (1, n)), dt, raise_on_error=False)
         widths = [v for v in (16, 8, 4) if v >= eb and n % (v // eb) == 0 and 64 % (v // eb) == 0]
         if widths:
-            assert p["path_name"] == "transpose" and p["vec_bytes"] == widths[0], (eb, n, p["vec_bytes"])
-            assert not p["unaligned"]
-            # 64-byte int8 source rows leave the XOR search a few cycles short of conflict-free: the
-            # plan still runs (with the cheapest swizzle) and reports why it is not the page's plan
-            assert not p["declined"] or ("XOR swizzle" in p["reason"] and p["write_conflicts"] + p["read_conflicts"] > 0)
+            # strict mode: the page's plan, the widest vector that divides
+            s = L.tc_plan(((n, 64), (64, 1)), ((n, 64), (1, n)), dt, flags=L.TC_FLAG_STRICT, raise_on_error=False)
+            assert s["path_name"] == "transpose" and s["vec_bytes"] == widths[0], (eb, n, s["vec_bytes"])
+            assert not s["unaligned"]
+            # 64-byte int8 source rows leave the XOR search a few cycles short of conflict-free:
+            # strict mode declines with the reason
+            assert s["status"] == L.TC_OK or "XOR swizzle" in s["reason"], s["reason"]
+            if widths[0] == 16:
+                assert p["path_name"] == "transpose" and p["vec_bytes"] == 16 and not p["unaligned"]
+                # (the cheapest swizzle runs, and the plan says why it is not the page's plan)
+                assert not p["declined"] or ("XOR swizzle" in p["reason"] and p["write_conflicts"] + p["read_conflicts"] > 0)
+            else:  # by default, 16-byte vectors at element alignment instead of narrower ones
+                assert p["path_name"] == "transpose" and p["vec_bytes"] == 16 and p["unaligned"], (eb, n, p)
+                assert not p["declined"] and "allows only %d-byte" % widths[0] in p["reason"], p["reason"]
         else:  # the page's rule declines; the transpose runs with vectors at element alignment
             assert p["path_name"] == "transpose" and p["unaligned"] and "no vector" in p["reason"]
             s = L.tc_plan(((n, 64), (64, 1)), ((n, 64), (1, n)), dt, flags=L.TC_FLAG_STRICT, raise_on_error=False)
             assert s["status"] == L.TC_E_DECLINED
-    # pointer alignment limits the vector
-    p = L.tc_plan(((64, 64), (64, 1)), ((64, 64), (1, 64)), dt, ptr_align=max(eb, 4))
+    # pointer alignment limits the vector of the page's plan
+    p = L.tc_plan(((64, 64), (64, 1)), ((64, 64), (1, 64)), dt, flags=L.TC_FLAG_STRICT, ptr_align=max(eb, 4),
+                  raise_on_error=False)
     assert p["vec_bytes"] == max(eb, 4) or p["path_name"] != "transpose"
 
 
