@@ -374,6 +374,9 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     if (k != p->mode_r && (std::llabs(j.m[k].d) * p->eb) % 128 != 0) dst_lines = false;
   const bool line_cfg = p->unaligned || (p->eb == 8 && !dst_lines);
   TuneCfg base = default_cfg(p->eb, batched, line_cfg);
+  // stride-2 int8 sources: row tiles first measured faster (the config-5 slice 1.64 -> 1.78
+  // TB/s; wider elements were 25-30% slower that way)
+  if (p->step == 2 && p->eb == 1) base.order = 1;
   if (ov.tile) base.tile = ov.tile;
   if (ov.threads) base.threads = ov.threads;
   if (ov.nt >= 0) base.nt = ov.nt;
