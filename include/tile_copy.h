@@ -80,7 +80,10 @@ enum tc_status {
   TC_E_DECLINED = -8,      /* strict mode: no integer [outer, threads, vec] partition,
                               no vector of >= 4 bytes, or no conflict-free swizzle */
   TC_E_HIP = -9,           /* a HIP runtime call failed (launch or device query) */
-  TC_E_RANGE = -10,        /* sizes beyond what the kernels index (e.g. > 2^31 vectors) */
+  TC_E_RANGE = -10,        /* sizes beyond what the kernels index: a transpose of 2^31 tiles or
+                              more, or a row-wise copy one of whose outermost indices holds more
+                              than 2^30 vectors (copies of 2^31 vectors and more otherwise run
+                              as several launches on the stream) */
   TC_E_ARG = -11           /* other invalid argument (bad slice, unknown flag) */
 };
 

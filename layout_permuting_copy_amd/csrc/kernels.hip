@@ -208,6 +208,31 @@ void launch_rows_t(const RowArgs& ra, int64_t wgs, hipStream_t s) {
   hipLaunchKernelGGL((dev::rows_kernel<VB, NT, kRowRounds, LDS, NTM, BURST>), dim3(uint32_t(wgs)), dim3(NT), 0, s, ra);
 }
 
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The rows-type kernel of a plan over the vectors of `ra`, in `wgs` workgroups.
+void launch_rows(const Plan& p, const RowArgs& ra, int64_t wgs, hipStream_t s) {
+  if (p.path == TC_PATH_ROUNDTRIP) {
+    if (p.vb == 16) launch_rows_t<16, kWave, true, 0>(ra, wgs, s);
+    if (p.vb == 8) launch_rows_t<8, kWave, true, 0>(ra, wgs, s);
+    if (p.vb == 4) launch_rows_t<4, kWave, true, 0>(ra, wgs, s);
+  } else if (p.path == TC_PATH_ROWS && p.row_burst) {
+    if (p.vb == 16) launch_rows_t<16, kRowThreads, false, 3, true>(ra, wgs, s);
+    if (p.vb == 8) launch_rows_t<8, kRowThreads, false, 3, true>(ra, wgs, s);
+    if (p.vb == 4) launch_rows_t<4, kRowThreads, false, 3, true>(ra, wgs, s);
+  } else if (p.path == TC_PATH_ROWS) {
+    if (p.vb == 16) launch_rows_t<16, kRowThreads, false, 3>(ra, wgs, s);
+    if (p.vb == 8) launch_rows_t<8, kRowThreads, false, 3>(ra, wgs, s);
+    if (p.vb == 4) launch_rows_t<4, kRowThreads, false, 3>(ra, wgs, s);
+  } else {
+    if (p.eb == 1) launch_rows_t<1, kGuardThreads, false, 0>(ra, wgs, s);
+    if (p.eb == 2) launch_rows_t<2, kGuardThreads, false, 0>(ra, wgs, s);
+    if (p.eb == 4) launch_rows_t<4, kGuardThreads, false, 0>(ra, wgs, s);
+    if (p.eb == 8) launch_rows_t<8, kGuardThreads, false, 0>(ra, wgs, s);
+    if (p.eb == 16) launch_rows_t<16, kGuardThreads, false, 0>(ra, wgs, s);
+  }
+}
+
 }  // namespace
 
 Div32 make_div32(uint32_t d) {
@@ -243,15 +268,26 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
     sa.dof = j.dof;
     sa.sB = p.mode_b >= 0 ? j.m[p.mode_b].s : 0;
     sa.dB = p.mode_b >= 0 ? j.m[p.mode_b].d : 0;
-    sa.nvec = j.count / 4;
-    const dim3 grid(uint32_t(p.workgroups)), block(kShuffleThreads);
-    switch (p.shuffle_c) {
-      case 8: hipLaunchKernelGGL((dev::shuffle_kernel<3, 3>), grid, block, 0, s, sa); break;
-      case 16: hipLaunchKernelGGL((dev::shuffle_kernel<4, 3>), grid, block, 0, s, sa); break;
-      case 32: hipLaunchKernelGGL((dev::shuffle_kernel<5, 3>), grid, block, 0, s, sa); break;
-      default:
-        *err = "no shuffle kernel for this block width";
-        return TC_E_ARG;
+    // one launch, or (2^31 vectors and more) launches of kLaunchVectors vectors, a whole number
+    // of blocks each (a block is C vectors)
+    const int64_t total = j.count / 4;
+    const int64_t per = total < (int64_t(1) << 31) ? total : kLaunchVectors;
+    for (int64_t v0 = 0; v0 < total; v0 += per) {
+      ShuffleArgs sc = sa;
+      const int64_t b0 = v0 / p.shuffle_c;
+      sc.so = sa.so + b0 * sa.sB;
+      sc.dof = sa.dof + b0 * sa.dB;
+      sc.nvec = std::min(per, total - v0);
+      const dim3 grid(uint32_t(ceil_div(sc.nvec, int64_t(kShuffleThreads) * kShuffleRounds))), block(kShuffleThreads);
+      switch (p.shuffle_c) {
+        case 8: hipLaunchKernelGGL((dev::shuffle_kernel<3, 3>), grid, block, 0, s, sc); break;
+        case 16: hipLaunchKernelGGL((dev::shuffle_kernel<4, 3>), grid, block, 0, s, sc); break;
+        case 32: hipLaunchKernelGGL((dev::shuffle_kernel<5, 3>), grid, block, 0, s, sc); break;
+        default:
+          *err = "no shuffle kernel for this block width";
+          return TC_E_ARG;
+      }
+      if (hipPeekAtLastError() != hipSuccess) break;
     }
   } else if (p.path == TC_PATH_TRANSPOSE || p.path == TC_PATH_GUARDED_TILE) {
     TransposeArgs ta{};
@@ -309,36 +345,38 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
     ra.dst_off = j.dof * p.eb;
     const int ve = p.vb / p.eb;
     ra.rank = j.rank;
+    int64_t ext[kMaxRank] = {};
     for (int k = 0; k < j.rank; ++k) {
       const bool inner = (p.path != TC_PATH_GUARDED_ROWS) && k == j.rank - 1;
-      const int64_t e = inner ? j.m[k].e / ve : j.m[k].e;
-      ra.ext[k] = uint32_t(e);
-      const Div32 dv = make_div32(uint32_t(e));
-      ra.mul[k] = dv.mul;
-      ra.shr[k] = dv.shr;
+      ext[k] = inner ? j.m[k].e / ve : j.m[k].e;
       ra.s[k] = j.m[k].s * p.eb * (inner ? ve : 1);
       ra.d[k] = j.m[k].d * p.eb * (inner ? ve : 1);
     }
-    ra.nvec = j.count / (p.path == TC_PATH_GUARDED_ROWS ? 1 : ve);
-    const int64_t wgs = p.workgroups;
-    if (p.path == TC_PATH_ROUNDTRIP) {
-      if (p.vb == 16) launch_rows_t<16, kWave, true, 0>(ra, wgs, s);
-      if (p.vb == 8) launch_rows_t<8, kWave, true, 0>(ra, wgs, s);
-      if (p.vb == 4) launch_rows_t<4, kWave, true, 0>(ra, wgs, s);
-    } else if (p.path == TC_PATH_ROWS && p.row_burst) {
-      if (p.vb == 16) launch_rows_t<16, kRowThreads, false, 3, true>(ra, wgs, s);
-      if (p.vb == 8) launch_rows_t<8, kRowThreads, false, 3, true>(ra, wgs, s);
-      if (p.vb == 4) launch_rows_t<4, kRowThreads, false, 3, true>(ra, wgs, s);
-    } else if (p.path == TC_PATH_ROWS) {
-      if (p.vb == 16) launch_rows_t<16, kRowThreads, false, 3>(ra, wgs, s);
-      if (p.vb == 8) launch_rows_t<8, kRowThreads, false, 3>(ra, wgs, s);
-      if (p.vb == 4) launch_rows_t<4, kRowThreads, false, 3>(ra, wgs, s);
-    } else {
-      if (p.eb == 1) launch_rows_t<1, kGuardThreads, false, 0>(ra, wgs, s);
-      if (p.eb == 2) launch_rows_t<2, kGuardThreads, false, 0>(ra, wgs, s);
-      if (p.eb == 4) launch_rows_t<4, kGuardThreads, false, 0>(ra, wgs, s);
-      if (p.eb == 8) launch_rows_t<8, kGuardThreads, false, 0>(ra, wgs, s);
-      if (p.eb == 16) launch_rows_t<16, kGuardThreads, false, 0>(ra, wgs, s);
+    const int64_t total = j.count / (p.path == TC_PATH_GUARDED_ROWS ? 1 : ve);
+    // one launch, or (2^31 vectors and more) launches over ranges of the outermost grid mode of
+    // at most kLaunchVectors vectors each (the planner has checked that one index fits)
+    const int64_t per0 = j.rank >= 1 ? total / ext[0] : 1;  // vectors per index of mode 0
+    const int64_t step0 = total < (int64_t(1) << 31) || j.rank < 1 ? std::max<int64_t>(ext[0], 1)
+                                                                    : std::max<int64_t>(kLaunchVectors / per0, 1);
+    for (int64_t i0 = 0; i0 < std::max<int64_t>(ext[0], 1); i0 += step0) {
+      RowArgs rc = ra;
+      if (j.rank >= 1) {
+        const int64_t n0 = std::min(step0, ext[0] - i0);
+        rc.src_off = ra.src_off + i0 * ra.s[0];
+        rc.dst_off = ra.dst_off + i0 * ra.d[0];
+        for (int k = 0; k < j.rank; ++k) {
+          const int64_t e = k == 0 ? n0 : ext[k];
+          rc.ext[k] = uint32_t(e);
+          const Div32 dv = make_div32(uint32_t(e));
+          rc.mul[k] = dv.mul;
+          rc.shr[k] = dv.shr;
+        }
+        rc.nvec = n0 * per0;
+      } else {
+        rc.nvec = total;
+      }
+      launch_rows(p, rc, ceil_div(rc.nvec, int64_t(p.threads) * kRowRounds), s);
+      if (hipPeekAtLastError() != hipSuccess) break;
     }
   }
   const hipError_t e = hipGetLastError();

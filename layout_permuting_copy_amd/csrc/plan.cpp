@@ -430,6 +430,13 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   return true;
 }
 
+// Rows-type copies of 2^31 vectors or more launch ranges of the outermost grid mode, at most
+// kLaunchVectors vectors each: one index of that mode must fit one launch.
+static bool rows_fit(const Joint& j, int64_t nvec) {
+  if (nvec < (int64_t(1) << 31) || j.rank <= 1) return true;
+  return nvec / j.m[0].e <= kLaunchVectors;
+}
+
 Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags, int ptr_align) {
   Plan p;
   std::string err;
@@ -517,9 +524,9 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     p.workgroups = ceil_div(nvec, per_wg);
     p.load_outer = p.store_outer = int(std::min<int64_t>(kRowRounds, ceil_div(nvec, p.threads)));
     p.lds_bytes = lds ? int(per_wg * p.vb) : 0;
-    if (nvec >= (int64_t(1) << 31)) {
+    if (!rows_fit(j, nvec)) {
       p.status = TC_E_RANGE;
-      p.reason = "more than 2^31 vectors";
+      p.reason = "more than 2^30 vectors per index of the outermost mode";
     }
     return p;
   }
@@ -543,11 +550,7 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
       p.load_outer = p.store_outer = kShuffleRounds;
       p.ntm = 3;
       const int64_t nvec = j.count / 4;
-      p.workgroups = ceil_div(nvec, int64_t(kShuffleThreads) * kShuffleRounds);
-      if (nvec >= (int64_t(1) << 31)) {
-        p.status = TC_E_RANGE;
-        p.reason = "more than 2^31 vectors";
-      }
+      p.workgroups = ceil_div(nvec, int64_t(kShuffleThreads) * kShuffleRounds);  // over all launches
       return p;
     }
   }
@@ -674,7 +677,10 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     p.threads = kGuardThreads;
     p.load_outer = p.store_outer = kRowRounds;
     p.workgroups = ceil_div(j.count, int64_t(kGuardThreads) * kRowRounds);
-    if (j.count >= (int64_t(1) << 31)) { p.status = TC_E_RANGE; p.reason = "more than 2^31 elements on the guarded path"; }
+    if (!rows_fit(j, j.count)) {
+      p.status = TC_E_RANGE;
+      p.reason = "more than 2^30 elements per index of the outermost mode on the guarded path";
+    }
   }
   return p;
 }

@@ -24,6 +24,9 @@ constexpr int kRowThreads = TC_ROW_THREADS;    // threads per workgroup on the r
 constexpr int kRowRounds = TC_ROW_ROUNDS;      // vectors per thread on the rows path
 constexpr int64_t kRowSmallBytes = int64_t(256) << 20;  // rows path: "small" contiguous copies
 constexpr int kGuardThreads = 256;             // threads per workgroup on the guarded paths
+// Rows-type and shuffle copies of 2^31 vectors or more run as several launches of at most this
+// many vectors each (the kernels index vectors and workgroups with 32-bit integers).
+constexpr int64_t kLaunchVectors = int64_t(1) << 30;
 
 // One joint mode: extent, source stride, destination stride (elements).
 struct Mode {

@@ -198,6 +198,14 @@ def make_source(w: Workload) -> np.ndarray:
     return make_values(w.dtype, w.values, storage_elems(w, "src"), w.seed)
 
 
+def device_bits(torch, nbytes: int, seed: int):
+    """`nbytes` uniformly random bytes generated on the GPU from a seeded torch generator, for
+    copies too large to stage through the host (tens of GiB)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda", generator=g)
+
+
 def sentinel_dst(w: Workload, byte: int = 0xA5) -> np.ndarray:
     """Destination storage prefilled with a sentinel byte, so writes outside the
     destination image are visible."""

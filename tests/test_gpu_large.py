@@ -1,0 +1,73 @@
+"""Copies of 2^31 vectors and more (32 GiB per side, sized for a GPU with 288 GB of HBM): they
+run as several launches.  Checked against the oracle's offsets on sampled elements (the whole
+copy is too large to redo on the host), bytes past the destination image against a sentinel,
+and the identity copy also whole on the device."""
+
+import numpy as np
+import pytest
+
+import layout_permuting_copy_amd as L
+import synth_inputs as SI
+from gpu_util import say
+from oracle import ref as R
+
+pytestmark = pytest.mark.gpu
+
+TAIL = 4096  # sentinel bytes past the destination image
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    free, _ = torch.cuda.mem_get_info()
+    if free < (112 << 30):
+        pytest.skip("needs 112 GiB of free device memory")
+    L.load_library()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _sampled(torch, src, dst, sl, dl, eb, count, seed):
+    rng = np.random.default_rng(seed)
+    flat = np.unique(np.concatenate([rng.integers(0, count, 1 << 16), [0, count - 1]]))
+    so, do = R.sample_offsets(sl, dl, flat)
+    s = src.view(-1, eb)
+    d = dst.view(-1, eb)
+    a = s[torch.from_numpy(so).to("cuda")].cpu().numpy()
+    b = d[torch.from_numpy(do).to("cuda")].cpu().numpy()
+    assert np.array_equal(a, b), f"{int((a != b).any(axis=1).sum())} of {len(flat)} sampled elements differ"
+
+
+def _run(torch, shape, ss, ds, eb, dtype, seed, expect):
+    count = int(np.prod(shape))
+    nbytes = count * eb
+    sl, dl = (shape, ss, 0), (shape, ds, 0)
+    say(f"[gpu-large] shape={shape} eb={eb} bytes={nbytes}")
+    src = SI.device_bits(torch, nbytes, seed)
+    dst = torch.full((nbytes + TAIL,), 0xA5, dtype=torch.uint8, device="cuda")
+    plan = L.tile_copy_ex(src, sl, dst, dl, dtype)
+    torch.cuda.synchronize()
+    assert plan["path_name"] == expect, plan
+    _sampled(torch, src, dst, sl, dl, eb, count, seed)
+    assert bool((dst[nbytes:] == 0xA5).all()), "bytes past the destination image were written"
+    return src, dst, nbytes
+
+
+def test_contiguous_copy_of_more_than_2_31_vectors():
+    import torch
+    n = (1 << 33) + (1 << 20)  # fp32 elements: 2^31 + 2^18 vectors, 32 GiB + 4 MiB
+    src, dst, nbytes = _run(torch, (n,), (1,), (1,), 4, L.TC_F32, 61, "rows")
+    assert torch.equal(src, dst[:nbytes])
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def test_shuffle_blocks_beyond_2_31_vectors():
+    import torch
+    b = (1 << 26) + 1000  # 4 x 32 fp32 blocks: 2^31 + 32000 vectors
+    src, dst, _ = _run(torch, (b, 4, 32), (128, 32, 1), (128, 1, 4), 4, L.TC_F32, 62, "shuffle")
+    del src, dst
+    torch.cuda.empty_cache()

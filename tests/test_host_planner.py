@@ -302,6 +302,28 @@ def test_interior_kernel_only_for_exact_tilings():
     assert edge((8190, 4095), (8192, 2), (1, 8190), L.TC_F16, 8192) == 1   # stride-2 source
 
 
+def test_copies_beyond_2_31_vectors_plan():
+    """Contiguous and shuffle copies of 2^31 vectors or more (32 GiB and up, sized for a 288 GB
+    GPU) plan as several launches; only a single outermost index of more than 2^30 vectors is
+    out of range."""
+    n = 1 << 33  # fp32 elements: 2^31 16-byte vectors
+    p = L.tc_plan(((n,), (1,)), ((n,), (1,)), L.TC_F32)
+    assert p["path_name"] == "rows" and p["workgroups"] == (1 << 31) // (p["threads"] * p["load_outer"])
+    # two non-mergeable rows of 2^32 elements (2^30 vectors each): fits one launch per row
+    p = L.tc_plan(((2, 1 << 32), ((1 << 32) + 64, 1)), ((2, 1 << 32), (1 << 32, 1)), L.TC_F32)
+    assert p["status"] == L.TC_OK and p["path_name"] == "rows", p["error"]
+    # a row of 2^33 elements (2^31 vectors) under an outer mode: out of range
+    p = L.tc_plan(((2, 1 << 33), ((1 << 33) + 64, 1)), ((2, 1 << 33), (1 << 33, 1)), L.TC_F32, raise_on_error=False)
+    assert p["status"] == L.TC_E_RANGE and "outermost" in p["error"]
+    # 2^26 scale-factor blocks of 4 x 32 fp32: 2^31 vectors on the register butterfly
+    b = 1 << 26
+    p = L.tc_plan(((b, 4, 32), (128, 32, 1)), ((b, 4, 32), (128, 1, 4)), L.TC_F32)
+    assert p["path_name"] == "shuffle" and p["workgroups"] == (b * 32) // (256 * 8)
+    # element-wise guarded rows of 2^31 elements
+    p = L.tc_plan(((1 << 31,), (3,)), ((1 << 31,), (2,)), L.TC_I8)
+    assert p["status"] == L.TC_OK and p["path_name"] == "guarded_rows", p
+
+
 def test_no_kernel_uses_scratch_memory():
     """Every kernel keeps its per-lane data in registers: the compiler reports no scratch (a
     private array it cannot promote would turn into extra memory instructions per tile)."""
