@@ -71,3 +71,13 @@ def test_shuffle_blocks_beyond_2_31_vectors():
     src, dst, _ = _run(torch, (b, 4, 32), (128, 32, 1), (128, 1, 4), 4, L.TC_F32, 62, "shuffle")
     del src, dst
     torch.cuda.empty_cache()
+
+
+def test_transpose_of_32_gib():
+    """A bf16 transpose of 2^17 x 2^17 (2^34 elements, 32 GiB per side): 64-bit offsets on every
+    path of the tile kernel."""
+    import torch
+    n = 1 << 17
+    src, dst, _ = _run(torch, (n, n), (n, 1), (1, n), 2, L.TC_BF16, 63, "transpose")
+    del src, dst
+    torch.cuda.empty_cache()
