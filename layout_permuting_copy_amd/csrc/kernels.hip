@@ -4,8 +4,10 @@
 // rows_kernel: both sides contiguous along one mode; vectors are staged in registers (or, for
 //   the round-trip variant, through LDS as in the gmem_smem demonstration program).  With one
 //   element per "vector" it is also the guarded element-wise fallback.
+// shuffle_kernel: batches of 4 x C blocks of 4-byte elements, transposed by exchanging 16-byte
+//   vectors between lanes (ds_swizzle), no LDS.
 // guarded_tile_kernel: fallback LDS tile with element-wide accesses and per-element guards,
-//   for extents or strides that admit no vector (odd extents, strided slices).
+//   for layouts the vector paths do not take (FORCE_GUARDED, or no unit-stride mode to vectorize).
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -84,8 +86,6 @@ __global__ void __launch_bounds__(NT) rows_kernel(RowArgs a) {
   if (BURST && (int64_t(blockIdx.x) + 1) * NT * ROUNDS <= a.nvec) rows_body<VB, NT, ROUNDS, USE_LDS, NTM, false, BURST>(a, lds);
   else rows_body<VB, NT, ROUNDS, USE_LDS, NTM, true, BURST>(a, lds);
 }
-
-// Fallback tile: element-wide accesses, padded LDS rows, guards on every element.
 
 // Fallback tile: element-wide accesses, padded LDS rows, guards on every element.
 template <int EB>
