@@ -178,24 +178,41 @@ __device__ __forceinline__ uint32_t udiv(uint32_t n, const Div32& d) {
 }
 
 // Tile `tile` of the grid: column tiles fastest, then row tiles (or the other way round when
-// a.order is 1), then batch tiles, then the remaining grid modes (innermost last).  Returns the
+// a.order is 1; XCD super-tiles when it is 2), then batch tiles, then the remaining grid modes (innermost last).  Returns the
 // tile's first element on both sides and how much of each tile extent lies inside the copy.
 struct TileAt {
   int64_t sbase, dbase;
   int64_t remR, remC, remB;
+  bool valid;  // false: a padding workgroup of order 2 (no tile; it returns at once)
 };
 
 __device__ __forceinline__ TileAt tile_at(const TransposeArgs& a, uint32_t tile) {
-  uint32_t idx = tile;
-  const Div32& first = a.order ? a.tilesR : a.tilesC;
-  const Div32& second = a.order ? a.tilesC : a.tilesR;
-  uint32_t q = udiv(idx, first);
-  const uint32_t i0 = idx - q * first.d;
-  idx = q;
-  q = udiv(idx, second);
-  const uint32_t i1 = idx - q * second.d;
-  const uint32_t tcI = a.order ? i1 : i0, trI = a.order ? i0 : i1;
-  idx = q;
+  uint32_t idx = tile, q, tcI, trI;
+  bool valid = true;
+  if (a.order == 2) {
+    // XCD x = idx % kXcds takes super-tiles x, x + kXcds, ..; the kSuper^2 tiles of a super-tile
+    // are consecutive in that XCD's share of the grid, column tiles fastest inside it
+    const uint32_t x = idx % kXcds, k = idx / kXcds;
+    const uint32_t w = k % (kSuper * kSuper);
+    const uint32_t gst = (k / (kSuper * kSuper)) * kXcds + x;  // super-tile over all slices
+    const uint32_t slice = gst / a.nst, st = gst - slice * a.nst;
+    q = udiv(st, a.stC);
+    trI = q * kSuper + w / kSuper;
+    tcI = (st - q * a.stC.d) * kSuper + w % kSuper;
+    valid = slice < a.nslices && trI < a.tilesR.d && tcI < a.tilesC.d;
+    idx = valid ? slice : 0;
+  } else {
+    const Div32& first = a.order ? a.tilesR : a.tilesC;
+    const Div32& second = a.order ? a.tilesC : a.tilesR;
+    q = udiv(idx, first);
+    const uint32_t i0 = idx - q * first.d;
+    idx = q;
+    q = udiv(idx, second);
+    const uint32_t i1 = idx - q * second.d;
+    tcI = a.order ? i1 : i0;
+    trI = a.order ? i0 : i1;
+    idx = q;
+  }
   q = udiv(idx, a.tilesB);
   const uint32_t tbI = idx - q * a.tilesB.d;
   idx = q;
@@ -214,6 +231,7 @@ __device__ __forceinline__ TileAt tile_at(const TransposeArgs& a, uint32_t tile)
   t.remR = a.eR - r0;
   t.remC = a.eC - c0;
   t.remB = a.eB - b0;
+  t.valid = valid;
   return t;
 }
 

@@ -99,6 +99,7 @@ __global__ void __launch_bounds__(kGuardThreads) guarded_tile_kernel(TransposeAr
   constexpr int PITCH = COLS + PAD;
   __shared__ V lds[ROWS * PITCH];
   const TileAt tl = tile_at(a, blockIdx.x);
+  if (!tl.valid) return;
   const int64_t sbase = tl.sbase, dbase = tl.dbase, remR = tl.remR, remC = tl.remC;
   const V* __restrict__ src = reinterpret_cast<const V*>(a.src);
   V* __restrict__ dst = reinterpret_cast<V*>(a.dst);
@@ -321,6 +322,13 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
       ta.xcmask = p.g.cmask;
       ta.order = p.g.order;
       fill_batch(p, &ta, p.mode_r, p.mode_c, p.mode_b);
+      if (p.g.order == 2) {  // (after fill_batch: the slices count the batch modes)
+        const uint32_t stC = (ta.tilesC.d + kSuper - 1) / kSuper, stR = (ta.tilesR.d + kSuper - 1) / kSuper;
+        ta.stC = make_div32(stC);
+        ta.nst = stR * stC;
+        ta.nslices = ta.tilesB.d;
+        for (int k = 0; k < ta.nbatch; ++k) ta.nslices *= ta.bdiv[k].d;
+      }
       const TransposeCfg cfg{p.vb, p.g.U, p.g.tile_bytes, p.g.NT, p.g.ntm, p.g.step, p.g.wave_local, p.g.edges};
       if (!launch_transpose(p.eb, cfg, &ta, p.workgroups, stream)) {
         *err = "no transpose kernel instance for this element width, vector width, tile size and thread count";

@@ -83,7 +83,8 @@ struct TileGeom {
   int NT = 256;                   // threads per workgroup
   int tile_bytes = 16384;         // LDS tile per workgroup
   int ntm = 0;                    // nontemporal global accesses: bit 0 loads, bit 1 stores
-  int order = 0;                  // grid order: 0 column tiles fastest, 1 row tiles fastest
+  int order = 0;                  // grid order: 0 column tiles fastest, 1 row tiles fastest,
+                                  // 2 XCD super-tiles (see tile_at)
   int step = 1;                   // source element stride along the column mode (1, or 2: every
                                   // vector read as two contiguous ones and compacted in registers)
   bool wave_local = false;        // every wave reads back only LDS units it wrote itself: the
@@ -162,7 +163,10 @@ struct TransposeArgs {
   int32_t lTR, lTC, lNB;     // log2 of the tile extents
   int32_t xshift, xmask, xtbit;
   int32_t xcshift, xcmask;
-  int32_t order;             // 0: column tiles fastest, 1: row tiles fastest
+  int32_t order;             // 0: column tiles fastest, 1: row tiles fastest, 2: XCD super-tiles
+  Div32 stC;                 // order 2: super-tiles along the column mode, per 2-D slice
+  uint32_t nst;              // order 2: super-tiles per 2-D slice
+  uint32_t nslices;          // order 2: 2-D slices (batch tiles times the other grid modes)
 };
 
 // The shuffle path: nvec 16-byte vectors, C/4 per block row; block b starts at element
@@ -188,6 +192,12 @@ struct RowArgs {
   int64_t s[kMaxRank], d[kMaxRank];  // element strides per step of each grid mode
   int64_t nvec;              // vectors in the whole copy
 };
+
+// Order 2: super-tiles of kSuper x kSuper tiles, each run on one XCD (the dispatcher sends
+// workgroup i to XCD i % kXcds), so that neighbouring tiles, which share cache lines when the
+// layouts are not line-aligned, meet in one L2.
+constexpr int kSuper = 8;
+constexpr int kXcds = 8;
 
 // ---- launch (kernels.hip) ------------------------------------------------------------------------
 int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::string* err);

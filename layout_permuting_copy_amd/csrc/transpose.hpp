@@ -207,6 +207,7 @@ __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   typedef Geo<EB, VB, U, TILE, NT> G;
   __shared__ __attribute__((aligned(16))) unsigned char lds[TILE];
   const TileAt t = tile_at(a, blockIdx.x);
+  if (!t.valid) return;  // padding of the XCD super-tile order (whole workgroup, before any barrier)
   TileRegs<G> r;
   const bool full = !EDGE || (tile_full(a, t) && (S == 1 || t.remC > (int64_t(1) << a.lTC)));
   if constexpr (!EDGE) load_tile<EB, VB, G, NT, NTM, S, false>(a, t, r);

@@ -147,6 +147,19 @@ def test_transpose_unaligned(eb, n, m, soff, doff, batch):
         assert sp["vec_bytes"] == max(eb, 4) and not sp["unaligned"], sp
 
 
+@pytest.mark.parametrize("eb,shape", [(1, (1000, 700)), (1, (3, 1001, 1300)), (1, (2047, 1023)), (8, (301, 299)),
+                                      (8, (2, 515, 1031)), (8, (1101, 93))])
+def test_transpose_xcd_super_tiles(eb, shape):
+    """The XCD super-tile grid order of the element-aligned int8 and fp64 plans: 8 x 8 tiles per
+    super-tile, padding workgroups where the tile grid is not a multiple of it."""
+    n, m = shape[-2], shape[-1]
+    ss, ds = (m, 1), (1, n)
+    if len(shape) == 3:
+        ss, ds = (n * m,) + ss, (n * m,) + ds
+    p = _check(shape, ss, ds, eb, seed=n * 3 + m + eb, expect="transpose")
+    assert p["unaligned"] and p["grid_order"] == 2, p
+
+
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("n,m,pitch,soff", [(40, 30, 60, 0), (129, 67, 140, 3), (64, 64, 128, 0), (33, 300, 601, 1),
                                             (7, 5, 11, 0), (300, 257, 515, 2)])
