@@ -387,7 +387,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   base.trb = ov.trb;
   base.unit = ov.unit;
   // candidate configurations: the tall tile where it pays (not under TC_TUNE), then the default
-  TuneCfg cands[2];
+  TuneCfg cands[3];
   int ncand = 0;
   TuneCfg tall;
   const int64_t others = j.count / (R.e * C.e);
@@ -395,6 +395,14 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   if (!pinned && !batched && (!line_cfg || (p->unaligned && p->eb == 16)) && p->vb == 16 && p->step == 1 &&
       tall_cfg(p->eb, R.e, C.e, others, &tall))
     cands[ncand++] = tall;
+  // Element-aligned 2-byte plans read with unit stride: tall 512 x 64 tiles with plain stores in
+  // the XCD super-tile order (fp16 8191 x 8190 3.86 -> 4.15 TB/s; with column tiles first such
+  // tiles had been slower than 64 x 64 ones)
+  if (!pinned && !batched && p->unaligned && p->eb == 2 && p->step == 1 && R.e >= 512 && C.e >= 64) {
+    TuneCfg t;
+    t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 0; t.order = 2;
+    cands[ncand++] = t;
+  }
   cands[ncand++] = base;
   if (flags & TC_FLAG_NO_SWIZZLE) ncand = 1;  // the swizzle is measured on the default plan's tile
   // wave-local phases drop the workgroup barrier where the library holds such an instance

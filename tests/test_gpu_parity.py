@@ -148,10 +148,11 @@ def test_transpose_unaligned(eb, n, m, soff, doff, batch):
 
 
 @pytest.mark.parametrize("eb,shape", [(1, (1000, 700)), (1, (3, 1001, 1300)), (1, (2047, 1023)), (8, (301, 299)),
-                                      (8, (2, 515, 1031)), (8, (1101, 93))])
+                                      (8, (2, 515, 1031)), (8, (1101, 93)), (2, (1000, 700)), (2, (2, 515, 1031)),
+                                      (2, (4097, 65))])
 def test_transpose_xcd_super_tiles(eb, shape):
-    """The XCD super-tile grid order of the element-aligned int8 and fp64 plans: 8 x 8 tiles per
-    super-tile, padding workgroups where the tile grid is not a multiple of it."""
+    """The XCD super-tile grid order of the element-aligned int8, fp16 and fp64 plans: 8 x 8 tiles
+    per super-tile, padding workgroups where the tile grid is not a multiple of it."""
     n, m = shape[-2], shape[-1]
     ss, ds = (m, 1), (1, n)
     if len(shape) == 3:
