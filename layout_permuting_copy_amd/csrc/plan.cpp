@@ -364,22 +364,21 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   const bool batched = pow2ceil(R.e) * p->eb < 128;
   const TuneCfg ov = tune_override();
   const bool pinned = ov.tile || ov.threads || ov.nt >= 0 || ov.order >= 0 || ov.trb || ov.unit;
-  // 8-byte elements whose destination columns do not start on 128-byte lines (a line-aligned base
-  // pointer assumed): the configuration of the element-aligned plans (plain stores, 16 KiB
-  // tiles, column tiles first) measured faster than the tall tiles with nontemporal stores, fp64
-  // 8190 x 8192 3.63 -> 5.24 TB/s and 8184 x 8184 3.71 -> 4.97.  (fp32, bf16 and fp16 copies of
-  // such pitches measured no better with it.)
+  // 1-, 2- and 8-byte elements whose destination columns do not start on 128-byte lines (a
+  // line-aligned base pointer assumed): the configurations of the element-aligned plans (plain
+  // stores; below) measured faster than the tall tiles with nontemporal stores: fp64 8190 x 8192
+  // 3.63 -> 5.24 TB/s and 8184 x 8184 3.71 -> 4.97, fp16 8184 x 8184 3.59 -> 4.22, int8 8176 x 8192
+  // 3.34 -> 3.51.  (fp32 such copies were 4-7% slower with it, 16-byte elements equal.)
   bool dst_lines = (j.dof * p->eb) % 128 == 0;
   for (int k = 0; k < j.rank; ++k)
     if (k != p->mode_r && (std::llabs(j.m[k].d) * p->eb) % 128 != 0) dst_lines = false;
-  const bool line_cfg = p->unaligned || (p->eb == 8 && !dst_lines);
+  const bool line_cfg = p->unaligned || ((p->eb == 1 || p->eb == 2 || p->eb == 8) && !dst_lines);
   TuneCfg base = default_cfg(p->eb, batched, line_cfg);
-  // Element-aligned plans of 1-byte elements, and of 8-byte elements read with unit stride: the
-  // XCD super-tile order, so that the neighbouring tiles that share cache lines at element
-  // alignment run in one L2 (measured: int8 8191 x 8190 3.02 -> 3.20 TB/s, the int8 slice
-  // 1.75 -> 2.06, fp64 8191 x 8190 4.81 -> 5.17; 2-byte elements equal, the 8- and 16-byte
-  // slices 8-10% slower with it)
-  if (p->unaligned && (p->eb == 1 || (p->eb == 8 && p->step == 1))) base.order = 2;
+  // 1-byte elements there, and element-aligned 8-byte elements read with unit stride: the XCD
+  // super-tile order, so that the neighbouring tiles that share cache lines at element alignment
+  // run in one L2 (measured: int8 8191 x 8190 3.02 -> 3.20 TB/s, the int8 slice 1.75 -> 2.06,
+  // fp64 8191 x 8190 4.81 -> 5.17; the 8- and 16-byte slices 8-10% slower with it)
+  if (line_cfg && (p->eb == 1 || (p->eb == 8 && p->unaligned && p->step == 1))) base.order = 2;
   if (ov.tile) base.tile = ov.tile;
   if (ov.threads) base.threads = ov.threads;
   if (ov.nt >= 0) base.nt = ov.nt;
@@ -395,10 +394,10 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   if (!pinned && !batched && (!line_cfg || (p->unaligned && p->eb == 16)) && p->vb == 16 && p->step == 1 &&
       tall_cfg(p->eb, R.e, C.e, others, &tall))
     cands[ncand++] = tall;
-  // Element-aligned 2-byte plans read with unit stride: tall 512 x 64 tiles with plain stores in
-  // the XCD super-tile order (fp16 8191 x 8190 3.86 -> 4.15 TB/s; with column tiles first such
-  // tiles had been slower than 64 x 64 ones)
-  if (!pinned && !batched && p->unaligned && p->eb == 2 && p->step == 1 && R.e >= 512 && C.e >= 64) {
+  // 2-byte elements there, read with unit stride: tall 512 x 64 tiles with plain stores in the XCD
+  // super-tile order (fp16 8191 x 8190 3.86 -> 4.15 TB/s; with column tiles first such tiles had
+  // been slower than 64 x 64 ones)
+  if (!pinned && !batched && line_cfg && p->eb == 2 && p->step == 1 && R.e >= 512 && C.e >= 64) {
     TuneCfg t;
     t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 0; t.order = 2;
     cands[ncand++] = t;

@@ -188,10 +188,11 @@ def test_transpose_tall_tiles(eb, n, m):
     assert p["lds_read_bytes"] == 16 and p["grid_order"] == 1
 
 
-@pytest.mark.parametrize("eb,n,m,tile", [(1, 8208, 8224, (512, 256)), (2, 16392, 16392, (1024, 64)),
+@pytest.mark.parametrize("eb,n,m,tile", [(1, 8320, 8224, (512, 256)), (2, 16448, 16392, (1024, 64)),
                                           (8, 8208, 8208, (256, 64))])
 def test_transpose_128k_tiles_ragged(eb, n, m, tile):
-    """128 KiB tiles (one workgroup per CU), with partial tiles along both tile modes."""
+    """128 KiB tiles (one workgroup per CU), with partial tiles along both tile modes (destination
+    columns on 128-byte lines: other pitches take the element-aligned plans' configuration)."""
     p = _check((n, m), (m, 1), (1, n), eb, seed=n + m + eb, expect="transpose")
     assert p["lds_bytes"] == 131072 and (p["tile_r"], p["tile_c"]) == tile, p
 
