@@ -10,7 +10,14 @@
 //     local_idx = (access_idx // threads) * vec + flat % vec).
 // The copy declines ("What it accepts", divisibility) when the element count is not a multiple
 // of the thread count of a wavefront (64 on gfx950): there is no integer [outer, threads, vec]
-// split.  Strict mode reports that; otherwise a guarded element-wise path runs.
+// split.  Strict mode reports that (TC_E_DECLINED); otherwise the transpose kernel runs with
+// 16-byte vectors at element alignment where the layouts have unit-stride (or stride-2 source)
+// modes, else a guarded path.  Outside strict mode the same element-aligned vectors also replace
+// the page's 8- and 4-byte ones, which measured slower.
+//
+// Tile shapes, thread counts, nontemporal hints and grid orders are chosen per element width
+// and layout class from measurements on MI355X (each rule below names what it measured);
+// TC_TUNE (environment) overrides them for sweeps.
 //
 // When the source- and destination-contiguous modes differ, a workgroup stages a tile through
 // LDS.  The swizzle of that tile is chosen as in TVM TIRx docs, "permute_layout", Algorithm
@@ -79,8 +86,9 @@ static void decline(Plan* p, int flags, const std::string& why) {
 // Tile bytes, threads per workgroup and the nontemporal hint are chosen per element width from
 // measurements on MI355X (16384x16384 / 8192x8192 transposes and the batched 4x32 scale-factor
 // tiles, HIP-event timed, HBM-resident inputs).  TC_TUNE (environment, read once) overrides
-// them for tuning sweeps: "tile=32768,threads=512,nt=3,order=0,trb=128,unit=4,wl=0" (wl=0: keep the
-// workgroup barrier even where the phases are wave-local).
+// them for tuning sweeps: "tile=32768,threads=512,nt=3,order=0,trb=128,unit=4,wl=0" (order: 0
+// column tiles first, 1 row tiles first, 2 XCD super-tiles; wl=0: keep the workgroup barrier even
+// where the phases are wave-local).
 struct TuneCfg {
   int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1;
 };
@@ -117,12 +125,12 @@ static TuneCfg tune_override() {
 
 // Defaults per element width: {tile bytes, threads, nontemporal mode, grid order}.  `batched` =
 // the destination-contiguous extent is shorter than one 128-byte run, so the tile is filled from
-// a batch mode (the scale-factor case).  `unaligned` = vectors at element alignment: there a
-// destination cache line is shared by two tiles, and nontemporal stores of such partial lines
-// were measured 1.5-2x slower than plain ones, as were large tiles.
-static TuneCfg default_cfg(int eb, bool batched, bool unaligned) {
+// a batch mode (the scale-factor case).  `lines_shared` = vectors at element alignment, or
+// destination columns off the 128-byte lines: neighbouring tiles then share cache lines, and
+// nontemporal stores of partial lines were measured 1.5-2x slower than plain ones.
+static TuneCfg default_cfg(int eb, bool batched, bool lines_shared) {
   TuneCfg c;
-  if (unaligned) {
+  if (lines_shared) {
     c.tile = eb == 2 ? 8192 : 16384;
     c.threads = eb == 2 ? 256 : 512;
     c.nt = 0;
