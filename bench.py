@@ -86,7 +86,7 @@ def _time_workload(torch, L, w: SI.Workload, steps: int, warmup: int, host_src, 
     pair_bytes = (SI.storage_elems(w, "src") + SI.storage_elems(w, "dst")) * w.eb
     # rotate so that more than 2x the MALL is touched between reuses of a pair (cap: 8 GiB)
     pairs = max(2, -(-2 * MALL_BYTES // pair_bytes) + 1)
-    pairs = max(1, min(pairs, (8 << 30) // pair_bytes))
+    pairs = max(1, min(pairs, (8 << 30) // pair_bytes, 64))  # (tiny copies: latency, not bandwidth)
     srcs, dsts = device_tensors(torch, w, pairs, host_src, seed)
     # marshalled once, as a caller issuing the same copy repeatedly would
     sl = L.make_layout(w.src.shape, w.src.stride, w.src.offset)
@@ -131,6 +131,7 @@ def _time_workload(torch, L, w: SI.Workload, steps: int, warmup: int, host_src, 
     out["gbs_kernel_median"] = bytes_step / (out["kernel_ms_median"] * 1e-3) / 1e9
     out["gbs_event_pair"] = bytes_step / (out["event_pair_ms_mean"] * 1e-3) / 1e9
     out["pct_peak_kernel"] = 100 * out["gbs_kernel"] / PEAK_HBM_GBS
+    out["us_per_launch"] = out["kernel_ms_mean"] * 1e3
     # sampled parity of the last destination written against the oracle's offsets
     out["_last"] = (srcs[(steps - 1) % pairs], dsts[(steps - 1) % pairs])
     del srcs, dsts
@@ -305,7 +306,8 @@ def main() -> int:
         torch.cuda.empty_cache()
         # the alternatives the planner does not pick, for comparison: the SF tiles on the LDS tile
         # kernel, the (0,2,1,3) permute staged through LDS
-        runs = [(sw, 0) for sw in [identity_workload()] + sweep_workloads()]
+        # (the 32 x 32 round trip by one wave is a latency case: see its us_per_launch)
+        runs = [(sw, 0) for sw in [SI.tile32_roundtrip(), identity_workload()] + sweep_workloads()]
         runs += [(SI.sf_transpose(), L.TC_FLAG_NO_SHUFFLE), (SI.permute0213(), L.TC_FLAG_FORCE_LDS)]
         for sw, fl in runs:
             s = time_workload(torch, L, sw, 30, 3, seed=11, flags=fl)
