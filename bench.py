@@ -272,7 +272,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the copy has no multi-GPU path "
-                                   "in this build (--gpus must be 1)"}))
+                                   "(--gpus must be 1)"}))
         return 2
     for k in ("RANK", "WORLD_SIZE"):
         if int(os.environ.get(k, "0" if k == "RANK" else "1")) != (0 if k == "RANK" else 1):

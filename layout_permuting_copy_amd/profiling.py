@@ -1,6 +1,6 @@
 """rocprofv3 collection and summaries for the tile-copy kernels.
 
-    python -m layout_permuting_copy_amd.profiling --raw gpurun_out/prof --out profiles [--quick]
+    python -m layout_permuting_copy_amd.profiling --raw <raw output dir> --out profiles [--quick]
 
 runs, as child processes (this process never touches the GPU):
 
@@ -27,6 +27,7 @@ import json
 import os
 import re
 import subprocess
+import tempfile
 import sys
 from collections import defaultdict
 
@@ -234,7 +235,7 @@ def collect_wave_permute(raw: str, out: str) -> None:
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--raw", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--raw", default=os.path.join(tempfile.gettempdir(), "tile_copy_prof"))
     ap.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     ap.add_argument("--quick", action="store_true", help="counters for the benchmark workload and calibration only")
     ap.add_argument("--wave-permute", action="store_true", help="only the device wave permute's counters")
