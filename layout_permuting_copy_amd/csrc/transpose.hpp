@@ -236,10 +236,11 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 }  // namespace dev
 }  // namespace tc
 
-// Instantiation list of one element width: every (vector bytes, tile bytes, threads,
-// nontemporal mode, source step, phase ordering) the planner can choose, with the smallest LDS
-// unit.  Step 2 (strided sources) only in the configurations of the element-aligned plans;
-// wave-local ordering in the small batched tiles, where it occurs.
+// Instantiation list of one element width: every (vector bytes, LDS unit, tile bytes, threads,
+// nontemporal mode, source step, phase ordering, edge code) the planner can choose.  16- and
+// 8-byte LDS units for the tall tiles; step 2 (strided sources) only in the configurations of the
+// element-aligned plans; wave-local ordering in the small batched tiles, where it occurs; the
+// interior-only variants (EDGE = false) of the nontemporal configurations.
 #define TC_TRANSPOSE_DISPATCH(EB)                                                                           \
   bool launch_transpose_eb##EB(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream) {   \
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);                                             \
