@@ -87,6 +87,60 @@ __global__ void __launch_bounds__(NT) rows_kernel(RowArgs a) {
   else rows_body<VB, NT, ROUNDS, USE_LDS, NTM, true, BURST>(a, lds);
 }
 
+// Copies n < 16 bytes in at most four accesses of 8, 4, 2 and 1 bytes (at any alignment: gfx950
+// global memory takes unaligned accesses), rather than one access per element.
+__device__ __forceinline__ void copy_short(const unsigned char* __restrict__ p, unsigned char* __restrict__ q, int n) {
+  int o = 0;
+  if (n & 8) {
+    *reinterpret_cast<uint64_t*>(q) = *reinterpret_cast<const uint64_t*>(p);
+    o = 8;
+  }
+  if (n & 4) {
+    *reinterpret_cast<uint32_t*>(q + o) = *reinterpret_cast<const uint32_t*>(p + o);
+    o += 4;
+  }
+  if (n & 2) {
+    *reinterpret_cast<uint16_t*>(q + o) = *reinterpret_cast<const uint16_t*>(p + o);
+    o += 2;
+  }
+  if (n & 1) q[o] = p[o];
+}
+
+// Element-aligned rows: 16-byte vectors at element alignment along rows of `row_elems` elements
+// (both sides contiguous along them); a row's short last vector is copied in the store phase in at
+// most four accesses (copy_short).  All offsets first, then every load of a thread, then the
+// stores; whole vectors nontemporal (measured 5-12% faster than plain accesses here).
+template <int EB, int NT, int ROUNDS>
+__global__ void __launch_bounds__(NT) rows_unaligned_kernel(RowArgs a) {
+  constexpr int VE = 16 / EB;
+  const int t = threadIdx.x;
+  const int64_t base = int64_t(blockIdx.x) * NT * ROUNDS;
+  int64_t soff[ROUNDS], doff[ROUNDS];
+  int cnt[ROUNDS];
+  uint32_t reg[ROUNDS][4];
+#pragma unroll
+  for (int f = 0; f < ROUNDS; ++f) {
+    const int64_t v = base + f * NT + t;
+    cnt[f] = 0;
+    if (v < a.nvec) {
+      const uint32_t inner = a.ext[a.rank - 1];
+      const uint32_t k = uint32_t(v) - uint32_t((uint64_t(__umulhi(uint32_t(v), a.mul[a.rank - 1])) + uint32_t(v)) >>
+                                                a.shr[a.rank - 1]) * inner;  // vector index within its row
+      row_offsets(a, uint32_t(v), &soff[f], &doff[f]);
+      const int64_t left = a.row_elems - int64_t(k) * VE;
+      cnt[f] = left < VE ? int(left) : VE;
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < ROUNDS; ++f)
+    if (cnt[f] == VE) gload<16, 3>(a.src + soff[f], reg[f]);
+#pragma unroll
+  for (int f = 0; f < ROUNDS; ++f) {
+    if (cnt[f] == VE) gstore<16, 3>(a.dst + doff[f], reg[f]);
+    else if (cnt[f] > 0) copy_short(a.src + soff[f], a.dst + doff[f], cnt[f] * EB);
+  }
+}
+
 // Fallback tile: element-wide accesses, padded LDS rows, guards on every element.
 template <int EB>
 __global__ void __launch_bounds__(kGuardThreads) guarded_tile_kernel(TransposeArgs a) {
@@ -213,7 +267,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // The rows-type kernel of a plan over the vectors of `ra`, in `wgs` workgroups.
 void launch_rows(const Plan& p, const RowArgs& ra, int64_t wgs, hipStream_t s) {
-  if (p.path == TC_PATH_ROUNDTRIP) {
+  if (p.path == TC_PATH_ROWS && p.unaligned) {
+    const dim3 grid = dim3(uint32_t(wgs)), block = dim3(kRowThreads);
+    if (p.eb == 1) hipLaunchKernelGGL((dev::rows_unaligned_kernel<1, kRowThreads, kRowRounds>), grid, block, 0, s, ra);
+    if (p.eb == 2) hipLaunchKernelGGL((dev::rows_unaligned_kernel<2, kRowThreads, kRowRounds>), grid, block, 0, s, ra);
+    if (p.eb == 4) hipLaunchKernelGGL((dev::rows_unaligned_kernel<4, kRowThreads, kRowRounds>), grid, block, 0, s, ra);
+    if (p.eb == 8) hipLaunchKernelGGL((dev::rows_unaligned_kernel<8, kRowThreads, kRowRounds>), grid, block, 0, s, ra);
+  } else if (p.path == TC_PATH_ROUNDTRIP) {
     if (p.vb == 16) launch_rows_t<16, kWave, true, 0>(ra, wgs, s);
     if (p.vb == 8) launch_rows_t<8, kWave, true, 0>(ra, wgs, s);
     if (p.vb == 4) launch_rows_t<4, kWave, true, 0>(ra, wgs, s);
@@ -354,13 +414,16 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
     const int ve = p.vb / p.eb;
     ra.rank = j.rank;
     int64_t ext[kMaxRank] = {};
+    int64_t total = 1;
     for (int k = 0; k < j.rank; ++k) {
       const bool inner = (p.path != TC_PATH_GUARDED_ROWS) && k == j.rank - 1;
-      ext[k] = inner ? j.m[k].e / ve : j.m[k].e;
+      // (element-aligned rows: the last vector of a row may be short)
+      ext[k] = inner ? (j.m[k].e + ve - 1) / ve : j.m[k].e;
       ra.s[k] = j.m[k].s * p.eb * (inner ? ve : 1);
       ra.d[k] = j.m[k].d * p.eb * (inner ? ve : 1);
+      total *= ext[k];
     }
-    const int64_t total = j.count / (p.path == TC_PATH_GUARDED_ROWS ? 1 : ve);
+    ra.row_elems = j.rank >= 1 ? j.m[j.rank - 1].e : 1;
     // one launch, or (2^31 vectors and more) launches over ranges of the outermost grid mode of
     // at most kLaunchVectors vectors each (the planner has checked that one index fits)
     const int64_t per0 = j.rank >= 1 ? total / ext[0] : 1;  // vectors per index of mode 0

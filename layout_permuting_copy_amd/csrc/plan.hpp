@@ -121,7 +121,7 @@ struct Plan {
   Joint j;
   int vb = 0;                       // global vector bytes
   int ntm = 0;                      // rows path: nontemporal global accesses (bit 0 loads, bit 1 stores)
-  bool unaligned = false;           // transpose with vectors at element alignment (extents or strides
+  bool unaligned = false;           // transpose or rows with vectors at element alignment (extents or strides
                                     // not multiples of the vector; edges element by element)
   int step = 1;                     // source stride of the transpose's column mode (1 or 2)
   int shuffle_c = 0;                // shuffle path: block columns C (8, 16 or 32; 4 rows)
@@ -183,14 +183,15 @@ struct ShuffleArgs {
 struct RowArgs {
   const unsigned char* src;
   unsigned char* dst;
-  int64_t src_off, dst_off;  // elements
+  int64_t src_off, dst_off;  // bytes
   int32_t rank;              // modes of the vector grid, innermost last
   int32_t pad0;
   uint32_t ext[kMaxRank];    // extents; the innermost counts vectors
   uint32_t mul[kMaxRank];    // fast division: q = (umulhi(n, mul) + n) >> shr
   uint32_t shr[kMaxRank];
-  int64_t s[kMaxRank], d[kMaxRank];  // element strides per step of each grid mode
-  int64_t nvec;              // vectors in the whole copy
+  int64_t s[kMaxRank], d[kMaxRank];  // byte strides per step of each grid mode
+  int64_t nvec;              // vectors in the whole copy (of this launch)
+  int64_t row_elems;         // element-aligned rows: elements per row (its last vector may be short)
 };
 
 // Order 2: super-tiles of kSuper x kSuper tiles, each run on one XCD (the dispatcher sends

@@ -219,6 +219,26 @@ def test_transpose_vector_widths(eb, n):
         assert n % ve == 0 and all(n % (v // eb) for v in (16, 8) if v > sp["vec_bytes"] and v >= eb)
 
 
+@pytest.mark.parametrize("eb", [1, 2, 4, 8])
+@pytest.mark.parametrize("shape,pitch,soff,doff", [((37, 45), 50, 3, 0), ((64, 64), 65, 65 + 1, 7), ((5, 3), 9, 1, 2),
+                                                    ((300, 129), 130, 131, 0), ((2, 33, 70), 71, 5, 3),
+                                                    ((1000,), 1, 1, 0), ((4096,), 1, 3, 5), ((7, 1), 2, 1, 0)])
+def test_rows_at_element_alignment(eb, shape, pitch, soff, doff):
+    """Co-contiguous copies the aligned rule declines (windows of a matrix, odd offsets, row
+    lengths that are not multiples of a vector): rows of 16-byte vectors at element alignment, a
+    row's short last vector element by element."""
+    if len(shape) == 1:
+        ss, ds = (1,), (1,)
+    elif len(shape) == 2:
+        ss, ds = (pitch, 1), (shape[1], 1)
+    else:
+        ss, ds = (shape[1] * pitch, pitch, 1), (shape[1] * shape[2], shape[2], 1)
+    p = _check(shape, ss, ds, eb, s_off=soff, d_off=doff, seed=sum(shape) + eb)
+    assert p["path_name"] in ("rows", "roundtrip", "guarded_rows"), p
+    if p["path_name"] == "rows" and p["vec_bytes"] == 16:
+        assert p["unaligned"] or (soff % (16 // eb) == 0 and doff % (16 // eb) == 0)
+
+
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
 def test_transpose_with_offsets_and_pitches(eb):
     # source rows of pitch 80 starting at element 16, destination columns of pitch 40 at 8

@@ -324,6 +324,24 @@ def test_copies_beyond_2_31_vectors_plan():
     assert p["status"] == L.TC_OK and p["path_name"] == "guarded_rows", p
 
 
+def test_window_copies_take_element_aligned_rows():
+    """A [1:8191, 1:8191] window of an 8192^2 matrix into a dense buffer: the page's rule declines
+    (no integer split), strict mode reports it, the default runs rows of 16-byte vectors at element
+    alignment; an odd element offset on a 1-D copy likewise."""
+    for dt in (L.TC_I8, L.TC_F16, L.TC_F32, L.TC_F64):
+        src, dst = ((8190, 8190), (8192, 1), 8193), ((8190, 8190), (8190, 1))
+        p = L.tc_plan(src, dst, dt)
+        assert p["path_name"] == "rows" and p["unaligned"] and p["vec_bytes"] == 16, p
+        eb = p["elem_bytes"]
+        assert p["workgroups"] == -(-8190 * -(-8190 // (16 // eb)) // (p["threads"] * 4))
+        assert L.tc_plan(src, dst, dt, flags=L.TC_FLAG_STRICT, raise_on_error=False)["status"] == L.TC_E_DECLINED
+        p = L.tc_plan(((1 << 20,), (1,), 1), ((1 << 20,), (1,)), dt)
+        assert p["path_name"] == "rows" and p["unaligned"] and p["vec_bytes"] == 16, p
+        # the page's plan in strict mode: the widest aligned vector (4 bytes at most here)
+        sp = L.tc_plan(((1 << 20,), (1,), 1), ((1 << 20,), (1,)), dt, flags=L.TC_FLAG_STRICT, raise_on_error=False)
+        assert sp["status"] == L.TC_E_DECLINED or (sp["vec_bytes"] == eb and not sp["unaligned"]), sp
+
+
 def test_no_kernel_uses_scratch_memory():
     """Every kernel keeps its per-lane data in registers: the compiler reports no scratch (a
     private array it cannot promote would turn into extra memory instructions per tile)."""
