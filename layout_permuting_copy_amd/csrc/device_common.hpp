@@ -88,13 +88,51 @@ __device__ __forceinline__ void gstore(unsigned char* p, const uint32_t* w) {
   }
 }
 
-// The first n (0 < n <= VB/EB) elements of a VB-byte vector whose elements lie S elements apart
-// in memory, one element access each (the vector reaches past an extent of the copy, or is the
-// last of a strided row); the other bytes of w are zero.
+// Bytes at offset o of a VB-byte register vector w: `v` (b <= 4 bytes, o % b == 0) is or-ed in, or
+// a word is read out from there, by masks rather than by indexing w with a run-time value (which
+// would move w to scratch memory).
+template <int VB>
+__device__ __forceinline__ void put_bytes(uint32_t* w, int o, uint32_t v) {
+  const uint32_t x = v << (8 * (o & 3));
+  const int q = o >> 2;
+#pragma unroll
+  for (int k = 0; k < VB / 4; ++k) w[k] |= x & (0u - uint32_t(q == k));
+}
+template <int VB>
+__device__ __forceinline__ uint32_t get_word(const uint32_t* w, int o) {
+  const int q = o >> 2;
+  uint32_t r = 0;
+#pragma unroll
+  for (int k = 0; k < VB / 4; ++k) r |= w[k] & (0u - uint32_t(q == k));
+  return r >> (8 * (o & 3));
+}
+
+// The first n (0 < n < VB/EB) elements of a VB-byte vector whose elements lie S elements apart
+// in memory (the vector reaches past an extent of the copy, or is the last of a strided row);
+// the other bytes of w are zero.  S = 1: the n*EB bytes in at most four accesses of 8, 4, 2 and 1
+// bytes, largest first (gfx950 global memory takes unaligned accesses); S = 2: one access per
+// element.
 template <int EB, int VB, int S = 1>
 __device__ __forceinline__ void gload_partial(const unsigned char* p, int n, uint32_t* w) {
 #pragma unroll
   for (int k = 0; k < VB / 4; ++k) w[k] = 0;
+  if constexpr (S == 1 && EB < VB) {
+    const int nb = n * EB;
+    if constexpr (VB == 16) {
+      if (nb & 8) {
+        const uint64_t v = *reinterpret_cast<const uint64_t*>(p);
+        w[0] = uint32_t(v);
+        w[1] = uint32_t(v >> 32);
+      }
+    }
+    if constexpr (VB >= 8 && EB <= 4)
+      if (nb & 4) put_bytes<VB>(w, nb & 8, *reinterpret_cast<const uint32_t*>(p + (nb & 8)));
+    if constexpr (EB <= 2)
+      if (nb & 2) put_bytes<VB>(w, nb & 12, *reinterpret_cast<const uint16_t*>(p + (nb & 12)));
+    if constexpr (EB == 1)
+      if (nb & 1) put_bytes<VB>(w, nb & 14, p[nb & 14]);
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < VB / EB; ++e) {
     if (e < n) {
@@ -135,8 +173,23 @@ __device__ __forceinline__ void gload_step(const unsigned char* p, uint32_t* w) 
   }
 }
 
+// The first n (0 < n < VB/EB) elements of w to consecutive elements at p, in at most four accesses
+// of 8, 4, 2 and 1 bytes, largest first.
 template <int EB, int VB>
 __device__ __forceinline__ void gstore_partial(unsigned char* p, int n, const uint32_t* w) {
+  if constexpr (EB < VB) {
+    const int nb = n * EB;
+    if constexpr (VB == 16) {
+      if (nb & 8) *reinterpret_cast<uint64_t*>(p) = uint64_t(w[0]) | (uint64_t(w[1]) << 32);
+    }
+    if constexpr (VB >= 8 && EB <= 4)
+      if (nb & 4) *reinterpret_cast<uint32_t*>(p + (nb & 8)) = get_word<VB>(w, nb & 8);
+    if constexpr (EB <= 2)
+      if (nb & 2) *reinterpret_cast<uint16_t*>(p + (nb & 12)) = uint16_t(get_word<VB>(w, nb & 12));
+    if constexpr (EB == 1)
+      if (nb & 1) p[nb & 14] = uint8_t(get_word<VB>(w, nb & 14));
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < VB / EB; ++e) {
     if (e < n) {
