@@ -255,7 +255,7 @@ __device__ __forceinline__ TileAt tile_at(const TransposeArgs& a, uint32_t tile)
     valid = slice < a.nslices && trI < a.tilesR.d && tcI < a.tilesC.d;
     idx = valid ? slice : 0;
   } else {
-    const Div32& first = a.order ? a.tilesR : a.tilesC;
+    const Div32& first = a.order ? a.tilesRg : a.tilesC;
     const Div32& second = a.order ? a.tilesC : a.tilesR;
     q = udiv(idx, first);
     const uint32_t i0 = idx - q * first.d;
@@ -265,6 +265,9 @@ __device__ __forceinline__ TileAt tile_at(const TransposeArgs& a, uint32_t tile)
     tcI = a.order ? i1 : i0;
     trI = a.order ? i0 : i1;
     idx = q;
+    // order 1 with a padded row-tile count: the neighbours along a source row are a multiple of
+    // kXcds workgroups apart, so on one XCD, where they share the cache lines they both read
+    valid = trI < a.tilesR.d;
   }
   q = udiv(idx, a.tilesB);
   const uint32_t tbI = idx - q * a.tilesB.d;

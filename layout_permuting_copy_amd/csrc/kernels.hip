@@ -368,6 +368,10 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
     ta.lTC = lg(p.g.TC);
     ta.tilesR = make_div32(uint32_t((R.e + p.g.TR - 1) / p.g.TR));
     ta.tilesC = make_div32(uint32_t((C.e + p.g.TC - 1) / p.g.TC));
+    {
+      const uint32_t tR = uint32_t((R.e + p.g.TR - 1) / p.g.TR);
+      ta.tilesRg = make_div32(p.g.pad_rows ? (tR + kXcds - 1) / kXcds * kXcds : tR);
+    }
     if (p.path == TC_PATH_TRANSPOSE) {
       const bool hasB = p.mode_b >= 0;
       ta.eB = hasB ? j.m[p.mode_b].e : 1;

@@ -90,6 +90,8 @@ struct TileGeom {
   bool wave_local = false;        // every wave reads back only LDS units it wrote itself: the
                                   // phases are ordered per wave, without a workgroup barrier
   bool edges = true;              // some tile reaches past an extent (the kernel needs its guards)
+  bool pad_rows = false;          // order 1 with source rows off the 128-byte lines: the row-tile
+                                  // count of the grid is padded to a multiple of kXcds (tile_at)
   int loads = 4, stores = 4;  // accesses per thread per phase
   int ww = 16, rw = 4;        // LDS write / read instruction bytes
   int k = 0, shift = 0, tbit = 0;
@@ -157,6 +159,7 @@ struct TransposeArgs {
   int64_t sR, sC, sB;        // source strides of R, C, B
   int64_t dR, dC, dB;        // destination strides of R, C, B
   Div32 tilesR, tilesC, tilesB;
+  Div32 tilesRg;             // order 1: row tiles per column of the grid (tilesR, or padded)
   int32_t nbatch;            // further modes walked by the grid, innermost last
   Div32 bdiv[kMaxRank];      // their extents
   int64_t bs[kMaxRank], bd[kMaxRank];
