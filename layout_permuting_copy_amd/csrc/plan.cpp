@@ -380,11 +380,14 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   bool dst_lines = (j.dof * p->eb) % 128 == 0;
   for (int k = 0; k < j.rank; ++k)
     if (k != p->mode_r && (std::llabs(j.m[k].d) * p->eb) % 128 != 0) dst_lines = false;
-  // (and whether the source rows start on 128-byte lines)
+  // (and whether the source rows start on 128-byte lines: for 1-byte elements either side off
+  // the lines takes the element-aligned configuration, int8 8192 x 8208 3.9 -> 4.5 TB/s and
+  // 8320 x 8224 3.84 -> 4.77)
   bool src_lines = (j.so * p->eb) % 128 == 0;
   for (int k = 0; k < j.rank; ++k)
     if (k != p->mode_c && (std::llabs(j.m[k].s) * p->eb) % 128 != 0) src_lines = false;
-  const bool line_cfg = p->unaligned || ((p->eb == 1 || p->eb == 2 || p->eb == 8) && !dst_lines);
+  const bool line_cfg = p->unaligned || ((p->eb == 1 || p->eb == 2 || p->eb == 8) && !dst_lines) ||
+                        (p->eb == 1 && !src_lines);
   TuneCfg base = default_cfg(p->eb, batched, line_cfg);
   // 1-byte elements there, and element-aligned 8-byte elements read with unit stride: the XCD
   // super-tile order, so that the neighbouring tiles that share cache lines at element alignment

@@ -188,7 +188,7 @@ def test_transpose_tall_tiles(eb, n, m):
     assert p["lds_read_bytes"] == 16 and p["grid_order"] == 1
 
 
-@pytest.mark.parametrize("eb,n,m,tile", [(1, 8320, 8224, (512, 256)), (2, 16448, 16392, (1024, 64)),
+@pytest.mark.parametrize("eb,n,m,tile", [(1, 8320, 8320, (512, 256)), (2, 16448, 16392, (1024, 64)),
                                           (8, 8208, 8208, (256, 64))])
 def test_transpose_128k_tiles_ragged(eb, n, m, tile):
     """128 KiB tiles (one workgroup per CU), with partial tiles along both tile modes (destination
