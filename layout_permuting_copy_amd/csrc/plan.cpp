@@ -365,6 +365,16 @@ static bool plan_with_cfg(const Plan& p, int flags, TuneCfg cfg, bool tile_pinne
   return have;
 }
 
+// The tile configuration of a transpose.  Three classes of layout, each configuration measured on
+// MI355X (TC_TUNE pins one for sweeps):
+//  - both sides on 128-byte lines: the tall tiles where tall_cfg has them (row tiles first,
+//    nontemporal accesses), else default_cfg;
+//  - neighbouring tiles sharing cache lines (`line_cfg`): vectors at element alignment, or, for
+//    1-, 2- and 8-byte elements, destination columns off the lines, or, for 1-byte elements,
+//    source rows off the lines: plain stores and the element-aligned configuration of the width
+//    (int8 small tiles and fp16 tall tiles in the XCD super-tile order, fp64 16 KiB tiles);
+//  - row tiles first with source rows off the lines: the row-tile count padded to a multiple of
+//    kXcds (with_phase_order below).
 static bool plan_transpose_tile(Plan* p, int flags) {
   const Joint& j = p->j;
   const Mode& R = j.m[p->mode_r];
@@ -422,8 +432,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   // wave-local phases drop the workgroup barrier where the library holds such an instance
   // Row tiles first with source rows off the lines: neighbouring column tiles read the same lines.
   // They are tilesR workgroups apart, so the grid pads tilesR to a multiple of kXcds and puts them
-  // on one XCD (bf16 16448 x 16392 3.48 -> 4.9 TB/s; with tilesR already a multiple of 8, as for
-  // 16384 x 16392, it runs at that rate unpadded).
+  // on one XCD (bf16 16448 x 16392 3.48 -> 4.3 TB/s, fp32 16416 x 16400 5.07 -> 5.4).
   auto with_phase_order = [&](TileGeom g) {
     g.pad_rows = g.order == 1 && !src_lines;
     g.wave_local = ov.wl != 0 && tile_wave_local(g) &&
