@@ -94,8 +94,8 @@ enum tc_status {
 #define TC_FLAG_FORCE_REGS    0x04 /* co-contiguous copies: stage through registers only */
 #define TC_FLAG_FORCE_LDS     0x08 /* co-contiguous copies: stage through LDS */
 #define TC_FLAG_NO_SWIZZLE    0x10 /* transposes: no XOR swizzle (k = 0), to measure its effect */
-#define TC_FLAG_NO_SHUFFLE    0x20 /* small batched 4-row transposes: the LDS tile kernel instead
-                                      of the in-register butterfly, to measure its effect */
+#define TC_FLAG_NO_SHUFFLE    0x20 /* the LDS tile kernel instead of the register paths (the 4-row
+                                      butterfly, the channel interleave), to measure their effect */
 #define TC_FLAG_ALL           0x3f
 
 /* Which kernel a plan runs. */
@@ -109,10 +109,13 @@ enum tc_path {
                               global with the [outer, threads, vec] partition */
   TC_PATH_GUARDED_TILE = 4,/* fallback: LDS tile with element-wide accesses and guards */
   TC_PATH_GUARDED_ROWS = 5,/* fallback: element-wise, destination order, guarded */
-  TC_PATH_SHUFFLE = 6      /* batches of 4 x C blocks of 4-byte elements (C = 8, 16, 32), each
+  TC_PATH_SHUFFLE = 6,     /* batches of 4 x C blocks of 4-byte elements (C = 8, 16, 32), each
                               block contiguous on both sides (e.g. the scale-factor tiles):
                               16-byte vectors exchanged between lanes by a two-stage butterfly
                               (ds_swizzle), no LDS */
+  TC_PATH_INTERLEAVE = 7   /* a few (2, 3, 4 or 8) interleaved channels to planes or back (e.g.
+                              NHWC <-> NCHW with 3 channels): each lane moves 16/elem_bytes
+                              pixels of every channel, transposed within its registers */
 };
 
 /*

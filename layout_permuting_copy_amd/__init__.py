@@ -45,9 +45,9 @@ TC_FLAG_NO_SHUFFLE = 0x20
 
 # paths (enum tc_path)
 TC_PATH_EMPTY, TC_PATH_TRANSPOSE, TC_PATH_ROWS, TC_PATH_ROUNDTRIP, TC_PATH_GUARDED_TILE, \
-    TC_PATH_GUARDED_ROWS, TC_PATH_SHUFFLE = range(7)
+    TC_PATH_GUARDED_ROWS, TC_PATH_SHUFFLE, TC_PATH_INTERLEAVE = range(8)
 PATH_NAMES = {0: "empty", 1: "transpose", 2: "rows", 3: "roundtrip", 4: "guarded_tile", 5: "guarded_rows",
-              6: "shuffle"}
+              6: "shuffle", 7: "interleave"}
 
 
 class TcLayout(ctypes.Structure):

@@ -141,6 +141,71 @@ __global__ void __launch_bounds__(NT) rows_unaligned_kernel(RowArgs a) {
   }
 }
 
+// Interleave path: CH channels between interleaved and planar layouts (e.g. NHWC <-> NCHW).  A
+// lane holds one group of VE = 16/EB pixels of every channel: element (pixel p, channel c) of the
+// interleaved side is element p*CH + c of its CH registers vectors, of the planar side element
+// c*VE + p.  The move between the two is a fixed permutation of register bytes (its indices are
+// compile-time constants).  TO: interleaved source, planar destination.
+template <int EB, int CH, bool TO>
+__device__ __forceinline__ void interleave_regs(const uint32_t* in, uint32_t* out) {
+  constexpr int VE = 16 / EB, N = CH * VE;
+  if constexpr (EB >= 4) {
+    constexpr int W = EB / 4;
+#pragma unroll
+    for (int o = 0; o < N; ++o) {
+      const int i = TO ? (o % VE) * CH + o / VE : (o % CH) * VE + o / CH;
+#pragma unroll
+      for (int m = 0; m < W; ++m) out[o * W + m] = in[i * W + m];
+    }
+  } else {
+    constexpr int PER = 4 / EB;  // elements per dword
+    constexpr uint32_t MASK = EB == 1 ? 0xFFu : 0xFFFFu;
+#pragma unroll
+    for (int k = 0; k < CH * 4; ++k) out[k] = 0;
+#pragma unroll
+    for (int o = 0; o < N; ++o) {
+      const int i = TO ? (o % VE) * CH + o / VE : (o % CH) * VE + o / CH;
+      out[o / PER] |= ((in[i / PER] >> (8 * EB * (i % PER))) & MASK) << (8 * EB * (o % PER));
+    }
+  }
+}
+
+template <int EB, int CH, bool TO, bool GUARD>
+__device__ __forceinline__ void interleave_body(const RowArgs& a, int64_t plane) {
+  constexpr int R = kInterleaveRounds, NT = kRowThreads;
+  const int t = threadIdx.x;
+  const int64_t base = int64_t(blockIdx.x) * NT * R;
+  int64_t so[R], dof[R];
+  bool ok[R];
+  uint32_t in[R][CH * 4];
+#pragma unroll
+  for (int f = 0; f < R; ++f) {
+    const int64_t v = base + f * NT + t;
+    ok[f] = !GUARD || v < a.nvec;
+    if (ok[f]) row_offsets(a, uint32_t(v), &so[f], &dof[f]);
+  }
+#pragma unroll
+  for (int f = 0; f < R; ++f)
+    if (ok[f])
+#pragma unroll
+      for (int k = 0; k < CH; ++k) gload<16, 3>(a.src + so[f] + (TO ? int64_t(k) * 16 : k * plane), in[f] + 4 * k);
+#pragma unroll
+  for (int f = 0; f < R; ++f) {
+    if (!ok[f]) continue;
+    uint32_t out[CH * 4];
+    interleave_regs<EB, CH, TO>(in[f], out);
+#pragma unroll
+    for (int k = 0; k < CH; ++k) gstore<16, 3>(a.dst + dof[f] + (TO ? k * plane : int64_t(k) * 16), out + 4 * k);
+  }
+}
+
+// Workgroups wholly inside the copy run unguarded (all loads in flight); the last one guarded.
+template <int EB, int CH, bool TO>
+__global__ void __launch_bounds__(kRowThreads) interleave_kernel(RowArgs a, int64_t plane) {
+  if ((int64_t(blockIdx.x) + 1) * kRowThreads * kInterleaveRounds <= a.nvec) interleave_body<EB, CH, TO, false>(a, plane);
+  else interleave_body<EB, CH, TO, true>(a, plane);
+}
+
 // Fallback tile: element-wide accesses, padded LDS rows, guards on every element.
 template <int EB>
 __global__ void __launch_bounds__(kGuardThreads) guarded_tile_kernel(TransposeArgs a) {
@@ -350,6 +415,42 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
       }
       if (hipPeekAtLastError() != hipSuccess) break;
     }
+  } else if (p.path == TC_PATH_INTERLEAVE) {
+    // grid of pixel groups: the modes other than the two of the exchange, then the pixel mode
+    const int ve = 16 / p.eb;
+    const int px = p.to_planes ? p.mode_r : p.mode_c, ch = p.to_planes ? p.mode_c : p.mode_r;
+    RowArgs ra{};
+    ra.src = static_cast<const unsigned char*>(src);
+    ra.dst = static_cast<unsigned char*>(dst);
+    ra.src_off = j.so * p.eb;
+    ra.dst_off = j.dof * p.eb;
+    int n = 0;
+    for (int k = 0; k <= j.rank; ++k) {
+      if (k == px || k == ch) continue;
+      const bool pix = k == j.rank;  // the pixel mode goes last (innermost)
+      const Mode& m = pix ? j.m[px] : j.m[k];
+      const int64_t e = pix ? m.e / ve : m.e;
+      ra.ext[n] = uint32_t(e);
+      const Div32 dv = make_div32(uint32_t(e));
+      ra.mul[n] = dv.mul;
+      ra.shr[n] = dv.shr;
+      ra.s[n] = m.s * p.eb * (pix ? ve : 1);
+      ra.d[n] = m.d * p.eb * (pix ? ve : 1);
+      ++n;
+    }
+    ra.rank = n;
+    ra.nvec = j.count / (int64_t(ve) * p.shuffle_c);
+    const int64_t plane = (p.to_planes ? j.m[ch].d : j.m[ch].s) * p.eb;
+    const dim3 grid = dim3(uint32_t(p.workgroups)), block = dim3(kRowThreads);
+#define TC_IL(E, CHN)                                                                                      \
+  if (p.eb == E && p.shuffle_c == CHN) {                                                                   \
+    if (p.to_planes) hipLaunchKernelGGL((dev::interleave_kernel<E, CHN, true>), grid, block, 0, s, ra, plane); \
+    else hipLaunchKernelGGL((dev::interleave_kernel<E, CHN, false>), grid, block, 0, s, ra, plane);        \
+  }
+#define TC_IL4(E) TC_IL(E, 2) TC_IL(E, 3) TC_IL(E, 4) TC_IL(E, 8)
+    TC_IL4(1) TC_IL4(2) TC_IL4(4) TC_IL4(8)
+#undef TC_IL4
+#undef TC_IL
   } else if (p.path == TC_PATH_TRANSPOSE || p.path == TC_PATH_GUARDED_TILE) {
     TransposeArgs ta{};
     ta.src = static_cast<const unsigned char*>(src);

@@ -27,6 +27,7 @@ constexpr int kGuardThreads = 256;             // threads per workgroup on the g
 // Rows-type and shuffle copies of 2^31 vectors or more run as several launches of at most this
 // many vectors each (the kernels index vectors and workgroups with 32-bit integers).
 constexpr int64_t kLaunchVectors = int64_t(1) << 30;
+constexpr int kInterleaveRounds = 2;  // pixel groups per lane on the interleave path
 
 // One joint mode: extent, source stride, destination stride (elements).
 struct Mode {
@@ -126,7 +127,9 @@ struct Plan {
   bool unaligned = false;           // transpose or rows with vectors at element alignment (extents or strides
                                     // not multiples of the vector; edges element by element)
   int step = 1;                     // source stride of the transpose's column mode (1 or 2)
-  int shuffle_c = 0;                // shuffle path: block columns C (8, 16 or 32; 4 rows)
+  int shuffle_c = 0;                // shuffle path: block columns C (8, 16 or 32; 4 rows); interleave
+                                    // path: the channels (2, 3, 4 or 8)
+  bool to_planes = false;           // interleave path: interleaved source, planar destination
   bool row_burst = false;           // rows path: every load of a thread issued at once (else one at
                                     // a time, each after its offsets are decoded)
   int mode_r = -1, mode_c = -1, mode_b = -1;

@@ -220,6 +220,34 @@ def test_transpose_vector_widths(eb, n):
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])
+@pytest.mark.parametrize("ch", [2, 3, 4, 8])
+@pytest.mark.parametrize("to_planes", [True, False])
+def test_interleave_channels(eb, ch, to_planes):
+    """A few interleaved channels to planes (NHWC -> NCHW): each lane transposes 16/eb pixels of
+    every channel in its registers (where that path is chosen; the way back and the wider pixels
+    take the transpose kernel).  With element offsets of 16, and a pixel count that is not a
+    multiple of the group."""
+    n, h, w = 3, 17, 48
+    hw = h * w
+    if to_planes:  # (n, h, w, c) interleaved -> (n, c, h, w) planes
+        shape, ss, ds = (n, h, w, ch), (hw * ch, w * ch, ch, 1), (ch * hw, w, 1, hw)
+    else:          # (n, c, h, w) planes -> (n, h, w, c) interleaved
+        shape, ss, ds = (n, ch, h, w), (ch * hw, hw, w, 1), (hw * ch, 1, w * ch, ch)
+    interleave = to_planes and (ch * eb <= 12 or eb == 8)
+    p = _check(shape, ss, ds, eb, s_off=16, d_off=32, seed=ch * 10 + eb,
+               expect="interleave" if interleave else None)
+    if interleave:
+        assert p["tile_c"] == ch and p["tile_r"] == 16 // eb
+    w2 = w - 1  # 17 * 47 pixels: not a multiple of 16 / eb for eb < 8
+    hw2 = h * w2
+    if to_planes:
+        shape, ss, ds = (n, h, w2, ch), (hw2 * ch, w2 * ch, ch, 1), (ch * hw2, w2, 1, hw2)
+    else:
+        shape, ss, ds = (n, ch, h, w2), (ch * hw2, hw2, w2, 1), (hw2 * ch, 1, w2 * ch, ch)
+    _check(shape, ss, ds, eb, seed=ch * 10 + eb + 1)
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8])
 @pytest.mark.parametrize("shape,pitch,soff,doff", [((37, 45), 50, 3, 0), ((64, 64), 65, 65 + 1, 7), ((5, 3), 9, 1, 2),
                                                     ((300, 129), 130, 131, 0), ((2, 33, 70), 71, 5, 3),
                                                     ((1000,), 1, 1, 0), ((4096,), 1, 3, 5), ((7, 1), 2, 1, 0)])

@@ -342,6 +342,30 @@ def test_window_copies_take_element_aligned_rows():
         assert sp["status"] == L.TC_E_DECLINED or (sp["vec_bytes"] == eb and not sp["unaligned"]), sp
 
 
+def test_interleave_path_selection():
+    """NHWC -> NCHW with 3 channels takes the interleave path at every width; the way back, 5
+    channels, misaligned planes, strict mode and TC_FLAG_NO_SHUFFLE do not; the scale-factor
+    blocks keep the butterfly."""
+    n, h, w, ch = 2, 224, 224, 3
+    hw = h * w
+    to = (((n, h, w, ch), (hw * ch, w * ch, ch, 1)), ((n, h, w, ch), (ch * hw, w, 1, hw)))
+    back = (((n, ch, h, w), (ch * hw, hw, w, 1)), ((n, ch, h, w), (hw * ch, 1, w * ch, ch)))
+    for dt in (L.TC_U8, L.TC_BF16, L.TC_F32, L.TC_F64):
+        p = L.tc_plan(*to, dt)
+        assert p["path_name"] == "interleave" and p["tile_c"] == ch, p
+        assert L.tc_plan(*to, dt, flags=L.TC_FLAG_NO_SHUFFLE)["path_name"] == "transpose"
+        assert L.tc_plan(*to, dt, flags=L.TC_FLAG_STRICT, raise_on_error=False)["path_name"] != "interleave"
+        # planes to interleaved channels: the transpose kernel (measured faster)
+        assert L.tc_plan(*back, dt)["path_name"] == "transpose"
+    # 5 channels, or a plane stride that breaks 16-byte alignment: the transpose kernel
+    five = (((n, h, w, 5), (hw * 5, w * 5, 5, 1)), ((n, h, w, 5), (5 * hw, w, 1, hw)))
+    assert L.tc_plan(*five, L.TC_F32)["path_name"] == "transpose"
+    odd = (((n, h, w, ch), (hw * ch, w * ch, ch, 1)), ((n, h, w, ch), (ch * (hw + 1), w, 1, hw + 1)))
+    assert L.tc_plan(*odd, L.TC_F32)["path_name"] == "transpose"
+    sf = ((65536, 2, 1, 4, 32), (256, 128, 128, 32, 1)), ((65536, 2, 1, 4, 32), (256, 128, 128, 1, 4))
+    assert L.tc_plan(*sf, L.TC_F32)["path_name"] == "shuffle"
+
+
 def test_no_kernel_uses_scratch_memory():
     """Every kernel keeps its per-lane data in registers: the compiler reports no scratch (a
     private array it cannot promote would turn into extra memory instructions per tile)."""
