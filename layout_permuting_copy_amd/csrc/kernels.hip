@@ -34,35 +34,46 @@ __device__ __forceinline__ void row_offsets(const RowArgs& a, uint32_t n, int64_
 }
 
 // [outer, threads, vec] copy: access v = blockIdx * NT*ROUNDS + f*NT + t.  With USE_LDS the
-// vectors make the round trip global -> LDS -> global of the gmem_smem demonstration.
-template <int VB, int NT, int ROUNDS, bool USE_LDS, int NTM, bool GUARD, bool BURST>
+// vectors make the round trip global -> LDS -> global of the gmem_smem demonstration.  BUF:
+// 16-byte buffer accesses from the bases a.sbuf / a.dbuf (the host has checked that every offset
+// of the launch fits in 32 bits) with the streaming cache policies.
+template <int VB, int NT, int ROUNDS, bool USE_LDS, int NTM, bool GUARD, bool BURST, bool BUF>
 __device__ __forceinline__ void rows_body(const RowArgs& a, typename Bytes<VB>::T* lds) {
   typedef typename Bytes<VB>::T V;
+  static_assert(!BUF || (VB == 16 && !USE_LDS), "buffer accesses: 16-byte vectors in registers");
   const int t = threadIdx.x;
   const int64_t base = int64_t(blockIdx.x) * NT * ROUNDS;
+  const Rsrc rs = make_rsrc(a.src + a.sbuf), rd = make_rsrc(a.dst + a.dbuf);
   V reg[ROUNDS];
   int64_t soff[ROUNDS], doff[ROUNDS];
+  bool live[ROUNDS];
+  auto load = [&](int f) {
+    if constexpr (BUF) reg[f] = bload16(rs, uint32_t(soff[f] - a.sbuf));
+    else reg[f] = gload_v<V, NTM>(reinterpret_cast<const V*>(a.src + soff[f]));
+  };
   if constexpr (BURST) {
     // all offsets first (the decode loop has a run-time trip count), then every load back to back
 #pragma unroll
     for (int f = 0; f < ROUNDS; ++f) {
       const int64_t v = base + f * NT + t;
-      soff[f] = doff[f] = -1;
-      if (!GUARD || v < a.nvec) row_offsets(a, uint32_t(v), &soff[f], &doff[f]);
+      live[f] = !GUARD || v < a.nvec;
+      if (live[f]) row_offsets(a, uint32_t(v), &soff[f], &doff[f]);
     }
 #pragma unroll
     for (int f = 0; f < ROUNDS; ++f)
-      if (!GUARD || doff[f] >= 0) reg[f] = gload_v<V, NTM>(reinterpret_cast<const V*>(a.src + soff[f]));
+      if (live[f]) load(f);
   } else {
-    // each load right after its offsets: the decode loop between them leaves one load in flight
+    // paced: each load after its offsets, and one load in flight per lane (an explicit wait before
+    // the next decode); measured faster than all loads at once for permuted rows and large copies
 #pragma unroll
     for (int f = 0; f < ROUNDS; ++f) {
       const int64_t v = base + f * NT + t;
-      doff[f] = -1;
-      if (!GUARD || v < a.nvec) {
+      live[f] = !GUARD || v < a.nvec;
+      if (live[f]) {
         row_offsets(a, uint32_t(v), &soff[f], &doff[f]);
-        reg[f] = gload_v<V, NTM>(reinterpret_cast<const V*>(a.src + soff[f]));
+        load(f);
       }
+      if (f + 1 < ROUNDS) wait_vmem();
     }
   }
   if constexpr (USE_LDS) {
@@ -73,18 +84,23 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, typename Bytes<VB>::
     for (int f = 0; f < ROUNDS; ++f) reg[f] = lds[f * NT + t];
   }
 #pragma unroll
-  for (int f = 0; f < ROUNDS; ++f)
-    if (!GUARD || doff[f] >= 0) gstore_v<V, NTM>(reinterpret_cast<V*>(a.dst + doff[f]), reg[f]);
+  for (int f = 0; f < ROUNDS; ++f) {
+    if (!live[f]) continue;
+    if constexpr (BUF) bstore16(rd, uint32_t(doff[f] - a.dbuf), reg[f]);
+    else gstore_v<V, NTM>(reinterpret_cast<V*>(a.dst + doff[f]), reg[f]);
+  }
 }
 
 // BURST: workgroups wholly inside the copy take the unguarded body, all loads in flight.  Else
 // every workgroup takes the guarded body, whose per-vector branch paces the loads one at a time.
-template <int VB, int NT, int ROUNDS, bool USE_LDS, int NTM, bool BURST = false>
+template <int VB, int NT, int ROUNDS, bool USE_LDS, int NTM, bool BURST = false, bool BUF = false>
 __global__ void __launch_bounds__(NT) rows_kernel(RowArgs a) {
   typedef typename Bytes<VB>::T V;
   __shared__ __attribute__((aligned(16))) V lds[USE_LDS ? NT * ROUNDS : 1];
-  if (BURST && (int64_t(blockIdx.x) + 1) * NT * ROUNDS <= a.nvec) rows_body<VB, NT, ROUNDS, USE_LDS, NTM, false, BURST>(a, lds);
-  else rows_body<VB, NT, ROUNDS, USE_LDS, NTM, true, BURST>(a, lds);
+  if (BURST && (int64_t(blockIdx.x) + 1) * NT * ROUNDS <= a.nvec)
+    rows_body<VB, NT, ROUNDS, USE_LDS, NTM, false, BURST, BUF>(a, lds);
+  else
+    rows_body<VB, NT, ROUNDS, USE_LDS, NTM, true, BURST, BUF>(a, lds);
 }
 
 // Copies n < 16 bytes in at most four accesses of 8, 4, 2 and 1 bytes (at any alignment: gfx950
@@ -254,7 +270,7 @@ __device__ __forceinline__ uint32_t xor_lanes(uint32_t v) {
   return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x1F | (DIST << 10)));
 }
 
-template <int LC, int NTM, bool GUARD>
+template <int LC, int NTM, bool GUARD, bool BUF>
 __device__ __forceinline__ void shuffle_rounds(const ShuffleArgs& a) {
   constexpr int LQ = LC - 2;  // log2 of the vectors per block row
   constexpr int R = kShuffleRounds, NT = kShuffleThreads;
@@ -263,6 +279,10 @@ __device__ __forceinline__ void shuffle_rounds(const ShuffleArgs& a) {
   const int row = (lane >> LQ) & 3, q = lane & ((1 << LQ) - 1);
   const int col = 4 * q + row;  // destination column after the exchanges
   const int64_t g0 = int64_t(blockIdx.x) * R * NT + threadIdx.x;
+  // BUF: buffer bases at the workgroup's first block (the host has checked that the workgroup's
+  // blocks lie within 4 GiB above it on both sides)
+  const int64_t blk0 = (int64_t(blockIdx.x) * R * NT) >> LC;
+  const Rsrc rs = make_rsrc(a.src + (a.so + blk0 * a.sB) * 4), rd = make_rsrc(a.dst + (a.dof + blk0 * a.dB) * 4);
   u32x4 v[R];
 #pragma unroll
   for (int f = 0; f < R; ++f) {
@@ -272,6 +292,8 @@ __device__ __forceinline__ void shuffle_rounds(const ShuffleArgs& a) {
     if constexpr (GUARD) {
       v[f] = u32x4{0, 0, 0, 0};
       if (g < a.nvec) v[f] = gload_v<u32x4, NTM>(p);
+    } else if constexpr (BUF) {
+      v[f] = bload16(rs, uint32_t(((blk - blk0) * a.sB + (row * (1 << LQ) + q) * 4) * 4));
     } else {
       v[f] = gload_v<u32x4, NTM>(p);
     }
@@ -290,16 +312,17 @@ __device__ __forceinline__ void shuffle_rounds(const ShuffleArgs& a) {
     const int64_t g = g0 + int64_t(f) * NT;
     const int64_t blk = g >> LC;
     u32x4* p = reinterpret_cast<u32x4*>(a.dst) + ((a.dof + blk * a.dB) >> 2) + col;
-    if (!GUARD || g < a.nvec) gstore_v<u32x4, NTM>(p, u32x4{w0, w1, w2, w3});
+    if constexpr (!GUARD && BUF) bstore16(rd, uint32_t(((blk - blk0) * a.dB + col * 4) * 4), u32x4{w0, w1, w2, w3});
+    else if (!GUARD || g < a.nvec) gstore_v<u32x4, NTM>(p, u32x4{w0, w1, w2, w3});
   }
 }
 
 // Workgroups wholly inside the copy run with no per-lane condition (all loads in flight); the
 // last one, if ragged, is guarded.
-template <int LC, int NTM>
+template <int LC, int NTM, bool BUF>
 __global__ void __launch_bounds__(kShuffleThreads) shuffle_kernel(ShuffleArgs a) {
-  if ((int64_t(blockIdx.x) + 1) * kShuffleRounds * kShuffleThreads <= a.nvec) shuffle_rounds<LC, NTM, false>(a);
-  else shuffle_rounds<LC, NTM, true>(a);
+  if ((int64_t(blockIdx.x) + 1) * kShuffleRounds * kShuffleThreads <= a.nvec) shuffle_rounds<LC, NTM, false, BUF>(a);
+  else shuffle_rounds<LC, NTM, true, BUF>(a);
 }
 
 }  // namespace dev
@@ -323,12 +346,37 @@ int lg(int64_t x) {
   return r;
 }
 
-template <int VB, int NT, bool LDS, int NTM, bool BURST = false>
+template <int VB, int NT, bool LDS, int NTM, bool BURST = false, bool BUF = false, int ROUNDS = kRowRounds>
 void launch_rows_t(const RowArgs& ra, int64_t wgs, hipStream_t s) {
-  hipLaunchKernelGGL((dev::rows_kernel<VB, NT, kRowRounds, LDS, NTM, BURST>), dim3(uint32_t(wgs)), dim3(NT), 0, s, ra);
+  hipLaunchKernelGGL((dev::rows_kernel<VB, NT, ROUNDS, LDS, NTM, BURST, BUF>), dim3(uint32_t(wgs)), dim3(NT), 0, s, ra);
+}
+
+// The 16-byte rows kernel for `rounds` vectors per thread, paced or burst loads, global or
+// buffer accesses.
+template <bool BURST, bool BUF>
+void launch_rows16(int rounds, const RowArgs& ra, int64_t wgs, hipStream_t s) {
+  if (rounds == 1) launch_rows_t<16, kRowThreads, false, 3, BURST, BUF, 1>(ra, wgs, s);
+  if (rounds == 2) launch_rows_t<16, kRowThreads, false, 3, BURST, BUF, 2>(ra, wgs, s);
+  if (rounds == 4) launch_rows_t<16, kRowThreads, false, 3, BURST, BUF, 4>(ra, wgs, s);
+}
+
+// Lowest byte offset of a launch's accesses on one side (offset `off`, grid extents `ext`, byte
+// strides `st`, accesses of `vb` bytes) and whether all of them lie within kBufSpan bytes of it.
+bool buffer_window(int64_t off, const uint32_t* ext, const int64_t* st, int rank, int vb, int64_t* lo) {
+  int64_t mn = off, mx = off;
+  for (int k = 0; k < rank; ++k) {
+    if (ext[k] == 0) return false;
+    const int64_t step = int64_t(ext[k] - 1) * st[k];
+    if (step < 0) mn += step;
+    else mx += step;
+  }
+  *lo = mn;
+  return mx + vb - mn <= dev::kBufSpan;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int64_t kNoBuffer = INT64_MIN;  // RowArgs::sbuf of a launch that uses global accesses
 
 // The rows-type kernel of a plan over the vectors of `ra`, in `wgs` workgroups.
 void launch_rows(const Plan& p, const RowArgs& ra, int64_t wgs, hipStream_t s) {
@@ -342,13 +390,17 @@ void launch_rows(const Plan& p, const RowArgs& ra, int64_t wgs, hipStream_t s) {
     if (p.vb == 16) launch_rows_t<16, kWave, true, 0>(ra, wgs, s);
     if (p.vb == 8) launch_rows_t<8, kWave, true, 0>(ra, wgs, s);
     if (p.vb == 4) launch_rows_t<4, kWave, true, 0>(ra, wgs, s);
+  } else if (p.path == TC_PATH_ROWS && p.vb == 16) {
+    // buffer accesses where every offset of this launch fits (the caller has set sbuf / dbuf)
+    const bool buf = p.buffers && ra.sbuf != kNoBuffer;
+    if (p.row_burst && buf) launch_rows16<true, true>(p.row_rounds, ra, wgs, s);
+    if (p.row_burst && !buf) launch_rows16<true, false>(p.row_rounds, ra, wgs, s);
+    if (!p.row_burst && buf) launch_rows16<false, true>(p.row_rounds, ra, wgs, s);
+    if (!p.row_burst && !buf) launch_rows16<false, false>(p.row_rounds, ra, wgs, s);
   } else if (p.path == TC_PATH_ROWS && p.row_burst) {
-    if (p.vb == 16) launch_rows_t<16, kRowThreads, false, 3, true>(ra, wgs, s);
     if (p.vb == 8) launch_rows_t<8, kRowThreads, false, 3, true>(ra, wgs, s);
     if (p.vb == 4) launch_rows_t<4, kRowThreads, false, 3, true>(ra, wgs, s);
   } else if (p.path == TC_PATH_ROWS) {
-    if (p.vb == 16) launch_rows_t<16, kRowThreads, false, 3>(ra, wgs, s);
-    if (p.vb == 8) launch_rows_t<8, kRowThreads, false, 3>(ra, wgs, s);
     if (p.vb == 4) launch_rows_t<4, kRowThreads, false, 3>(ra, wgs, s);
   } else {
     if (p.eb == 1) launch_rows_t<1, kGuardThreads, false, 0>(ra, wgs, s);
@@ -405,14 +457,23 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
       sc.dof = sa.dof + b0 * sa.dB;
       sc.nvec = std::min(per, total - v0);
       const dim3 grid(uint32_t(ceil_div(sc.nvec, int64_t(kShuffleThreads) * kShuffleRounds))), block(kShuffleThreads);
+      // buffer accesses: a workgroup's blocks (4 x C elements each) within 4 GiB above its first
+      const int64_t bpw = int64_t(kShuffleRounds) * kShuffleThreads / p.shuffle_c;
+      const bool buf = p.buffers && sa.sB >= 0 && sa.dB >= 0 &&
+                       ((bpw - 1) * sa.sB + 4 * p.shuffle_c) * 4 <= dev::kBufSpan &&
+                       ((bpw - 1) * sa.dB + 4 * p.shuffle_c) * 4 <= dev::kBufSpan;
+#define TC_SH(LC)                                                                  \
+  if (buf) hipLaunchKernelGGL((dev::shuffle_kernel<LC, 3, true>), grid, block, 0, s, sc); \
+  else hipLaunchKernelGGL((dev::shuffle_kernel<LC, 3, false>), grid, block, 0, s, sc)
       switch (p.shuffle_c) {
-        case 8: hipLaunchKernelGGL((dev::shuffle_kernel<3, 3>), grid, block, 0, s, sc); break;
-        case 16: hipLaunchKernelGGL((dev::shuffle_kernel<4, 3>), grid, block, 0, s, sc); break;
-        case 32: hipLaunchKernelGGL((dev::shuffle_kernel<5, 3>), grid, block, 0, s, sc); break;
+        case 8: TC_SH(3); break;
+        case 16: TC_SH(4); break;
+        case 32: TC_SH(5); break;
         default:
           *err = "no shuffle kernel for this block width";
           return TC_E_ARG;
       }
+#undef TC_SH
       if (hipPeekAtLastError() != hipSuccess) break;
     }
   } else if (p.path == TC_PATH_INTERLEAVE) {
@@ -551,7 +612,14 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
       } else {
         rc.nvec = total;
       }
-      launch_rows(p, rc, ceil_div(rc.nvec, int64_t(p.threads) * kRowRounds), s);
+      rc.sbuf = rc.dbuf = kNoBuffer;
+      int64_t slo = 0, dlo = 0;
+      if (p.buffers && buffer_window(rc.src_off, rc.ext, rc.s, rc.rank, p.vb, &slo) &&
+          buffer_window(rc.dst_off, rc.ext, rc.d, rc.rank, p.vb, &dlo)) {
+        rc.sbuf = slo;
+        rc.dbuf = dlo;
+      }
+      launch_rows(p, rc, ceil_div(rc.nvec, int64_t(p.threads) * p.row_rounds), s);
       if (hipPeekAtLastError() != hipSuccess) break;
     }
   }

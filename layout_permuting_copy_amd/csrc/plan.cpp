@@ -86,11 +86,12 @@ static void decline(Plan* p, int flags, const std::string& why) {
 // Tile bytes, threads per workgroup and the nontemporal hint are chosen per element width from
 // measurements on MI355X (16384x16384 / 8192x8192 transposes and the batched 4x32 scale-factor
 // tiles, HIP-event timed, HBM-resident inputs).  TC_TUNE (environment, read once) overrides
-// them for tuning sweeps: "tile=32768,threads=512,nt=3,order=0,trb=128,unit=4,wl=0" (order: 0
-// column tiles first, 1 row tiles first, 2 XCD super-tiles; wl=0: keep the workgroup barrier even
-// where the phases are wave-local).
+// them for tuning sweeps: "tile=32768,threads=512,nt=3,order=0,trb=128,unit=4,wl=0,rr=2,buf=0"
+// (order: 0 column tiles first, 1 row tiles first, 2 XCD super-tiles; wl=0: keep the workgroup
+// barrier even where the phases are wave-local; rr: vectors per thread of the 16-byte rows path;
+// buf=0: global instead of buffer accesses on the rows and shuffle paths).
 struct TuneCfg {
-  int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1;
+  int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1;
 };
 
 static TuneCfg tune_override() {
@@ -115,12 +116,23 @@ static TuneCfg tune_override() {
         else if (k == "trb") c.trb = v;
         else if (k == "unit") c.unit = v;
         else if (k == "wl") c.wl = v;
+        else if (k == "rr") c.rr = v;
+        else if (k == "buf") c.buf = v;
       }
       pos = end + 1;
     }
     return c;
   }();
   return cfg;
+}
+
+// Vectors per thread on the 16-byte rows path (buffer accesses), measured on MI355X: one
+// contiguous mode: 2 up to 256 MiB each way, 1 beyond (a 64 MiB copy 6.15 TB/s with 2, 5.93-6.06
+// with 1, 5.93-6.00 with 4; 1 GiB 6.52 with 1, 6.43-6.46 with 2, 6.37-6.39 with 4); permuted rows
+// 4 (the (0,2,1,3) bf16 permute 6.23-6.25 TB/s with 4, 5.71-5.73 with 1 or 2).
+static int row_rounds(const Joint& j, int eb) {
+  if (j.rank != 1) return 4;
+  return j.count * eb <= kRowSmallBytes ? 2 : 1;
 }
 
 // Defaults per element width: {tile bytes, threads, nontemporal mode, grid order}.  `batched` =
@@ -574,9 +586,15 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     // faster there); one at a time elsewhere: permuted rows (the (0,2,1,3) permute: 6.2 vs 5.8
     // TB/s) and large contiguous copies (6.33 vs 6.26 TB/s) ran faster with the paced loads.
     p.row_burst = !lds && j.rank == 1 && j.count * p.eb <= kRowSmallBytes;
-    const int64_t per_wg = int64_t(p.threads) * kRowRounds;
+    if (!lds && p.vb == 16) {
+      const TuneCfg tc = tune_override();
+      p.buffers = tc.buf != 0;
+      p.row_rounds = row_rounds(j, p.eb);
+      if (tc.rr == 1 || tc.rr == 2 || tc.rr == 4) p.row_rounds = tc.rr;
+    }
+    const int64_t per_wg = int64_t(p.threads) * p.row_rounds;
     p.workgroups = ceil_div(nvec, per_wg);
-    p.load_outer = p.store_outer = int(std::min<int64_t>(kRowRounds, ceil_div(nvec, p.threads)));
+    p.load_outer = p.store_outer = int(std::min<int64_t>(p.row_rounds, ceil_div(nvec, p.threads)));
     p.lds_bytes = lds ? int(per_wg * p.vb) : 0;
     if (!rows_fit(j, nvec)) {
       p.status = TC_E_RANGE;
@@ -603,6 +621,7 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
       p.threads = kShuffleThreads;
       p.load_outer = p.store_outer = kShuffleRounds;
       p.ntm = 3;
+      p.buffers = tune_override().buf != 0;
       const int64_t nvec = j.count / 4;
       p.workgroups = ceil_div(nvec, int64_t(kShuffleThreads) * kShuffleRounds);  // over all launches
       return p;

@@ -132,6 +132,9 @@ struct Plan {
   bool to_planes = false;           // interleave path: interleaved source, planar destination
   bool row_burst = false;           // rows path: every load of a thread issued at once (else one at
                                     // a time, each after its offsets are decoded)
+  int row_rounds = kRowRounds;      // rows path: vectors per thread (1, 2 or 4)
+  bool buffers = false;             // rows (16-byte vectors) and shuffle paths: buffer accesses with
+                                    // streaming cache policies, in every launch whose offsets fit
   int mode_r = -1, mode_c = -1, mode_b = -1;
   TileGeom g;
   int threads = 0, load_outer = 0, store_outer = 0;
@@ -198,6 +201,8 @@ struct RowArgs {
   int64_t s[kMaxRank], d[kMaxRank];  // byte strides per step of each grid mode
   int64_t nvec;              // vectors in the whole copy (of this launch)
   int64_t row_elems;         // element-aligned rows: elements per row (its last vector may be short)
+  int64_t sbuf, dbuf;        // buffer accesses: byte offsets of the buffer bases (the lowest bytes
+                             // the launch reads / writes) from src / dst
 };
 
 // Order 2: super-tiles of kSuper x kSuper tiles, each run on one XCD (the dispatcher sends

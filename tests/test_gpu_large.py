@@ -1,5 +1,6 @@
 """Copies of 2^31 vectors and more (32 GiB per side, sized for a GPU with 288 GB of HBM): they
-run as several launches.  Checked against the oracle's offsets on sampled elements (the whole
+run as several launches.  Copies whose accesses span more than 4 GiB take global instead of
+buffer accesses (32-bit offsets).  Checked against the oracle's offsets on sampled elements (the whole
 copy is too large to redo on the host), bytes past the destination image against a sentinel,
 and the identity copy also whole on the device."""
 
@@ -79,5 +80,46 @@ def test_transpose_of_32_gib():
     import torch
     n = 1 << 17
     src, dst, _ = _run(torch, (n, n), (n, 1), (1, n), 2, L.TC_BF16, 63, "transpose")
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def test_rows_spanning_more_than_4_gib():
+    """Two rows of 4096 fp32 elements 8 GiB apart in the source, and the same rows written 8 GiB
+    apart: the launch's offsets do not fit 32 bits, so the rows path uses global accesses."""
+    import torch
+    cols, gap = 4096, 1 << 31  # elements
+    say(f"[gpu-large] rows 8 GiB apart")
+    big = torch.full(((gap + cols) * 4,), 0x5A, dtype=torch.uint8, device="cuda")
+    rows = SI.device_bits(torch, 2 * cols * 4, 64)
+    big[:cols * 4] = rows[:cols * 4]
+    big[gap * 4:] = rows[cols * 4:]
+    dense = torch.full((2 * cols * 4,), 0xA5, dtype=torch.uint8, device="cuda")
+    plan = L.tile_copy_ex(big, ((2, cols), (gap, 1), 0), dense, ((2, cols), (cols, 1), 0), L.TC_F32)
+    torch.cuda.synchronize()
+    assert plan["path_name"] == "rows", plan
+    assert torch.equal(dense, rows)
+    big.fill_(0xA5)
+    plan = L.tile_copy_ex(rows, ((2, cols), (cols, 1), 0), big, ((2, cols), (gap, 1), 0), L.TC_F32)
+    torch.cuda.synchronize()
+    assert torch.equal(big[:cols * 4], rows[:cols * 4]) and torch.equal(big[gap * 4:], rows[cols * 4:])
+    assert bool((big[cols * 4:cols * 4 + (1 << 20)] == 0xA5).all()) and bool((big[gap * 4 - (1 << 20):gap * 4] == 0xA5).all())
+    del big, rows, dense
+    torch.cuda.empty_cache()
+
+
+def test_shuffle_blocks_spanning_more_than_4_gib():
+    """4 x 32 fp32 blocks 128 MiB apart in the source: a workgroup's 64 blocks span 8 GiB, so the
+    butterfly uses global accesses; checked whole against a strided view on the device."""
+    import torch
+    nb, sb = 70, 1 << 25  # blocks, source batch stride (elements)
+    say(f"[gpu-large] shuffle blocks 128 MiB apart")
+    src = SI.device_bits(torch, ((nb - 1) * sb + 128) * 4, 65)
+    dst = torch.full((nb * 128 * 4,), 0xA5, dtype=torch.uint8, device="cuda")
+    plan = L.tile_copy_ex(src, ((nb, 4, 32), (sb, 32, 1), 0), dst, ((nb, 4, 32), (128, 1, 4), 0), L.TC_F32)
+    torch.cuda.synchronize()
+    assert plan["path_name"] == "shuffle", plan
+    s32, d32 = src.view(torch.int32), dst.view(torch.int32)
+    assert torch.equal(s32.as_strided((nb, 4, 32), (sb, 32, 1)), d32.as_strided((nb, 4, 32), (128, 1, 4)))
     del src, dst
     torch.cuda.empty_cache()

@@ -302,6 +302,38 @@ def test_guarded_paths(eb):
     _check((64, 64), (64, 1), (1, 64), eb, flags=L.TC_FLAG_FORCE_GUARDED, seed=eb, expect="guarded_tile")
 
 
+@pytest.mark.parametrize("n", [3 * 65536 + 36, (1 << 26) + 4100])
+def test_rows_with_negative_layout_offsets(n):
+    """Pointers into the middle of the buffers with negative layout offsets (an offset is any
+    element displacement from the pointer): every element below the pointers is copied, on the
+    rows path with all loads at once (up to 256 MiB) and with paced loads beyond, both with
+    buffer bases at the lowest byte of the copy.  The bytes around the destination keep the
+    sentinel."""
+    import torch
+    eb, k, m, pad = 4, 1000, 2048, 4096
+    say(f"[gpu] rows n={n} with offsets -{k} / -{m}")
+    src = SI.device_bits(torch, n * eb, 17)
+    dst = torch.full((n * eb + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    plan = L.tile_copy_ex(src.data_ptr() + k * eb, ((n,), (1,), -k), dst.data_ptr() + pad + m * eb,
+                          ((n,), (1,), -m), L.TC_F32)
+    torch.cuda.synchronize()
+    assert plan["path_name"] == "rows" and plan["vec_bytes"] == 16, plan
+    assert torch.equal(dst[pad:pad + n * eb], src)
+    assert bool((dst[:pad] == 0xA5).all()) and bool((dst[pad + n * eb:] == 0xA5).all())
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def test_rows_and_blocks_with_negative_strides():
+    """A row-flipped destination on the rows path (its buffer base is the last row) and a
+    negative batch stride on the scale-factor butterfly (global accesses there)."""
+    _check((300, 256), (256, 1), (-256, 1), 4, d_off=299 * 256, seed=21, expect="rows")
+    _check((1000, 4, 32), (-128, 32, 1), (128, 1, 4), 4, s_off=999 * 128, src_elems=1000 * 128, seed=22,
+           expect="shuffle")
+    _check((1000, 4, 32), (128, 32, 1), (-128, 1, 4), 4, d_off=999 * 128, dst_elems=1000 * 128, seed=23,
+           expect="shuffle")
+
+
 def test_no_swizzle_flag_same_result():
     plan = _check((256, 256), (256, 1), (1, 256), 4, flags=L.TC_FLAG_NO_SWIZZLE, seed=3)
     assert plan["xor_k"] == 0 and plan["xor_cmask"] == 0
