@@ -161,7 +161,8 @@ typedef struct tc_plan_info {
   int32_t edge_tiles;       /* transpose: 1 if the kernel carries its guarded code for tiles that
                                reach past an extent; 0 if every tile lies inside the copy and the
                                interior-only kernel runs */
-  int32_t reserved0;
+  int32_t loads_in_flight;  /* transpose: most global loads a lane keeps outstanding in the load
+                               phase (a wait after each load beyond them); 0 = all at once */
   int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
   char reason[192];         /* why the fast path was declined ("" if it was not) */
 } tc_plan_info;

@@ -237,6 +237,13 @@ constexpr int64_t kBufSpan = (int64_t(1) << 32) - 256;  // largest byte span a l
 // vector memory accesses.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N): waits until at most N of the lane's vector memory accesses are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_at_most() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediates below 16");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 __device__ __forceinline__ Rsrc make_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, kRsrcWord3);
 }

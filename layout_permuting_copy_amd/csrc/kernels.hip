@@ -555,7 +555,7 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
         ta.nslices = ta.tilesB.d;
         for (int k = 0; k < ta.nbatch; ++k) ta.nslices *= ta.bdiv[k].d;
       }
-      const TransposeCfg cfg{p.vb, p.g.U, p.g.tile_bytes, p.g.NT, p.g.ntm, p.g.step, p.g.wave_local, p.g.edges};
+      const TransposeCfg cfg = transpose_cfg(p.g);
       if (!launch_transpose(p.eb, cfg, &ta, p.workgroups, stream)) {
         *err = "no transpose kernel instance for this element width, vector width, tile size and thread count";
         return TC_E_ARG;

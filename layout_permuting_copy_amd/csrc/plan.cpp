@@ -86,12 +86,13 @@ static void decline(Plan* p, int flags, const std::string& why) {
 // Tile bytes, threads per workgroup and the nontemporal hint are chosen per element width from
 // measurements on MI355X (16384x16384 / 8192x8192 transposes and the batched 4x32 scale-factor
 // tiles, HIP-event timed, HBM-resident inputs).  TC_TUNE (environment, read once) overrides
-// them for tuning sweeps: "tile=32768,threads=512,nt=3,order=0,trb=128,unit=4,wl=0,rr=2,buf=0"
+// them for tuning sweeps: "tile=32768,threads=512,nt=3,order=0,trb=128,unit=4,wl=0,rr=2,buf=0,cap=0"
 // (order: 0 column tiles first, 1 row tiles first, 2 XCD super-tiles; wl=0: keep the workgroup
 // barrier even where the phases are wave-local; rr: vectors per thread of the 16-byte rows path;
-// buf=0: global instead of buffer accesses on the rows and shuffle paths).
+// buf=0: global instead of buffer accesses on the rows and shuffle paths; cap: loads in flight
+// per lane in the transpose's load phase, 0 = all, where the library holds such an instance).
 struct TuneCfg {
-  int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1;
+  int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1, cap = -1;
 };
 
 static TuneCfg tune_override() {
@@ -118,6 +119,7 @@ static TuneCfg tune_override() {
         else if (k == "wl") c.wl = v;
         else if (k == "rr") c.rr = v;
         else if (k == "buf") c.buf = v;
+        else if (k == "cap") c.cap = v;
       }
       pos = end + 1;
     }
@@ -256,15 +258,21 @@ static bool search_swizzle(const TileGeom& g, bool no_swizzle, TileGeom* out, in
 // to give every CU many of them: bf16 16384^2 as 1024 x 64 on 1024 lanes 5730 -> 5830, fp64 8192^2
 // as 256 x 64 5750 -> 5980, int8 8192^2 as 512 x 256 5000 -> 5190 (the default tile for 1-byte
 // elements otherwise); fp32 and smaller fp16 copies are faster on 64 KiB tiles.
+// Loads in flight per lane (`cap`): all of a lane's loads at once had been the rule, but for the
+// tall tiles of 1-, 2- and 8-byte elements fewer measured faster (a wait in the load phase keeps
+// at most `cap` outstanding): bf16 16384^2 5.86 -> 6.05-6.12 TB/s with 2, fp16 8192^2 5.30 ->
+// 5.51-5.57, int8 8192^2 5.15 -> 5.34-5.35, fp64 8192^2 (16 loads per lane) 6.00 -> 6.48-6.50 with
+// 8.  fp32 (6.24 with all in flight, 6.04-6.19 with 1-6) and the element-aligned plans keep all.
 static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c) {
   c->nt = 3;
   c->order = 1;
   c->unit = 16;
+  c->cap = 0;
   auto tiles = [&](int64_t tr, int64_t tc) { return ceil_div(eR, tr) * ceil_div(eC, tc) * others; };
   switch (eb) {
     case 1:
       if (eR < 512 || eC < 256 || tiles(512, 256) < 512) return false;
-      c->tile = 131072; c->threads = 512; c->trb = 512;  // 512 x 256
+      c->tile = 131072; c->threads = 512; c->trb = 512; c->cap = 2;  // 512 x 256
       return true;
     case 16:
       if (eR < 64 || eC < 8) return false;
@@ -272,7 +280,7 @@ static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c)
       return true;
     case 8:
       if (eR < 128 || eC < 16) return false;
-      if (tiles(256, 64) >= 4096) { c->tile = 131072; c->threads = 512; c->trb = 2048; }  // 256 x 64
+      if (tiles(256, 64) >= 4096) { c->tile = 131072; c->threads = 512; c->trb = 2048; c->cap = 8; }  // 256 x 64
       else if (tiles(256, 32) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 2048; }  // 256 x 32
       else { c->tile = 16384; c->threads = 256; c->trb = 1024; }                          // 128 x 16
       return true;
@@ -286,6 +294,7 @@ static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c)
       if (tiles(1024, 64) >= 4096) { c->tile = 131072; c->threads = 1024; c->trb = 2048; }  // 1024 x 64
       else if (tiles(512, 64) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 1024; }  // 512 x 64
       else { c->tile = 32768; c->threads = 256; c->trb = 512; }                          // 256 x 64
+      c->cap = 2;
       return true;
     default:
       return false;
@@ -310,7 +319,8 @@ static bool plan_with_cfg(const Plan& p, int flags, TuneCfg cfg, bool tile_pinne
   // the same tile with 256 threads, else 16 KiB tiles of 256 threads (every vector width)
   const int unit0 = cfg.unit ? cfg.unit : unit_min;
   auto instance = [&](int tile, int threads) {
-    return launch_transpose(p.eb, TransposeCfg{p.vb, unit0, tile, threads, cfg.nt, p.step, false}, nullptr, 0, nullptr);
+    return launch_transpose(p.eb, TransposeCfg{p.vb, unit0, tile, threads, cfg.nt, p.step, false, true, std::max(cfg.cap, 0)},
+                            nullptr, 0, nullptr);
   };
   if (!instance(cfg.tile, cfg.threads)) {
     if (instance(cfg.tile, 256)) {
@@ -340,6 +350,7 @@ static bool plan_with_cfg(const Plan& p, int flags, TuneCfg cfg, bool tile_pinne
     g.ntm = cfg.nt;
     g.order = cfg.order;
     g.step = p.step;
+    g.cap = std::max(cfg.cap, 0);
     if (unit < p.eb || unit < 4 || unit > p.vb) continue;
     const int ve = p.vb / p.eb;
     const int bmin = unit / p.eb;
@@ -360,7 +371,8 @@ static bool plan_with_cfg(const Plan& p, int flags, TuneCfg cfg, bool tile_pinne
     if (dup || nseen >= 64) continue;
     seen[nseen][0] = g.TR; seen[nseen][1] = g.TC; seen[nseen][2] = g.NB; seen[nseen][3] = g.U; ++nseen;
     if (!finish_geom(&g)) continue;
-    if (!launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, false}, nullptr, 0, nullptr))
+    if (!launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, false, true, g.cap}, nullptr,
+                          0, nullptr))
       continue;
     TileGeom c;
     int64_t wc, rc;
@@ -441,6 +453,8 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   }
   cands[ncand++] = base;
   if (flags & TC_FLAG_NO_SWIZZLE) ncand = 1;  // the swizzle is measured on the default plan's tile
+  if (ov.cap >= 0)
+    for (int i = 0; i < ncand; ++i) cands[i].cap = ov.cap;
   // wave-local phases drop the workgroup barrier where the library holds such an instance
   // Row tiles first with source rows off the lines: neighbouring column tiles read the same lines.
   // They are tilesR workgroups apart, so the grid pads tilesR to a multiple of kXcds and puts them
@@ -448,8 +462,8 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   auto with_phase_order = [&](TileGeom g) {
     g.pad_rows = g.order == 1 && !src_lines;
     g.wave_local = ov.wl != 0 && tile_wave_local(g) &&
-                   launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, true}, nullptr,
-                                    0, nullptr);
+                   launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, true, true, g.cap},
+                                    nullptr, 0, nullptr);
     return g;
   };
   bool have = false;
@@ -874,6 +888,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
     info->lds_write_bytes = p.g.ww;
     info->lds_read_bytes = p.g.rw;
     info->edge_tiles = p.g.edges ? 1 : 0;
+    info->loads_in_flight = p.g.cap;
     info->write_conflicts = p.wconf;
     info->read_conflicts = p.rconf;
   }

@@ -93,6 +93,7 @@ struct TileGeom {
   bool edges = true;              // some tile reaches past an extent (the kernel needs its guards)
   bool pad_rows = false;          // order 1 with source rows off the 128-byte lines: the row-tile
                                   // count of the grid is padded to a multiple of kXcds (tile_at)
+  int cap = 0;                    // loads a lane keeps in flight in the interior load phase (0: all)
   int loads = 4, stores = 4;  // accesses per thread per phase
   int ww = 16, rw = 4;        // LDS write / read instruction bytes
   int k = 0, shift = 0, tbit = 0;
@@ -226,7 +227,12 @@ struct TransposeCfg {
   int vb, unit, tile, threads, ntm, step;
   bool wave_local;
   bool edges = true;  // false: every tile lies wholly inside the copy (the interior-only kernel)
+  int cap = 0;        // loads in flight per lane in the load phase (0: all of them)
 };
+// The kernel configuration a planned tile geometry runs with (every field of it).
+inline TransposeCfg transpose_cfg(const TileGeom& g) {
+  return TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, g.wave_local, g.edges, g.cap};
+}
 bool launch_transpose_eb1(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
 bool launch_transpose_eb2(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
 bool launch_transpose_eb4(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);

@@ -46,7 +46,7 @@ struct TileRegs {
 // stride of the column mode (1, or 2: each vector is read as two contiguous ones, which stay
 // inside the allocation as long as the row's next element exists; the vector holding a row's
 // last element is loaded element by element).
-template <int EB, int VB, typename G, int NT, int NTM, int S, bool GUARD>
+template <int EB, int VB, typename G, int NT, int NTM, int S, bool GUARD, int CAP = 0>
 __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& t, TileRegs<G>& r) {
   const int lTRu = a.lTR - G::LB;
   const int lnCV = a.lTC - G::LVE;  // load vectors per unit-row
@@ -76,7 +76,11 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < G::B; ++i) gload_step<EB, VB, S, NTM>(p + i * sR * EB, r.w[f][i]);
+      for (int i = 0; i < G::B; ++i) {
+        gload_step<EB, VB, S, NTM>(p + i * sR * EB, r.w[f][i]);
+        if constexpr (CAP > 0)
+          if (f * G::B + i >= CAP) wait_vmem_at_most<CAP>();
+      }
     }
   }
 }
@@ -202,7 +206,10 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
 // EDGE = false: the host has shown that every tile lies wholly inside the copy, and the guarded
 // code is not compiled in (it needs more registers than the interior code, which can then
 // lower the number of workgroups per CU).
-template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL, bool EDGE = true>
+//
+// CAP > 0: the interior load phase keeps at most CAP loads of a lane outstanding (measured faster
+// than all at once for the tall tiles of 1-, 2- and 8-byte elements).
+template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL, bool EDGE = true, int CAP = 0>
 __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   typedef Geo<EB, VB, U, TILE, NT> G;
   __shared__ __attribute__((aligned(16))) unsigned char lds[TILE];
@@ -210,8 +217,8 @@ __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   if (!t.valid) return;  // padding of the XCD super-tile order (whole workgroup, before any barrier)
   TileRegs<G> r;
   const bool full = !EDGE || (tile_full(a, t) && (S == 1 || t.remC > (int64_t(1) << a.lTC)));
-  if constexpr (!EDGE) load_tile<EB, VB, G, NT, NTM, S, false>(a, t, r);
-  else if (full) load_tile<EB, VB, G, NT, NTM, S, false>(a, t, r);
+  if constexpr (!EDGE) load_tile<EB, VB, G, NT, NTM, S, false, CAP>(a, t, r);
+  else if (full) load_tile<EB, VB, G, NT, NTM, S, false, CAP>(a, t, r);
   else load_tile<EB, VB, G, NT, NTM, S, true>(a, t, r);
   write_lds<EB, VB, U, G, NT>(a, lds, r);
   if constexpr (WL) wave_lds_sync();
@@ -222,12 +229,12 @@ __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
 }
 
 // Launches the instance (ta != nullptr) or only reports whether it exists (ta == nullptr).
-template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL = false, bool EDGE = true>
+template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL = false, bool EDGE = true, int CAP = 0>
 bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
   if constexpr (Geo<EB, VB, U, TILE, NT>::valid) {
     if (ta)
-      hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM, S, WL, EDGE>), dim3(uint32_t(wgs)), dim3(NT), 0, s,
-                         *ta);
+      hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM, S, WL, EDGE, CAP>), dim3(uint32_t(wgs)), dim3(NT), 0,
+                         s, *ta);
     return true;
   }
   return false;
@@ -246,6 +253,10 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);                                             \
     const int vb = c.vb, tile = c.tile, nt = c.threads, ntm = c.ntm;                                         \
     constexpr int U = EB < 4 ? 4 : EB;                                                                       \
+    if (c.cap != 0) {                                                                                        \
+      TC_CAPS_EB##EB                                                                                         \
+      return false;                                                                                          \
+    }                                                                                                        \
     if (c.unit == 16 && U != 16) {                                                                           \
       TC_CFG_UNIT(EB, 16, 16384, 256) TC_CFG_UNIT(EB, 16, 32768, 256) TC_CFG_UNIT(EB, 16, 65536, 256)         \
       TC_CFG_UNIT(EB, 16, 32768, 512) TC_CFG_UNIT(EB, 16, 65536, 512) TC_CFG_UNIT(EB, 16, 65536, 1024)       \
@@ -285,6 +296,20 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
     if (ntm == 3) return dev::launch_transpose_cfg<EB, 16, UNIT, TILE, NT, 3, 1>(ta, wgs, s);                \
     if (ntm == 0) return dev::launch_transpose_cfg<EB, 16, UNIT, TILE, NT, 0, 1>(ta, wgs, s);                \
   }
+
+// The tall configurations that run with a load cap (plan.cpp, tall_cfg): 16-byte LDS units,
+// nontemporal accesses, with and without the edge code.
+#define TC_CFG_CAP(EB, TILE, NT, CAP)                                                                        \
+  if (c.cap == CAP && c.unit == 16 && vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local &&  \
+      ntm == 3) {                                                                                            \
+    if (!c.edges) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, false, CAP>(ta, wgs, s);  \
+    return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP>(ta, wgs, s);               \
+  }
+#define TC_CAPS_EB1 TC_CFG_CAP(1, 131072, 512, 2)
+#define TC_CAPS_EB2 TC_CFG_CAP(2, 131072, 1024, 2) TC_CFG_CAP(2, 65536, 512, 2) TC_CFG_CAP(2, 32768, 256, 2)
+#define TC_CAPS_EB4
+#define TC_CAPS_EB8 TC_CFG_CAP(8, 131072, 512, 8)
+#define TC_CAPS_EB16
 
 #define TC_CFG_WL(EB, U, TILE, NT)                                                                           \
   if (vb == 16 && tile == TILE && nt == NT && c.step == 1 && ntm == 3 && c.wave_local)                       \

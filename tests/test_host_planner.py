@@ -302,6 +302,24 @@ def test_interior_kernel_only_for_exact_tilings():
     assert edge((8190, 4095), (8192, 2), (1, 8190), L.TC_F16, 8192) == 1   # stride-2 source
 
 
+def test_load_caps_of_the_tall_tiles():
+    """The tall tiles of 1-, 2- and 8-byte elements keep a bounded number of loads in flight per
+    lane (2, 2, 8); fp32, 16-byte elements, element-aligned plans and the smaller fp64 tiles keep
+    all of them in flight (0)."""
+    def cap(shape, ss, ds, dt):
+        p = L.tc_plan((shape, ss), (shape, ds), dt)
+        assert p["path_name"] == "transpose", p
+        return p["loads_in_flight"]
+    assert cap((16384, 16384), (16384, 1), (1, 16384), L.TC_BF16) == 2
+    assert cap((8192, 8192), (8192, 1), (1, 8192), L.TC_F16) == 2
+    assert cap((8192, 8192), (8192, 1), (1, 8192), L.TC_I8) == 2
+    assert cap((8192, 8192), (8192, 1), (1, 8192), L.TC_F64) == 8
+    assert cap((16384, 16384), (16384, 1), (1, 16384), L.TC_F32) == 0
+    assert cap((8192, 8192), (8192, 1), (1, 8192), L.TC_B128) == 0
+    assert cap((8191, 8190), (8190, 1), (1, 8191), L.TC_F16) == 0        # element-aligned vectors
+    assert cap((8192, 4096), (4096, 1), (1, 8192), L.TC_F64) == 0        # 128 x 16 tiles
+
+
 def test_copies_beyond_2_31_vectors_plan():
     """Contiguous and shuffle copies of 2^31 vectors or more (32 GiB and up, sized for a 288 GB
     GPU) plan as several launches; only a single outermost index of more than 2^30 vectors is
