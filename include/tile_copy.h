@@ -149,7 +149,8 @@ typedef struct tc_plan_info {
   int32_t xor_k, xor_shift, xor_mask, xor_tbit;
   int32_t xor_cshift, xor_cmask;
   int32_t grid_order;       /* transpose grid: 0 column tiles fastest, 1 row tiles fastest, 2 super-tiles
-                               of 8 x 8 tiles, each on one XCD (workgroup i runs on XCD i mod 8) */
+                               of 8 x 8 tiles, each on one XCD (workgroup i runs on XCD i mod 8);
+                               rows path: 0 destination order, 1 the outer modes in source order */
   int32_t nontemporal;      /* nontemporal global accesses: bit 0 loads, bit 1 stores */
   int32_t unaligned;        /* 1: declined split run by the transpose kernel with 16-byte vectors at
                                element alignment and element accesses at the edges of the copy */

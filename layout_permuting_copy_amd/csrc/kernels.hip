@@ -571,37 +571,38 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
 #undef TC_G
     }
   } else {
-    // rows: grid modes in canonical (destination) order; the contiguous mode counts vectors
+    // rows: grid modes in the plan's grid order (rows_grid); the contiguous mode counts vectors
+    const Joint jg = rows_grid(p);
     RowArgs ra{};
     ra.src = static_cast<const unsigned char*>(src);
     ra.dst = static_cast<unsigned char*>(dst);
-    ra.src_off = j.so * p.eb;
-    ra.dst_off = j.dof * p.eb;
+    ra.src_off = jg.so * p.eb;
+    ra.dst_off = jg.dof * p.eb;
     const int ve = p.vb / p.eb;
-    ra.rank = j.rank;
+    ra.rank = jg.rank;
     int64_t ext[kMaxRank] = {};
     int64_t total = 1;
-    for (int k = 0; k < j.rank; ++k) {
-      const bool inner = (p.path != TC_PATH_GUARDED_ROWS) && k == j.rank - 1;
+    for (int k = 0; k < jg.rank; ++k) {
+      const bool inner = (p.path != TC_PATH_GUARDED_ROWS) && k == jg.rank - 1;
       // (element-aligned rows: the last vector of a row may be short)
-      ext[k] = inner ? (j.m[k].e + ve - 1) / ve : j.m[k].e;
-      ra.s[k] = j.m[k].s * p.eb * (inner ? ve : 1);
-      ra.d[k] = j.m[k].d * p.eb * (inner ? ve : 1);
+      ext[k] = inner ? (jg.m[k].e + ve - 1) / ve : jg.m[k].e;
+      ra.s[k] = jg.m[k].s * p.eb * (inner ? ve : 1);
+      ra.d[k] = jg.m[k].d * p.eb * (inner ? ve : 1);
       total *= ext[k];
     }
-    ra.row_elems = j.rank >= 1 ? j.m[j.rank - 1].e : 1;
+    ra.row_elems = jg.rank >= 1 ? jg.m[jg.rank - 1].e : 1;
     // one launch, or (2^31 vectors and more) launches over ranges of the outermost grid mode of
     // at most kLaunchVectors vectors each (the planner has checked that one index fits)
-    const int64_t per0 = j.rank >= 1 ? total / ext[0] : 1;  // vectors per index of mode 0
-    const int64_t step0 = total < (int64_t(1) << 31) || j.rank < 1 ? std::max<int64_t>(ext[0], 1)
+    const int64_t per0 = jg.rank >= 1 ? total / ext[0] : 1;  // vectors per index of mode 0
+    const int64_t step0 = total < (int64_t(1) << 31) || jg.rank < 1 ? std::max<int64_t>(ext[0], 1)
                                                                     : std::max<int64_t>(kLaunchVectors / per0, 1);
     for (int64_t i0 = 0; i0 < std::max<int64_t>(ext[0], 1); i0 += step0) {
       RowArgs rc = ra;
-      if (j.rank >= 1) {
+      if (jg.rank >= 1) {
         const int64_t n0 = std::min(step0, ext[0] - i0);
         rc.src_off = ra.src_off + i0 * ra.s[0];
         rc.dst_off = ra.dst_off + i0 * ra.d[0];
-        for (int k = 0; k < j.rank; ++k) {
+        for (int k = 0; k < jg.rank; ++k) {
           const int64_t e = k == 0 ? n0 : ext[k];
           rc.ext[k] = uint32_t(e);
           const Div32 dv = make_div32(uint32_t(e));

@@ -90,9 +90,10 @@ static void decline(Plan* p, int flags, const std::string& why) {
 // (order: 0 column tiles first, 1 row tiles first, 2 XCD super-tiles; wl=0: keep the workgroup
 // barrier even where the phases are wave-local; rr: vectors per thread of the 16-byte rows path;
 // buf=0: global instead of buffer accesses on the rows and shuffle paths; cap: loads in flight
-// per lane in the transpose's load phase, 0 = all, where the library holds such an instance).
+// per lane in the transpose's load phase, 0 = all, where the library holds such an instance;
+// so: 1 / 0 the rows path's outer grid modes in source / destination order).
 struct TuneCfg {
-  int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1, cap = -1;
+  int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1, cap = -1, so = -1;
 };
 
 static TuneCfg tune_override() {
@@ -120,6 +121,7 @@ static TuneCfg tune_override() {
         else if (k == "rr") c.rr = v;
         else if (k == "buf") c.buf = v;
         else if (k == "cap") c.cap = v;
+        else if (k == "so") c.so = v;
       }
       pos = end + 1;
     }
@@ -128,12 +130,32 @@ static TuneCfg tune_override() {
   return cfg;
 }
 
+Joint rows_grid(const Plan& p) {
+  Joint g = p.j;
+  if (p.row_src_order && g.rank > 2)
+    std::stable_sort(g.m, g.m + g.rank - 1,
+                     [](const Mode& x, const Mode& y) { return std::llabs(x.s) > std::llabs(y.s); });
+  return g;
+}
+
+// Permuted rows shorter than 1 KiB walk the source order (reads contiguous, each row written to
+// its place), where it differs from the destination's: the (0,2,1,3) bf16 permute with 256-byte
+// rows 6.11 -> 6.44 TB/s, with 128-byte rows 6.21 -> 6.47-6.50, fp32 with 128-byte rows 6.16 ->
+// 6.44; 8 heads of 256-byte rows equal (6.17); 1 KiB rows 6.25 against 6.23 in source order.
+static bool row_src_order(const Joint& j, int eb) {
+  if (j.rank < 3 || j.m[j.rank - 1].e * eb >= 1024) return false;
+  for (int k = 0; k + 2 < j.rank; ++k)
+    if (std::llabs(j.m[k].s) < std::llabs(j.m[k + 1].s)) return true;
+  return false;
+}
+
 // Vectors per thread on the 16-byte rows path (buffer accesses), measured on MI355X: one
 // contiguous mode: 2 up to 256 MiB each way, 1 beyond (a 64 MiB copy 6.15 TB/s with 2, 5.93-6.06
 // with 1, 5.93-6.00 with 4; 1 GiB 6.52 with 1, 6.43-6.46 with 2, 6.37-6.39 with 4); permuted rows
-// 4 (the (0,2,1,3) bf16 permute 6.23-6.25 TB/s with 4, 5.71-5.73 with 1 or 2).
-static int row_rounds(const Joint& j, int eb) {
-  if (j.rank != 1) return 4;
+// in source order 2 (the (0,2,1,3) permute 6.44 TB/s, 5.89-5.93 with 1, 6.32-6.33 with 4), in
+// destination order 4 (6.23-6.25 TB/s with 4, 5.71-5.73 with 1 or 2).
+static int row_rounds(const Joint& j, int eb, bool src_order) {
+  if (j.rank != 1) return src_order ? 2 : 4;
   return j.count * eb <= kRowSmallBytes ? 2 : 1;
 }
 
@@ -603,14 +625,15 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     if (!lds && p.vb == 16) {
       const TuneCfg tc = tune_override();
       p.buffers = tc.buf != 0;
-      p.row_rounds = row_rounds(j, p.eb);
+      p.row_src_order = tc.so >= 0 ? tc.so == 1 : row_src_order(j, p.eb);
+      p.row_rounds = row_rounds(j, p.eb, p.row_src_order);
       if (tc.rr == 1 || tc.rr == 2 || tc.rr == 4) p.row_rounds = tc.rr;
     }
     const int64_t per_wg = int64_t(p.threads) * p.row_rounds;
     p.workgroups = ceil_div(nvec, per_wg);
     p.load_outer = p.store_outer = int(std::min<int64_t>(p.row_rounds, ceil_div(nvec, p.threads)));
     p.lds_bytes = lds ? int(per_wg * p.vb) : 0;
-    if (!rows_fit(j, nvec)) {
+    if (!rows_fit(rows_grid(p), nvec)) {
       p.status = TC_E_RANGE;
       p.reason = "more than 2^30 vectors per index of the outermost mode";
     }
@@ -865,6 +888,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
   info->workgroups = p.workgroups;
   info->lds_bytes = p.lds_bytes;
   if (p.path == TC_PATH_ROWS || p.path == TC_PATH_SHUFFLE) info->nontemporal = p.ntm;
+  if (p.path == TC_PATH_ROWS) info->grid_order = p.row_src_order ? 1 : 0;
   if (p.path == TC_PATH_SHUFFLE) {
     info->tile_r = 4;
     info->tile_c = p.shuffle_c;

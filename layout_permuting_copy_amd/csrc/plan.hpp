@@ -42,6 +42,11 @@ struct Joint {
   int64_t count = 1;
 };
 
+struct Plan;
+// The joint modes in the rows path's grid order, innermost last: the destination's (canonical)
+// order, or with row_src_order the outer modes by descending source stride.
+Joint rows_grid(const Plan& p);
+
 // ---- layout algebra (layout.cpp) -------------------------------------------------------------
 int make_joint(const tc_layout& src, const tc_layout& dst, Joint* out, std::string* err);
 // Sort by destination stride (descending |d|, stable) and merge adjacent modes that are
@@ -134,6 +139,7 @@ struct Plan {
   bool row_burst = false;           // rows path: every load of a thread issued at once (else one at
                                     // a time, each after its offsets are decoded)
   int row_rounds = kRowRounds;      // rows path: vectors per thread (1, 2 or 4)
+  bool row_src_order = false;       // rows path: the outer grid modes in source order (see rows_grid)
   bool buffers = false;             // rows (16-byte vectors) and shuffle paths: buffer accesses with
                                     // streaming cache policies, in every launch whose offsets fit
   int mode_r = -1, mode_c = -1, mode_b = -1;

@@ -84,6 +84,16 @@ def test_transpose_of_32_gib():
     torch.cuda.empty_cache()
 
 
+def test_permuted_rows_beyond_2_31_vectors():
+    """The (0,2,1,3) permute of (2, 64, 2^20, 128) bf16 (32 GiB per side): permuted rows in source
+    order, split into launches over the source-ordered outermost mode."""
+    import torch
+    b, h, s, d = 2, 64, 1 << 20, 128
+    src, dst, _ = _run(torch, (b, h, s, d), (h * s * d, s * d, d, 1), (h * s * d, d, h * d, 1), 2, L.TC_BF16, 66, "rows")
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def test_rows_spanning_more_than_4_gib():
     """Two rows of 4096 fp32 elements 8 GiB apart in the source, and the same rows written 8 GiB
     apart: the launch's offsets do not fit 32 bits, so the rows path uses global accesses."""

@@ -320,6 +320,26 @@ def test_load_caps_of_the_tall_tiles():
     assert cap((8192, 4096), (4096, 1), (1, 8192), L.TC_F64) == 0        # 128 x 16 tiles
 
 
+def test_permuted_rows_walk_the_source_order():
+    """Rows shorter than 1 KiB whose outer modes are ordered differently on the two sides run in
+    source order with 2 vectors per lane (grid_order 1); longer rows, and copies whose sides agree,
+    keep the destination order with 4 paced vectors (grid_order 0)."""
+    def rows(w):
+        p = L.tc_plan((w.src.shape, w.src.stride), (w.dst.shape, w.dst.stride), L.DTYPE_BY_NAME[w.dtype])
+        assert p["path_name"] == "rows", p
+        return p["grid_order"], p["load_outer"]
+    assert rows(SI.permute0213()) == (1, 2)
+    assert rows(SI.permute0213(d=32, dtype="float32")) == (1, 2)
+    assert rows(SI.permute0213(b=8, h=16, s=1024, d=512)) == (0, 4)          # 1 KiB rows
+    box = SI.Workload("box", SI.Side((64, 128, 256), (65536, 512, 1)), SI.Side((64, 128, 256), (32768, 256, 1)),
+                      "float32", "bits", 1)
+    assert rows(box) == (0, 4)                                                 # both sides in one order
+    # the split into launches follows the source-ordered outermost mode
+    p = L.tc_plan(((2, 64, 1 << 20, 128), (64 << 27, 128 << 20, 128, 1)),
+                  ((2, 64, 1 << 20, 128), (64 << 27, 128, 128 * 64, 1)), L.TC_BF16)
+    assert p["path_name"] == "rows" and p["grid_order"] == 1 and p["status"] == 0, p
+
+
 def test_copies_beyond_2_31_vectors_plan():
     """Contiguous and shuffle copies of 2^31 vectors or more (32 GiB and up, sized for a 288 GB
     GPU) plan as several launches; only a single outermost index of more than 2^30 vectors is
