@@ -43,7 +43,8 @@ __device__ __forceinline__ void rows_body(const RowArgs& a, typename Bytes<VB>::
   static_assert(!BUF || (VB == 16 && !USE_LDS), "buffer accesses: 16-byte vectors in registers");
   const int t = threadIdx.x;
   const int64_t base = int64_t(blockIdx.x) * NT * ROUNDS;
-  const Rsrc rs = make_rsrc(a.src + a.sbuf), rd = make_rsrc(a.dst + a.dbuf);
+  // (the buffer bases exist only in the BUF instances: a.sbuf / a.dbuf are not offsets otherwise)
+  const Rsrc rs = make_rsrc(BUF ? a.src + a.sbuf : a.src), rd = make_rsrc(BUF ? a.dst + a.dbuf : a.dst);
   V reg[ROUNDS];
   int64_t soff[ROUNDS], doff[ROUNDS];
   bool live[ROUNDS];

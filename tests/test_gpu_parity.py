@@ -324,6 +324,24 @@ def test_rows_with_negative_layout_offsets(n):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("b,h,sq,d,eb", [(3, 5, 37, 64, 2), (4, 7, 33, 32, 4), (2, 9, 65, 256, 1), (4, 3, 41, 16, 8),
+                                         (4, 4, 29, 8, 16), (2, 16, 300, 64, 2)])
+def test_permuted_rows_in_source_order(b, h, sq, d, eb):
+    """(0,2,1,3) permutes with rows shorter than 1 KiB: the rows grid walks the source order with 2
+    vectors per lane (ragged last workgroups); the same copies with a head-reversed destination and
+    an offset source."""
+    shape = (b, h, sq, d)
+    ss = (h * sq * d, sq * d, d, 1)
+    ds = (sq * h * d, d, h * d, 1)
+    p = _check(shape, ss, ds, eb, seed=b * 100 + d + eb, expect="rows")
+    assert p["grid_order"] == 1 and p["load_outer"] == 2, p
+    ds_rev = (sq * h * d, -d, h * d, 1)
+    n = b * h * sq * d
+    p = _check(shape, ss, ds_rev, eb, s_off=16 // eb, d_off=(h - 1) * d, src_elems=n + 16 // eb, dst_elems=n,
+               seed=b * 100 + d + eb + 1, expect="rows")
+    assert p["grid_order"] == 1, p
+
+
 def test_rows_and_blocks_with_negative_strides():
     """A row-flipped destination on the rows path (its buffer base is the last row) and a
     negative batch stride on the scale-factor butterfly (global accesses there)."""
