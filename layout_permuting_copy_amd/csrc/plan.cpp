@@ -281,10 +281,12 @@ static bool search_swizzle(const TileGeom& g, bool no_swizzle, TileGeom* out, in
 // as 256 x 64 5750 -> 5980, int8 8192^2 as 512 x 256 5000 -> 5190 (the default tile for 1-byte
 // elements otherwise); fp32 and smaller fp16 copies are faster on 64 KiB tiles.
 // Loads in flight per lane (`cap`): all of a lane's loads at once had been the rule, but for the
-// tall tiles of 1-, 2- and 8-byte elements fewer measured faster (a wait in the load phase keeps
-// at most `cap` outstanding): bf16 16384^2 5.86 -> 6.05-6.12 TB/s with 2, fp16 8192^2 5.30 ->
-// 5.51-5.57, int8 8192^2 5.15 -> 5.34-5.35, fp64 8192^2 (16 loads per lane) 6.00 -> 6.48-6.50 with
-// 8.  fp32 (6.24 with all in flight, 6.04-6.19 with 1-6) and the element-aligned plans keep all.
+// tall tiles of 1- and 2-byte elements two measured faster (a wait in the load phase keeps at most
+// `cap` outstanding), on every buffer placement tried: bf16 16384^2 5.85-5.89 -> 6.09-6.19 TB/s,
+// int8 8192^2 5.20-5.39 -> 5.51-5.62, fp16 8192^2 5.30-5.41 -> 5.54-5.60.  fp64 with 8 of its 16
+// loads ran at 6.4-6.6 TB/s on some placements of the same buffers and 5.6-5.9 on others (mean no
+// better than 6.0 with all in flight), fp32 at 6.04-6.19 against 6.24; they keep all in flight, as
+// do the element-aligned plans.
 static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c) {
   c->nt = 3;
   c->order = 1;
@@ -302,7 +304,7 @@ static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c)
       return true;
     case 8:
       if (eR < 128 || eC < 16) return false;
-      if (tiles(256, 64) >= 4096) { c->tile = 131072; c->threads = 512; c->trb = 2048; c->cap = 8; }  // 256 x 64
+      if (tiles(256, 64) >= 4096) { c->tile = 131072; c->threads = 512; c->trb = 2048; }  // 256 x 64
       else if (tiles(256, 32) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 2048; }  // 256 x 32
       else { c->tile = 16384; c->threads = 256; c->trb = 1024; }                          // 128 x 16
       return true;

@@ -208,7 +208,7 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
 // lower the number of workgroups per CU).
 //
 // CAP > 0: the interior load phase keeps at most CAP loads of a lane outstanding (measured faster
-// than all at once for the tall tiles of 1-, 2- and 8-byte elements).
+// than all at once for the tall tiles of 1- and 2-byte elements).
 template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL, bool EDGE = true, int CAP = 0>
 __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   typedef Geo<EB, VB, U, TILE, NT> G;
@@ -308,7 +308,7 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 #define TC_CAPS_EB1 TC_CFG_CAP(1, 131072, 512, 2)
 #define TC_CAPS_EB2 TC_CFG_CAP(2, 131072, 1024, 2) TC_CFG_CAP(2, 65536, 512, 2) TC_CFG_CAP(2, 32768, 256, 2)
 #define TC_CAPS_EB4
-#define TC_CAPS_EB8 TC_CFG_CAP(8, 131072, 512, 8)
+#define TC_CAPS_EB8
 #define TC_CAPS_EB16
 
 #define TC_CFG_WL(EB, U, TILE, NT)                                                                           \
