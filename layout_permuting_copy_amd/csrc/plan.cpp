@@ -475,6 +475,15 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 0; t.order = 2;
     cands[ncand++] = t;
   }
+  // 1-byte elements at vector alignment whose destination columns alone are off the lines: the
+  // tall 512 x 256 tiles with 2 loads in flight, plain stores and XCD super-tiles (int8 8176 x 8192
+  // 3.56-3.57 -> 4.02-4.08 TB/s; the odd and source-misaligned int8 copies ran slower on them)
+  if (!pinned && !batched && line_cfg && p->eb == 1 && !p->unaligned && src_lines && p->step == 1 && R.e >= 512 &&
+      C.e >= 256 && ceil_div(R.e, 512) * ceil_div(C.e, 256) * others >= 512) {
+    TuneCfg t;
+    t.tile = 131072; t.threads = 512; t.trb = 512; t.unit = 16; t.nt = 0; t.order = 2; t.cap = 2;
+    cands[ncand++] = t;
+  }
   cands[ncand++] = base;
   if (flags & TC_FLAG_NO_SWIZZLE) ncand = 1;  // the swizzle is measured on the default plan's tile
   if (ov.cap >= 0)

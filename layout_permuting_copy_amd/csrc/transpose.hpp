@@ -298,14 +298,19 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
   }
 
 // The tall configurations that run with a load cap (plan.cpp, tall_cfg): 16-byte LDS units,
-// nontemporal accesses, with and without the edge code.
+// nontemporal accesses, with and without the edge code; and (TC_CFG_CAP_PLAIN) plain stores with
+// the edge code, for destinations off the cache lines.
 #define TC_CFG_CAP(EB, TILE, NT, CAP)                                                                        \
   if (c.cap == CAP && c.unit == 16 && vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local &&  \
       ntm == 3) {                                                                                            \
     if (!c.edges) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, false, CAP>(ta, wgs, s);  \
     return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP>(ta, wgs, s);               \
   }
-#define TC_CAPS_EB1 TC_CFG_CAP(1, 131072, 512, 2)
+#define TC_CFG_CAP_PLAIN(EB, TILE, NT, CAP)                                                                  \
+  if (c.cap == CAP && c.unit == 16 && vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local &&  \
+      ntm == 0)                                                                                              \
+    return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 0, 1, false, true, CAP>(ta, wgs, s);
+#define TC_CAPS_EB1 TC_CFG_CAP(1, 131072, 512, 2) TC_CFG_CAP_PLAIN(1, 131072, 512, 2)
 #define TC_CAPS_EB2 TC_CFG_CAP(2, 131072, 1024, 2) TC_CFG_CAP(2, 65536, 512, 2) TC_CFG_CAP(2, 32768, 256, 2)
 #define TC_CAPS_EB4
 #define TC_CAPS_EB8

@@ -161,6 +161,15 @@ def test_transpose_xcd_super_tiles(eb, shape):
     assert p["unaligned"] and p["grid_order"] == 2, p
 
 
+@pytest.mark.parametrize("n,m", [(8176, 8192), (16368, 4224)])
+def test_int8_tall_tiles_destination_off_the_lines(n, m):
+    """int8 transposes whose destination columns alone start off the 128-byte lines: 512 x 256
+    tiles with 2 loads in flight, plain stores and XCD super-tiles (ragged tiles along both modes in
+    the second shape)."""
+    p = _check((n, m), (m, 1), (1, n), 1, seed=n + m, expect="transpose")
+    assert (p["tile_r"], p["tile_c"], p["loads_in_flight"], p["nontemporal"], p["grid_order"]) == (512, 256, 2, 0, 2), p
+
+
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("n,m,pitch,soff", [(40, 30, 60, 0), (129, 67, 140, 3), (64, 64, 128, 0), (33, 300, 601, 1),
                                             (7, 5, 11, 0), (300, 257, 515, 2)])
