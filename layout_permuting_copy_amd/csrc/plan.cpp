@@ -819,8 +819,14 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     p.unaligned = true;
     p.ntm = 3;
     p.threads = kRowThreads;
-    p.workgroups = ceil_div(nvec, int64_t(kRowThreads) * kRowRounds);
-    p.load_outer = p.store_outer = int(std::min<int64_t>(kRowRounds, ceil_div(nvec, p.threads)));
+    {
+      const TuneCfg tc = tune_override();
+      p.buffers = tc.buf != 0;
+      p.row_rounds = kRowRounds;
+      if (tc.rr == 1 || tc.rr == 2 || tc.rr == 4) p.row_rounds = tc.rr;
+    }
+    p.workgroups = ceil_div(nvec, int64_t(kRowThreads) * p.row_rounds);
+    p.load_outer = p.store_outer = int(std::min<int64_t>(p.row_rounds, ceil_div(nvec, p.threads)));
     if (!rows_fit(j, nvec)) {
       p.status = TC_E_RANGE;
       p.reason = "more than 2^30 vectors per index of the outermost mode";

@@ -259,11 +259,13 @@ def test_interleave_channels(eb, ch, to_planes):
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])
 @pytest.mark.parametrize("shape,pitch,soff,doff", [((37, 45), 50, 3, 0), ((64, 64), 65, 65 + 1, 7), ((5, 3), 9, 1, 2),
                                                     ((300, 129), 130, 131, 0), ((2, 33, 70), 71, 5, 3),
-                                                    ((1000,), 1, 1, 0), ((4096,), 1, 3, 5), ((7, 1), 2, 1, 0)])
+                                                    ((1000,), 1, 1, 0), ((4096,), 1, 3, 5), ((7, 1), 2, 1, 0),
+                                                    ((300, 128), 130, 131, 0), ((100003,), 1, 1, 0)])
 def test_rows_at_element_alignment(eb, shape, pitch, soff, doff):
     """Co-contiguous copies the aligned rule declines (windows of a matrix, odd offsets, row
     lengths that are not multiples of a vector): rows of 16-byte vectors at element alignment, a
-    row's short last vector element by element."""
+    row's short last vector element by element; with the destination vectors on the 16-byte grid
+    (the last two shapes, and the 1000-element copy) as buffer accesses."""
     if len(shape) == 1:
         ss, ds = (1,), (1,)
     elif len(shape) == 2:
