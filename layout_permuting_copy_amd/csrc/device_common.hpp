@@ -221,7 +221,7 @@ __device__ __forceinline__ void gstore_v(V* p, V v) {
 // Buffer accesses of 16 bytes.  A raw buffer resource (no swizzle, no index stride, 32-bit data
 // format, no range limit below 4 GiB) over the memory above a base address that is the same for
 // the whole workgroup; lanes address it with 32-bit byte offsets, so the host only takes this
-// form where every offset of a launch (or a workgroup) fits.  Unlike the global instructions
+// form where every offset of a launch (or a workgroup) stays below 2^31 (kBufSpan).  Unlike the global instructions
 // these carry the CDNA cache-policy bits directly: loads nontemporal (nt), stores written through
 // at device scope (sc1).  Measured on MI355X against global accesses with nontemporal loads and
 // stores: contiguous copies of 1 GiB 6.21-6.29 -> 6.52 TB/s (one vector per lane), the batched
@@ -231,7 +231,9 @@ typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr int kRsrcWord3 = 0x00020000;  // buffer data format: 32 bits
 constexpr int kPolNT = 2;               // cache policy: nontemporal
 constexpr int kPolSC1 = 16;             // cache policy: device scope (write-through)
-constexpr int64_t kBufSpan = (int64_t(1) << 32) - 256;  // largest byte span a launch may use
+// Largest byte span (highest offset + access bytes) a launch may address this way: every offset
+// then stays below 2^31, where the offset register reads the same as a signed or unsigned value.
+constexpr int64_t kBufSpan = int64_t(1) << 31;
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): waits for the lane's outstanding
 // vector memory accesses.

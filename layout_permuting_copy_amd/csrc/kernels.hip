@@ -36,7 +36,7 @@ __device__ __forceinline__ void row_offsets(const RowArgs& a, uint32_t n, int64_
 // [outer, threads, vec] copy: access v = blockIdx * NT*ROUNDS + f*NT + t.  With USE_LDS the
 // vectors make the round trip global -> LDS -> global of the gmem_smem demonstration.  BUF:
 // 16-byte buffer accesses from the bases a.sbuf / a.dbuf (the host has checked that every offset
-// of the launch fits in 32 bits) with the streaming cache policies.
+// of the launch stays below 2^31) with the streaming cache policies.
 template <int VB, int NT, int ROUNDS, bool USE_LDS, int NTM, bool GUARD, bool BURST, bool BUF>
 __device__ __forceinline__ void rows_body(const RowArgs& a, typename Bytes<VB>::T* lds) {
   typedef typename Bytes<VB>::T V;
@@ -295,7 +295,7 @@ __device__ __forceinline__ void shuffle_rounds(const ShuffleArgs& a) {
   const int col = 4 * q + row;  // destination column after the exchanges
   const int64_t g0 = int64_t(blockIdx.x) * R * NT + threadIdx.x;
   // BUF: buffer bases at the workgroup's first block (the host has checked that the workgroup's
-  // blocks lie within 4 GiB above it on both sides)
+  // blocks lie within 2 GiB above it on both sides)
   const int64_t blk0 = (int64_t(blockIdx.x) * R * NT) >> LC;
   const Rsrc rs = make_rsrc(a.src + (a.so + blk0 * a.sB) * 4), rd = make_rsrc(a.dst + (a.dof + blk0 * a.dB) * 4);
   u32x4 v[R];
@@ -478,7 +478,7 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
       sc.dof = sa.dof + b0 * sa.dB;
       sc.nvec = std::min(per, total - v0);
       const dim3 grid(uint32_t(ceil_div(sc.nvec, int64_t(kShuffleThreads) * kShuffleRounds))), block(kShuffleThreads);
-      // buffer accesses: a workgroup's blocks (4 x C elements each) within 4 GiB above its first
+      // buffer accesses: a workgroup's blocks (4 x C elements each) within 2 GiB above its first
       const int64_t bpw = int64_t(kShuffleRounds) * kShuffleThreads / p.shuffle_c;
       const bool buf = p.buffers && sa.sB >= 0 && sa.dB >= 0 &&
                        ((bpw - 1) * sa.sB + 4 * p.shuffle_c) * 4 <= dev::kBufSpan &&

@@ -1,6 +1,6 @@
 """Copies of 2^31 vectors and more (32 GiB per side, sized for a GPU with 288 GB of HBM): they
-run as several launches.  Copies whose accesses span more than 4 GiB take global instead of
-buffer accesses (32-bit offsets).  Checked against the oracle's offsets on sampled elements (the whole
+run as several launches.  Copies whose accesses span more than 2 GiB take global instead of
+buffer accesses (offsets below 2^31).  Checked against the oracle's offsets on sampled elements (the whole
 copy is too large to redo on the host), bytes past the destination image against a sentinel,
 and the identity copy also whole on the device."""
 
@@ -94,12 +94,24 @@ def test_permuted_rows_beyond_2_31_vectors():
     torch.cuda.empty_cache()
 
 
-def test_rows_spanning_more_than_4_gib():
-    """Two rows of 4096 fp32 elements 8 GiB apart in the source, and the same rows written 8 GiB
-    apart: the launch's offsets do not fit 32 bits, so the rows path uses global accesses."""
+def test_contiguous_copy_at_the_buffer_limit():
+    """A contiguous fp32 copy spanning exactly 2 GiB per side: the largest the buffer form takes
+    (its highest offset just below 2^31); checked whole, and the bytes past it against a sentinel."""
     import torch
-    cols, gap = 4096, 1 << 31  # elements
-    say(f"[gpu-large] rows 8 GiB apart")
+    n = 1 << 29
+    src, dst, nbytes = _run(torch, (n,), (1,), (1,), 4, L.TC_F32, 67, "rows")
+    assert torch.equal(src, dst[:nbytes])
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("gap", [3 << 28, 1 << 31])
+def test_rows_spanning_more_than_2_gib(gap):
+    """Two rows of 4096 fp32 elements 3 or 8 GiB apart in the source, and the same rows written as
+    far apart: the launch's offsets do not stay below 2^31, so the rows path uses global accesses."""
+    import torch
+    cols = 4096
+    say(f"[gpu-large] rows {gap * 4 >> 30} GiB apart")
     big = torch.full(((gap + cols) * 4,), 0x5A, dtype=torch.uint8, device="cuda")
     rows = SI.device_bits(torch, 2 * cols * 4, 64)
     big[:cols * 4] = rows[:cols * 4]
@@ -118,7 +130,7 @@ def test_rows_spanning_more_than_4_gib():
     torch.cuda.empty_cache()
 
 
-def test_shuffle_blocks_spanning_more_than_4_gib():
+def test_shuffle_blocks_spanning_more_than_2_gib():
     """4 x 32 fp32 blocks 128 MiB apart in the source: a workgroup's 64 blocks span 8 GiB, so the
     butterfly uses global accesses; checked whole against a strided view on the device."""
     import torch
