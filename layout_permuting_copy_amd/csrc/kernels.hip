@@ -285,6 +285,11 @@ __device__ __forceinline__ uint32_t xor_lanes(uint32_t v) {
   return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x1F | (DIST << 10)));
 }
 
+// The value of the lane 8 apart within the lane's 16-lane row (DPP row_ror:8).
+__device__ __forceinline__ uint32_t xor8_in_row(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x128, 0xF, 0xF, false));
+}
+
 template <int LC, int NTM, bool GUARD, bool BUF>
 __device__ __forceinline__ void shuffle_rounds(const ShuffleArgs& a) {
   constexpr int LQ = LC - 2;  // log2 of the vectors per block row
@@ -316,14 +321,29 @@ __device__ __forceinline__ void shuffle_rounds(const ShuffleArgs& a) {
 #pragma unroll
   for (int f = 0; f < R; ++f) {
     uint32_t w0 = v[f].x, w1 = v[f].y, w2 = v[f].z, w3 = v[f].w;
-    uint32_t t = xor_lanes<(2 << LQ)>(hi1 ? w0 : w2);
-    if (hi1) w0 = t; else w2 = t;
-    t = xor_lanes<(2 << LQ)>(hi1 ? w1 : w3);
-    if (hi1) w1 = t; else w3 = t;
-    t = xor_lanes<(1 << LQ)>(hi0 ? w0 : w1);
-    if (hi0) w0 = t; else w1 = t;
-    t = xor_lanes<(1 << LQ)>(hi0 ? w2 : w3);
-    if (hi0) w2 = t; else w3 = t;
+    if constexpr (LC == 5) {
+      // C = 32: the distance-16 exchanges are row swaps (v_permlane16_swap swaps the odd 16-lane
+      // rows of its first register with the even rows of its second: odd-row lanes take the
+      // partner's w2 / w3 into w0 / w1 and even-row lanes the partner's w0 / w1 into w2 / w3), the
+      // distance-8 ones DPP moves (row_ror:8 is the xor-8 partner within a row): no LDS-pipe
+      // instructions
+      const auto s02 = __builtin_amdgcn_permlane16_swap(w0, w2, false, false);
+      const auto s13 = __builtin_amdgcn_permlane16_swap(w1, w3, false, false);
+      w0 = s02[0]; w2 = s02[1]; w1 = s13[0]; w3 = s13[1];
+      uint32_t t = xor8_in_row(hi0 ? w0 : w1);
+      if (hi0) w0 = t; else w1 = t;
+      t = xor8_in_row(hi0 ? w2 : w3);
+      if (hi0) w2 = t; else w3 = t;
+    } else {
+      uint32_t t = xor_lanes<(2 << LQ)>(hi1 ? w0 : w2);
+      if (hi1) w0 = t; else w2 = t;
+      t = xor_lanes<(2 << LQ)>(hi1 ? w1 : w3);
+      if (hi1) w1 = t; else w3 = t;
+      t = xor_lanes<(1 << LQ)>(hi0 ? w0 : w1);
+      if (hi0) w0 = t; else w1 = t;
+      t = xor_lanes<(1 << LQ)>(hi0 ? w2 : w3);
+      if (hi0) w2 = t; else w3 = t;
+    }
     const int64_t g = g0 + int64_t(f) * NT;
     const int64_t blk = g >> LC;
     u32x4* p = reinterpret_cast<u32x4*>(a.dst) + ((a.dof + blk * a.dB) >> 2) + col;
