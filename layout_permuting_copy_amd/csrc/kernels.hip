@@ -275,8 +275,8 @@ __global__ void __launch_bounds__(kGuardThreads) guarded_tile_kernel(TransposeAr
 // partner lane move register bit 1 against lane bit log2(C/2) and register bit 0 against lane bit
 // log2(C/4) -- afterwards lane l = a (C/4) + q holds column 4q + a, rows 0..3: one 16-byte vector
 // of the column-major destination.  ds_swizzle (bit mode, xor within 32 lanes) does the
-// exchanges; every lane takes part (lanes past the end load and store nothing, and whole blocks
-// are past the end together).  The permute page's register-staged exchange, with the staging
+// exchanges for C = 8 and 16, v_permlane16_swap and a DPP move for C = 32; every lane takes part
+// (lanes past the end load and store nothing, and whole blocks are past the end together).  The permute page's register-staged exchange, with the staging
 // done by cross-lane moves instead of shared memory (TVM TIRx docs, "permute_layout", Algorithm
 // step 3).
 template <int DIST>
