@@ -285,9 +285,11 @@ __device__ __forceinline__ uint32_t xor_lanes(uint32_t v) {
   return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x1F | (DIST << 10)));
 }
 
-// The value of the lane 8 apart within the lane's 16-lane row (DPP row_ror:8).
-__device__ __forceinline__ uint32_t xor8_in_row(uint32_t v) {
-  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x128, 0xF, 0xF, false));
+// In the DPP banks of BANKS (4 lanes each, 4 per 16-lane row): `src` of the lane 8 apart within the
+// row (row_ror:8); in the other banks: `keep`.
+template <int BANKS>
+__device__ __forceinline__ uint32_t xor8_in_row(uint32_t keep, uint32_t src) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(keep), int(src), 0x128, 0xF, BANKS, false));
 }
 
 template <int LC, int NTM, bool GUARD, bool BUF>
@@ -330,10 +332,11 @@ __device__ __forceinline__ void shuffle_rounds(const ShuffleArgs& a) {
       const auto s02 = __builtin_amdgcn_permlane16_swap(w0, w2, false, false);
       const auto s13 = __builtin_amdgcn_permlane16_swap(w1, w3, false, false);
       w0 = s02[0]; w2 = s02[1]; w1 = s13[0]; w3 = s13[1];
-      uint32_t t = xor8_in_row(hi0 ? w0 : w1);
-      if (hi0) w0 = t; else w1 = t;
-      t = xor8_in_row(hi0 ? w2 : w3);
-      if (hi0) w2 = t; else w3 = t;
+      // lanes 8-15 of a row (hi0, DPP banks 2 and 3) take the partner's w1 / w3 into w0 / w2, lanes
+      // 0-7 (banks 0 and 1) the partner's w0 / w2 into w1 / w3; both moves read the old registers
+      const uint32_t n0 = xor8_in_row<0xC>(w0, w1), n1 = xor8_in_row<0x3>(w1, w0);
+      const uint32_t n2 = xor8_in_row<0xC>(w2, w3), n3 = xor8_in_row<0x3>(w3, w2);
+      w0 = n0; w1 = n1; w2 = n2; w3 = n3;
     } else {
       uint32_t t = xor_lanes<(2 << LQ)>(hi1 ? w0 : w2);
       if (hi1) w0 = t; else w2 = t;
