@@ -274,9 +274,9 @@ __global__ void __launch_bounds__(kGuardThreads) guarded_tile_kernel(TransposeAr
 // columns 4q.. of block row i, l the lane's index within the block), then two exchanges with the
 // partner lane move register bit 1 against lane bit log2(C/2) and register bit 0 against lane bit
 // log2(C/4) -- afterwards lane l = a (C/4) + q holds column 4q + a, rows 0..3: one 16-byte vector
-// of the column-major destination.  ds_swizzle (bit mode, xor within 32 lanes) does the
-// exchanges for C = 8 and 16, v_permlane16_swap and a DPP move for C = 32; every lane takes part
-// (lanes past the end load and store nothing, and whole blocks are past the end together).  The permute page's register-staged exchange, with the staging
+// of the column-major destination.  The exchanges are row swaps and bank-masked DPP moves
+// (ds_swizzle only for the 2-lane distance of C = 8; `exchange`); every lane takes part (lanes past
+// the end load and store nothing, and whole blocks are past the end together).  The permute page's register-staged exchange, with the staging
 // done by cross-lane moves instead of shared memory (TVM TIRx docs, "permute_layout", Algorithm
 // step 3).
 template <int DIST>
@@ -285,11 +285,38 @@ __device__ __forceinline__ uint32_t xor_lanes(uint32_t v) {
   return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x1F | (DIST << 10)));
 }
 
-// In the DPP banks of BANKS (4 lanes each, 4 per 16-lane row): `src` of the lane 8 apart within the
-// row (row_ror:8); in the other banks: `keep`.
-template <int BANKS>
-__device__ __forceinline__ uint32_t xor8_in_row(uint32_t keep, uint32_t src) {
-  return uint32_t(__builtin_amdgcn_update_dpp(int(keep), int(src), 0x128, 0xF, BANKS, false));
+// DPP move within 16-lane rows (CTRL: row_ror:N = 0x120 + N, lane i takes lane i - N mod 16) into
+// the banks of BANKS (4 lanes each, 4 per row); the other banks keep `keep`.
+template <int CTRL, int BANKS>
+__device__ __forceinline__ uint32_t dpp_into(uint32_t keep, uint32_t src) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(keep), int(src), CTRL, 0xF, BANKS, false));
+}
+
+// One butterfly exchange between lanes D apart (D = 2, 4, 8, 16): a lane whose lane bit log2(D) is
+// set takes its partner's b into a, the others take the partner's a into b.  D = 16: the gfx950 row
+// swap (odd 16-lane rows of the first register with even rows of the second); D = 8 and 4: DPP row
+// rotations whose bank masks pick the receiving lanes (8: banks 2-3 from 0-1 and back; 4: odd banks
+// from even with ror 4, even from odd with ror 12); D = 2 (partners in one bank): ds_swizzle and
+// selects.
+template <int D>
+__device__ __forceinline__ void exchange(uint32_t& a, uint32_t& b, bool hi) {
+  if constexpr (D == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+  } else if constexpr (D == 8) {
+    const uint32_t na = dpp_into<0x128, 0xC>(a, b), nb = dpp_into<0x128, 0x3>(b, a);
+    a = na;
+    b = nb;
+  } else if constexpr (D == 4) {
+    const uint32_t na = dpp_into<0x124, 0xA>(a, b), nb = dpp_into<0x12C, 0x5>(b, a);
+    a = na;
+    b = nb;
+  } else {
+    const uint32_t t = xor_lanes<D>(hi ? a : b);
+    if (hi) a = t;
+    else b = t;
+  }
 }
 
 template <int LC, int NTM, bool GUARD, bool BUF>
@@ -323,30 +350,10 @@ __device__ __forceinline__ void shuffle_rounds(const ShuffleArgs& a) {
 #pragma unroll
   for (int f = 0; f < R; ++f) {
     uint32_t w0 = v[f].x, w1 = v[f].y, w2 = v[f].z, w3 = v[f].w;
-    if constexpr (LC == 5) {
-      // C = 32: the distance-16 exchanges are row swaps (v_permlane16_swap swaps the odd 16-lane
-      // rows of its first register with the even rows of its second: odd-row lanes take the
-      // partner's w2 / w3 into w0 / w1 and even-row lanes the partner's w0 / w1 into w2 / w3), the
-      // distance-8 ones DPP moves (row_ror:8 is the xor-8 partner within a row): no LDS-pipe
-      // instructions
-      const auto s02 = __builtin_amdgcn_permlane16_swap(w0, w2, false, false);
-      const auto s13 = __builtin_amdgcn_permlane16_swap(w1, w3, false, false);
-      w0 = s02[0]; w2 = s02[1]; w1 = s13[0]; w3 = s13[1];
-      // lanes 8-15 of a row (hi0, DPP banks 2 and 3) take the partner's w1 / w3 into w0 / w2, lanes
-      // 0-7 (banks 0 and 1) the partner's w0 / w2 into w1 / w3; both moves read the old registers
-      const uint32_t n0 = xor8_in_row<0xC>(w0, w1), n1 = xor8_in_row<0x3>(w1, w0);
-      const uint32_t n2 = xor8_in_row<0xC>(w2, w3), n3 = xor8_in_row<0x3>(w3, w2);
-      w0 = n0; w1 = n1; w2 = n2; w3 = n3;
-    } else {
-      uint32_t t = xor_lanes<(2 << LQ)>(hi1 ? w0 : w2);
-      if (hi1) w0 = t; else w2 = t;
-      t = xor_lanes<(2 << LQ)>(hi1 ? w1 : w3);
-      if (hi1) w1 = t; else w3 = t;
-      t = xor_lanes<(1 << LQ)>(hi0 ? w0 : w1);
-      if (hi0) w0 = t; else w1 = t;
-      t = xor_lanes<(1 << LQ)>(hi0 ? w2 : w3);
-      if (hi0) w2 = t; else w3 = t;
-    }
+    exchange<(2 << LQ)>(w0, w2, hi1);
+    exchange<(2 << LQ)>(w1, w3, hi1);
+    exchange<(1 << LQ)>(w0, w1, hi0);
+    exchange<(1 << LQ)>(w2, w3, hi0);
     const int64_t g = g0 + int64_t(f) * NT;
     const int64_t blk = g >> LC;
     u32x4* p = reinterpret_cast<u32x4*>(a.dst) + ((a.dof + blk * a.dB) >> 2) + col;
