@@ -11,7 +11,7 @@ pages define, with each function naming the passage it follows:
   ``dst[dst_layout(i)] = src[src_layout(i)]`` (TVM TIRx docs "copy -> gmem_smem",
   intro / "What it accepts"; "permute_layout", intro);
 * the TileLang default loop partition (TileLang tutorial "loop_mapping.py",
-  module docstring formula: flatten -> access_idx -> thread / local_idx);
+  module docstring: the nest's points in row-major order, grouped into vectors dealt to threads);
 * the ``[outer, threads, vec]`` global<->shared partition and its vector-width
   rule (TVM TIRx docs "copy -> gmem_smem", Algorithm steps 1-2, the
   "Generated TIRx IR" listing and the dtype table of "How inputs change");
@@ -76,21 +76,21 @@ def common_modes(src: Layout, dst: Layout) -> List[Tuple[int, int, int]]:
     return [(e, s, d) for (e, s), (_, d) in zip(a, b)]
 
 
-def unflatten(flat: int, extents: Sequence[int]) -> Tuple[int, ...]:
-    """Row-major decomposition (TileLang loop_mapping.py ``unflatten``)."""
-    out = [0] * len(extents)
-    for k in range(len(extents) - 1, -1, -1):
-        out[k] = flat % extents[k]
-        flat //= extents[k]
-    return tuple(out)
+def index_of_flat(flat: int, extents: Sequence[int]) -> Tuple[int, ...]:
+    """The multi-index at row-major position ``flat`` of a nest with these extents (the last mode
+    varies fastest; TileLang loop_mapping.py: the nest is linearised row-major).  NumPy's
+    ``unravel_index`` does the decomposition."""
+    if len(extents) == 0:
+        return ()
+    return tuple(int(i) for i in np.unravel_index(int(flat), tuple(int(e) for e in extents)))
 
 
-def flatten(index: Sequence[int], extents: Sequence[int]) -> int:
-    """Row-major linearisation (TileLang loop_mapping.py ``flatten``)."""
-    flat = 0
-    for i, e in zip(index, extents):
-        flat = flat * e + i
-    return flat
+def flat_of_index(index: Sequence[int], extents: Sequence[int]) -> int:
+    """Row-major position of a multi-index (the inverse of ``index_of_flat``; NumPy's
+    ``ravel_multi_index``)."""
+    if len(extents) == 0:
+        return 0
+    return int(np.ravel_multi_index(tuple(int(i) for i in index), tuple(int(e) for e in extents)))
 
 
 # ----------------------------------------------------------------------------------------------
@@ -185,22 +185,29 @@ def sample_offsets(src_lay: Layout, dst_lay: Layout, flat: np.ndarray) -> Tuple[
 
 
 # ----------------------------------------------------------------------------------------------
-# TileLang default loop partition (TileLang tutorial "loop_mapping.py", module docstring):
-#   flattened  = row-major flatten of the nest index
-#   access_idx = flattened // vector_size
-#   thread     = access_idx % num_thread
-#   local_idx  = (access_idx // num_thread) * vector_size + flattened % vector_size
+# TileLang default loop partition (TileLang tutorial "loop_mapping.py", module docstring).  The
+# points of the loop nest, taken in row-major order, are grouped into vectors of `vector_size`
+# consecutive points; vector number a goes to thread a mod T, and a thread's vectors follow one
+# another in its local slots, each vector's points in order.  Computed here for every point of the
+# nest at once, as NumPy arrays shaped like the nest.
 # ----------------------------------------------------------------------------------------------
 
-def loop_partition(extents: Sequence[int], num_thread: int, vector_size: int) -> Dict[Tuple[int, ...], Tuple[int, int]]:
-    result = {}
-    for index in itertools.product(*(range(e) for e in extents)):
-        flat = flatten(index, extents)
-        access_idx = flat // vector_size
-        thread = access_idx % num_thread
-        local_idx = (access_idx // num_thread) * vector_size + flat % vector_size
-        result[index] = (thread, local_idx)
-    return result
+def loop_partition_arrays(extents: Sequence[int], num_thread: int, vector_size: int):
+    """(thread, slot): two integer arrays of shape ``extents``; entry [idx] is the thread that
+    runs point idx and the local slot it uses."""
+    shape = tuple(int(e) for e in extents)
+    pos = np.arange(math.prod(shape), dtype=np.int64).reshape(shape)  # row-major position
+    vector_no = pos // vector_size
+    thread = vector_no % num_thread
+    slot = (vector_no // num_thread) * vector_size + pos % vector_size
+    return thread, slot
+
+
+def loop_partition(extents: Sequence[int], num_thread: int,
+                   vector_size: int) -> Dict[Tuple[int, ...], Tuple[int, int]]:
+    """{point: (thread, slot)} for every point of the nest (see loop_partition_arrays)."""
+    thread, slot = loop_partition_arrays(extents, num_thread, vector_size)
+    return {idx: (int(thread[idx]), int(slot[idx])) for idx in np.ndindex(*thread.shape)}
 
 
 # ----------------------------------------------------------------------------------------------
@@ -228,7 +235,7 @@ def gmem_smem_partition(g_lay: Layout, s_lay: Layout, num_thread: int, elem_byte
                 "reason": f"element count {count} is not divisible by thread count {num_thread}"}
 
     def offsets(flat):
-        idx = unflatten(flat, extents)
+        idx = index_of_flat(flat, extents)
         g = g_lay[2] + sum(i * gs for i, (_, gs, _) in zip(idx, modes))
         s = s_lay[2] + sum(i * ss for i, (_, _, ss) in zip(idx, modes))
         return g, s
@@ -386,7 +393,7 @@ def permute_access(extent, src_str, dst_str, lanes, k, shift, r, lane):
     j = r ^ ((lane >> shift) & mask), idx = decompose(lane + j*lanes, extent)."""
     mask = (1 << k) - 1
     j = r ^ ((lane >> shift) & mask)
-    idx = unflatten(lane + j * lanes, extent)
+    idx = index_of_flat(lane + j * lanes, extent)
     return project(idx, src_str), project(idx, dst_str)
 
 
@@ -399,7 +406,7 @@ def _phase_conflicts(extent, strides, elem_bytes, model, k, shift, op):
         for lane in range(lanes):
             mask = (1 << k) - 1
             j = r ^ ((lane >> shift) & mask)
-            idx = unflatten(lane + j * lanes, extent)
+            idx = index_of_flat(lane + j * lanes, extent)
             addrs.append(project(idx, strides) * elem_bytes)
         worst += conflict_cycles(addrs, elem_bytes, op, model)
     return worst
@@ -555,11 +562,10 @@ def lds_tile_conflicts(eb, vb, TR, TC, NB, NT=256, k=0, shift=0, tbit=0, cshift=
     return wc, rc
 
 
-def lds_tile_swizzle(eb, vb, TR, TC, NB, NT=256, model=None, U=None):
-    """Smallest-k XOR swizzle of the tile that leaves both phases conflict-free (the permute
-    page's search, Algorithm step 2, on the tile above).  Candidates in order: k ascending, then
-    shift, then tbit, then the column term -- none, then (cshift, cmask) by increasing cshift and
-    cmask in (1, 3, 7).  Returns a dict, or None when no candidate is conflict-free."""
+def lds_tile_candidates(eb, vb, TR, TC, NB, U=None):
+    """The swizzles of the tile in the search order (the permute page's Algorithm step 2: k
+    ascending; for each k the row shift, then the target bit, then the column term -- none, then
+    (cshift, cmask) by increasing cshift and cmask in (1, 3, 7)).  Yields dicts."""
     U, B, VE, CW, RPV, TRu, WW = _tile_units(eb, vb, TR, TC, NB, U)
     chunks = TC // CW
     chunk_bits = chunks.bit_length() - 1
@@ -573,9 +579,28 @@ def lds_tile_swizzle(eb, vb, TR, TC, NB, NT=256, model=None, U=None):
                 for cs, cm in cols:
                     if cm and (1 << cs) >= chunks:
                         continue
-                    w, r = lds_tile_conflicts(eb, vb, TR, TC, NB, NT, k, shift, tbit, cs, cm, model,
-                                              stop_at_first=True, U=U)
-                    if w == 0 and r == 0:
-                        return {"k": k, "shift": shift, "tbit": tbit, "cshift": cs, "cmask": cm,
-                                "mask": (1 << k) - 1}
+                    yield {"k": k, "shift": shift, "tbit": tbit, "cshift": cs, "cmask": cm, "mask": (1 << k) - 1}
+
+
+def lds_tile_swizzle(eb, vb, TR, TC, NB, NT=256, model=None, U=None):
+    """Smallest-k XOR swizzle of the tile that leaves both phases conflict-free (the first such
+    candidate of lds_tile_candidates).  Returns a dict, or None when no candidate is
+    conflict-free."""
+    for c in lds_tile_candidates(eb, vb, TR, TC, NB, U):
+        w, r = lds_tile_conflicts(eb, vb, TR, TC, NB, NT, c["k"], c["shift"], c["tbit"], c["cshift"], c["cmask"],
+                                  model, stop_at_first=True, U=U)
+        if w == 0 and r == 0:
+            return c
     return None
+
+
+def lds_tile_cheapest_per_k(eb, vb, TR, TC, NB, NT=256, model=None, U=None):
+    """{k: (candidate, write cycles, read cycles)}: for every k, the first candidate in search order
+    with the fewest extra cycles per tile."""
+    best = {}
+    for c in lds_tile_candidates(eb, vb, TR, TC, NB, U):
+        w, r = lds_tile_conflicts(eb, vb, TR, TC, NB, NT, c["k"], c["shift"], c["tbit"], c["cshift"], c["cmask"],
+                                  model, U=U)
+        if c["k"] not in best or w + r < sum(best[c["k"]][1:]):
+            best[c["k"]] = (c, w, r)
+    return best

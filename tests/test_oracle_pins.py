@@ -213,7 +213,7 @@ def test_loop_partition_nesting(oracle_lib, extents, T, vec):
     total = math.prod(extents)
     by_flat = {}
     for idx, (t, slot) in plan.items():
-        by_flat[R.flatten(idx, extents)] = (t, slot)
+        by_flat[R.flat_of_index(idx, extents)] = (t, slot)
     assert len(set(plan.values())) == total  # every (thread, slot) is used once
     for flat in range(total):
         t, slot = by_flat[flat]
@@ -253,7 +253,7 @@ def test_loop_partition_agrees_with_gmem_smem_listing(oracle_lib):
     for idx, (t, slot) in plan.items():
         f = slot // 4
         if slot % 4 == 0:
-            assert R.flatten(idx, (32, 32)) == f * 128 + t * 4
+            assert R.flat_of_index(idx, (32, 32)) == f * 128 + t * 4
 
 
 # ---------------------------------------------------------------------------------------------
