@@ -1,19 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the layout-permuting tile copy on one MI355X.
 
-A step is one tile_copy of the scale-factor transpose workload: 65536 tiles of shape
-(2, 1, 4, 32) float32, source strides (256, 128, 128, 32, 1) -> destination strides
-(256, 128, 128, 1, 4), tiles contiguous in HBM -- every step runs the whole hot path (layout
-algebra and plan lookup, [outer, threads, vec] partition, swizzled LDS tile kernel).  The
-inputs are resident in HBM before timing starts; successive steps rotate over several
-source/destination pairs so that more than 512 MiB is touched between reuses of a pair and
-the 256 MB MALL cannot serve them.
+A step is one tile_copy of the largest workload that fits one GPU: the dense transpose of a
+16384 x 16384 float32 matrix, source strides (16384, 1) -> destination strides (1, 16384), 2 GiB
+moved -- every step runs the whole hot path (layout algebra and plan lookup, [outer, threads, vec]
+partition, swizzled LDS tile kernel).  The inputs are resident in HBM before timing starts;
+successive steps rotate over two source/destination pairs (4 GiB touched between reuses of a pair,
+so the 256 MB MALL cannot serve them).
 
 Prints one JSON line: throughput as achieved HBM GB/s (algorithmic bytes read + written per
 second of wall clock over the timed steps), the roofline of the kernel (average launch duration:
 HIP events on the launch stream around the timed region, divided by the launches; against
-8 TB/s), the oracle's CPU throughput on a bounded sample of the same workload, and a sweep of
-the other workloads (same metric, context only).
+8 TB/s), the oracle's CPU throughput on a bounded sample of the same workload, and a compact sweep
+of the other workloads (same metric, context only: one short record each).
 """
 
 from __future__ import annotations
@@ -120,18 +119,21 @@ def _time_workload(torch, L, w: SI.Workload, steps: int, warmup: int, host_src, 
     kms = [a.elapsed_time(b) for a, b in ev]
     out = {"workload": w.name, "path": plan["path_name"], "elem_bytes": w.eb, "elements": int(np.prod(w.src.shape)),
            "bytes_per_step": bytes_step, "ms_per_step": wall * 1e3 / steps,
-           "kernel_ms_mean": region_ms / steps, "event_pair_ms_mean": float(np.mean(kms)),
-           "kernel_ms_median": float(np.median(kms)),
-           "kernel_ms_min": float(np.min(kms)), "rotating_pairs": pairs,
-           "tile": [plan["tile_r"], plan["tile_c"], plan["tile_b"]], "vec_bytes": plan["vec_bytes"],
+           "region_ms_per_launch": region_ms / steps, "event_pair_ms_mean": float(np.mean(kms)),
+           "event_pair_ms_median": float(np.median(kms)),
+           "event_pair_ms_min": float(np.min(kms)), "rotating_pairs": pairs,
+           "tile": [plan["tile_r"], plan["tile_c"], plan["tile_b"]], "threads": plan["threads"],
+           "vec_bytes": plan["vec_bytes"], "lds_write_bytes": plan["lds_write_bytes"],
+           "lds_read_bytes": plan["lds_read_bytes"],
            "xor": [plan["xor_k"], plan["xor_shift"], plan["xor_tbit"], plan["xor_cshift"], plan["xor_cmask"]],
+           "planned_conflicts": [plan["write_conflicts"], plan["read_conflicts"]],
+           "edge_tiles": plan["edge_tiles"], "grid_order": plan["grid_order"],
            "workgroups": plan["workgroups"]}
     out["gbs_wall"] = bytes_step / (out["ms_per_step"] * 1e-3) / 1e9
-    out["gbs_kernel"] = bytes_step / (out["kernel_ms_mean"] * 1e-3) / 1e9
-    out["gbs_kernel_median"] = bytes_step / (out["kernel_ms_median"] * 1e-3) / 1e9
-    out["gbs_event_pair"] = bytes_step / (out["event_pair_ms_mean"] * 1e-3) / 1e9
-    out["pct_peak_kernel"] = 100 * out["gbs_kernel"] / PEAK_HBM_GBS
-    out["us_per_launch"] = out["kernel_ms_mean"] * 1e3
+    out["gbs_region"] = bytes_step / (out["region_ms_per_launch"] * 1e-3) / 1e9
+    out["gbs_event_pair_median"] = bytes_step / (out["event_pair_ms_median"] * 1e-3) / 1e9
+    out["pct_peak_region"] = 100 * out["gbs_region"] / PEAK_HBM_GBS
+    out["us_per_launch"] = out["region_ms_per_launch"] * 1e3
     # sampled parity of the last destination written against the oracle's offsets
     out["_last"] = (srcs[(steps - 1) % pairs], dsts[(steps - 1) % pairs])
     del srcs, dsts
@@ -203,8 +205,8 @@ def time_memcpy(torch, nbytes: int = 1 << 30, steps: int = 30):
     ms = float(np.mean([x.elapsed_time(y) for x, y in ev]))
     del a, b
     return {"workload": f"memcpy_dtod_{nbytes >> 20}MiB", "path": "hipMemcpy (context)", "bytes_per_step": 2 * nbytes,
-            "kernel_ms_mean": ms, "gbs_kernel": 2 * nbytes / (ms * 1e-3) / 1e9,
-            "pct_peak_kernel": 100 * 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            "event_pair_ms_mean": ms, "gbs_region": 2 * nbytes / (ms * 1e-3) / 1e9,
+            "pct_peak_region": 100 * 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
 
 def time_device_permute(torch, tiles: int = 65536, steps: int = 30, seed: int = 21):
@@ -244,8 +246,8 @@ def time_device_permute(torch, tiles: int = 65536, steps: int = 30, seed: int = 
         ok = ok and bool(np.array_equal(dsts[last][t * 1024:(t + 1) * 1024].cpu().numpy(), want))
     del srcs, dsts
     return {"workload": "sf_transpose_65536x2x1x4x32_f32 via device primitives", "path": "tcd::wave_permute (context)",
-            "k": k, "shift": shift, "bytes_per_step": 2 * nbytes, "kernel_ms_mean": ms,
-            "gbs_kernel": 2 * nbytes / (ms * 1e-3) / 1e9, "pct_peak_kernel": 100 * 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "k": k, "shift": shift, "bytes_per_step": 2 * nbytes, "region_ms_per_launch": ms,
+            "gbs_region": 2 * nbytes / (ms * 1e-3) / 1e9, "pct_peak_region": 100 * 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "sampled_parity": ok}
 
 
@@ -254,11 +256,43 @@ def identity_workload(n: int = 1 << 28) -> SI.Workload:
 
 
 def sweep_workloads():
-    ws = [SI.transpose2d(dtype="float32"), SI.transpose2d(dtype="bfloat16"), SI.permute0213()]
+    ws = [SI.sf_transpose(), SI.transpose2d(dtype="bfloat16"), SI.permute0213()]
     ws += [SI.sweep_dense(dt) for dt in SI.SWEEP_DTYPES]
     ws += [SI.sweep_odd(dt) for dt in SI.SWEEP_DTYPES]
     ws += [SI.sweep_slice(dt) for dt in SI.SWEEP_DTYPES]
     return ws
+
+
+def headline_workload() -> SI.Workload:
+    """The largest single-GPU configuration: the 16384 x 16384 float32 transpose (2 GiB moved)."""
+    return SI.transpose2d(dtype="float32")
+
+
+def compact(r: dict) -> dict:
+    """One short sweep record: workload, path, flags, GB/s and % of peak over the timed region of
+    back-to-back launches, and the sampled parity."""
+    out = {"w": r["workload"], "path": r.get("path")}
+    if r.get("flags"):
+        out["flags"] = r["flags"]
+    out["GBs"] = round(r["gbs_region"], 1)
+    out["pct"] = round(r["pct_peak_region"], 2)
+    if "sampled_parity" in r:
+        out["ok"] = r["sampled_parity"]
+    for k in ("us_per_launch", "k", "shift"):
+        if k in r and (k != "us_per_launch" or r["bytes_per_step"] < (1 << 20)):
+            out[k] = round(r[k], 3) if isinstance(r[k], float) else r[k]
+    return out
+
+
+def run_only(torch, L, name: str, flags: int, steps: int, warmup: int) -> dict:
+    """One workload alone (profiling runs): its timing, plan and sampled parity."""
+    if name.startswith("memcpy_dtod"):
+        return time_memcpy(torch, steps=steps)
+    w = next(w for w in [headline_workload(), identity_workload()] + sweep_workloads() if w.name == name)
+    r = time_workload(torch, L, w, steps, warmup, seed=11, flags=flags)
+    s_src, s_dst = r.pop("_last")
+    r["sampled_parity"] = sampled_parity(torch, w, s_src, s_dst, 1 << 14)
+    return r
 
 
 def main() -> int:
@@ -268,7 +302,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-sweep", action="store_true", help="skip the per-workload context sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", default=None, help="time only the named sweep workload (profiling runs)")
+    ap.add_argument("--only", default=None, help="time only the named workload (profiling runs)")
+    ap.add_argument("--flags", type=int, default=0, help="TC_FLAG_* bits for --only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the copy has no multi-GPU path "
@@ -285,13 +320,11 @@ def main() -> int:
         return 2
     L.load_library()
     if args.only:
-        w = next(w for w in [SI.sf_transpose(), identity_workload()] + sweep_workloads() if w.name == args.only)
-        r = time_workload(torch, L, w, args.steps, args.warmup)
-        r.pop("_last")
-        print(json.dumps(r))
-        return 0
+        r = run_only(torch, L, args.only, args.flags, args.steps, args.warmup)
+        print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}), flush=True)
+        return 0 if r.get("sampled_parity", True) else 1
 
-    w = SI.sf_transpose()
+    w = headline_workload()
     host_src = SI.make_source(w)
     r = time_workload(torch, L, w, args.steps, args.warmup, host_src=host_src)
     src_d, dst_d = r.pop("_last")
@@ -300,9 +333,9 @@ def main() -> int:
     torch.cuda.empty_cache()
     sweep = []
     if not args.no_sweep:
-        sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in time_memcpy(torch).items()})
+        sweep.append(compact(time_memcpy(torch)))
         torch.cuda.empty_cache()
-        sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in time_device_permute(torch).items()})
+        sweep.append(compact(time_device_permute(torch)))
         torch.cuda.empty_cache()
         # the alternatives the planner does not pick, for comparison: the SF tiles on the LDS tile
         # kernel, the (0,2,1,3) permute staged through LDS
@@ -315,9 +348,9 @@ def main() -> int:
             s["sampled_parity"] = sampled_parity(torch, sw, s_src, s_dst, 1 << 14)
             del s_src, s_dst
             torch.cuda.empty_cache()
-            sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in s.items()})
+            sweep.append(compact(s))
     traffic = traffic_from_profiles(w.name, r["bytes_per_step"])
-    achieved = r["gbs_kernel"]
+    achieved = r["gbs_region"]
     line = {
         "metric": METRIC,
         "value": round(r["gbs_wall"], 2),
@@ -334,13 +367,13 @@ def main() -> int:
         "config": {"workload": w.name, "shape": list(w.src.shape), "src_stride": list(w.src.stride),
                    "dst_stride": list(w.dst.stride), "element": "float32 moved as raw 32-bit words",
                    "bytes_per_step": r["bytes_per_step"], "path": r["path"], "tile": r["tile"],
-                   "vec_bytes": r["vec_bytes"], "xor": r["xor"], "workgroups": r["workgroups"],
-                   "rotating_buffer_pairs": r["rotating_pairs"], "sampled_parity": parity,
-                   "pct_of_peak_wall": round(100 * r["gbs_wall"] / PEAK_HBM_GBS, 2)},
+                   "threads": r["threads"], "vec_bytes": r["vec_bytes"], "xor": r["xor"],
+                   "workgroups": r["workgroups"], "rotating_buffer_pairs": r["rotating_pairs"],
+                   "sampled_parity": parity, "pct_of_peak_wall": round(100 * r["gbs_wall"] / PEAK_HBM_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel_us_mean": round(r["kernel_ms_mean"] * 1e3, 3),
-                     "kernel_us_median_event_pair": round(r["kernel_ms_median"] * 1e3, 3),
+                     "region_us_per_launch": round(r["region_ms_per_launch"] * 1e3, 3),
+                     "event_pair_us_median": round(r["event_pair_ms_median"] * 1e3, 3),
                      "timing": "HIP events on the launch stream around the timed region of back-to-back "
                                "launches, divided by the launches",
                      "algorithmic_bytes_per_launch": r["bytes_per_step"]},

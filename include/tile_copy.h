@@ -88,8 +88,14 @@ enum tc_status {
 };
 
 /* Flags for tc_set_flags / tc_plan.  Unknown bits are rejected (TC_E_ARG). */
-#define TC_FLAG_STRICT        0x01 /* decline (TC_E_DECLINED) instead of falling back (to the
-                                      transpose with unaligned vectors, or the guarded paths) */
+#define TC_FLAG_STRICT        0x01 /* the pages' acceptance rules as written: decline
+                                      (TC_E_DECLINED) where TVM TIRx "copy -> gmem_smem", "What it
+                                      accepts", rejects the copy (element count not divisible by
+                                      the thread count; no aligned vector of 16, 8 or 4 bytes) or
+                                      where no XOR swizzle is conflict-free ("permute_layout",
+                                      "What it accepts": the dispatch fails if no k is found),
+                                      instead of falling back (to the transpose with unaligned
+                                      vectors, or the guarded paths) */
 #define TC_FLAG_FORCE_GUARDED 0x02 /* always take the guarded element-wise path */
 #define TC_FLAG_FORCE_REGS    0x04 /* co-contiguous copies: stage through registers only */
 #define TC_FLAG_FORCE_LDS     0x08 /* co-contiguous copies: stage through LDS */
@@ -111,8 +117,10 @@ enum tc_path {
   TC_PATH_GUARDED_ROWS = 5,/* fallback: element-wise, destination order, guarded */
   TC_PATH_SHUFFLE = 6,     /* batches of 4 x C blocks of 4-byte elements (C = 8, 16, 32), each
                               block contiguous on both sides (e.g. the scale-factor tiles):
-                              16-byte vectors exchanged between lanes by a two-stage butterfly
-                              (ds_swizzle), no LDS */
+                              16-byte vectors exchanged between lanes by a two-stage butterfly,
+                              no LDS (a v_permlane16_swap row swap at lane distance 16, bank-masked
+                              DPP row rotations at distances 8 and 4, ds_swizzle only at
+                              distance 2) */
   TC_PATH_INTERLEAVE = 7   /* a few (2, 3, 4 or 8) interleaved channels to planes or back (e.g.
                               NHWC <-> NCHW with 3 channels): each lane moves 16/elem_bytes
                               pixels of every channel, transposed within its registers */
@@ -195,13 +203,40 @@ int tile_copy_ex(const void* src, const tc_layout* src_layout, void* dst, const 
 int tc_plan(const tc_layout* src_layout, const tc_layout* dst_layout, int dtype, int flags,
             int ptr_align, tc_plan_info* out);
 
-/* The reason for the last error on this host thread ("" after success). */
+/* The reason for the last error on this host thread ("" after success): the
+ * counterpart of the pages' acceptance predicates, which return a reason with
+ * their verdict (TVM TIRx docs, "copy -> gmem_smem", "What it accepts"; the
+ * rejection reasons of "permute_layout", "What it accepts").  A declined copy's
+ * text is the page's reason, e.g. "... the [outer, threads, vec] split has no
+ * integer solution".  The string is owned by the library and stays valid until
+ * the next call of an entry point on the same thread. */
 const char* tc_last_error(void);
 
-/* Process-wide default flags for tile_copy.  Returns the previous flags, or
- * TC_E_ARG for unknown bits. */
+/* Process-wide default flags for tile_copy (tile_copy_ex takes its own).
+ * TC_FLAG_STRICT selects the pages' acceptance rules as written (see above);
+ * the other bits pick among paths that give the same bytes, for measurement.
+ * Returns the previous flags, or TC_E_ARG for unknown bits (the flags are then
+ * unchanged).  Thread safe; affects copies planned after the call. */
 int tc_set_flags(int flags);
 int tc_get_flags(void);
+
+/*
+ * Tuning override (environment variable TC_TUNE, read once, at the first plan
+ * of the process), for measurement sweeps only: a comma-separated list of
+ * key=value integers that pins the planner's measured choices --
+ *   tile, threads, trb, unit   transpose tile bytes, threads per workgroup,
+ *                              destination run in bytes, LDS unit bytes
+ *   nt, order, wl, cap         nontemporal bits, grid order, wave-local phases
+ *                              (0 = keep the barrier), loads in flight per lane
+ *   rr, so, buf                rows path: vectors per lane, source-order grid,
+ *                              buffer accesses (0 = global accesses)
+ *   xk, xs, xt, xcs, xcm       the transpose's XOR swizzle (k, shift, target
+ *                              bit, column shift, column mask) forced onto the
+ *                              chosen tile, conflict-free or not
+ * Every setting gives the same bytes.  A setting no compiled kernel instance
+ * matches makes the copy fail with TC_E_ARG ("internal: no tile geometry");
+ * unknown keys are ignored.  Unset, the planner's own choices apply.
+ */
 
 /*
  * Region slice of a layout (TVM TIRx "copy -> gmem_smem", demonstration

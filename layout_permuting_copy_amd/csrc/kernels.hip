@@ -5,7 +5,8 @@
 //   the round-trip variant, through LDS as in the gmem_smem demonstration program).  With one
 //   element per "vector" it is also the guarded element-wise fallback.
 // shuffle_kernel: batches of 4 x C blocks of 4-byte elements, transposed by exchanging 16-byte
-//   vectors between lanes (ds_swizzle), no LDS.
+//   vectors between lanes, no LDS: a v_permlane16_swap row swap at lane distance 16, bank-masked
+//   DPP row rotations at distances 8 and 4, ds_swizzle only at distance 2.
 // guarded_tile_kernel: fallback LDS tile with element-wide accesses and per-element guards,
 //   for layouts the vector paths do not take (FORCE_GUARDED, or no unit-stride mode to vectorize).
 #include <hip/hip_runtime.h>
@@ -276,9 +277,9 @@ __global__ void __launch_bounds__(kGuardThreads) guarded_tile_kernel(TransposeAr
 // log2(C/4) -- afterwards lane l = a (C/4) + q holds column 4q + a, rows 0..3: one 16-byte vector
 // of the column-major destination.  The exchanges are row swaps and bank-masked DPP moves
 // (ds_swizzle only for the 2-lane distance of C = 8; `exchange`); every lane takes part (lanes past
-// the end load and store nothing, and whole blocks are past the end together).  The permute page's register-staged exchange, with the staging
-// done by cross-lane moves instead of shared memory (TVM TIRx docs, "permute_layout", Algorithm
-// step 3).
+// the end load and store nothing, and whole blocks are past the end together).  The permute page's
+// register-staged exchange, with the staging done by cross-lane moves instead of shared memory
+// (TVM TIRx docs, "permute_layout", Algorithm step 3).
 template <int DIST>
 __device__ __forceinline__ uint32_t xor_lanes(uint32_t v) {
   static_assert(DIST >= 1 && DIST <= 16, "ds_swizzle bit mode exchanges within 32 lanes");

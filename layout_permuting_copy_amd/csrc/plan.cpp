@@ -91,9 +91,14 @@ static void decline(Plan* p, int flags, const std::string& why) {
 // barrier even where the phases are wave-local; rr: vectors per thread of the 16-byte rows path;
 // buf=0: global instead of buffer accesses on the rows and shuffle paths; cap: loads in flight
 // per lane in the transpose's load phase, 0 = all, where the library holds such an instance;
-// so: 1 / 0 the rows path's outer grid modes in source / destination order).
+// so: 1 / 0 the rows path's outer grid modes in source / destination order; xk, xs, xt, xcs, xcm:
+// the transpose's XOR swizzle (k, shift, target bit, column shift, column mask) forced onto the
+// tile the planner picks, conflict-free or not, so that the bank model can be checked against the
+// hardware counter on swizzles the search passes over).  A setting no kernel instance matches
+// makes the copy fail with TC_E_ARG ("no tile geometry").
 struct TuneCfg {
   int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1, cap = -1, so = -1;
+  int xk = -1, xs = 0, xt = 0, xcs = 0, xcm = 0;
 };
 
 static TuneCfg tune_override() {
@@ -122,6 +127,11 @@ static TuneCfg tune_override() {
         else if (k == "buf") c.buf = v;
         else if (k == "cap") c.cap = v;
         else if (k == "so") c.so = v;
+        else if (k == "xk") c.xk = v;
+        else if (k == "xs") c.xs = v;
+        else if (k == "xt") c.xt = v;
+        else if (k == "xcs") c.xcs = v;
+        else if (k == "xcm") c.xcm = v;
       }
       pos = end + 1;
     }
@@ -499,6 +509,18 @@ static bool plan_transpose_tile(Plan* p, int flags) {
                                     nullptr, 0, nullptr);
     return g;
   };
+  // a swizzle forced by the tuning override replaces the chosen one on the chosen tile
+  auto forced_swizzle = [&](TileGeom* g, int64_t* wc, int64_t* rc) {
+    if (ov.xk < 0) return true;
+    g->k = ov.xk;
+    g->shift = ov.xs;
+    g->tbit = ov.xt;
+    g->cshift = ov.xcs;
+    g->cmask = ov.xcm;
+    if (!finish_geom(g)) return false;
+    simulate_tile(*g, wc, rc);
+    return true;
+  };
   bool have = false;
   TileGeom best;
   int64_t best_w = 0, best_r = 0;
@@ -507,9 +529,10 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     int64_t wc, rc;
     if (!plan_with_cfg(*p, flags, cands[i], ov.tile != 0, &g, &wc, &rc)) continue;
     if (wc + rc == 0) {
+      if (!forced_swizzle(&g, &wc, &rc)) return false;
       p->g = with_phase_order(g);
-      p->wconf = 0;
-      p->rconf = 0;
+      p->wconf = wc;
+      p->rconf = rc;
       return true;
     }
     if (!have || wc + rc < best_w + best_r) {
@@ -520,6 +543,13 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     }
   }
   if (!have) return false;
+  if (ov.xk >= 0) {
+    if (!forced_swizzle(&best, &best_w, &best_r)) return false;
+    p->g = with_phase_order(best);
+    p->wconf = best_w;
+    p->rconf = best_r;
+    return true;
+  }
   p->g = with_phase_order(best);
   p->wconf = best_w;
   p->rconf = best_r;

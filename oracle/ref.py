@@ -468,8 +468,10 @@ def permute_layout_py(src: np.ndarray, src_lay: Layout, dst: np.ndarray, dst_lay
 # ----------------------------------------------------------------------------------------------
 # LDS tile of the global -> LDS -> global transpose on gfx950 (the library's kernel design; the
 # pages fix the method -- the [outer, threads, vec] partition of each phase and the smallest-k XOR
-# search over both phases -- but not this tile, so it is pinned by brute force, the measured bank
-# model and the hardware conflict counter, not by printed values).
+# search over both phases -- but not this tile, so it is pinned by the hardware instead of printed
+# values: SQ_LDS_BANK_CONFLICT and SQ_INSTS_LDS per dispatch of the kernel, on tiles with the
+# swizzle off, with swizzles the search passes over and with the chosen ones, equal what the
+# functions below simulate, non-zero counts included; and by a hand-derived closed form).
 #
 # The tile holds NB x TR x TC elements (TR along the destination-contiguous mode, TC along the
 # source-contiguous mode).  In LDS it is a grid of units of U bytes (U in {4, 8, 16}, U >= eb,
@@ -525,6 +527,15 @@ def tile_wave_local(eb, vb, TR, TC, NB, NT, U=None, wave=64):
                 if owner.get(pos) != t // wave:
                     return False
     return True
+
+
+def lds_tile_wave_instructions(eb, vb, TR, TC, NB, NT=256, U=None, wave=64):
+    """LDS instructions one tile issues, counted per wave (an instruction of a wave with at least
+    one lane that accesses LDS), over both phases."""
+    total = 0
+    for op, width, lanes in _tile_instructions(eb, vb, TR, TC, NB, NT, U):
+        total += len({t // wave for t in lanes})
+    return total
 
 
 _TILE_CACHE = {}

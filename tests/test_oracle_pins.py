@@ -429,3 +429,73 @@ def test_wave64_permute_reproduces_page_result_on_4x64():
     ext, ss, ds, _, _ = R.permute_shard(R.layout((2, 1, 4, 32), (128, 128, 32, 1)), R.layout((2, 1, 4, 32), (128, 128, 1, 4)))
     assert R.choose_xor_k(ext, ss, ds, 4, m) is None
     assert R.permute_conflicts(ext, ss, ds, 4, 0, 0, m) == (0, 24)
+
+
+# ---------------------------------------------------------------------------------------------
+# LDS tile of the global -> LDS -> global transpose: the oracle's bank simulation against the
+# hardware counter (SQ_LDS_BANK_CONFLICT per dispatch) and a closed form
+# ---------------------------------------------------------------------------------------------
+
+def _bank_pin_cases():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles",
+                        "bank_pin_transpose_tiles.json")
+    with open(path) as f:
+        return json.load(f)["cases"]
+
+
+def test_transpose_tile_hardware_counts_match_oracle(oracle_lib):
+    """Every measured tile -- swizzle off, swizzles the search passes over, and the chosen ones, on
+    4-, 8- and 16-byte LDS units and 1- to 16-byte elements -- costs exactly the extra cycles the
+    oracle simulates (per tile, times the tiles), and issues the LDS instructions its two TileLang
+    partitions imply.  Non-zero counts in both phases are among them."""
+    R = oracle_lib
+    cases = _bank_pin_cases()
+    assert len(cases) >= 20
+    nonzero_w = nonzero_r = 0
+    for c in cases:
+        tr, tc, nb = c["tile"]
+        k, shift, tbit, cshift, cmask = c["xor"]
+        args = (c["elem_bytes"], c["vec_bytes"], tr, tc, nb, c["threads"])
+        w, r = R.lds_tile_conflicts(*args, k, shift, tbit, cshift, cmask, U=c["lds_unit_bytes"])
+        assert (w + r) * c["tiles"] == c["SQ_LDS_BANK_CONFLICT"], c["label"]
+        assert R.lds_tile_wave_instructions(*args, U=c["lds_unit_bytes"]) * c["tiles"] == c["SQ_INSTS_LDS"], c["label"]
+        assert c["sampled_parity"] and c["edge_tiles"] in (0, 1)
+        nonzero_w += w > 0
+        nonzero_r += r > 0
+    assert nonzero_w >= 5 and nonzero_r >= 15
+
+
+def test_transpose_tile_swizzle_is_minimal_on_hardware(oracle_lib):
+    """The permute page's rule (Algorithm step 2): the smallest k that leaves both phases
+    conflict-free.  For each measured geometry the oracle's search lands on the swizzle the
+    hardware counted 0 for, and every measured swizzle with fewer bits conflicts on the hardware."""
+    R = oracle_lib
+    cases = _bank_pin_cases()
+    geom = lambda c: (c["elem_bytes"], c["vec_bytes"], *c["tile"], c["threads"], c["lds_unit_bytes"])
+    chosen = [c for c in cases if c["label"].endswith("chosen")]
+    assert len(chosen) >= 3
+    for c in chosen:
+        eb, vb, tr, tc, nb, nt, u = geom(c)
+        best = R.lds_tile_swizzle(eb, vb, tr, tc, nb, nt, U=u)
+        assert [best[x] for x in ("k", "shift", "tbit", "cshift", "cmask")] == c["xor"], c["label"]
+        assert c["SQ_LDS_BANK_CONFLICT"] == 0
+        fewer = [o for o in cases if geom(o) == geom(c) and o["xor"][0] < best["k"]]
+        assert {0, best["k"] - 1} <= {o["xor"][0] for o in fewer}, c["label"]  # k = 0 and k* - 1 measured
+        for o in fewer:
+            assert o["SQ_LDS_BANK_CONFLICT"] > 0, o["label"]
+
+
+@pytest.mark.parametrize("TR,TC", [(64, 64), (32, 64), (128, 32), (16, 128), (64, 256)])
+def test_unswizzled_4byte_unit_tile_closed_form(oracle_lib, TR, TC):
+    """Hand-derived count for 4-byte elements in 4-byte LDS units, no swizzle, 256 lanes.  Store
+    phase: a read instruction's lanes cover columns of TR/4 row vectors each; with TC a multiple of
+    32 a column's units all sit in one bank, so each 32-lane group of a 4-byte read (gfx950: 32
+    banks, 32 lanes) has TR/4 dwords in one bank -> TR/4 - 1 extra cycles, two groups per wave
+    instruction, TR*TC/64 wave instructions per tile.  Load phase: a 16-byte write of 8 lanes
+    covers 32 consecutive dwords of one row -> conflict-free."""
+    R = oracle_lib
+    w, r = R.lds_tile_conflicts(4, 16, TR, TC, 1, 256, U=4)
+    assert w == 0
+    assert r == (TR * TC // 64) * 2 * (TR // 4 - 1)
