@@ -251,6 +251,41 @@ def time_device_permute(torch, tiles: int = 65536, steps: int = 30, seed: int = 
             "sampled_parity": ok}
 
 
+def time_tile_stream(torch, mode: int, steps: int = 30, seed: int = 23):
+    """Context row for the device primitives' staging step: 64 x 64 bf16 tiles of a 16384 x 16384
+    matrix, g2s into an LDS tile and s2g back in place, one workgroup of 256 lanes per tile (mode 0
+    plain LDS tile, 1 XOR-swizzled tile with the recognised rounds lowered to adds, 2 the swizzled
+    tile with the swizzle applied every round); rotating buffer pairs; a sample of the result is
+    checked against the source (a copy in place is the identity on the tiles)."""
+    import layout_permuting_copy_amd.dev as D
+    n = 16384
+    nbytes = n * n * 2
+    pairs = 2
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    srcs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_(0, 256, generator=g) for _ in range(pairs)]
+    dsts = [torch.empty(nbytes, dtype=torch.uint8, device="cuda") for _ in range(pairs)]
+    stream = torch.cuda.current_stream()
+    for i in range(3):
+        D.tile_stream(srcs[i % pairs], dsts[i % pairs], n // 64, n // 64, mode, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(steps):
+        D.tile_stream(srcs[i % pairs], dsts[i % pairs], n // 64, n // 64, mode, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    last = (steps - 1) % pairs
+    idx = torch.from_numpy(np.random.default_rng(seed).integers(0, nbytes, 1 << 16)).to("cuda")
+    ok = bool(torch.equal(srcs[last][idx], dsts[last][idx]))
+    del srcs, dsts
+    names = {0: "plain LDS tile", 1: "swizzled tile, recognised rounds", 2: "swizzled tile, general rounds"}
+    return {"workload": f"tcd g2s/s2g 64x64 bf16 tiles of 16384^2: {names[mode]}", "path": "device primitives",
+            "bytes_per_step": 2 * nbytes, "region_ms_per_launch": ms, "gbs_region": 2 * nbytes / (ms * 1e-3) / 1e9,
+            "pct_peak_region": 100 * 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "sampled_parity": ok}
+
+
 def identity_workload(n: int = 1 << 28) -> SI.Workload:
     return SI.Workload(f"identity_{n}_float32", SI.Side((n,), (1,)), SI.Side((n,), (1,)), "float32", "bits", 12)
 
@@ -337,6 +372,9 @@ def main() -> int:
         torch.cuda.empty_cache()
         sweep.append(compact(time_device_permute(torch)))
         torch.cuda.empty_cache()
+        for mode in (0, 1, 2):
+            sweep.append(compact(time_tile_stream(torch, mode)))
+            torch.cuda.empty_cache()
         # the alternatives the planner does not pick, for comparison: the SF tiles on the LDS tile
         # kernel, the (0,2,1,3) permute staged through LDS
         # (the 32 x 32 round trip by one wave is a latency case: see its us_per_launch)

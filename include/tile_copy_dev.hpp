@@ -27,6 +27,8 @@
  *       then writes them through the destination layout.  dst and src may be the same buffer
  *       (alias-safe).  k and shift come from tc_wave_permute_plan (tile_copy.h), which
  *       simulates gfx950's LDS banks for both phases and picks the smallest conflict-free k.
+ *       Any other k and shift stay in bounds: the XOR mask is cut to P - 1 (to 0 when P is not a
+ *       power of two) and the shift to 0..6, so every step still touches only the tile.
  *
  * Layouts are compile-time types: tcd::layout<tcd::ints<extents...>, tcd::ints<strides...>,
  * offset, swizzle>, in elements.  Pointers are typed by the element (1, 2, 4, 8 or 16 bytes;
@@ -240,6 +242,60 @@ constexpr copy_plan_t make_copy_plan(modes m, int eb, int threads, int soff, int
   return p;
 }
 
+/* Element offset of row-major position `flat` of the joint modes on one side (innermost last). */
+constexpr int side_offset(const modes& m, int flat, bool src, int base) {
+  int off = base;
+  for (int k = m.n - 1; k >= 0; --k) {
+    const int i = flat % m.e[k];
+    flat /= m.e[k];
+    off += i * (src ? m.s[k] : m.d[k]);
+  }
+  return off;
+}
+
+/* Recognised rounds: for every lane t and round f of the split, the (swizzled) offsets on both
+ * sides are those of round 0 plus a per-round constant, i.e.
+ *     swz(off(f * NT * V + t * V)) == swz(off(t * V)) + delta[f].
+ * Then a lane decomposes and swizzles its first access once and every later round is an add of
+ * a compile-time constant (TVM TIRx docs, "copy -> gmem_smem", "How inputs change the
+ * algorithm": a recognised swizzle becomes a few register adds per round, otherwise the swizzle
+ * is applied every round).  This holds, for example, when a round covers whole periods of an XOR
+ * swizzle (2^(BASE + SHIFT + BITS) elements) and whole rows of both layouts.  Checked
+ * exhaustively at compile time for splits of at most kAffineChecks accesses (else: not
+ * recognised, the general path runs). */
+constexpr int kMaxAffineRounds = 64;
+constexpr int kAffineChecks = 16384;
+struct round_deltas {
+  bool ok = false;
+  int s[kMaxAffineRounds] = {};
+  int d[kMaxAffineRounds] = {};
+};
+
+template <class SrcSwz, class DstSwz>
+constexpr round_deltas affine_rounds(const copy_plan_t& p, int threads, int soff, int doff) {
+  round_deltas r;
+  if (p.outer > kMaxAffineRounds || p.outer * threads > kAffineChecks) return r;
+  const int step = threads * p.vec;
+  for (int f = 0; f < p.outer; ++f) {
+    r.s[f] = SrcSwz::apply(side_offset(p.m, f * step, true, soff)) - SrcSwz::apply(side_offset(p.m, 0, true, soff));
+    r.d[f] = DstSwz::apply(side_offset(p.m, f * step, false, doff)) - DstSwz::apply(side_offset(p.m, 0, false, doff));
+  }
+  for (int t = 0; t < threads; ++t) {
+    if (t * p.vec >= p.m.count) break;
+    const int s0 = SrcSwz::apply(side_offset(p.m, t * p.vec, true, soff));
+    const int d0 = DstSwz::apply(side_offset(p.m, t * p.vec, false, doff));
+    for (int f = 1; f < p.outer; ++f) {
+      const int flat = f * step + t * p.vec;
+      if (flat >= p.m.count) break;
+      if (SrcSwz::apply(side_offset(p.m, flat, true, soff)) != s0 + r.s[f] ||
+          DstSwz::apply(side_offset(p.m, flat, false, doff)) != d0 + r.d[f])
+        return round_deltas{};
+    }
+  }
+  r.ok = true;
+  return r;
+}
+
 template <int N>
 struct bytes_t;
 template <> struct bytes_t<1> { typedef uint8_t t; };
@@ -263,18 +319,23 @@ struct copy_plan {
   static constexpr int outer = plan.outer;
   static constexpr bool exact = plan.exact;
   static constexpr int count = joint.count;
+  /* Recognised rounds (see detail::affine_rounds): per-round offsets are compile-time adds. */
+  static constexpr detail::round_deltas rounds =
+      detail::affine_rounds<typename Src::swizzle, typename Dst::swizzle>(plan, Scope::threads, Src::offset,
+                                                                          Dst::offset);
+  static constexpr bool lowered = rounds.ok;
 };
 
 /* ---- copy ----------------------------------------------------------------------------------- */
 
+namespace detail {
+/* The general rounds: every round decomposes its access index and applies both swizzles. */
 template <class Scope, drive Drive, class Dst, class Src, typename T>
-__device__ __forceinline__ void copy(T* __restrict__ dst, const T* __restrict__ src) {
+__device__ __forceinline__ void copy_general(T* __restrict__ dst, const T* __restrict__ src) {
   using P = copy_plan<Scope, Drive, Dst, Src, T>;
-  constexpr detail::copy_plan_t plan = P::plan;
+  constexpr copy_plan_t plan = P::plan;
   constexpr int V = plan.vec, NT = Scope::threads;
-  static_assert(sizeof(T) == 1 || sizeof(T) == 2 || sizeof(T) == 4 || sizeof(T) == 8 || sizeof(T) == 16,
-                "tcd::copy: element of 1, 2, 4, 8 or 16 bytes");
-  typedef typename detail::bytes_t<V * sizeof(T) <= 16 ? V * sizeof(T) : 16>::t vec_t;
+  typedef typename bytes_t<V * sizeof(T) <= 16 ? V * sizeof(T) : 16>::t vec_t;
   const int t = Scope::rank();
 #pragma unroll
   for (int f = 0; f < plan.outer; ++f) {
@@ -291,6 +352,30 @@ __device__ __forceinline__ void copy(T* __restrict__ dst, const T* __restrict__ 
     so = Src::swizzle::apply(so);
     d_o = Dst::swizzle::apply(d_o);
     *reinterpret_cast<vec_t*>(dst + d_o) = *reinterpret_cast<const vec_t*>(src + so);
+  }
+}
+}  // namespace detail
+
+template <class Scope, drive Drive, class Dst, class Src, typename T>
+__device__ __forceinline__ void copy(T* __restrict__ dst, const T* __restrict__ src) {
+  using P = copy_plan<Scope, Drive, Dst, Src, T>;
+  constexpr detail::copy_plan_t plan = P::plan;
+  constexpr int V = plan.vec, NT = Scope::threads;
+  static_assert(sizeof(T) == 1 || sizeof(T) == 2 || sizeof(T) == 4 || sizeof(T) == 8 || sizeof(T) == 16,
+                "tcd::copy: element of 1, 2, 4, 8 or 16 bytes");
+  if constexpr (P::lowered) {
+    typedef typename detail::bytes_t<V * sizeof(T) <= 16 ? V * sizeof(T) : 16>::t vec_t;
+    const int t = Scope::rank();
+    // round 0 decomposed and swizzled once; later rounds add compile-time constants
+    const int s0 = Src::swizzle::apply(detail::side_offset(plan.m, t * V, true, Src::offset));
+    const int d0 = Dst::swizzle::apply(detail::side_offset(plan.m, t * V, false, Dst::offset));
+#pragma unroll
+    for (int f = 0; f < plan.outer; ++f) {
+      if (!plan.exact && (f * NT + t) * V >= plan.m.count) break;
+      *reinterpret_cast<vec_t*>(dst + d0 + P::rounds.d[f]) = *reinterpret_cast<const vec_t*>(src + s0 + P::rounds.s[f]);
+    }
+  } else {
+    detail::copy_general<Scope, Drive, Dst, Src, T>(dst, src);
   }
 }
 
@@ -320,7 +405,13 @@ __device__ __forceinline__ void wave_permute(T* dst, const T* src, int k, int sh
   constexpr detail::modes m = PP::m;
   constexpr int P = PP::P;
   const int lane = int(threadIdx.x) & 63;
-  const int mask = (1 << k) - 1;
+  // An XOR of k bits permutes the steps [0, P) only when P is a power of two and 2^k <= P: the
+  // mask is cut to P - 1 there and to 0 otherwise (k = 0), and the shift to the lane bits, so
+  // that j stays in [0, P) for any k and shift a caller passes.
+  constexpr bool kPow2 = (P & (P - 1)) == 0;
+  const int kk = k < 0 ? 0 : (k > 30 ? 30 : k);
+  const int mask = kPow2 ? (((1 << kk) - 1) & (P - 1)) : 0;
+  shift = shift < 0 ? 0 : (shift > 6 ? 6 : shift);
   T regs[P];
   int doff[P];
 #pragma unroll

@@ -70,6 +70,37 @@ __global__ void __launch_bounds__(256) swizzled_transpose(const uint16_t* __rest
   tcd::s2g<tcd::workgroup_scope<256>, typename G::dst, SwzT>(dst + tc * 64 * LD_DST + tr * 64, s);
 }
 
+// 64 x 64 bf16 tiles of a row-major matrix of pitch 16384 staged through LDS by a workgroup of
+// 256 lanes and written back to the same place of the destination (a tile copy through LDS, as
+// a consumer kernel would stage its operand): mode 0 a plain LDS tile, mode 1 the XOR-swizzled
+// tile with the recognised rounds lowered to adds, mode 2 the same swizzled tile with the swizzle
+// applied every round (the general path), for timing the lowering against both.
+constexpr int kStreamLd = 16384;
+using StreamG = layout<ints<64, 64>, ints<kStreamLd, 1>>;
+using StreamPlain = layout<ints<64, 64>, ints<64, 1>>;
+
+template <int MODE>
+__global__ void __launch_bounds__(256) tile_stream(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                    int tiles_c) {
+  __shared__ __attribute__((aligned(16))) uint16_t s[64 * 64];
+  const int tr = int(blockIdx.x) / tiles_c, tc = int(blockIdx.x) % tiles_c;
+  const int64_t base = int64_t(tr) * 64 * kStreamLd + tc * 64;
+  using WG = tcd::workgroup_scope<256>;
+  if constexpr (MODE == 0) {
+    tcd::g2s<WG, StreamPlain, StreamG>(s, src + base);
+    __syncthreads();
+    tcd::s2g<WG, StreamG, StreamPlain>(dst + base, s);
+  } else if constexpr (MODE == 1) {
+    tcd::g2s<WG, SwzT, StreamG>(s, src + base);
+    __syncthreads();
+    tcd::s2g<WG, StreamG, SwzT>(dst + base, s);
+  } else {
+    tcd::detail::copy_general<WG, tcd::drive::src, SwzT, StreamG>(s, src + base);
+    __syncthreads();
+    tcd::detail::copy_general<WG, tcd::drive::dst, StreamG, SwzT>(dst + base, s);
+  }
+}
+
 // One lane copies a (3, 5, 7) int8 tile: source strides (80, 9, 1) (row pitch 9, plane pitch 80)
 // -> destination strides (1, 3, 15) (fully transposed order).
 using LaneSrc = layout<ints<3, 5, 7>, ints<80, 9, 1>>;
@@ -92,6 +123,14 @@ __global__ void __launch_bounds__(128) waves2_copy(const uint16_t* __restrict__ 
 }
 
 int status() { return int(hipGetLastError()); }
+
+template <class P>
+void plan_out(int* out) {
+  out[0] = P::vec;
+  out[1] = P::outer;
+  out[2] = P::exact;
+  out[3] = P::lowered;
+}
 
 }  // namespace
 
@@ -125,6 +164,20 @@ int tcd_ex_swizzled_transpose(const uint16_t* src, uint16_t* dst, uint16_t* lds_
   return status();
 }
 
+/* (64 tiles_r) x (64 tiles_c) bf16 tiles of a row-major matrix of pitch 16384 (tiles_r, tiles_c in
+ * 1..256; src and dst hold 64 tiles_r x 16384 elements) copied tile by tile through LDS by one
+ * workgroup per tile: mode 0 plain LDS tile, 1 XOR-swizzled tile (recognised rounds, adds), 2 the
+ * swizzled tile with the swizzle applied every round. */
+int tcd_ex_tile_stream(const uint16_t* src, uint16_t* dst, int tiles_r, int tiles_c, int mode, void* stream) {
+  if (tiles_r < 1 || tiles_c < 1 || tiles_r > kStreamLd / 64 || tiles_c > kStreamLd / 64 || mode < 0 || mode > 2)
+    return int(hipErrorInvalidValue);
+  const dim3 grid(tiles_r * tiles_c);
+  if (mode == 0) hipLaunchKernelGGL(tile_stream<0>, grid, dim3(256), 0, hipStream_t(stream), src, dst, tiles_c);
+  else if (mode == 1) hipLaunchKernelGGL(tile_stream<1>, grid, dim3(256), 0, hipStream_t(stream), src, dst, tiles_c);
+  else hipLaunchKernelGGL(tile_stream<2>, grid, dim3(256), 0, hipStream_t(stream), src, dst, tiles_c);
+  return status();
+}
+
 /* (3, 5, 7) int8 tile by one lane: src holds 240 bytes, dst 105. */
 int tcd_ex_lane_copy(const uint8_t* src, uint8_t* dst, void* stream) {
   hipLaunchKernelGGL(lane_copy, dim3(1), dim3(64), 0, hipStream_t(stream), src, dst);
@@ -138,21 +191,23 @@ int tcd_ex_waves2_copy(const uint16_t* src, uint16_t* dst, void* stream) {
 }
 
 /* The [outer, threads, vec] plans the examples compile to, for inspection:
- * out[0..2] = (vec, outer, exact) of: 0 roundtrip32 load, 1 swizzled load, 2 swizzled
- * transposed store, 3 lane copy, 4 two-wave load.  Returns 0, or -1 for an unknown index. */
+ * out[0..3] = (vec, outer, exact, lowered) of: 0 roundtrip32 load, 1 swizzled load, 2 swizzled
+ * transposed store, 3 lane copy, 4 two-wave load, 5 the stream example's swizzled load, 6 its
+ * swizzled store, 7 its plain load.  lowered = 1: the rounds were recognised (per-round adds of
+ * compile-time constants).  Returns 0, or -1 for an unknown index. */
 int tcd_ex_plan(int which, int* out) {
-  int v = 0, o = 0, e = 0;
+  using WG = tcd::workgroup_scope<256>;
   switch (which) {
-    case 0: { using P = tcd::copy_plan<tcd::wave_scope, tcd::drive::src, L32, L32, float>; v = P::vec; o = P::outer; e = P::exact; break; }
-    case 1: { using P = tcd::copy_plan<tcd::workgroup_scope<256>, tcd::drive::src, SwzT, SwzGlobal<192, 192>::src, uint16_t>; v = P::vec; o = P::outer; e = P::exact; break; }
-    case 2: { using P = tcd::copy_plan<tcd::workgroup_scope<256>, tcd::drive::dst, SwzGlobal<192, 192>::dst, SwzT, uint16_t>; v = P::vec; o = P::outer; e = P::exact; break; }
-    case 3: { using P = tcd::copy_plan<tcd::lane_scope, tcd::drive::src, LaneDst, LaneSrc, uint8_t>; v = P::vec; o = P::outer; e = P::exact; break; }
-    case 4: { using P = tcd::copy_plan<tcd::waves_scope<2>, tcd::drive::src, W2Lds, W2Src, uint16_t>; v = P::vec; o = P::outer; e = P::exact; break; }
+    case 0: plan_out<tcd::copy_plan<tcd::wave_scope, tcd::drive::src, L32, L32, float>>(out); break;
+    case 1: plan_out<tcd::copy_plan<WG, tcd::drive::src, SwzT, SwzGlobal<192, 192>::src, uint16_t>>(out); break;
+    case 2: plan_out<tcd::copy_plan<WG, tcd::drive::dst, SwzGlobal<192, 192>::dst, SwzT, uint16_t>>(out); break;
+    case 3: plan_out<tcd::copy_plan<tcd::lane_scope, tcd::drive::src, LaneDst, LaneSrc, uint8_t>>(out); break;
+    case 4: plan_out<tcd::copy_plan<tcd::waves_scope<2>, tcd::drive::src, W2Lds, W2Src, uint16_t>>(out); break;
+    case 5: plan_out<tcd::copy_plan<WG, tcd::drive::src, SwzT, StreamG, uint16_t>>(out); break;
+    case 6: plan_out<tcd::copy_plan<WG, tcd::drive::dst, StreamG, SwzT, uint16_t>>(out); break;
+    case 7: plan_out<tcd::copy_plan<WG, tcd::drive::src, StreamPlain, StreamG, uint16_t>>(out); break;
     default: return -1;
   }
-  out[0] = v;
-  out[1] = o;
-  out[2] = e;
   return 0;
 }
 

@@ -23,7 +23,8 @@ def load_dev_library(path: str = DEV_LIB_PATH):
     vp, i = ctypes.c_void_p, ctypes.c_int
     for name, args in [("tcd_ex_roundtrip32", [vp, vp, vp]), ("tcd_ex_permute_tiles", [vp, vp, i, i, i, i, vp]),
                        ("tcd_ex_swizzled_transpose", [vp, vp, vp, i, i, vp]), ("tcd_ex_lane_copy", [vp, vp, vp]),
-                       ("tcd_ex_waves2_copy", [vp, vp, vp]), ("tcd_ex_plan", [i, ctypes.POINTER(ctypes.c_int)])]:
+                       ("tcd_ex_waves2_copy", [vp, vp, vp]), ("tcd_ex_plan", [i, ctypes.POINTER(ctypes.c_int)]),
+                       ("tcd_ex_tile_stream", [vp, vp, i, i, i, vp])]:
         getattr(lib, name).argtypes = args
         getattr(lib, name).restype = ctypes.c_int
     _dev = lib
@@ -57,12 +58,23 @@ def waves2_copy(src, dst, stream=None) -> None:
     _ok(load_dev_library().tcd_ex_waves2_copy(_ptr(src), _ptr(dst), _stream(stream)), "tcd_ex_waves2_copy")
 
 
-def example_plan(which: int) -> dict:
-    """(vec, outer, exact) the example's copy compiled to (see tcd_ex_plan)."""
-    out = (ctypes.c_int * 3)()
+def tile_stream(src, dst, tiles_r: int, tiles_c: int, mode: int, stream=None) -> None:
+    """64 x 64 bf16 tiles of a pitch-16384 matrix staged through LDS and written back in place
+    (mode 0 plain LDS tile, 1 swizzled with recognised rounds, 2 swizzled with the general rounds)."""
+    _ok(load_dev_library().tcd_ex_tile_stream(_ptr(src), _ptr(dst), int(tiles_r), int(tiles_c), int(mode),
+                                              _stream(stream)), "tcd_ex_tile_stream")
+
+
+def example_plan(which: int, lowered: bool = False) -> dict:
+    """(vec, outer, exact) the example's copy compiled to (see tcd_ex_plan); with lowered=True
+    also whether its rounds were recognised (per-round adds)."""
+    out = (ctypes.c_int * 4)()
     if load_dev_library().tcd_ex_plan(int(which), out) != 0:
         raise ValueError(f"no example plan {which}")
-    return {"vec": out[0], "outer": out[1], "exact": bool(out[2])}
+    d = {"vec": out[0], "outer": out[1], "exact": bool(out[2])}
+    if lowered:
+        d["lowered"] = bool(out[3])
+    return d
 
 
 def _main(argv=None) -> int:

@@ -44,7 +44,7 @@ def test_library_exports_device_examples():
     out = subprocess.run(["nm", "-D", "--defined-only", D.DEV_LIB_PATH], capture_output=True, text=True).stdout
     names = {line.split()[-1] for line in out.splitlines() if " T " in line}
     assert {"tcd_ex_roundtrip32", "tcd_ex_permute_tiles", "tcd_ex_swizzled_transpose", "tcd_ex_lane_copy",
-            "tcd_ex_waves2_copy", "tcd_ex_plan"} <= names
+            "tcd_ex_waves2_copy", "tcd_ex_plan", "tcd_ex_tile_stream"} <= names
     assert "tc_wave_permute_plan" in subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
                                                      text=True).stdout
 
@@ -67,6 +67,36 @@ def test_example_plans_match_oracle_partition():
     o = R.gmem_smem_partition(R.layout((45, 40), (56, 1)), R.layout((45, 40), (40, 1)), 128, 2)
     assert o["declined"]
     assert D.example_plan(4) == {"vec": 1, "outer": 15, "exact": False}
+
+
+def test_recognised_rounds_match_oracle():
+    """The copy lowers a swizzled copy to per-round adds exactly where the oracle's partition shows
+    that every lane's offsets on both sides (swizzle applied) are its round-0 offsets plus a
+    per-round constant (TVM TIRx "copy -> gmem_smem", "How inputs change the algorithm", last
+    paragraph).  Examples 1, 5, 6: global <-> the XOR-swizzled 64 x 64 bf16 tile (16-byte chunks,
+    chunk ^= row % 8), rounds of 32 whole rows -> recognised; example 2: the transposed store from
+    it, rounds of 4 columns -> the swizzle changes within a round, not recognised."""
+    import layout_permuting_copy_amd.dev as D
+    swz = lambda o: R.xor_swizzle(o, 3, 3, 3)
+    ident = lambda o: o
+    cases = {  # which: (global layout, LDS layout, threads, elem bytes, swizzle of the LDS side)
+        0: (R.layout((32, 32), (32, 1)), R.layout((32, 32), (32, 1)), 64, 4, ident),
+        1: (R.layout((64, 64), (192, 1)), R.layout((64, 64), (64, 1)), 256, 2, swz),
+        2: (R.layout((64, 64), (1, 192)), R.layout((64, 64), (64, 1)), 256, 2, swz),
+        5: (R.layout((64, 64), (16384, 1)), R.layout((64, 64), (64, 1)), 256, 2, swz),
+        6: (R.layout((64, 64), (16384, 1)), R.layout((64, 64), (64, 1)), 256, 2, swz),
+        7: (R.layout((64, 64), (16384, 1)), R.layout((64, 64), (64, 1)), 256, 2, ident),
+    }
+    for which, (g, s, threads, eb, f_s) in cases.items():
+        o = R.gmem_smem_partition(g, s, threads, eb, vec_bits=(128, 64, 32))
+        gl = np.array(o["g_lin"])
+        sl = np.vectorize(f_s)(np.array(o["s_lin"]))
+        affine = all(len(set((gl[f] - gl[0]).tolist())) == 1 and len(set((sl[f] - sl[0]).tolist())) == 1
+                     for f in range(o["outer"]))
+        p = D.example_plan(which, lowered=True)
+        assert (p["vec"], p["outer"]) == (o["vec"], o["outer"]), which
+        assert p["lowered"] == affine, which
+    assert [D.example_plan(w, lowered=True)["lowered"] for w in (1, 2, 5)] == [True, False, True]
 
 
 # ---- GPU -------------------------------------------------------------------------------------
@@ -157,6 +187,27 @@ def test_swizzled_lds_transpose(tiles_r, tiles_c):
         image = np.empty(4096, dtype=np.uint16)
         image[sw] = tile
         assert np.array_equal(lds[t], image), t
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_tile_stream_through_lds(mode):
+    """64 x 64 bf16 tiles of a pitch-16384 matrix staged through a plain (0) or XOR-swizzled LDS
+    tile with recognised (1) or general (2) rounds and written back in place: bit-exact, and
+    nothing outside the tiles is written."""
+    torch = _torch()
+    import layout_permuting_copy_amd.dev as D
+    tiles_r, tiles_c = 3, 5
+    n_el = 64 * tiles_r * 16384
+    src = _bits(n_el * 2, 21 + mode)
+    s = torch.from_numpy(src).cuda()
+    d = torch.full((n_el * 2,), 0xA5, dtype=torch.uint8, device="cuda")
+    D.tile_stream(s, d, tiles_r, tiles_c, mode)
+    torch.cuda.synchronize()
+    want = np.full(n_el * 2, 0xA5, dtype=np.uint8)
+    lay = R.layout((64 * tiles_r, 64 * tiles_c), (16384, 1))
+    R.copy(src, lay, want, lay, 2)
+    assert np.array_equal(d.cpu().numpy(), want)
 
 
 @pytest.mark.gpu
