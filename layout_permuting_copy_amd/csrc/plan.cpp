@@ -99,7 +99,6 @@ static void decline(Plan* p, int flags, const std::string& why) {
 struct TuneCfg {
   int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1, cap = -1, so = -1;
   int xk = -1, xs = 0, xt = 0, xcs = 0, xcm = 0;
-  int tr = 0;
 };
 
 static TuneCfg tune_override() {
@@ -133,7 +132,6 @@ static TuneCfg tune_override() {
         else if (k == "xt") c.xt = v;
         else if (k == "xcs") c.xcs = v;
         else if (k == "xcm") c.xcm = v;
-        else if (k == "tr") c.tr = v;
       }
       pos = end + 1;
     }
@@ -458,36 +456,6 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     if (k != p->mode_c && (std::llabs(j.m[k].s) * p->eb) % 128 != 0) src_lines = false;
   const bool line_cfg = p->unaligned || ((p->eb == 1 || p->eb == 2 || p->eb == 8) && !dst_lines) ||
                         (p->eb == 1 && !src_lines);
-  // The row-major tile with LDS DMA and transposing LDS reads (1- and 2-byte elements, both sides
-  // on the lines, every tile inside the copy; 256-byte tile rows): tile bytes, threads, grid order
-  // and nontemporal bits from the override where given.
-  if (ov.tr > 0 && (p->eb == 1 || p->eb == 2) && p->vb == 16 && p->step == 1 && !line_cfg && !batched &&
-      p->mode_b < 0) {
-    TileGeom g;
-    g.eb = p->eb;
-    g.vb = 16;
-    g.tr = ov.tr;
-    g.U = 16;
-    g.B = 1;
-    g.VE = 16 / p->eb;
-    g.tile_bytes = ov.tile ? ov.tile : 131072;
-    g.NT = ov.threads ? ov.threads : 512;
-    g.TC = 256 / p->eb;
-    g.TR = g.tile_bytes / 256;
-    g.NB = 1;
-    g.ntm = ov.nt >= 0 ? ov.nt : 3;
-    g.order = ov.order >= 0 ? ov.order : 1;
-    g.edges = false;
-    g.loads = g.stores = g.tile_bytes / (g.NT * 16);
-    g.ww = 16;
-    g.rw = 8;
-    if (R.e % g.TR == 0 && C.e % g.TC == 0 &&
-        launch_transpose(g.eb, transpose_cfg(g), nullptr, 0, nullptr)) {
-      p->g = g;
-      p->wconf = p->rconf = 0;
-      return true;
-    }
-  }
   TuneCfg base = default_cfg(p->eb, batched, line_cfg);
   // 1-byte elements there, and element-aligned 8-byte elements read with unit stride: the XCD
   // super-tile order, so that the neighbouring tiles that share cache lines at element alignment
@@ -813,11 +781,6 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     // 16-byte elements 8192^2 -5% (5.70 against 6.00 TB/s), so those keep the guarded kernel.
     p.g.edges = j.m[r].e % p.g.TR != 0 || j.m[c].e % p.g.TC != 0 || eB % p.g.NB != 0 ||
                 p.g.step != 1 || p.eb == 16;
-    if (p.g.tr && p.g.edges) {
-      p.status = TC_E_ARG;
-      p.reason = "internal: the transposing-read tile needs every tile inside the copy";
-      return p;
-    }
     p.workgroups = transpose_workgroups(p, r, c, b);
     if (p.workgroups >= (int64_t(1) << 31)) {
       p.status = TC_E_RANGE;

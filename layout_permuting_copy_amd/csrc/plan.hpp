@@ -99,9 +99,6 @@ struct TileGeom {
   bool pad_rows = false;          // order 1 with source rows off the 128-byte lines: the row-tile
                                   // count of the grid is padded to a multiple of kXcds (tile_at)
   int cap = 0;                    // loads a lane keeps in flight in the interior load phase (0: all)
-  int tr = 0;                     // row-major LDS tile read by transposing LDS reads (1- and 2-byte
-                                  // elements; transpose_tr_kernel): 1 filled by LDS DMA, 2 through
-                                  // registers
   int loads = 4, stores = 4;  // accesses per thread per phase
   int ww = 16, rw = 4;        // LDS write / read instruction bytes
   int k = 0, shift = 0, tbit = 0;
@@ -237,11 +234,10 @@ struct TransposeCfg {
   bool wave_local;
   bool edges = true;  // false: every tile lies wholly inside the copy (the interior-only kernel)
   int cap = 0;        // loads in flight per lane in the load phase (0: all of them)
-  int tr = 0;         // transpose_tr_kernel: 1 LDS DMA loads, 2 register-staged loads
 };
 // The kernel configuration a planned tile geometry runs with (every field of it).
 inline TransposeCfg transpose_cfg(const TileGeom& g) {
-  return TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, g.wave_local, g.edges, g.cap, g.tr};
+  return TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, g.wave_local, g.edges, g.cap};
 }
 bool launch_transpose_eb1(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);
 bool launch_transpose_eb2(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream);

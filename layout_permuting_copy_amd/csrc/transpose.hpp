@@ -228,118 +228,6 @@ __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   else read_store<EB, VB, U, G, NT, NTM, true>(a, t, lds);
 }
 
-// Transpose of 1- and 2-byte elements through a row-major LDS tile, with gfx950's LDS DMA and
-// transposing LDS reads.  The tile is TR rows (destination-contiguous mode) of 256 bytes (source-
-// contiguous mode, TC = 256 / EB elements); NB = 1; every tile lies inside the copy.
-//  - Load phase: global_load_lds_dwordx4, the source rows' 16-byte chunks straight into LDS (no
-//    registers): a wave instruction fills 64 consecutive LDS chunks (4 rows); the XOR swizzle of
-//    the chunk positions is applied on the global side (lane l loads the source chunk that belongs
-//    at LDS chunk l), so the row segments of one transposing read fall into distinct banks.
-//  - Store phase: ds_read_b64_tr_b8 (EB = 1: a 16-lane group reads 8 rows x 16 bytes, lane i gets
-//    byte column i of the 8 rows) or ds_read_b64_tr_b16 (EB = 2: 4 rows x 16 halfwords, lane i gets
-//    halfword column i); two reads give a lane one 16-byte destination vector (16 or 8 rows of one
-//    column), which it stores.  The groups of a wave take consecutive row blocks, and the halves
-//    they read first alternate, so that the 32 lanes served together read distinct banks.
-// Swizzle: 16-byte chunk p of row r holds source chunk p ^ (r & 15) (EB = 1); 32-byte pair d of
-// row r holds source pair d ^ (r & 7) (EB = 2).
-template <int EB>
-__device__ __forceinline__ int tr_swizzle(int r) {
-  if constexpr (EB == 1) return r & 15;
-  else return (r & 7) << 1;
-}
-
-template <int EB, int TILE, int NT, int NTM, bool DMA = true>
-__global__ void __launch_bounds__(NT) transpose_tr_kernel(TransposeArgs a) {
-  static_assert(EB == 1 || EB == 2, "transposing LDS reads of 8- or 16-bit elements");
-  constexpr int ROWB = 256;                // LDS bytes per tile row
-  constexpr int TR = TILE / ROWB;
-  constexpr int NCH = ROWB / 16;           // 16-byte chunks per row
-  constexpr int WAVES = NT / 64;
-  constexpr int LOADS = TILE / (NT * 16);  // DMA instructions per wave
-  constexpr int RB = EB == 1 ? 64 : 32;    // rows of one store instruction of a wave
-  constexpr int CBS = EB == 1 ? 16 : 8;    // column blocks of 16 elements per row
-  constexpr int STORES = (TR / RB) * CBS / WAVES;
-  static_assert(TILE % (NT * 16) == 0 && (TR / RB) * CBS % WAVES == 0, "tile and threads");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[TILE];
-  const TileAt t = tile_at(a, blockIdx.x);
-  if (!t.valid) return;
-  const int lane = int(threadIdx.x) & 63;
-  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
-  constexpr int kAux = (NTM & 1) ? 2 : 0;  // cache policy: nontemporal loads
-  if constexpr (DMA) {
-#pragma unroll
-    for (int f = 0; f < LOADS; ++f) {
-      const int q0 = (f * WAVES + w) * 64;  // first LDS chunk of the wave instruction
-      const int q = q0 + lane;
-      const int r = q / NCH, pch = q % NCH;
-      const unsigned char* g = a.src + (t.sbase + int64_t(r) * a.sR) * EB + ((pch ^ tr_swizzle<EB>(r)) << 4);
-      __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds + q0 * 16), 16, 0, kAux);
-    }
-    wait_vmem();
-  } else {
-    // the same placement through registers: global loads, then 16-byte LDS writes
-    uint32_t v[LOADS][4];
-#pragma unroll
-    for (int f = 0; f < LOADS; ++f) {
-      const int q = (f * WAVES + w) * 64 + lane;
-      const int r = q / NCH, pch = q % NCH;
-      gload<16, NTM>(a.src + (t.sbase + int64_t(r) * a.sR) * EB + ((pch ^ tr_swizzle<EB>(r)) << 4), v[f]);
-    }
-#pragma unroll
-    for (int f = 0; f < LOADS; ++f) store_words<16>(lds + ((f * WAVES + w) * 64 + lane) * 16, v[f]);
-  }
-  __syncthreads();
-  const int grp = lane >> 4, i = lane & 15;
-  uint32_t out[STORES][4];
-#pragma unroll
-  for (int s = 0; s < STORES; ++s) {
-    const int bidx = s * WAVES + w;
-    const int rb = bidx % (TR / RB), cb = bidx / (TR / RB);
-    const int R = rb * RB + grp * (RB / 4);
-    // read h covers half h ^ odd of the lane's rows; the halves go to their places by selects (a
-    // run-time register index would move `out` to scratch memory)
-    const bool odd = grp & 1;
-    uint32_t x[2][2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int half = h ^ int(odd);
-      if constexpr (EB == 1) {
-        const int row = R + 8 * half + (i >> 1);
-        const int addr = row * ROWB + ((cb ^ tr_swizzle<1>(row)) << 4) + ((i & 1) << 3);
-        typedef int v2i __attribute__((ext_vector_type(2)));
-        const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(lds + addr));
-        x[h][0] = uint32_t(v.x);
-        x[h][1] = uint32_t(v.y);
-      } else {
-        const int row = R + 4 * half + (i >> 2);
-        const int addr = row * ROWB + (((2 * cb) ^ tr_swizzle<2>(row)) << 4) + ((i & 3) << 3);
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(lds + addr));
-        x[h][0] = uint32_t(uint16_t(v.x)) | (uint32_t(uint16_t(v.y)) << 16);
-        x[h][1] = uint32_t(uint16_t(v.z)) | (uint32_t(uint16_t(v.w)) << 16);
-      }
-    }
-    out[s][0] = odd ? x[1][0] : x[0][0];
-    out[s][1] = odd ? x[1][1] : x[0][1];
-    out[s][2] = odd ? x[0][0] : x[1][0];
-    out[s][3] = odd ? x[0][1] : x[1][1];
-  }
-#pragma unroll
-  for (int s = 0; s < STORES; ++s) {
-    const int bidx = s * WAVES + w;
-    const int rb = bidx % (TR / RB), cb = bidx / (TR / RB);
-    const int R = rb * RB + grp * (RB / 4);
-    unsigned char* p = a.dst + (t.dbase + int64_t(cb * 16 + i) * a.dC + R) * EB;
-    gstore<16, NTM>(p, out[s]);
-  }
-}
-
-template <int EB, int TILE, int NT, int NTM, bool DMA>
-bool launch_transpose_tr_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
-  if (ta) hipLaunchKernelGGL((transpose_tr_kernel<EB, TILE, NT, NTM, DMA>), dim3(uint32_t(wgs)), dim3(NT), 0, s, *ta);
-  return true;
-}
-
 // Launches the instance (ta != nullptr) or only reports whether it exists (ta == nullptr).
 template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL = false, bool EDGE = true, int CAP = 0>
 bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
@@ -365,10 +253,6 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);                                             \
     const int vb = c.vb, tile = c.tile, nt = c.threads, ntm = c.ntm;                                         \
     constexpr int U = EB < 4 ? 4 : EB;                                                                       \
-    if (c.tr) {                                                                                              \
-      TC_TR_EB##EB                                                                                           \
-      return false;                                                                                          \
-    }                                                                                                        \
     if (c.cap != 0) {                                                                                        \
       TC_CAPS_EB##EB                                                                                         \
       return false;                                                                                          \
@@ -431,20 +315,6 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 #define TC_CAPS_EB4
 #define TC_CAPS_EB8
 #define TC_CAPS_EB16
-
-// The row-major tile with LDS DMA and transposing reads (1- and 2-byte elements, interior tiles)
-#define TC_CFG_TR(EB, TILE, NT)                                                                              \
-  if (tile == TILE && nt == NT && vb == 16 && c.step == 1 && !c.edges) {                                     \
-    if (ntm == 3) return c.tr == 2 ? dev::launch_transpose_tr_cfg<EB, TILE, NT, 3, false>(ta, wgs, s)       \
-                                   : dev::launch_transpose_tr_cfg<EB, TILE, NT, 3, true>(ta, wgs, s);        \
-    if (ntm == 1) return c.tr == 2 ? dev::launch_transpose_tr_cfg<EB, TILE, NT, 1, false>(ta, wgs, s)       \
-                                   : dev::launch_transpose_tr_cfg<EB, TILE, NT, 1, true>(ta, wgs, s);        \
-  }
-#define TC_TR_EB1 TC_CFG_TR(1, 131072, 512) TC_CFG_TR(1, 131072, 1024) TC_CFG_TR(1, 65536, 256) TC_CFG_TR(1, 65536, 512)
-#define TC_TR_EB2 TC_CFG_TR(2, 131072, 512) TC_CFG_TR(2, 131072, 1024) TC_CFG_TR(2, 65536, 256) TC_CFG_TR(2, 65536, 512)
-#define TC_TR_EB4
-#define TC_TR_EB8
-#define TC_TR_EB16
 
 #define TC_CFG_WL(EB, U, TILE, NT)                                                                           \
   if (vb == 16 && tile == TILE && nt == NT && c.step == 1 && ntm == 3 && c.wave_local)                       \
