@@ -288,12 +288,13 @@ __device__ __forceinline__ TileAt tile_at(const TransposeArgs& a, uint32_t tile)
     // XCD x = idx % kXcds takes super-tiles x, x + kXcds, ..; the kSuper^2 tiles of a super-tile
     // are consecutive in that XCD's share of the grid, column tiles fastest inside it
     const uint32_t x = idx % kXcds, k = idx / kXcds;
-    const uint32_t w = k % (kSuper * kSuper);
-    const uint32_t gst = (k / (kSuper * kSuper)) * kXcds + x;  // super-tile over all slices
+    const uint32_t per = 1u << (a.lsr + a.lsc);  // tiles per super-tile
+    const uint32_t w = k & (per - 1);
+    const uint32_t gst = (k >> (a.lsr + a.lsc)) * kXcds + x;  // super-tile over all slices
     const uint32_t slice = gst / a.nst, st = gst - slice * a.nst;
     q = udiv(st, a.stC);
-    trI = q * kSuper + w / kSuper;
-    tcI = (st - q * a.stC.d) * kSuper + w % kSuper;
+    trI = (q << a.lsr) + (w >> a.lsc);
+    tcI = ((st - q * a.stC.d) << a.lsc) + (w & ((1u << a.lsc) - 1));
     valid = slice < a.nslices && trI < a.tilesR.d && tcI < a.tilesC.d;
     idx = valid ? slice : 0;
   } else {

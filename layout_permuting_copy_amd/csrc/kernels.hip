@@ -601,7 +601,10 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
       ta.order = p.g.order;
       fill_batch(p, &ta, p.mode_r, p.mode_c, p.mode_b);
       if (p.g.order == 2) {  // (after fill_batch: the slices count the batch modes)
-        const uint32_t stC = (ta.tilesC.d + kSuper - 1) / kSuper, stR = (ta.tilesR.d + kSuper - 1) / kSuper;
+        const uint32_t sr = 1u << p.g.lsr, sc = 1u << p.g.lsc;
+        ta.lsr = p.g.lsr;
+        ta.lsc = p.g.lsc;
+        const uint32_t stC = (ta.tilesC.d + sc - 1) / sc, stR = (ta.tilesR.d + sr - 1) / sr;
         ta.stC = make_div32(stC);
         ta.nst = stR * stC;
         ta.nslices = ta.tilesB.d;

@@ -99,6 +99,7 @@ static void decline(Plan* p, int flags, const std::string& why) {
 struct TuneCfg {
   int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1, cap = -1, so = -1;
   int xk = -1, xs = 0, xt = 0, xcs = 0, xcm = 0;
+  int ssr = 0, ssc = 0;  // order 2: super-tile extents in tiles (powers of two)
 };
 
 static TuneCfg tune_override() {
@@ -132,6 +133,8 @@ static TuneCfg tune_override() {
         else if (k == "xt") c.xt = v;
         else if (k == "xcs") c.xcs = v;
         else if (k == "xcm") c.xcm = v;
+        else if (k == "ssr") c.ssr = v;
+        else if (k == "ssc") c.ssc = v;
       }
       pos = end + 1;
     }
@@ -502,8 +505,11 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   // Row tiles first with source rows off the lines: neighbouring column tiles read the same lines.
   // They are tilesR workgroups apart, so the grid pads tilesR to a multiple of kXcds and puts them
   // on one XCD (bf16 16448 x 16392 3.48 -> 4.3 TB/s, fp32 16416 x 16400 5.07 -> 5.4).
+  auto lg2 = [](int v) { int l = 0; while ((1 << l) < v) ++l; return l; };
   auto with_phase_order = [&](TileGeom g) {
     g.pad_rows = g.order == 1 && !src_lines;
+    if (ov.ssr > 0) g.lsr = lg2(ov.ssr);
+    if (ov.ssc > 0) g.lsc = lg2(ov.ssc);
     g.wave_local = ov.wl != 0 && tile_wave_local(g) &&
                    launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, true, true, g.cap},
                                     nullptr, 0, nullptr);
@@ -569,8 +575,8 @@ static int64_t transpose_workgroups(const Plan& p, int r, int c, int b) {
   for (int k = 0; k < j.rank; ++k)
     if (k != r && k != c && k != b) slices *= j.m[k].e;
   if (p.g.order != 2) return tR * tC * slices;
-  const int64_t nst = ceil_div(tR, kSuper) * ceil_div(tC, kSuper);
-  return ceil_div(nst * slices, kXcds) * kXcds * kSuper * kSuper;
+  const int64_t nst = ceil_div(tR, int64_t(1) << p.g.lsr) * ceil_div(tC, int64_t(1) << p.g.lsc);
+  return ceil_div(nst * slices, kXcds) * kXcds * (int64_t(1) << (p.g.lsr + p.g.lsc));
 }
 
 // Rows-type copies of 2^31 vectors or more launch ranges of the outermost grid mode, at most

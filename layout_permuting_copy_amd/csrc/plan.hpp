@@ -28,6 +28,7 @@ constexpr int kGuardThreads = 256;             // threads per workgroup on the g
 // many vectors each (the kernels index vectors and workgroups with 32-bit integers).
 constexpr int64_t kLaunchVectors = int64_t(1) << 30;
 constexpr int kInterleaveRounds = 2;  // pixel groups per lane on the interleave path
+constexpr int kSuperLog = 3;          // transpose grid order 2: super-tiles of 8 x 8 tiles by default
 
 // One joint mode: extent, source stride, destination stride (elements).
 struct Mode {
@@ -99,6 +100,7 @@ struct TileGeom {
   bool pad_rows = false;          // order 1 with source rows off the 128-byte lines: the row-tile
                                   // count of the grid is padded to a multiple of kXcds (tile_at)
   int cap = 0;                    // loads a lane keeps in flight in the interior load phase (0: all)
+  int lsr = kSuperLog, lsc = kSuperLog;  // order 2: log2 of the super-tile extents in tiles
   int loads = 4, stores = 4;  // accesses per thread per phase
   int ww = 16, rw = 4;        // LDS write / read instruction bytes
   int k = 0, shift = 0, tbit = 0;
@@ -183,6 +185,7 @@ struct TransposeArgs {
   Div32 stC;                 // order 2: super-tiles along the column mode, per 2-D slice
   uint32_t nst;              // order 2: super-tiles per 2-D slice
   uint32_t nslices;          // order 2: 2-D slices (batch tiles times the other grid modes)
+  int32_t lsr, lsc;          // order 2: log2 of the super-tile's extents in tiles (rows, columns)
 };
 
 // The shuffle path: nvec 16-byte vectors, C/4 per block row; block b starts at element
@@ -212,10 +215,9 @@ struct RowArgs {
                              // the launch reads / writes) from src / dst
 };
 
-// Order 2: super-tiles of kSuper x kSuper tiles, each run on one XCD (the dispatcher sends
-// workgroup i to XCD i % kXcds), so that neighbouring tiles, which share cache lines when the
-// layouts are not line-aligned, meet in one L2.
-constexpr int kSuper = 8;
+// Order 2: super-tiles of 2^lsr x 2^lsc tiles (rows x columns; kSuperLog each by default), each run
+// on one XCD (the dispatcher sends workgroup i to XCD i % kXcds), so that neighbouring tiles, which
+// share cache lines when the layouts are not line-aligned, meet in one L2.
 constexpr int kXcds = 8;
 
 // ---- launch (kernels.hip) ------------------------------------------------------------------------
