@@ -375,11 +375,17 @@ def main() -> int:
         for mode in (0, 1, 2):
             sweep.append(compact(time_tile_stream(torch, mode)))
             torch.cuda.empty_cache()
-        # the alternatives the planner does not pick, for comparison: the SF tiles on the LDS tile
-        # kernel, the (0,2,1,3) permute staged through LDS
-        # (the 32 x 32 round trip by one wave is a latency case: see its us_per_launch)
-        runs = [(sw, 0) for sw in [SI.tile32_roundtrip(), identity_workload()] + sweep_workloads()]
+        # context first (the 32 x 32 round trip by one wave is a latency case: see its
+        # us_per_launch; the odd and sliced copies; the alternatives the planner does not pick: the
+        # SF tiles on the LDS tile kernel, the (0,2,1,3) permute staged through LDS), then the
+        # configurations with the 80% target, last so that they end the line
+        target = [SI.sf_transpose(), SI.transpose2d(dtype="bfloat16"), SI.permute0213()]
+        target += [SI.sweep_dense(dt) for dt in SI.SWEEP_DTYPES]
+        context = [SI.tile32_roundtrip(), identity_workload()]
+        context += [SI.sweep_odd(dt) for dt in SI.SWEEP_DTYPES] + [SI.sweep_slice(dt) for dt in SI.SWEEP_DTYPES]
+        runs = [(sw, 0) for sw in context]
         runs += [(SI.sf_transpose(), L.TC_FLAG_NO_SHUFFLE), (SI.permute0213(), L.TC_FLAG_FORCE_LDS)]
+        runs += [(sw, 0) for sw in target]
         for sw, fl in runs:
             s = time_workload(torch, L, sw, 30, 3, seed=11, flags=fl)
             s_src, s_dst = s.pop("_last")

@@ -233,6 +233,8 @@ int tc_get_flags(void);
  *   xk, xs, xt, xcs, xcm       the transpose's XOR swizzle (k, shift, target
  *                              bit, column shift, column mask) forced onto the
  *                              chosen tile, conflict-free or not
+ *   ssr, ssc                   grid order 2: super-tile extents in tiles
+ *                              (powers of two; 8 x 8 by default)
  * Every setting gives the same bytes.  A setting no compiled kernel instance
  * matches makes the copy fail with TC_E_ARG ("internal: no tile geometry");
  * unknown keys are ignored.  Unset, the planner's own choices apply.
