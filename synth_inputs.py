@@ -248,6 +248,51 @@ def random_layouts(seed: int = 1234, count: int = 60):
         yield shape, s_stride, tuple(d_stride), eb, acc * int(np.prod(steps)) + 1
 
 
+def random_layouts_large(seed: int = 777, count: int = 60, max_elems: int = 3 << 20):
+    """Multi-tile layout pairs for the tiled paths: two large modes (extents up to a few
+    thousand, so that copies span many tiles and end in ragged ones), an optional small batch
+    mode, padded pitches on both sides (so rows start off the 16-byte and 128-byte grids), a
+    source step of 1 or 2 along its innermost mode, element offsets, and a destination that is
+    dense in a random mode order with its own padding.  Yields (shape, src_stride, src_offset,
+    dst_stride, dst_offset, elem_bytes, src_elems, dst_elems); every offset a layout reaches lies
+    in [0, *_elems), and the destination is injective."""
+    rng = np.random.default_rng(seed)
+    made = 0
+    while made < count:
+        eb = int(rng.choice([1, 2, 4, 8, 16]))
+        big = [int(rng.integers(1, 3000)), int(rng.integers(1, 3000))]
+        rank = int(rng.integers(2, 4))
+        shape = big + [int(rng.integers(1, 6)) for _ in range(rank - 2)]
+        order = list(rng.permutation(rank))
+        if int(np.prod(shape)) > max_elems // max(1, eb // 4) or int(np.prod(shape)) == 0:
+            continue
+        # source: row-major in `order` (last = innermost), innermost step 1 or 2, padded pitches
+        step = int(rng.choice([1, 1, 1, 2]))
+        ss = [0] * rank
+        acc = step
+        ss[order[-1]] = step
+        acc = shape[order[-1]] * step
+        for k in reversed(order[:-1]):
+            acc += int(rng.integers(0, 40))
+            ss[k] = acc
+            acc *= shape[k]
+        so = int(rng.integers(0, 9))
+        # destination: dense in another order, padded pitches
+        dorder = list(rng.permutation(rank))
+        ds = [0] * rank
+        ds[dorder[-1]] = 1
+        dacc = shape[dorder[-1]]
+        for k in reversed(dorder[:-1]):
+            dacc += int(rng.integers(0, 40))
+            ds[k] = dacc
+            dacc *= shape[k]
+        do = int(rng.integers(0, 9))
+        span_s = so + sum((e - 1) * st for e, st in zip(shape, ss)) + step
+        span_d = do + sum((e - 1) * d for e, d in zip(shape, ds)) + 1
+        made += 1
+        yield tuple(shape), tuple(ss), so, tuple(ds), do, eb, span_s, span_d
+
+
 def random_layouts_wide(seed: int = 4321, count: int = 120):
     """Like random_layouts, plus negative source strides, broadcast (stride-0) source modes,
     inserted extent-1 modes with arbitrary strides, and element offsets on both sides.  Yields

@@ -426,6 +426,21 @@ def test_random_layouts_wide():
     assert len(paths) >= 3, paths
 
 
+def test_random_layouts_large():
+    """Multi-tile copies with ragged edges: padded pitches off the 16- and 128-byte grids, stride-2
+    sources, offsets, a small batch mode, every element width (element-aligned and stride-2
+    transposes in both grid orders, rows, guarded paths)."""
+    paths = set()
+    for case, (shape, ss, so, ds, do, eb, ns, nd) in enumerate(SI.random_layouts_large(777, 150)):
+        src = _bits(ns * eb, 5000 + case)
+        sl, dl = (shape, ss, so), (shape, ds, do)
+        say(f"[gpu] large case {case}: src={sl} dst={dl} eb={eb}")
+        got, plan = run_copy(src, sl, nd, dl, eb, dtype_code(DT_BY_EB[eb]))
+        assert_same(got, oracle_copy(src, sl, nd, dl, eb), eb, f"large {case}")
+        paths.add((plan["path_name"], plan["src_step"], plan["grid_order"]))
+    assert len(paths) >= 5, paths
+
+
 def test_adjacent_buffers_are_not_aliases():
     """A destination that starts right after the source's last byte (or ends right before its
     first) shares no byte: the copy runs."""
