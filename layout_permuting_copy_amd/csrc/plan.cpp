@@ -291,8 +291,9 @@ static bool search_swizzle(const TileGeom& g, bool no_swizzle, TileGeom* out, in
 // 5780, 16-byte elements 8192^2 5520 -> 5950.  64 KiB tiles where they still give 8192
 // workgroups, else smaller.  128 KiB tiles (one workgroup per CU) where the copy is large enough
 // to give every CU many of them: bf16 16384^2 as 1024 x 64 on 1024 lanes 5730 -> 5830, fp64 8192^2
-// as 256 x 64 5750 -> 5980, int8 8192^2 as 512 x 256 5000 -> 5190 (the default tile for 1-byte
-// elements otherwise); fp32 and smaller fp16 copies are faster on 64 KiB tiles.
+// as 256 x 64 5750 -> 5980 and then as 128 x 128 on 1024 lanes (1 KiB runs on both sides) 6.00 ->
+// 6.10 TB/s, int8 8192^2 as 512 x 256 5000 -> 5190 (the default tile for 1-byte elements
+// otherwise); fp32 and smaller fp16 copies are faster on 64 KiB tiles.
 // Loads in flight per lane (`cap`): all of a lane's loads at once had been the rule, but for the
 // tall tiles of 1- and 2-byte elements two measured faster (a wait in the load phase keeps at most
 // `cap` outstanding), on every buffer placement tried: bf16 16384^2 5.85-5.89 -> 6.09-6.19 TB/s,
@@ -317,7 +318,10 @@ static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c)
       return true;
     case 8:
       if (eR < 128 || eC < 16) return false;
-      if (tiles(256, 64) >= 4096) { c->tile = 131072; c->threads = 512; c->trb = 2048; }  // 256 x 64
+      // 128 KiB: square 128 x 128 tiles on 1024 lanes, 1 KiB runs on both sides (fp64 8192^2 6.00
+      // -> 6.10 TB/s against 256 x 64 on 512 lanes, interleaved over 7 placements; on 512 lanes
+      // the square tile ran at 5.96)
+      if (tiles(128, 128) >= 4096) { c->tile = 131072; c->threads = 1024; c->trb = 1024; }
       else if (tiles(256, 32) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 2048; }  // 256 x 32
       else { c->tile = 16384; c->threads = 256; c->trb = 1024; }                          // 128 x 16
       return true;

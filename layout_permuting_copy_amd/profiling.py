@@ -258,7 +258,13 @@ BANK_PIN_CASES = [
     ("int8 512x256 u16 k=1", "transpose_8192x8192_int8", 0, "xk=1,xs=0,xt=0,xcs=4,xcm=7"),
     ("int8 512x256 u16 k=2 shift 1 tbit 1", "transpose_8192x8192_int8", 0, "xk=2,xs=1,xt=1,xcs=3,xcm=3"),
     ("fp16 256x64 u16 no swizzle", "transpose_8192x8192_float16", 0x10, ""),
-    ("fp64 256x64 u16 no swizzle", "transpose_8192x8192_float64", 0x10, ""),
+    ("fp64 256x64 u16 no swizzle", "transpose_8192x8192_float64", 0x10,
+     "tile=131072,threads=512,trb=2048,unit=16,order=1,nt=3"),
+    ("fp64 128x128 u16 no swizzle", "transpose_8192x8192_float64", 0x10, ""),
+    ("fp64 128x128 u16 chosen", "transpose_8192x8192_float64", 0, ""),
+    ("fp64 128x128 u16 k=3", "transpose_8192x8192_float64", 0, "xk=3,xs=0,xt=0,xcs=3,xcm=1"),
+    ("fp64 128x128 u16 k=2", "transpose_8192x8192_float64", 0, "xk=2,xs=0,xt=0,xcs=3,xcm=1"),
+    ("fp64 128x128 u16 k=1", "transpose_8192x8192_float64", 0, "xk=1,xs=0,xt=0,xcs=3,xcm=1"),
     ("16-byte 64x8 u16 no swizzle", "transpose_8192x8192_int4vec", 0x10, ""),
     ("SF 4x32x16 u4 LDS tile", "sf_transpose_65536x2x1x4x32_f32", 0x20, ""),
     ("fp32 64x64 u4 no swizzle", "transpose_16384x16384_float32", 0x10, _U4),

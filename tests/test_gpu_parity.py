@@ -207,7 +207,7 @@ def test_transpose_tall_tiles(eb, n, m):
 
 
 @pytest.mark.parametrize("eb,n,m,tile", [(1, 8320, 8320, (512, 256)), (2, 16448, 16392, (1024, 64)),
-                                          (8, 8208, 8208, (256, 64))])
+                                          (8, 8208, 8208, (128, 128))])
 def test_transpose_128k_tiles_ragged(eb, n, m, tile):
     """128 KiB tiles (one workgroup per CU), with partial tiles along both tile modes (destination
     columns on 128-byte lines: other pitches take the element-aligned plans' configuration)."""
