@@ -311,6 +311,13 @@ static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c)
     case 1:
       if (eR < 512 || eC < 256 || tiles(512, 256) < 512) return false;
       c->tile = 131072; c->threads = 512; c->trb = 512; c->cap = 2;  // 512 x 256
+      // XCD super-tiles of 16 row tiles by 2 column tiles: an XCD's 32 workgroups (one per CU)
+      // are one super-tile, and the chip runs 16 x 16 tiles at a time, whatever the extents.
+      // Against row tiles first: int8 16384^2 4.79 -> 5.37-5.43 TB/s, 16384 x 8192 4.70 -> 5.12,
+      // 32768 x 4096 4.41 -> 5.30, 4096 x 32768 5.28 -> 5.63-5.73, 12288^2 4.96 -> 5.27, 8192^2
+      // 5.32-5.34 -> 5.42-5.43 (8192 x 16384 level); 8 x 8, 8 x 4, 16 x 4 or 32 x 1 super-tiles
+      // were slower than 16 x 2 on 16384^2 and 8192^2
+      c->order = 2; c->ssr = 16; c->ssc = 2;
       return true;
     case 16:
       if (eR < 64 || eC < 8) return false;
@@ -340,6 +347,13 @@ static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c)
     default:
       return false;
   }
+}
+
+// log2 of a power of two (the next one up otherwise)
+static int ilog2(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
 }
 
 // The tile geometries of one configuration, in the candidate order of destination run length
@@ -392,6 +406,8 @@ static bool plan_with_cfg(const Plan& p, int flags, TuneCfg cfg, bool tile_pinne
     g.order = cfg.order;
     g.step = p.step;
     g.cap = std::max(cfg.cap, 0);
+    if (cfg.ssr > 0) g.lsr = ilog2(cfg.ssr);
+    if (cfg.ssc > 0) g.lsc = ilog2(cfg.ssc);
     if (unit < p.eb || unit < 4 || unit > p.vb) continue;
     const int ve = p.vb / p.eb;
     const int bmin = unit / p.eb;
@@ -493,12 +509,15 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     cands[ncand++] = t;
   }
   // 1-byte elements at vector alignment whose destination columns alone are off the lines: the
-  // tall 512 x 256 tiles with 2 loads in flight, plain stores and XCD super-tiles (int8 8176 x 8192
-  // 3.56-3.57 -> 4.02-4.08 TB/s; the odd and source-misaligned int8 copies ran slower on them)
+  // tall 512 x 256 tiles with 2 loads in flight, plain stores and XCD super-tiles of 16 x 2 tiles
+  // as in tall_cfg (int8 8176 x 8192 3.56-3.57 -> 4.02-4.08 TB/s with 8 x 8 super-tiles, 4.08-4.17
+  // with 16 x 2; 8160 x 8192 3.63-3.64 -> 4.10-4.16; the odd and source-misaligned int8 copies ran
+  // slower on these tiles)
   if (!pinned && !batched && line_cfg && p->eb == 1 && !p->unaligned && src_lines && p->step == 1 && R.e >= 512 &&
       C.e >= 256 && ceil_div(R.e, 512) * ceil_div(C.e, 256) * others >= 512) {
     TuneCfg t;
     t.tile = 131072; t.threads = 512; t.trb = 512; t.unit = 16; t.nt = 0; t.order = 2; t.cap = 2;
+    t.ssr = 16; t.ssc = 2;
     cands[ncand++] = t;
   }
   cands[ncand++] = base;
@@ -509,11 +528,10 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   // Row tiles first with source rows off the lines: neighbouring column tiles read the same lines.
   // They are tilesR workgroups apart, so the grid pads tilesR to a multiple of kXcds and puts them
   // on one XCD (bf16 16448 x 16392 3.48 -> 4.3 TB/s, fp32 16416 x 16400 5.07 -> 5.4).
-  auto lg2 = [](int v) { int l = 0; while ((1 << l) < v) ++l; return l; };
   auto with_phase_order = [&](TileGeom g) {
     g.pad_rows = g.order == 1 && !src_lines;
-    if (ov.ssr > 0) g.lsr = lg2(ov.ssr);
-    if (ov.ssc > 0) g.lsc = lg2(ov.ssc);
+    if (ov.ssr > 0) g.lsr = ilog2(ov.ssr);
+    if (ov.ssc > 0) g.lsc = ilog2(ov.ssc);
     g.wave_local = ov.wl != 0 && tile_wave_local(g) &&
                    launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, true, true, g.cap},
                                     nullptr, 0, nullptr);
