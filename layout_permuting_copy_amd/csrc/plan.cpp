@@ -503,9 +503,27 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   // 2-byte elements there, read with unit stride: tall 512 x 64 tiles with plain stores in the XCD
   // super-tile order (fp16 8191 x 8190 3.86 -> 4.15 TB/s; with column tiles first such tiles had
   // been slower than 64 x 64 ones)
+  // Where the source rows are on the lines and only the destination is off them, with nontemporal
+  // accesses and 2 loads in flight (fp16 8191 x 8192 4.28-4.36 -> 4.55-4.57 TB/s, 16383 x 8192 4.66
+  // -> 5.05-5.06, 8190 x 8192 4.41 -> 4.80-4.81, 8191 x 16384 4.41 -> 4.60-4.61; with the source off
+  // the lines too they measured slower: 8191 x 8190 4.33 -> 3.84-3.86)
   if (!pinned && !batched && line_cfg && p->eb == 2 && p->step == 1 && R.e >= 512 && C.e >= 64) {
     TuneCfg t;
     t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 0; t.order = 2;
+    if (src_lines) { t.nt = 3; t.cap = 2; }
+    cands[ncand++] = t;
+  }
+  // 1-byte elements whose vectors are at element alignment only on the destination side (source
+  // rows on the lines): the tall 512 x 256 tiles of tall_cfg, nontemporal accesses, 2 loads in
+  // flight, 16 x 2 super-tiles (int8 8191 x 8192 3.64-3.66 -> 4.01-4.05 TB/s, 8191 x 16384 3.63 ->
+  // 3.97-3.98, 12287^2 3.37-3.39 -> 3.85, 8190 x 8192 3.53-3.59 -> 4.09-4.11, 16383 x 8192 level;
+  // a source off the lines makes these tiles slower than the small ones: 8191 x 8190 3.67 -> 2.70,
+  // 8192 x 8190 4.07 -> 3.30)
+  if (!pinned && !batched && p->unaligned && p->eb == 1 && src_lines && p->step == 1 && R.e >= 512 &&
+      C.e >= 256 && ceil_div(R.e, 512) * ceil_div(C.e, 256) * others >= 512) {
+    TuneCfg t;
+    t.tile = 131072; t.threads = 512; t.trb = 512; t.unit = 16; t.nt = 3; t.order = 2; t.cap = 2;
+    t.ssr = 16; t.ssc = 2;
     cands[ncand++] = t;
   }
   // 1-byte elements at vector alignment whose destination columns alone are off the lines: the

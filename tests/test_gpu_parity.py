@@ -173,6 +173,17 @@ def test_int8_tall_tiles_destination_off_the_lines(n, m):
     assert (p["tile_r"], p["tile_c"], p["loads_in_flight"], p["nontemporal"], p["grid_order"]) == (512, 256, 2, 0, 2), p
 
 
+@pytest.mark.parametrize("eb,n,m", [(1, 8191, 8192), (1, 8193, 8320), (2, 8191, 8192), (2, 1025, 256), (2, 2047, 4160)])
+def test_tall_tiles_destination_at_element_alignment(eb, n, m):
+    """Source rows on the 128-byte lines, destination columns at element alignment only (odd
+    destination pitch): int8 on the 512 x 256 tiles and fp16 on 512 x 64 tiles, both with
+    nontemporal accesses, 2 loads in flight and XCD super-tiles, ragged tiles along both modes."""
+    p = _check((n, m), (m, 1), (1, n), eb, seed=n + 7 * m + eb, expect="transpose")
+    want_tile = (512, 256) if eb == 1 else (512, 64)
+    assert p["unaligned"] and (p["tile_r"], p["tile_c"]) == want_tile, p
+    assert (p["loads_in_flight"], p["nontemporal"], p["grid_order"]) == (2, 3, 2), p
+
+
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("n,m,pitch,soff", [(40, 30, 60, 0), (129, 67, 140, 3), (64, 64, 128, 0), (33, 300, 601, 1),
                                             (7, 5, 11, 0), (300, 257, 515, 2)])

@@ -303,9 +303,10 @@ def test_interior_kernel_only_for_exact_tilings():
 
 
 def test_load_caps_of_the_tall_tiles():
-    """The tall tiles of 1- and 2-byte elements keep at most 2 loads in flight per lane (also int8
-    with only the destination off the cache lines); fp32, fp64, 16-byte elements and the
-    element-aligned plans keep all of them in flight (0)."""
+    """The tall tiles of 1- and 2-byte elements keep at most 2 loads in flight per lane (also where
+    only the destination is off the cache lines or at element alignment, the source rows on them);
+    fp32, fp64, 16-byte elements and the plans with the source at element alignment keep all of
+    them in flight (0)."""
     def cap(shape, ss, ds, dt):
         p = L.tc_plan((shape, ss), (shape, ds), dt)
         assert p["path_name"] == "transpose", p
@@ -318,7 +319,8 @@ def test_load_caps_of_the_tall_tiles():
     assert cap((8192, 8192), (8192, 1), (1, 8192), L.TC_B128) == 0
     assert cap((8191, 8190), (8190, 1), (1, 8191), L.TC_F16) == 0        # element-aligned vectors
     assert cap((8176, 8192), (8192, 1), (1, 8176), L.TC_U8) == 2         # int8, destination off the lines
-    assert cap((8191, 8192), (8192, 1), (1, 8191), L.TC_U8) == 0         # int8 at element alignment
+    assert cap((8191, 8192), (8192, 1), (1, 8191), L.TC_U8) == 2         # int8, destination at element alignment
+    assert cap((8191, 8190), (8190, 1), (1, 8191), L.TC_U8) == 0         # int8, both sides at element alignment
     assert cap((8192, 4096), (4096, 1), (1, 8192), L.TC_F64) == 0
 
 
