@@ -157,8 +157,9 @@ typedef struct tc_plan_info {
   int32_t xor_k, xor_shift, xor_mask, xor_tbit;
   int32_t xor_cshift, xor_cmask;
   int32_t grid_order;       /* transpose grid: 0 column tiles fastest, 1 row tiles fastest, 2 super-tiles
-                               of 8 x 8 tiles, each on one XCD (workgroup i runs on XCD i mod 8);
-                               rows path: 0 destination order, 1 the outer modes in source order */
+                               of super_rows x super_cols tiles, each on one XCD (workgroup i runs on
+                               XCD i mod 8); rows path: 0 destination order, 1 the outer modes in
+                               source order */
   int32_t nontemporal;      /* nontemporal global accesses: bit 0 loads, bit 1 stores */
   int32_t unaligned;        /* 1: declined split run by the transpose kernel with 16-byte vectors at
                                element alignment and element accesses at the edges of the copy */
@@ -172,6 +173,8 @@ typedef struct tc_plan_info {
                                interior-only kernel runs */
   int32_t loads_in_flight;  /* transpose: most global loads a lane keeps outstanding in the load
                                phase (a wait after each load beyond them); 0 = all at once */
+  int32_t super_rows, super_cols; /* grid_order 2: super-tile extents in row and column tiles;
+                                     0 otherwise */
   int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
   char reason[192];         /* why the fast path was declined ("" if it was not) */
 } tc_plan_info;
@@ -234,7 +237,8 @@ int tc_get_flags(void);
  *                              bit, column shift, column mask) forced onto the
  *                              chosen tile, conflict-free or not
  *   ssr, ssc                   grid order 2: super-tile extents in tiles
- *                              (powers of two; 8 x 8 by default)
+ *                              (powers of two; the plan's own by default:
+ *                              16 x 2 on the int8 tall tiles, else 8 x 8)
  * Every setting gives the same bytes.  A setting no compiled kernel instance
  * matches makes the copy fail with TC_E_ARG ("internal: no tile geometry");
  * unknown keys are ignored.  Unset, the planner's own choices apply.

@@ -69,8 +69,11 @@ class TcPlanInfo(ctypes.Structure):
                 ("mode_c", ctypes.c_int32), ("mode_b", ctypes.c_int32), ("tile_r", ctypes.c_int32),
                 ("tile_c", ctypes.c_int32), ("tile_b", ctypes.c_int32), ("workgroups", ctypes.c_int64),
                 ("lds_bytes", ctypes.c_int32), ("xor_k", ctypes.c_int32), ("xor_shift", ctypes.c_int32),
-                ("xor_mask", ctypes.c_int32), ("xor_tbit", ctypes.c_int32), ("xor_cshift", ctypes.c_int32), ("xor_cmask", ctypes.c_int32), ("grid_order", ctypes.c_int32), ("nontemporal", ctypes.c_int32), ("unaligned", ctypes.c_int32), ("src_step", ctypes.c_int32), ("wave_local", ctypes.c_int32), ("lds_write_bytes", ctypes.c_int32),
-                ("lds_read_bytes", ctypes.c_int32), ("edge_tiles", ctypes.c_int32), ("loads_in_flight", ctypes.c_int32),
+                ("xor_mask", ctypes.c_int32), ("xor_tbit", ctypes.c_int32), ("xor_cshift", ctypes.c_int32),
+                ("xor_cmask", ctypes.c_int32), ("grid_order", ctypes.c_int32), ("nontemporal", ctypes.c_int32),
+                ("unaligned", ctypes.c_int32), ("src_step", ctypes.c_int32), ("wave_local", ctypes.c_int32),
+                ("lds_write_bytes", ctypes.c_int32), ("lds_read_bytes", ctypes.c_int32), ("edge_tiles", ctypes.c_int32),
+                ("loads_in_flight", ctypes.c_int32), ("super_rows", ctypes.c_int32), ("super_cols", ctypes.c_int32),
                 ("write_conflicts", ctypes.c_int64),
                 ("read_conflicts", ctypes.c_int64), ("reason", ctypes.c_char * 192)]
 

@@ -273,8 +273,9 @@ __device__ __forceinline__ uint32_t udiv(uint32_t n, const Div32& d) {
 }
 
 // Tile `tile` of the grid: column tiles fastest, then row tiles (or the other way round when
-// a.order is 1; XCD super-tiles when it is 2), then batch tiles, then the remaining grid modes (innermost last).  Returns the
-// tile's first element on both sides and how much of each tile extent lies inside the copy.
+// a.order is 1; XCD super-tiles of 2^lsr x 2^lsc tiles when it is 2), then batch tiles, then the
+// remaining grid modes (innermost last).  Returns the tile's first element on both sides and how
+// much of each tile extent lies inside the copy.
 struct TileAt {
   int64_t sbase, dbase;
   int64_t remR, remC, remB;
@@ -285,7 +286,7 @@ __device__ __forceinline__ TileAt tile_at(const TransposeArgs& a, uint32_t tile)
   uint32_t idx = tile, q, tcI, trI;
   bool valid = true;
   if (a.order == 2) {
-    // XCD x = idx % kXcds takes super-tiles x, x + kXcds, ..; the kSuper^2 tiles of a super-tile
+    // XCD x = idx % kXcds takes super-tiles x, x + kXcds, ..; the 2^(lsr + lsc) tiles of a super-tile
     // are consecutive in that XCD's share of the grid, column tiles fastest inside it
     const uint32_t x = idx % kXcds, k = idx / kXcds;
     const uint32_t per = 1u << (a.lsr + a.lsc);  // tiles per super-tile

@@ -1006,6 +1006,8 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
     info->lds_read_bytes = p.g.rw;
     info->edge_tiles = p.g.edges ? 1 : 0;
     info->loads_in_flight = p.g.cap;
+    info->super_rows = p.g.order == 2 ? 1 << p.g.lsr : 0;
+    info->super_cols = p.g.order == 2 ? 1 << p.g.lsc : 0;
     info->write_conflicts = p.wconf;
     info->read_conflicts = p.rconf;
   }

@@ -229,8 +229,9 @@ int set_last_error(int code, const std::string& why);
 int wave_permute_plan(const tc_layout& src, const tc_layout& dst, int dtype, tc_permute_info* out, std::string* err);
 
 // A transpose kernel configuration: vector bytes, LDS unit bytes, tile bytes, threads,
-// nontemporal mode, source step and wave-local phase ordering.  One launcher per element width holds the instances it was built with: it
-// launches `ta` on `stream`, or with ta == nullptr only reports whether the instance exists.
+// nontemporal mode, source step, wave-local phase ordering, edge code and load cap.  One launcher
+// per element width holds the instances it was built with: it launches `ta` on `stream`, or with
+// ta == nullptr only reports whether the instance exists.
 struct TransposeCfg {
   int vb, unit, tile, threads, ntm, step;
   bool wave_local;

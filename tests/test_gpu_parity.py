@@ -162,6 +162,7 @@ def test_transpose_xcd_super_tiles(eb, shape):
         ss, ds = (n * m,) + ss, (n * m,) + ds
     p = _check(shape, ss, ds, eb, seed=n * 3 + m + eb, expect="transpose")
     assert p["unaligned"] and p["grid_order"] == 2, p
+    assert (p["super_rows"], p["super_cols"]) == (8, 8), p
 
 
 @pytest.mark.parametrize("n,m", [(8176, 8192), (16368, 4224)])
@@ -171,6 +172,7 @@ def test_int8_tall_tiles_destination_off_the_lines(n, m):
     the second shape)."""
     p = _check((n, m), (m, 1), (1, n), 1, seed=n + m, expect="transpose")
     assert (p["tile_r"], p["tile_c"], p["loads_in_flight"], p["nontemporal"], p["grid_order"]) == (512, 256, 2, 0, 2), p
+    assert (p["super_rows"], p["super_cols"]) == (16, 2), p
 
 
 @pytest.mark.parametrize("eb,n,m", [(1, 8191, 8192), (1, 8193, 8320), (2, 8191, 8192), (2, 1025, 256), (2, 2047, 4160)])
@@ -182,6 +184,8 @@ def test_tall_tiles_destination_at_element_alignment(eb, n, m):
     want_tile = (512, 256) if eb == 1 else (512, 64)
     assert p["unaligned"] and (p["tile_r"], p["tile_c"]) == want_tile, p
     assert (p["loads_in_flight"], p["nontemporal"], p["grid_order"]) == (2, 3, 2), p
+    if eb == 1:
+        assert (p["super_rows"], p["super_cols"]) == (16, 2), p
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])

@@ -324,6 +324,23 @@ def test_load_caps_of_the_tall_tiles():
     assert cap((8192, 4096), (4096, 1), (1, 8192), L.TC_F64) == 0
 
 
+def test_super_tile_extents():
+    """The XCD super-tile extents the plans report: 16 x 2 tiles for the int8 tall tiles (aligned,
+    destination off the lines, destination at element alignment), 8 x 8 for the element-aligned
+    int8 and fp64 plans; 0 x 0 where the grid is not in super-tile order."""
+    def sup(shape, ss, ds, dt):
+        p = L.tc_plan((shape, ss), (shape, ds), dt)
+        return p["grid_order"], p["super_rows"], p["super_cols"]
+    assert sup((8192, 8192), (8192, 1), (1, 8192), L.TC_I8) == (2, 16, 2)
+    assert sup((16384, 16384), (16384, 1), (1, 16384), L.TC_I8) == (2, 16, 2)
+    assert sup((8176, 8192), (8192, 1), (1, 8176), L.TC_U8) == (2, 16, 2)
+    assert sup((8191, 8192), (8192, 1), (1, 8191), L.TC_U8) == (2, 16, 2)
+    assert sup((8191, 8190), (8190, 1), (1, 8191), L.TC_U8) == (2, 8, 8)
+    assert sup((8191, 8190), (8190, 1), (1, 8191), L.TC_F64) == (2, 8, 8)
+    assert sup((16384, 16384), (16384, 1), (1, 16384), L.TC_F32) == (1, 0, 0)
+    assert sup((8192, 8192), (8192, 1), (1, 8192), L.TC_F16) == (1, 0, 0)
+
+
 def test_permuted_rows_walk_the_source_order():
     """Rows shorter than 1 KiB whose outer modes are ordered differently on the two sides run in
     source order with 2 vectors per lane (grid_order 1); longer rows, and copies whose sides agree,
