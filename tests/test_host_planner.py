@@ -508,3 +508,59 @@ def test_planning_is_thread_safe():
         for _ in range(3):
             got = list(ex.map(cached, [cases[i] for i in ok]))
             assert got == [serial[i] for i in ok]
+
+
+# layouts planned cold from several threads at once (shapes no other test plans, so that the swizzle
+# search and its memo are exercised concurrently), with strict-mode declines and argument errors
+_THREAD_CASES = [
+    (((1000 + 64 * k, 960 + 32 * k), (960 + 32 * k, 1)), ((1000 + 64 * k, 960 + 32 * k), (1, 1000 + 64 * k)), dt, fl)
+    for k in range(6) for dt, fl in ((L.TC_I8, 0), (L.TC_F16, 0), (L.TC_F32, 0), (L.TC_F64, 0), (L.TC_B128, 0))
+] + [
+    (((1001, 37), (37, 1)), ((1001, 37), (1, 1001)), L.TC_F32, L.TC_FLAG_STRICT),   # declined: count % 64
+    (((64, 32), (32, 1)), ((64, 33), (1, 64)), L.TC_F32, 0),                       # extents differ
+    (((8, 4, 2), (8, 2, 1)), ((8, 4, 2), (1, 8, 32)), L.TC_BF16, L.TC_FLAG_STRICT),
+]
+
+
+def _plan_cases_json(cases):
+    out = []
+    for s, d, dt, fl in cases:
+        p = L.tc_plan(s, d, dt, flags=fl, raise_on_error=False)
+        out.append({k: (list(v) if isinstance(v, (list, tuple)) else v) for k, v in p.items()})
+    return out
+
+
+def test_planner_is_thread_safe():
+    """tc_plan from 8 threads at once (ctypes releases the GIL during the call), on a cold plan
+    cache: every result, including the reason of each decline or error (thread-local, read back by
+    the same thread), equals the one a separate process computes sequentially."""
+    import json
+    import sys
+    import threading
+    code = ("import json, sys; sys.path.insert(0, %r); sys.path.insert(0, %r)\n"
+            "import test_host_planner as T\nprint(json.dumps(T._plan_cases_json(T._THREAD_CASES)))\n"
+            % (ROOT, os.path.join(ROOT, "tests")))
+    want = json.loads(subprocess.check_output([sys.executable, "-c", code], cwd=ROOT, text=True))
+    got, errors = {}, []
+
+    def worker(t):
+        try:
+            order = list(range(len(_THREAD_CASES)))
+            order = order[t:] + order[:t]  # each thread starts at a different case
+            for _ in range(3):
+                for i in order:
+                    r = _plan_cases_json([_THREAD_CASES[i]])[0]
+                    if r != want[i]:
+                        errors.append((t, i, r, want[i]))
+                    got[(t, i)] = r
+        except Exception as e:  # surfaced below
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors[:3]
+    assert len(got) == 8 * len(_THREAD_CASES)
+    assert any(w["status"] == L.TC_E_DECLINED for w in want) and any(w["status"] == L.TC_E_EXTENT for w in want)
