@@ -492,7 +492,8 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   base.trb = ov.trb;
   base.unit = ov.unit;
   // candidate configurations: the tall tile where it pays (not under TC_TUNE), then the default
-  TuneCfg cands[3];
+  // (at most one of the rules below applies to a copy; room for all of them)
+  TuneCfg cands[5];
   int ncand = 0;
   TuneCfg tall;
   const int64_t others = j.count / (R.e * C.e);
@@ -542,10 +543,10 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   if (flags & TC_FLAG_NO_SWIZZLE) ncand = 1;  // the swizzle is measured on the default plan's tile
   if (ov.cap >= 0)
     for (int i = 0; i < ncand; ++i) cands[i].cap = ov.cap;
-  // wave-local phases drop the workgroup barrier where the library holds such an instance
   // Row tiles first with source rows off the lines: neighbouring column tiles read the same lines.
   // They are tilesR workgroups apart, so the grid pads tilesR to a multiple of kXcds and puts them
-  // on one XCD (bf16 16448 x 16392 3.48 -> 4.3 TB/s, fp32 16416 x 16400 5.07 -> 5.4).
+  // on one XCD (bf16 16448 x 16392 3.48 -> 4.3 TB/s, fp32 16416 x 16400 5.07 -> 5.4).  Wave-local
+  // phases drop the workgroup barrier where the library holds such an instance.
   auto with_phase_order = [&](TileGeom g) {
     g.pad_rows = g.order == 1 && !src_lines;
     if (ov.ssr > 0) g.lsr = ilog2(ov.ssr);
