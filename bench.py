@@ -286,6 +286,13 @@ def time_tile_stream(torch, mode: int, steps: int = 30, seed: int = 23):
             "pct_peak_region": 100 * 2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "sampled_parity": ok}
 
 
+def device_props(torch) -> dict:
+    """The GPU the line was measured on (name, architecture, compute units, memory)."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "cus": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2 ** 30, 1)}
+
+
 def identity_workload(n: int = 1 << 28) -> SI.Workload:
     return SI.Workload(f"identity_{n}_float32", SI.Side((n,), (1,)), SI.Side((n,), (1,)), "float32", "bits", 12)
 
@@ -425,6 +432,7 @@ def main() -> int:
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w, host_src)
         line["cpu_baseline"]["value"] = round(line["cpu_baseline"]["value"], 3)
+    line["device"] = device_props(torch)
     if sweep:
         line["sweep"] = sweep
     print(json.dumps(line), flush=True)
