@@ -81,9 +81,10 @@ enum tc_status {
                               no vector of >= 4 bytes, or no conflict-free swizzle */
   TC_E_HIP = -9,           /* a HIP runtime call failed (launch or device query) */
   TC_E_RANGE = -10,        /* sizes beyond what the kernels index: a transpose of 2^31 tiles or
-                              more, or a row-wise copy one of whose outermost indices holds more
+                              more, a row-wise copy one of whose outermost indices holds more
                               than 2^30 vectors (copies of 2^31 vectors and more otherwise run
-                              as several launches on the stream) */
+                              as several launches on the stream), or an element count or element
+                              offset beyond 2^58 (checked before anything else is computed) */
   TC_E_ARG = -11           /* other invalid argument (bad slice, unknown flag) */
 };
 

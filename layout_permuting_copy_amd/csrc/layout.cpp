@@ -9,6 +9,7 @@
 // modes, orders modes by stride, and merges neighbours that are contiguous on both sides;
 // the merged form is what the partition planner splits into [outer, threads, vec].
 #include <algorithm>
+#include <cstdint>
 #include <cstdlib>
 #include <unordered_set>
 #include <vector>
@@ -40,6 +41,27 @@ int make_joint(const tc_layout& src, const tc_layout& dst, Joint* out, std::stri
     for (int k = 0; k < nb; ++k) sb += (k ? "," : "") + std::to_string(b[k].e);
     *err = "extent mismatch: non-unit extents (" + sa + ") vs (" + sb + ")";
     return TC_E_EXTENT;
+  }
+  // Sizes a 64-bit address computation holds: the element count and every element offset of
+  // both sides (offset plus the extreme index sums) within 2^58, so that byte offsets of 16-byte
+  // elements stay below 2^62.  Products and sums in 128 bits, so nothing wraps before the check.
+  bool empty = false;
+  for (int k = 0; k < na; ++k) empty = empty || a[k].e == 0;
+  if (!empty) {
+    constexpr __int128 kLim = __int128(1) << 58;
+    __int128 cnt = 1, slo = src.offset, shi = src.offset, dlo = dst.offset, dhi = dst.offset;
+    bool fits = true;
+    for (int k = 0; k < na && fits; ++k) {
+      cnt *= a[k].e;
+      const __int128 ss = __int128(a[k].e - 1) * a[k].s, ds = __int128(a[k].e - 1) * b[k].d;
+      if (ss < 0) slo += ss; else shi += ss;
+      if (ds < 0) dlo += ds; else dhi += ds;
+      fits = cnt <= kLim && slo >= -kLim && shi <= kLim && dlo >= -kLim && dhi <= kLim;
+    }
+    if (!fits) {
+      *err = "element count or element offsets beyond 2^58 (64-bit byte addresses would overflow)";
+      return TC_E_RANGE;
+    }
   }
   Joint j;
   j.rank = na;
@@ -124,6 +146,7 @@ int slice_layout(const tc_layout& in, const int64_t* start, const int64_t* stop,
     const int64_t len = in.shape[k];
     const int64_t st = step[k];
     if (st == 0) { *err = "slice step must not be zero"; return TC_E_ARG; }
+    if (st == INT64_MIN) { *err = "slice step out of range"; return TC_E_RANGE; }
     if (len < 0) { *err = "negative extent"; return TC_E_EXTENT; }
     int64_t b = start[k], e = stop[k], n;
     if (st > 0) {
@@ -131,17 +154,24 @@ int slice_layout(const tc_layout& in, const int64_t* start, const int64_t* stop,
       if (e < 0) e += len;
       b = std::min(std::max<int64_t>(b, 0), len);
       e = std::min(std::max<int64_t>(e, 0), len);
-      n = e > b ? (e - b + st - 1) / st : 0;
+      n = e > b ? (e - b - 1) / st + 1 : 0;
     } else {
       if (b < 0) b += len;
       if (e < 0) e += len;
       b = std::min(std::max<int64_t>(b, -1), len - 1);
       e = std::min(std::max<int64_t>(e, -1), len - 1);
-      n = b > e ? (b - e + (-st) - 1) / (-st) : 0;
+      n = b > e ? (b - e - 1) / (-st) + 1 : 0;
     }
-    if (n > 0) o.offset += b * in.stride[k];
+    // offset and stride in 128 bits; a result that does not fit 64 bits is an error
+    const __int128 off = __int128(o.offset) + (n > 0 ? __int128(b) * in.stride[k] : 0);
+    const __int128 str = __int128(in.stride[k]) * st;
+    if (off > INT64_MAX || off < INT64_MIN || str > INT64_MAX || str < INT64_MIN) {
+      *err = "sliced offset or stride beyond 64 bits";
+      return TC_E_RANGE;
+    }
+    o.offset = int64_t(off);
     o.shape[k] = n;
-    o.stride[k] = in.stride[k] * st;
+    o.stride[k] = int64_t(str);
   }
   *out = o;
   return TC_OK;

@@ -564,3 +564,43 @@ def test_planner_is_thread_safe():
     assert not errors, errors[:3]
     assert len(got) == 8 * len(_THREAD_CASES)
     assert any(w["status"] == L.TC_E_DECLINED for w in want) and any(w["status"] == L.TC_E_EXTENT for w in want)
+
+
+def test_sizes_beyond_64_bit_addresses_are_rejected():
+    """Element counts or element offsets beyond 2^58 (byte offsets of 16-byte elements would pass
+    2^62) are TC_E_RANGE before any planning, rather than wrapping around: a 2^80-element copy
+    must not read as empty, nor a stride of 2^62 as a small one."""
+    big = [
+        (((1 << 40, 1 << 40), (1 << 40, 1)), ((1 << 40, 1 << 40), (1, 1 << 40))),  # count 2^80
+        (((1 << 62,), (1,)), ((1 << 62,), (1,))),                                 # count 2^62
+        (((3, 1 << 61), (1 << 61, 1)), ((3, 1 << 61), (1, 3))),                    # offsets 2^62
+        (((4, 4), (1 << 62, 1)), ((4, 4), (4, 1))),                                 # source stride
+        (((4, 4), (4, 1), 1 << 59), ((4, 4), (4, 1))),                              # source offset
+        (((4, 4), (4, 1)), ((4, 4), (-(1 << 60), 1), 1 << 62)),                     # negative side
+    ]
+    for s, d in big:
+        p = L.tc_plan(s, d, L.TC_B128, raise_on_error=False)
+        assert p["status"] == L.TC_E_RANGE and "2^58" in p["error"], (s, d, p["status"], p["error"])
+    # the limit itself, and an empty copy with huge strides, are fine
+    ok = [(((1 << 29, 4), (4, 1)), ((1 << 29, 4), (4, 1))),
+          (((0, 1 << 62), (1 << 62, 1)), ((0, 1 << 62), (1, 0)))]
+    for s, d in ok:
+        assert L.tc_plan(s, d, L.TC_I8, raise_on_error=False)["status"] == L.TC_OK, (s, d)
+
+
+def test_slices_beyond_64_bits_are_rejected():
+    """tc_layout_slice computes offsets and strides without wrapping: results beyond 64 bits, and
+    the one step whose negation does not exist, are TC_E_RANGE; ordinary extreme steps still give
+    the Python slice lengths."""
+    lay = ((1 << 40,), (1 << 30,), 0)
+    with pytest.raises(L.TileCopyError) as e:
+        L.tc_layout_slice(lay, [0], [1 << 40], [1 << 40])      # stride 2^70
+    assert e.value.code == L.TC_E_RANGE
+    with pytest.raises(L.TileCopyError) as e:
+        L.tc_layout_slice(((10,), (1,), 0), [0], [10], [-(1 << 63)])
+    assert e.value.code == L.TC_E_RANGE
+    big = (1 << 63) - 1
+    out = L.tc_layout_slice(((10,), (1,), 0), [0], [10], [big])
+    assert (out.shape[0], out.stride[0], out.offset) == (len(range(0, 10, big)), big, 0)
+    out = L.tc_layout_slice(((10,), (1,), 0), [9], [-11], [-big])
+    assert (out.shape[0], out.offset) == (len(range(10)[9::-big]), 9)
