@@ -176,6 +176,9 @@ typedef struct tc_plan_info {
                                phase (a wait after each load beyond them); 0 = all at once */
   int32_t super_rows, super_cols; /* grid_order 2: super-tile extents in row and column tiles;
                                      0 otherwise */
+  int32_t src_view_bytes;   /* transpose: bytes the source elements are read as -- elem_bytes, or 2
+                               for 1-byte elements of a stride-2 source read in pairs (src_step 2),
+                               whose low bytes are stored */
   int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
   char reason[192];         /* why the fast path was declined ("" if it was not) */
 } tc_plan_info;

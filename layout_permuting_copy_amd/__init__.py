@@ -74,6 +74,7 @@ class TcPlanInfo(ctypes.Structure):
                 ("unaligned", ctypes.c_int32), ("src_step", ctypes.c_int32), ("wave_local", ctypes.c_int32),
                 ("lds_write_bytes", ctypes.c_int32), ("lds_read_bytes", ctypes.c_int32), ("edge_tiles", ctypes.c_int32),
                 ("loads_in_flight", ctypes.c_int32), ("super_rows", ctypes.c_int32), ("super_cols", ctypes.c_int32),
+                ("src_view_bytes", ctypes.c_int32),
                 ("write_conflicts", ctypes.c_int64),
                 ("read_conflicts", ctypes.c_int64), ("reason", ctypes.c_char * 192)]
 

@@ -150,6 +150,15 @@ __device__ __forceinline__ void gload_partial(const unsigned char* p, int n, uin
   }
 }
 
+// The first n (0 < n <= 8) 2-byte pairs of a 16-byte vector read as pairs of 1-byte elements (a
+// stride-2 source read in pairs), when the vector holds its row's last element: the first n - 1
+// pairs whole (in at most four accesses), then only the low byte of the last pair, so that no
+// byte past the row's last element is read; the other bytes of w are zero.
+__device__ __forceinline__ void gload_pairs_last(const unsigned char* p, int n, uint32_t* w) {
+  gload_partial<2, 16>(p, n - 1, w);  // (n - 1 == 0: nothing loaded, w zeroed)
+  put_bytes<16>(w, 2 * (n - 1), uint32_t(p[2 * (n - 1)]));
+}
+
 // A VB-byte vector of elements S apart in memory (S = 1 or 2).  S = 2: the 2*VB contiguous bytes
 // from p are loaded as two vectors and every other element kept (v_perm_b32 for 1- and 2-byte
 // elements, dword selection for wider ones); the caller guarantees that those bytes lie inside

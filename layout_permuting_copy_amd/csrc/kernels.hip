@@ -610,8 +610,17 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
         ta.nslices = ta.tilesB.d;
         for (int k = 0; k < ta.nbatch; ++k) ta.nslices *= ta.bdiv[k].d;
       }
+      if (p.nar) {
+        // the source read as 2-byte pairs: its offset and strides (even, checked by the planner)
+        // in pairs; the destination stays in bytes
+        ta.src_off /= 2;
+        ta.sR /= 2;
+        ta.sC /= 2;
+        ta.sB /= 2;
+        for (int k = 0; k < ta.nbatch; ++k) ta.bs[k] /= 2;
+      }
       const TransposeCfg cfg = transpose_cfg(p.g);
-      if (!launch_transpose(p.eb, cfg, &ta, p.workgroups, stream)) {
+      if (!launch_transpose(p.nar ? 2 : p.eb, cfg, &ta, p.workgroups, stream)) {
         *err = "no transpose kernel instance for this element width, vector width, tile size and thread count";
         return TC_E_ARG;
       }

@@ -100,6 +100,7 @@ struct TuneCfg {
   int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1, cap = -1, so = -1;
   int xk = -1, xs = 0, xt = 0, xcs = 0, xcm = 0;
   int ssr = 0, ssc = 0;  // order 2: super-tile extents in tiles (powers of two)
+  int nar = 0;           // 1: the narrowing configuration (set by the planner, not by TC_TUNE)
 };
 
 static TuneCfg tune_override() {
@@ -374,7 +375,8 @@ static bool plan_with_cfg(const Plan& p, int flags, TuneCfg cfg, bool tile_pinne
   // the same tile with 256 threads, else 16 KiB tiles of 256 threads (every vector width)
   const int unit0 = cfg.unit ? cfg.unit : unit_min;
   auto instance = [&](int tile, int threads) {
-    return launch_transpose(p.eb, TransposeCfg{p.vb, unit0, tile, threads, cfg.nt, p.step, false, true, std::max(cfg.cap, 0)},
+    return launch_transpose(p.eb, TransposeCfg{p.vb, unit0, tile, threads, cfg.nt, p.step, false, true, std::max(cfg.cap, 0),
+                                               cfg.nar > 0},
                             nullptr, 0, nullptr);
   };
   if (!instance(cfg.tile, cfg.threads)) {
@@ -406,6 +408,7 @@ static bool plan_with_cfg(const Plan& p, int flags, TuneCfg cfg, bool tile_pinne
     g.order = cfg.order;
     g.step = p.step;
     g.cap = std::max(cfg.cap, 0);
+    g.nar = cfg.nar > 0;
     if (cfg.ssr > 0) g.lsr = ilog2(cfg.ssr);
     if (cfg.ssc > 0) g.lsc = ilog2(cfg.ssc);
     if (unit < p.eb || unit < 4 || unit > p.vb) continue;
@@ -428,8 +431,8 @@ static bool plan_with_cfg(const Plan& p, int flags, TuneCfg cfg, bool tile_pinne
     if (dup || nseen >= 64) continue;
     seen[nseen][0] = g.TR; seen[nseen][1] = g.TC; seen[nseen][2] = g.NB; seen[nseen][3] = g.U; ++nseen;
     if (!finish_geom(&g)) continue;
-    if (!launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, false, true, g.cap}, nullptr,
-                          0, nullptr))
+    if (!launch_transpose(g.eb, TransposeCfg{g.vb, g.U, g.tile_bytes, g.NT, g.ntm, g.step, false, true, g.cap, g.nar},
+                          nullptr, 0, nullptr))
       continue;
     TileGeom c;
     int64_t wc, rc;
@@ -462,6 +465,25 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   const Mode& C = j.m[p->mode_c];
   const bool batched = pow2ceil(R.e) * p->eb < 128;
   const TuneCfg ov = tune_override();
+  if (p->nar) {
+    // int8 with a stride-2 source read as 2-byte pairs (make_plan): the tall 512 x 64 tiles of
+    // 2-byte elements with nontemporal accesses, 2 loads in flight and super-tiles of 16 x 4
+    // tiles; the low byte of each pair is stored.  Measured on the 8192^2 slice [1:8191, 0:8190:2]
+    // against the stride-2 tile of 1-byte elements: 2.25-2.28 -> 2.75-2.76 TB/s (16 x 2, 32 x 2,
+    // 32 x 4, 16 x 8 and 8 x 8 super-tiles 2.53-2.63, row tiles first 2.44, 1024 x 64 tiles on
+    // 1024 lanes 2.47-2.66).  The same reading of a 2-byte source as 4-byte pairs measured slower
+    // than its own stride-2 tile (fp16 slice 2.80 against 2.19-2.50), so only 1-byte copies take it.
+    TuneCfg t;
+    t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 3; t.order = 2; t.cap = 2;
+    t.ssr = 16; t.ssc = 4; t.nar = 1;
+    TileGeom g;
+    int64_t wc, rc;
+    if (!plan_with_cfg(*p, flags, t, true, &g, &wc, &rc)) return false;
+    p->g = g;
+    p->wconf = wc;
+    p->rconf = rc;
+    return true;
+  }
   const bool pinned = ov.tile || ov.threads || ov.nt >= 0 || ov.order >= 0 || ov.trb || ov.unit;
   // 1-, 2- and 8-byte elements whose destination columns do not start on 128-byte lines (a
   // line-aligned base pointer assumed): the configurations of the element-aligned plans (plain
@@ -845,6 +867,59 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
   if (c2 < 0 || c2 == r)
     for (int k = 0; k < j.rank && (c2 < 0 || c2 == r); ++k)
       if (k != r && j.m[k].s == 2) c2 = k;
+  // 1-byte elements whose column mode has source stride 2, every other source stride and the
+  // source offset even, the source pointer 2-byte aligned: the source is read as 2-byte pairs (a
+  // dense 2-byte transpose of the pairs, on its tall tiles) and the low byte of each pair is
+  // stored.  Only bytes between the copy's first and last source byte are read: every pair ends
+  // before the row's next element, and the pair holding a row's last element is read as that one
+  // byte (the tiles holding it take the guarded code).
+  if (!forced_guarded && p.eb == 1 && r >= 0 && c2 >= 0 && r != c2 && j.m[c2].s == 2 && ptr_align >= 2 &&
+      j.so % 2 == 0 && j.m[r].e >= 512 && j.m[c2].e >= 64) {
+    bool even = true;
+    for (int k = 0; k < j.rank; ++k) even = even && j.m[k].s % 2 == 0;
+    if (even) {
+      Plan q = p;
+      q.eb = 2;
+      q.nar = true;
+      q.vb = 16;
+      q.unaligned = true;
+      q.step = 1;
+      q.j.so = j.so / 2;
+      for (int k = 0; k < j.rank; ++k) q.j.m[k].s = j.m[k].s / 2;
+      q.path = TC_PATH_TRANSPOSE;
+      q.mode_r = r;
+      q.mode_c = c2;
+      int b = -1;
+      for (int k = 0; k < j.rank; ++k) {
+        if (k == r || k == c2) continue;
+        if (b < 0 || std::llabs(j.m[k].s) + std::llabs(j.m[k].d) < std::llabs(j.m[b].s) + std::llabs(j.m[b].d)) b = k;
+      }
+      q.mode_b = b;
+      if (plan_transpose_tile(&q, flags & ~TC_FLAG_STRICT)) {
+        p.path = TC_PATH_TRANSPOSE;
+        p.nar = true;
+        p.g = q.g;
+        p.wconf = q.wconf;
+        p.rconf = q.rconf;
+        p.vb = 16;
+        p.unaligned = true;
+        p.step = 2;
+        p.mode_r = r;
+        p.mode_c = c2;
+        p.mode_b = b;
+        p.threads = p.g.NT;
+        p.load_outer = p.g.loads;
+        p.store_outer = p.g.stores;
+        p.lds_bytes = p.g.tile_bytes;
+        p.workgroups = transpose_workgroups(p, r, c2, b);
+        if (p.workgroups >= (int64_t(1) << 31)) {
+          p.status = TC_E_RANGE;
+          p.reason = "more than 2^31 workgroups";
+        }
+        return p;
+      }
+    }
+  }
   if (!forced_guarded && r >= 0 && c2 >= 0 && r != c2) {
     c = c2;
     p.vb = 16;
@@ -1007,6 +1082,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
     info->lds_read_bytes = p.g.rw;
     info->edge_tiles = p.g.edges ? 1 : 0;
     info->loads_in_flight = p.g.cap;
+    info->src_view_bytes = p.nar ? 2 : p.eb;
     info->super_rows = p.g.order == 2 ? 1 << p.g.lsr : 0;
     info->super_cols = p.g.order == 2 ? 1 << p.g.lsc : 0;
     info->write_conflicts = p.wconf;

@@ -46,7 +46,12 @@ struct TileRegs {
 // stride of the column mode (1, or 2: each vector is read as two contiguous ones, which stay
 // inside the allocation as long as the row's next element exists; the vector holding a row's
 // last element is loaded element by element).
-template <int EB, int VB, typename G, int NT, int NTM, int S, bool GUARD, int CAP = 0>
+//
+// NAR (EB = 2): the elements are 2-byte pairs of a 1-byte stride-2 source, of which the store
+// phase keeps the low bytes.  A pair must not be read whole where its high byte lies past the
+// row's last element: guarded tiles read the vector holding it with gload_pairs_last, and tiles
+// holding a row's last element always take the guarded code (see transpose_kernel).
+template <int EB, int VB, typename G, int NT, int NTM, int S, bool GUARD, int CAP = 0, bool NAR = false>
 __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& t, TileRegs<G>& r) {
   const int lTRu = a.lTR - G::LB;
   const int lnCV = a.lTC - G::LVE;  // load vectors per unit-row
@@ -70,9 +75,13 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
 #pragma unroll
       for (int i = 0; i < G::B; ++i) {
         const bool in_row = in_b && (int64_t(ru) << G::LB) + i < t.remR && cols > 0;
-        const bool whole = S == 1 ? cols >= G::VE : cols > G::VE;
-        if (in_row && whole) gload_step<EB, VB, S, NTM>(p + i * sR * EB, r.w[f][i]);
-        else if (in_row) gload_partial<EB, VB, S>(p + i * sR * EB, int(cols < G::VE ? cols : G::VE), r.w[f][i]);
+        const bool whole = S == 1 && !NAR ? cols >= G::VE : cols > G::VE;
+        if (in_row && whole) {
+          gload_step<EB, VB, S, NTM>(p + i * sR * EB, r.w[f][i]);
+        } else if (in_row) {
+          if constexpr (NAR) gload_pairs_last(p + i * sR * EB, int(cols < G::VE ? cols : G::VE), r.w[f][i]);
+          else gload_partial<EB, VB, S>(p + i * sR * EB, int(cols < G::VE ? cols : G::VE), r.w[f][i]);
+        }
       }
     } else {
 #pragma unroll
@@ -154,8 +163,9 @@ __device__ __forceinline__ void write_lds(const TransposeArgs& a, unsigned char*
 }
 
 // LDS -> registers (all reads first), then registers -> global.  GUARD skips stores of
-// positions outside the copy.
-template <int EB, int VB, int U, typename G, int NT, int NTM, bool GUARD>
+// positions outside the copy.  NAR: each 16-byte vector of 2-byte pairs is stored as the 8 low
+// bytes, the destination addressed in bytes.
+template <int EB, int VB, int U, typename G, int NT, int NTM, bool GUARD, bool NAR = false>
 __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt& t,
                                            const unsigned char* __restrict__ lds) {
   const int lTRu = a.lTR - G::LB;
@@ -184,6 +194,20 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
     const int rv = acc & ((1 << lnRV) - 1);
     const int c = (acc >> lnRV) & (TC - 1);
     const int nb = acc >> (lnRV + a.lTC);
+    if constexpr (NAR) {
+      static_assert(EB == 2 && VB == 16, "pairs of 1-byte elements in 16-byte vectors");
+      unsigned char* p = a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB)));
+      const uint32_t lo[2] = {perm(out[f][1], out[f][0], 0x06040200u), perm(out[f][3], out[f][2], 0x06040200u)};
+      if constexpr (GUARD) {
+        const int64_t rows = t.remR - (int64_t(rv) << (G::LRPV + G::LB));
+        const bool ok = nb < NB && nb < t.remB && c < t.remC && rows > 0;
+        if (ok && rows >= G::VE) gstore<8, NTM>(p, lo);
+        else if (ok) gstore_partial<1, 8>(p, int(rows), lo);
+      } else {
+        gstore<8, NTM>(p, lo);
+      }
+      continue;
+    }
     unsigned char* p = a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB))) * EB;
     if constexpr (GUARD) {
       // whole vectors as one store, vectors reaching past the row extent element by element
@@ -209,32 +233,36 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
 //
 // CAP > 0: the interior load phase keeps at most CAP loads of a lane outstanding (measured faster
 // than all at once for the tall tiles of 1- and 2-byte elements).
-template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL, bool EDGE = true, int CAP = 0>
+//
+// NAR: 2-byte pairs of a 1-byte stride-2 source, the low bytes stored (load_tile, read_store).
+template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL, bool EDGE = true, int CAP = 0,
+          bool NAR = false>
 __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   typedef Geo<EB, VB, U, TILE, NT> G;
   __shared__ __attribute__((aligned(16))) unsigned char lds[TILE];
   const TileAt t = tile_at(a, blockIdx.x);
   if (!t.valid) return;  // padding of the XCD super-tile order (whole workgroup, before any barrier)
   TileRegs<G> r;
-  const bool full = !EDGE || (tile_full(a, t) && (S == 1 || t.remC > (int64_t(1) << a.lTC)));
-  if constexpr (!EDGE) load_tile<EB, VB, G, NT, NTM, S, false, CAP>(a, t, r);
-  else if (full) load_tile<EB, VB, G, NT, NTM, S, false, CAP>(a, t, r);
-  else load_tile<EB, VB, G, NT, NTM, S, true>(a, t, r);
+  const bool full = !EDGE || (tile_full(a, t) && ((S == 1 && !NAR) || t.remC > (int64_t(1) << a.lTC)));
+  if constexpr (!EDGE) load_tile<EB, VB, G, NT, NTM, S, false, CAP, NAR>(a, t, r);
+  else if (full) load_tile<EB, VB, G, NT, NTM, S, false, CAP, NAR>(a, t, r);
+  else load_tile<EB, VB, G, NT, NTM, S, true, 0, NAR>(a, t, r);
   write_lds<EB, VB, U, G, NT>(a, lds, r);
   if constexpr (WL) wave_lds_sync();
   else __syncthreads();
-  if constexpr (!EDGE) read_store<EB, VB, U, G, NT, NTM, false>(a, t, lds);
-  else if (full) read_store<EB, VB, U, G, NT, NTM, false>(a, t, lds);
-  else read_store<EB, VB, U, G, NT, NTM, true>(a, t, lds);
+  if constexpr (!EDGE) read_store<EB, VB, U, G, NT, NTM, false, NAR>(a, t, lds);
+  else if (full) read_store<EB, VB, U, G, NT, NTM, false, NAR>(a, t, lds);
+  else read_store<EB, VB, U, G, NT, NTM, true, NAR>(a, t, lds);
 }
 
 // Launches the instance (ta != nullptr) or only reports whether it exists (ta == nullptr).
-template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL = false, bool EDGE = true, int CAP = 0>
+template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL = false, bool EDGE = true, int CAP = 0,
+          bool NAR = false>
 bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
   if constexpr (Geo<EB, VB, U, TILE, NT>::valid) {
     if (ta)
-      hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM, S, WL, EDGE, CAP>), dim3(uint32_t(wgs)), dim3(NT), 0,
-                         s, *ta);
+      hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM, S, WL, EDGE, CAP, NAR>), dim3(uint32_t(wgs)), dim3(NT),
+                         0, s, *ta);
     return true;
   }
   return false;
@@ -253,6 +281,10 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);                                             \
     const int vb = c.vb, tile = c.tile, nt = c.threads, ntm = c.ntm;                                         \
     constexpr int U = EB < 4 ? 4 : EB;                                                                       \
+    if (c.nar) {                                                                                             \
+      TC_NAR_EB##EB                                                                                          \
+      return false;                                                                                          \
+    }                                                                                                        \
     if (c.cap != 0) {                                                                                        \
       TC_CAPS_EB##EB                                                                                         \
       return false;                                                                                          \
@@ -315,6 +347,19 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 #define TC_CAPS_EB4
 #define TC_CAPS_EB8
 #define TC_CAPS_EB16
+
+// 2-byte pairs of a 1-byte stride-2 source, low bytes stored (plan.cpp, make_plan): the tall
+// 512 x 64 tiles of 2-byte elements with nontemporal accesses and 2 loads in flight, with the edge
+// code (the tiles holding a row's last element always need it)
+#define TC_CFG_NAR(EB, TILE, NT, CAP)                                                                        \
+  if (c.cap == CAP && c.unit == 16 && vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local &&  \
+      ntm == 3 && c.edges)                                                                                   \
+    return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, true>(ta, wgs, s);
+#define TC_NAR_EB1
+#define TC_NAR_EB2 TC_CFG_NAR(2, 65536, 512, 2)
+#define TC_NAR_EB4
+#define TC_NAR_EB8
+#define TC_NAR_EB16
 
 #define TC_CFG_WL(EB, U, TILE, NT)                                                                           \
   if (vb == 16 && tile == TILE && nt == NT && c.step == 1 && ntm == 3 && c.wave_local)                       \

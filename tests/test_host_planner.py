@@ -604,3 +604,27 @@ def test_slices_beyond_64_bits_are_rejected():
     assert (out.shape[0], out.stride[0], out.offset) == (len(range(0, 10, big)), big, 0)
     out = L.tc_layout_slice(((10,), (1,), 0), [9], [-11], [-big])
     assert (out.shape[0], out.offset) == (len(range(10)[9::-big]), 9)
+
+
+def test_int8_stride2_sources_read_in_pairs():
+    """1-byte copies whose column mode has source stride 2 read the source as 2-byte pairs
+    (src_view_bytes 2) where the source offset and every source stride are even, the source
+    pointer is 2-byte aligned and the tile is at least 512 x 64; otherwise the stride-2 tile of
+    1-byte elements (src_view_bytes 1).  Wider elements never take it."""
+    n = 8192
+    R, C = n - 2, (n - 1) // 2
+
+    def plan(ss, so, dt=L.TC_I8, align=16, shape=(R, C)):
+        p = L.tc_plan((shape, ss, so), (shape, (1, shape[0])), dt, ptr_align=align)
+        assert p["path_name"] == "transpose" and p["src_step"] == 2, p
+        return p["src_view_bytes"], p["tile_r"], p["tile_c"], p["grid_order"], p["super_rows"], p["super_cols"]
+
+    assert plan((n, 2), n) == (2, 512, 64, 2, 16, 4)
+    assert plan((n, 2), n, dt=L.TC_U8) == (2, 512, 64, 2, 16, 4)
+    assert plan((n, 2), n + 1)[0] == 1            # odd source offset
+    assert plan((n + 1, 2), n)[0] == 1            # odd row stride
+    assert plan((n, 2), n, align=1)[0] == 1       # source pointer not 2-byte aligned
+    assert plan((n, 2), n, shape=(511, C))[0] == 1  # rows too few for the 512-row tile
+    assert plan((n, 2), n, shape=(R, 63))[0] == 1   # columns too few for the 64-column tile
+    assert plan((n, 2), n, dt=L.TC_F16)[0] == 2   # 2-byte elements: their own width
+    assert plan((n, 2), n, dt=L.TC_F16)[1:3] != (512, 64)
