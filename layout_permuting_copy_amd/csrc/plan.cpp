@@ -476,6 +476,14 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     TuneCfg t;
     t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 3; t.order = 2; t.cap = 2;
     t.ssr = 16; t.ssc = 4; t.nar = 1;
+    // (the tuning override's tile, threads, trb, order, cap and super-tile keys apply here too)
+    if (ov.tile) t.tile = ov.tile;
+    if (ov.threads) t.threads = ov.threads;
+    if (ov.trb) t.trb = ov.trb;
+    if (ov.order >= 0) t.order = ov.order;
+    if (ov.cap >= 0) t.cap = ov.cap;
+    if (ov.ssr > 0) t.ssr = ov.ssr;
+    if (ov.ssc > 0) t.ssc = ov.ssc;
     TileGeom g;
     int64_t wc, rc;
     if (!plan_with_cfg(*p, flags, t, true, &g, &wc, &rc)) return false;
