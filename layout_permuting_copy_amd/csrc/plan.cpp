@@ -476,8 +476,9 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     TuneCfg t;
     t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 3; t.order = 2; t.cap = 2;
     t.ssr = 16; t.ssc = 4; t.nar = 1;
-    // (the tuning override's tile, threads, trb, order, cap and super-tile keys apply here too)
+    // (the tuning override's tile, threads, trb, nt, order, cap and super-tile keys apply here too)
     if (ov.tile) t.tile = ov.tile;
+    if (ov.nt >= 0) t.nt = ov.nt;
     if (ov.threads) t.threads = ov.threads;
     if (ov.trb) t.trb = ov.trb;
     if (ov.order >= 0) t.order = ov.order;
