@@ -159,6 +159,20 @@ __device__ __forceinline__ void gload_pairs_last(const unsigned char* p, int n, 
   put_bytes<16>(w, 2 * (n - 1), uint32_t(p[2 * (n - 1)]));
 }
 
+// The same for a vector holding its row's first element when the high bytes are kept: the 16
+// bytes from the first kept byte (one access; they end before the row's ninth element, so rows
+// of more than 8 elements are read inside the copy), moved up one byte in the registers so that
+// the kept bytes sit in the high bytes of the pairs.  Nothing before the row's first element is
+// read.
+__device__ __forceinline__ void gload_pairs_first(const unsigned char* p, uint32_t* w) {
+  uint32_t t[4];
+  load_words<16>(p + 1, t);
+  w[0] = t[0] << 8;
+  w[1] = __builtin_amdgcn_alignbyte(t[1], t[0], 3);
+  w[2] = __builtin_amdgcn_alignbyte(t[2], t[1], 3);
+  w[3] = __builtin_amdgcn_alignbyte(t[3], t[2], 3);
+}
+
 // A VB-byte vector of elements S apart in memory (S = 1 or 2).  S = 2: the 2*VB contiguous bytes
 // from p are loaded as two vectors and every other element kept (v_perm_b32 for 1- and 2-byte
 // elements, dword selection for wider ones); the caller guarantees that those bytes lie inside

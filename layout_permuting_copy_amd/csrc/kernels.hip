@@ -611,9 +611,9 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
         for (int k = 0; k < ta.nbatch; ++k) ta.nslices *= ta.bdiv[k].d;
       }
       if (p.nar) {
-        // the source read as 2-byte pairs: its offset and strides (even, checked by the planner)
-        // in pairs; the destination stays in bytes
-        ta.src_off /= 2;
+        // the source read as 2-byte pairs: its offset (of the pair holding the first element) and
+        // strides (even, checked by the planner) in pairs; the destination stays in bytes
+        ta.src_off = (p.nar == 1 ? ta.src_off : ta.src_off - 1) / 2;
         ta.sR /= 2;
         ta.sC /= 2;
         ta.sB /= 2;

@@ -100,7 +100,7 @@ struct TuneCfg {
   int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1, cap = -1, so = -1;
   int xk = -1, xs = 0, xt = 0, xcs = 0, xcm = 0;
   int ssr = 0, ssc = 0;  // order 2: super-tile extents in tiles (powers of two)
-  int nar = 0;           // 1: the narrowing configuration (set by the planner, not by TC_TUNE)
+  int nar = 0;           // 1, 2: the pair-reading configuration (set by the planner, not by TC_TUNE)
 };
 
 static TuneCfg tune_override() {
@@ -376,7 +376,7 @@ static bool plan_with_cfg(const Plan& p, int flags, TuneCfg cfg, bool tile_pinne
   const int unit0 = cfg.unit ? cfg.unit : unit_min;
   auto instance = [&](int tile, int threads) {
     return launch_transpose(p.eb, TransposeCfg{p.vb, unit0, tile, threads, cfg.nt, p.step, false, true, std::max(cfg.cap, 0),
-                                               cfg.nar > 0},
+                                               cfg.nar},
                             nullptr, 0, nullptr);
   };
   if (!instance(cfg.tile, cfg.threads)) {
@@ -408,7 +408,7 @@ static bool plan_with_cfg(const Plan& p, int flags, TuneCfg cfg, bool tile_pinne
     g.order = cfg.order;
     g.step = p.step;
     g.cap = std::max(cfg.cap, 0);
-    g.nar = cfg.nar > 0;
+    g.nar = cfg.nar;
     if (cfg.ssr > 0) g.lsr = ilog2(cfg.ssr);
     if (cfg.ssc > 0) g.lsc = ilog2(cfg.ssc);
     if (unit < p.eb || unit < 4 || unit > p.vb) continue;
@@ -475,7 +475,7 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     // than its own stride-2 tile (fp16 slice 2.80 against 2.19-2.50), so only 1-byte copies take it.
     TuneCfg t;
     t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 3; t.order = 2; t.cap = 2;
-    t.ssr = 16; t.ssc = 4; t.nar = 1;
+    t.ssr = 16; t.ssc = 4; t.nar = p->nar;
     // (the tuning override's tile, threads, trb, nt, order, cap and super-tile keys apply here too)
     if (ov.tile) t.tile = ov.tile;
     if (ov.nt >= 0) t.nt = ov.nt;
@@ -876,24 +876,27 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
   if (c2 < 0 || c2 == r)
     for (int k = 0; k < j.rank && (c2 < 0 || c2 == r); ++k)
       if (k != r && j.m[k].s == 2) c2 = k;
-  // 1-byte elements whose column mode has source stride 2, every other source stride and the
-  // source offset even, the source pointer 2-byte aligned: the source is read as 2-byte pairs (a
-  // dense 2-byte transpose of the pairs, on its tall tiles) and the low byte of each pair is
-  // stored.  Only bytes between the copy's first and last source byte are read: every pair ends
-  // before the row's next element, and the pair holding a row's last element is read as that one
-  // byte (the tiles holding it take the guarded code).
+  // 1-byte elements whose column mode has source stride 2, every other source stride even, the
+  // source pointer 2-byte aligned: the source is read as 2-byte pairs (a dense 2-byte transpose
+  // of the pairs, on its tall tiles) and one byte of each pair is stored: the low byte where the
+  // source offset is even, the high byte where it is odd.  Only bytes between the copy's first
+  // and last source byte are read: with low bytes kept a pair ends before its row's next element
+  // and the pair holding a row's last element is read as that one byte; with high bytes kept a
+  // pair starts after the row's previous element and the pair holding a row's first element is
+  // read as that one byte (the tiles holding them take the guarded code).
   if (!forced_guarded && p.eb == 1 && r >= 0 && c2 >= 0 && r != c2 && j.m[c2].s == 2 && ptr_align >= 2 &&
-      j.so % 2 == 0 && j.m[r].e >= 512 && j.m[c2].e >= 64) {
+      j.m[r].e >= 512 && j.m[c2].e >= 64) {
     bool even = true;
     for (int k = 0; k < j.rank; ++k) even = even && j.m[k].s % 2 == 0;
     if (even) {
+      const int sel = j.so % 2 == 0 ? 1 : 2;  // (offsets may be negative: so % 2 is then -1)
       Plan q = p;
       q.eb = 2;
-      q.nar = true;
+      q.nar = sel;
       q.vb = 16;
       q.unaligned = true;
       q.step = 1;
-      q.j.so = j.so / 2;
+      q.j.so = (sel == 1 ? j.so : j.so - 1) / 2;  // the pair holding the first element (exact)
       for (int k = 0; k < j.rank; ++k) q.j.m[k].s = j.m[k].s / 2;
       q.path = TC_PATH_TRANSPOSE;
       q.mode_r = r;
@@ -906,7 +909,7 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
       q.mode_b = b;
       if (plan_transpose_tile(&q, flags & ~TC_FLAG_STRICT)) {
         p.path = TC_PATH_TRANSPOSE;
-        p.nar = true;
+        p.nar = sel;
         p.g = q.g;
         p.wconf = q.wconf;
         p.rconf = q.rconf;

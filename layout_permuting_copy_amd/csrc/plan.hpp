@@ -100,8 +100,8 @@ struct TileGeom {
   bool pad_rows = false;          // order 1 with source rows off the 128-byte lines: the row-tile
                                   // count of the grid is padded to a multiple of kXcds (tile_at)
   int cap = 0;                    // loads a lane keeps in flight in the interior load phase (0: all)
-  bool nar = false;               // 1-byte elements of a stride-2 source read in 2-byte pairs, the
-                                  // low byte of each pair stored (eb is then the pair's 2 bytes)
+  int nar = 0;                    // 1-byte elements of a stride-2 source read in 2-byte pairs (eb is
+                                  // then the pair's 2 bytes), the low (1) or high (2) byte stored
   int lsr = kSuperLog, lsc = kSuperLog;  // order 2: log2 of the super-tile extents in tiles
   int loads = 4, stores = 4;  // accesses per thread per phase
   int ww = 16, rw = 4;        // LDS write / read instruction bytes
@@ -137,9 +137,10 @@ struct Plan {
   bool unaligned = false;           // transpose or rows with vectors at element alignment (extents or strides
                                     // not multiples of the vector; edges element by element)
   int step = 1;                     // source stride of the transpose's column mode (1 or 2)
-  bool nar = false;                 // transpose of 1-byte elements whose column mode has source
+  int nar = 0;                      // transpose of 1-byte elements whose column mode has source
                                     // stride 2, read as 2-byte pairs (the tile planned for eb = 2,
-                                    // source strides and offset halved at launch); see make_plan
+                                    // source strides and offset halved at launch), of which the
+                                    // low (1: even offset) or high (2: odd offset) byte is kept
   int shuffle_c = 0;                // shuffle path: block columns C (8, 16 or 32; 4 rows); interleave
                                     // path: the channels (2, 3, 4 or 8)
   bool to_planes = false;           // interleave path: interleaved source, planar destination
@@ -242,7 +243,7 @@ struct TransposeCfg {
   bool wave_local;
   bool edges = true;  // false: every tile lies wholly inside the copy (the interior-only kernel)
   int cap = 0;        // loads in flight per lane in the load phase (0: all of them)
-  bool nar = false;   // source read in 2-byte pairs, low bytes stored (1-byte copies)
+  int nar = 0;        // source read in 2-byte pairs, low (1) or high (2) bytes stored
 };
 // The kernel configuration a planned tile geometry runs with (every field of it).
 inline TransposeCfg transpose_cfg(const TileGeom& g) {

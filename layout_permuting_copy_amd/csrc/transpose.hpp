@@ -48,10 +48,11 @@ struct TileRegs {
 // last element is loaded element by element).
 //
 // NAR (EB = 2): the elements are 2-byte pairs of a 1-byte stride-2 source, of which the store
-// phase keeps the low bytes.  A pair must not be read whole where its high byte lies past the
-// row's last element: guarded tiles read the vector holding it with gload_pairs_last, and tiles
-// holding a row's last element always take the guarded code (see transpose_kernel).
-template <int EB, int VB, typename G, int NT, int NTM, int S, bool GUARD, int CAP = 0, bool NAR = false>
+// phase keeps the low (NAR = 1) or high (NAR = 2) bytes.  A pair must not be read whole where its
+// other byte lies past the row's last element (1) or before its first (2): guarded tiles read the
+// vector holding it with gload_pairs_last / gload_pairs_first, and tiles holding a row's last (1)
+// or first (2) element always take the guarded code (see transpose_kernel).
+template <int EB, int VB, typename G, int NT, int NTM, int S, bool GUARD, int CAP = 0, int NAR = 0>
 __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& t, TileRegs<G>& r) {
   const int lTRu = a.lTR - G::LB;
   const int lnCV = a.lTC - G::LVE;  // load vectors per unit-row
@@ -75,12 +76,20 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
 #pragma unroll
       for (int i = 0; i < G::B; ++i) {
         const bool in_row = in_b && (int64_t(ru) << G::LB) + i < t.remR && cols > 0;
-        const bool whole = S == 1 && !NAR ? cols >= G::VE : cols > G::VE;
+        // (NAR = 2: the row's first vector is the first one of the first column tile)
+        const bool first = NAR == 2 && cv == 0 && t.remC == a.eC;
+        const bool whole = (S == 1 && NAR != 1 ? cols >= G::VE : cols > G::VE) && !first;
+        const int n = int(cols < G::VE ? cols : G::VE);
         if (in_row && whole) {
           gload_step<EB, VB, S, NTM>(p + i * sR * EB, r.w[f][i]);
         } else if (in_row) {
-          if constexpr (NAR) gload_pairs_last(p + i * sR * EB, int(cols < G::VE ? cols : G::VE), r.w[f][i]);
-          else gload_partial<EB, VB, S>(p + i * sR * EB, int(cols < G::VE ? cols : G::VE), r.w[f][i]);
+          if constexpr (NAR == 1) gload_pairs_last(p + i * sR * EB, n, r.w[f][i]);
+          else if constexpr (NAR == 2) {
+            if (first) gload_pairs_first(p + i * sR * EB, r.w[f][i]);
+            else gload_partial<EB, VB, S>(p + i * sR * EB, n, r.w[f][i]);
+          } else {
+            gload_partial<EB, VB, S>(p + i * sR * EB, n, r.w[f][i]);
+          }
         }
       }
     } else {
@@ -163,9 +172,9 @@ __device__ __forceinline__ void write_lds(const TransposeArgs& a, unsigned char*
 }
 
 // LDS -> registers (all reads first), then registers -> global.  GUARD skips stores of
-// positions outside the copy.  NAR: each 16-byte vector of 2-byte pairs is stored as the 8 low
-// bytes, the destination addressed in bytes.
-template <int EB, int VB, int U, typename G, int NT, int NTM, bool GUARD, bool NAR = false>
+// positions outside the copy.  NAR: each 16-byte vector of 2-byte pairs is stored as its 8 low
+// (1) or high (2) bytes, the destination addressed in bytes.
+template <int EB, int VB, int U, typename G, int NT, int NTM, bool GUARD, int NAR = 0>
 __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt& t,
                                            const unsigned char* __restrict__ lds) {
   const int lTRu = a.lTR - G::LB;
@@ -197,7 +206,8 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
     if constexpr (NAR) {
       static_assert(EB == 2 && VB == 16, "pairs of 1-byte elements in 16-byte vectors");
       unsigned char* p = a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB)));
-      const uint32_t lo[2] = {perm(out[f][1], out[f][0], 0x06040200u), perm(out[f][3], out[f][2], 0x06040200u)};
+      constexpr uint32_t kSel = NAR == 1 ? 0x06040200u : 0x07050301u;  // bytes 0, 2 or 1, 3 of each word
+      const uint32_t lo[2] = {perm(out[f][1], out[f][0], kSel), perm(out[f][3], out[f][2], kSel)};
       if constexpr (GUARD) {
         const int64_t rows = t.remR - (int64_t(rv) << (G::LRPV + G::LB));
         const bool ok = nb < NB && nb < t.remB && c < t.remC && rows > 0;
@@ -234,16 +244,19 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
 // CAP > 0: the interior load phase keeps at most CAP loads of a lane outstanding (measured faster
 // than all at once for the tall tiles of 1- and 2-byte elements).
 //
-// NAR: 2-byte pairs of a 1-byte stride-2 source, the low bytes stored (load_tile, read_store).
+// NAR: 2-byte pairs of a 1-byte stride-2 source, the low (1) or high (2) bytes stored
+// (load_tile, read_store).
 template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL, bool EDGE = true, int CAP = 0,
-          bool NAR = false>
+          int NAR = 0>
 __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   typedef Geo<EB, VB, U, TILE, NT> G;
   __shared__ __attribute__((aligned(16))) unsigned char lds[TILE];
   const TileAt t = tile_at(a, blockIdx.x);
   if (!t.valid) return;  // padding of the XCD super-tile order (whole workgroup, before any barrier)
   TileRegs<G> r;
-  const bool full = !EDGE || (tile_full(a, t) && ((S == 1 && !NAR) || t.remC > (int64_t(1) << a.lTC)));
+  // (tiles holding a row's last element: guarded for S = 2 and NAR = 1; its first: for NAR = 2)
+  const bool full = !EDGE || (tile_full(a, t) && ((S == 1 && NAR != 1) || t.remC > (int64_t(1) << a.lTC)) &&
+                              (NAR != 2 || t.remC < a.eC));
   if constexpr (!EDGE) load_tile<EB, VB, G, NT, NTM, S, false, CAP, NAR>(a, t, r);
   else if (full) load_tile<EB, VB, G, NT, NTM, S, false, CAP, NAR>(a, t, r);
   else load_tile<EB, VB, G, NT, NTM, S, true, 0, NAR>(a, t, r);
@@ -257,7 +270,7 @@ __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
 
 // Launches the instance (ta != nullptr) or only reports whether it exists (ta == nullptr).
 template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL = false, bool EDGE = true, int CAP = 0,
-          bool NAR = false>
+          int NAR = 0>
 bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
   if constexpr (Geo<EB, VB, U, TILE, NT>::valid) {
     if (ta)
@@ -353,8 +366,10 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 // code (the tiles holding a row's last element always need it)
 #define TC_CFG_NAR(EB, TILE, NT, CAP)                                                                        \
   if (c.cap == CAP && c.unit == 16 && vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local &&  \
-      ntm == 3 && c.edges)                                                                                   \
-    return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, true>(ta, wgs, s);
+      ntm == 3 && c.edges) {                                                                                 \
+    if (c.nar == 1) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 1>(ta, wgs, s); \
+    if (c.nar == 2) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 2>(ta, wgs, s); \
+  }
 #define TC_NAR_EB1
 #define TC_NAR_EB2 TC_CFG_NAR(2, 65536, 512, 2)
 #define TC_NAR_EB4

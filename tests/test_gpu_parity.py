@@ -195,21 +195,27 @@ def test_tall_tiles_destination_at_element_alignment(eb, n, m):
     ((2049, 4095), (8192, 2), 8192),      # the slice [1:2050, 0:8190:2] of an 8192-wide matrix
     ((3, 700, 130), (700 * 262, 262, 2), 4),  # a batch mode
     ((800, 90), (-184, 2), 799 * 184),    # rows in reverse order
+    ((600, 100), (256, 2), 1),            # odd offsets: the high bytes of the pairs kept
+    ((1001, 333), (1000, 2), 999),
+    ((512, 64), (128, 2), 3),
+    ((3, 700, 130), (700 * 262, 262, 2), 5),
+    ((800, 90), (-184, 2), 799 * 184 + 1),
 ])
 def test_int8_stride2_source_read_in_pairs(shape, strides, soff):
-    """1-byte copies whose column mode has source stride 2 (even offset and strides): the source is
-    read as 2-byte pairs on the tall 2-byte tiles and the low bytes stored; the pair holding a row's
-    last element is read as that byte only (the source buffer ends at the copy's last byte)."""
+    """1-byte copies whose column mode has source stride 2 (even strides): the source is read as
+    2-byte pairs on the tall 2-byte tiles and the low (even offset) or high (odd offset) bytes
+    stored; the pair holding a row's last (low) or first (high) element is read as that byte
+    only."""
     n, m = shape[-2], shape[-1]
     ds = (1, n) if len(shape) == 2 else (n * m, 1, n)
     p = _check(shape, strides, ds, 1, s_off=soff, seed=n + m + len(shape), expect="transpose")
     assert p["src_view_bytes"] == 2 and p["src_step"] == 2 and (p["tile_r"], p["tile_c"]) == (512, 64), p
 
 
-def test_int8_stride2_pairs_not_taken_at_odd_offsets():
-    """An odd source offset (the kept bytes would be the high bytes of the pairs) keeps the stride-2
+def test_int8_stride2_pairs_not_taken_at_odd_strides():
+    """An odd row stride (rows alternate between low and high bytes of the pairs) keeps the stride-2
     tile of 1-byte elements; same bytes."""
-    p = _check((700, 130), (262, 2), (1, 700), 1, s_off=5, seed=77, expect="transpose")
+    p = _check((700, 130), (261, 2), (1, 700), 1, s_off=4, seed=77, expect="transpose")
     assert p["src_view_bytes"] == 1 and p["src_step"] == 2, p
 
 

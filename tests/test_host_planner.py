@@ -608,9 +608,9 @@ def test_slices_beyond_64_bits_are_rejected():
 
 def test_int8_stride2_sources_read_in_pairs():
     """1-byte copies whose column mode has source stride 2 read the source as 2-byte pairs
-    (src_view_bytes 2) where the source offset and every source stride are even, the source
-    pointer is 2-byte aligned and the tile is at least 512 x 64; otherwise the stride-2 tile of
-    1-byte elements (src_view_bytes 1).  Wider elements never take it."""
+    (src_view_bytes 2) where every source stride is even (the offset's parity picks the low or
+    high byte), the source pointer is 2-byte aligned and the tile is at least 512 x 64; otherwise
+    the stride-2 tile of 1-byte elements (src_view_bytes 1).  Wider elements never take it."""
     n = 8192
     R, C = n - 2, (n - 1) // 2
 
@@ -621,7 +621,8 @@ def test_int8_stride2_sources_read_in_pairs():
 
     assert plan((n, 2), n) == (2, 512, 64, 2, 16, 4)
     assert plan((n, 2), n, dt=L.TC_U8) == (2, 512, 64, 2, 16, 4)
-    assert plan((n, 2), n + 1)[0] == 1            # odd source offset
+    assert plan((n, 2), n + 1)[0] == 2            # odd source offset: high bytes kept
+    assert plan((-n, 2), n * (R - 1) - 1)[0] == 2  # negative row stride, odd offset
     assert plan((n + 1, 2), n)[0] == 1            # odd row stride
     assert plan((n, 2), n, align=1)[0] == 1       # source pointer not 2-byte aligned
     assert plan((n, 2), n, shape=(511, C))[0] == 1  # rows too few for the 512-row tile
