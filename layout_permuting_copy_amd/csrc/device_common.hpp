@@ -159,18 +159,16 @@ __device__ __forceinline__ void gload_pairs_last(const unsigned char* p, int n, 
   put_bytes<16>(w, 2 * (n - 1), uint32_t(p[2 * (n - 1)]));
 }
 
-// The same for a vector holding its row's first element when the high bytes are kept: the 16
-// bytes from the first kept byte (one access; they end before the row's ninth element, so rows
-// of more than 8 elements are read inside the copy), moved up one byte in the registers so that
-// the kept bytes sit in the high bytes of the pairs.  Nothing before the row's first element is
-// read.
-__device__ __forceinline__ void gload_pairs_first(const unsigned char* p, uint32_t* w) {
-  uint32_t t[4];
-  load_words<16>(p + 1, t);
-  w[0] = t[0] << 8;
-  w[1] = __builtin_amdgcn_alignbyte(t[1], t[0], 3);
-  w[2] = __builtin_amdgcn_alignbyte(t[2], t[1], 3);
-  w[3] = __builtin_amdgcn_alignbyte(t[3], t[2], 3);
+// A vector holding its row's first element when the high bytes of the pairs are kept is read
+// from that element on (16 bytes, ending before the row's ninth element, so inside the copy
+// for rows of more than 8 elements; nothing before the row's first element is read) and then
+// moved up one byte here, so that the kept bytes sit in the high bytes of the pairs.
+__device__ __forceinline__ void pairs_up_one_byte(uint32_t* w) {
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+  w[0] = w0 << 8;
+  w[1] = __builtin_amdgcn_alignbyte(w1, w0, 3);
+  w[2] = __builtin_amdgcn_alignbyte(w2, w1, 3);
+  w[3] = __builtin_amdgcn_alignbyte(w3, w2, 3);
 }
 
 // A VB-byte vector of elements S apart in memory (S = 1 or 2).  S = 2: the 2*VB contiguous bytes

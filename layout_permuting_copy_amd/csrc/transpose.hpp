@@ -73,25 +73,26 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
       // LDS contents are never stored)
       const bool in_b = nb < NB && nb < t.remB;
       const int64_t cols = t.remC - (int64_t(cv) << G::LVE);
+      const bool first = NAR == 2 && cv == 0 && t.remC == a.eC;
 #pragma unroll
       for (int i = 0; i < G::B; ++i) {
         const bool in_row = in_b && (int64_t(ru) << G::LB) + i < t.remR && cols > 0;
-        // (NAR = 2: the row's first vector is the first one of the first column tile)
-        const bool first = NAR == 2 && cv == 0 && t.remC == a.eC;
-        const bool whole = (S == 1 && NAR != 1 ? cols >= G::VE : cols > G::VE) && !first;
+        const bool whole = S == 1 && NAR != 1 ? cols >= G::VE : cols > G::VE;
         const int n = int(cols < G::VE ? cols : G::VE);
+        // NAR = 2: the row's first vector (the first one of the first column tile) is read from
+        // its first kept byte on, and moved up one byte below (pairs_up_one_byte)
+        const unsigned char* q = p + i * sR * EB + (first ? 1 : 0);
         if (in_row && whole) {
-          gload_step<EB, VB, S, NTM>(p + i * sR * EB, r.w[f][i]);
+          gload_step<EB, VB, S, NTM>(q, r.w[f][i]);
         } else if (in_row) {
-          if constexpr (NAR == 1) gload_pairs_last(p + i * sR * EB, n, r.w[f][i]);
-          else if constexpr (NAR == 2) {
-            if (first) gload_pairs_first(p + i * sR * EB, r.w[f][i]);
-            else gload_partial<EB, VB, S>(p + i * sR * EB, n, r.w[f][i]);
-          } else {
-            gload_partial<EB, VB, S>(p + i * sR * EB, n, r.w[f][i]);
-          }
+          if constexpr (NAR == 1) gload_pairs_last(q, n, r.w[f][i]);
+          else gload_partial<EB, VB, S>(q, n, r.w[f][i]);
         }
       }
+      if constexpr (NAR == 2)
+        if (first)
+#pragma unroll
+          for (int i = 0; i < G::B; ++i) pairs_up_one_byte(r.w[f][i]);
     } else {
 #pragma unroll
       for (int i = 0; i < G::B; ++i) {
