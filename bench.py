@@ -302,6 +302,7 @@ def sweep_workloads():
     ws += [SI.sweep_dense(dt) for dt in SI.SWEEP_DTYPES]
     ws += [SI.sweep_odd(dt) for dt in SI.SWEEP_DTYPES]
     ws += [SI.sweep_slice(dt) for dt in SI.SWEEP_DTYPES]
+    ws += [SI.sweep_slice_rows(dt) for dt in SI.SWEEP_DTYPES]
     return ws
 
 
@@ -390,6 +391,7 @@ def main() -> int:
         target += [SI.sweep_dense(dt) for dt in SI.SWEEP_DTYPES]
         context = [SI.tile32_roundtrip(), identity_workload()]
         context += [SI.sweep_odd(dt) for dt in SI.SWEEP_DTYPES] + [SI.sweep_slice(dt) for dt in SI.SWEEP_DTYPES]
+        context += [SI.sweep_slice_rows(dt) for dt in SI.SWEEP_DTYPES]
         runs = [(sw, 0) for sw in context]
         runs += [(SI.sf_transpose(), L.TC_FLAG_NO_SHUFFLE), (SI.permute0213(), L.TC_FLAG_FORCE_LDS)]
         runs += [(sw, 0) for sw in target]

@@ -111,7 +111,10 @@ enum tc_path {
   TC_PATH_TRANSPOSE = 1,   /* the source- and destination-contiguous modes differ:
                               LDS tile, 16/8/4-byte vectors, XOR swizzle */
   TC_PATH_ROWS = 2,        /* both sides contiguous along the same mode: vectors staged in
-                              registers (no LDS needed) */
+                              registers (no LDS needed); also a destination contiguous along the
+                              innermost mode with a source stepping 2, 3 or 4 elements along it
+                              (src_step): each vector gathered from 16-byte loads of the source
+                              bytes between its first and last element */
   TC_PATH_ROUNDTRIP = 3,   /* co-contiguous and small: one workgroup, global -> LDS ->
                               global with the [outer, threads, vec] partition */
   TC_PATH_GUARDED_TILE = 4,/* fallback: LDS tile with element-wide accesses and guards */
@@ -162,10 +165,13 @@ typedef struct tc_plan_info {
                                XCD i mod 8); rows path: 0 destination order, 1 the outer modes in
                                source order */
   int32_t nontemporal;      /* nontemporal global accesses: bit 0 loads, bit 1 stores */
-  int32_t unaligned;        /* 1: declined split run by the transpose kernel with 16-byte vectors at
-                               element alignment and element accesses at the edges of the copy */
+  int32_t unaligned;        /* 1: declined split run with 16-byte vectors at element alignment
+                               (transpose kernel: element accesses at the edges of the copy; rows:
+                               a row's short last vector copied in a few narrower accesses) */
   int32_t src_step;         /* transpose: source stride of mode_c, 1 or 2 (2: each vector read as two
-                               contiguous ones and compacted); 0 on the other paths */
+                               contiguous ones and compacted); rows: source stride of the innermost
+                               mode where it is 2, 3 or 4 (gathered vectors), else 0; 0 on the
+                               other paths */
   int32_t wave_local;       /* transpose: 1 if every wave reads back only LDS data it wrote itself,
                                so the phases are ordered per wave instead of by a workgroup barrier */
   int32_t lds_write_bytes, lds_read_bytes;       /* LDS instruction widths */
@@ -178,7 +184,8 @@ typedef struct tc_plan_info {
                                      0 otherwise */
   int32_t src_view_bytes;   /* transpose: bytes the source elements are read as -- elem_bytes, or 2
                                for 1-byte elements of a stride-2 source read in pairs (src_step 2),
-                               whose low bytes are stored */
+                               of which the low byte is stored where the source offset is even and
+                               the high byte where it is odd */
   int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
   char reason[192];         /* why the fast path was declined ("" if it was not) */
 } tc_plan_info;

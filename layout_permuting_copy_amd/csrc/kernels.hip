@@ -124,21 +124,77 @@ __device__ __forceinline__ void copy_short(const unsigned char* __restrict__ p, 
   if (n & 1) q[o] = p[o];
 }
 
+// A destination vector of 16/EB elements gathered from a source that steps K elements along the
+// row: its elements lie in the L = ((VE - 1) * K + 1) * EB bytes from its first element to its
+// last, read as NL 16-byte loads at byte offsets 0, 16, ..., 16 * (NL - 2) and L - 16 (the last
+// overlapping its neighbour), so that no byte outside that span is read.  K = 1 is the plain
+// vector (L = 16, one load).  (Loads at 16 * m up to the next vector's first element, for all but
+// a row's last vector, measured no faster.)
+template <int EB, int K>
+struct Span {
+  static constexpr int VE = 16 / EB;
+  static constexpr int L = ((VE - 1) * K + 1) * EB;
+  static constexpr int NL = (L + 15) / 16;
+  static constexpr int last = L - 16;
+  // the loaded word (of the NL * 4) and the byte in it that hold byte P of the span
+  static constexpr int word(int P) { return P < 16 * (NL - 1) ? P / 4 : 4 * (NL - 1) + (P - last) / 4; }
+  static constexpr int byte(int P) { return P < 16 * (NL - 1) ? P % 4 : (P - last) % 4; }
+  // the span byte that byte b of the destination vector comes from
+  static constexpr int from(int b) { return b / EB * K * EB + b % EB; }
+  // nontemporal loads only for two loads of 4- or 8-byte elements (measured on 8192-row copies
+  // on MI355X: fp32 with K = 2 3.94 against 3.77 TB/s, fp64 4.00 against 3.74; 1- and 2-byte
+  // elements 2-3% slower, and K = 3 or 4 25-35% slower: int8 K = 4 1.42 against 1.96 TB/s, fp32
+  // K = 4 1.63 against 2.15, as each line is read by K load instructions one after another)
+  static constexpr int NTM = K == 1 || (K == 2 && EB >= 4) ? 3 : 2;
+};
+
+// Word O of a gathered vector from the loaded words w: one byte permute where its four bytes come
+// from at most two words, else two (each half from at most two words, the other half zero: v_perm
+// selector 0x0c) or-ed together.  Every index and selector is a compile-time constant.
+template <int EB, int K, int O>
+__device__ __forceinline__ uint32_t gather_word(const uint32_t* w) {
+  using S = Span<EB, K>;
+  constexpr int w0 = S::word(S::from(4 * O)), w1 = S::word(S::from(4 * O + 1));
+  constexpr int w2 = S::word(S::from(4 * O + 2)), w3 = S::word(S::from(4 * O + 3));
+  constexpr int b0 = S::byte(S::from(4 * O)), b1 = S::byte(S::from(4 * O + 1));
+  constexpr int b2 = S::byte(S::from(4 * O + 2)), b3 = S::byte(S::from(4 * O + 3));
+  // a second word besides w0 among the four, if any
+  constexpr int wb = w1 != w0 ? w1 : w2 != w0 ? w2 : w3;
+  constexpr bool two = (w1 == w0 || w1 == wb) && (w2 == w0 || w2 == wb) && (w3 == w0 || w3 == wb);
+  if constexpr (two) {
+    constexpr uint32_t sel = uint32_t(b0) | uint32_t(w1 == w0 ? b1 : 4 + b1) << 8 |
+                             uint32_t(w2 == w0 ? b2 : 4 + b2) << 16 | uint32_t(w3 == w0 ? b3 : 4 + b3) << 24;
+    if constexpr (sel == 0x03020100u) return w[w0];
+    else return perm(w[wb], w[w0], sel);
+  } else {
+    constexpr uint32_t lo = uint32_t(b0) | uint32_t(w1 == w0 ? b1 : 4 + b1) << 8 | 0x0c0c0000u;
+    constexpr uint32_t hi = 0x00000c0cu | uint32_t(b2) << 16 | uint32_t(w3 == w2 ? b3 : 4 + b3) << 24;
+    return perm(w[w1], w[w0], lo) | perm(w[w3], w[w2], hi);
+  }
+}
+
 // Element-aligned rows: 16-byte vectors at element alignment along rows of `row_elems` elements
-// (both sides contiguous along them); a row's short last vector is copied in the store phase in at
-// most four accesses (copy_short).  All offsets first, then every load of a thread, then the
-// stores; whole vectors nontemporal (measured 5-12% faster than plain accesses here).  BUF: the
-// whole vectors as buffer accesses from the bases a.sbuf / a.dbuf (destination vectors on the
-// 16-byte grid: an fp32 copy at an odd element offset 6.21 -> 6.39 TB/s).
-template <int EB, int NT, int ROUNDS, bool BUF = false>
+// (the destination contiguous along them).  A row's short last vector: K = 1, copied in the store
+// phase in at most four accesses (copy_short); K > 1, moved back to end at the row's end (a whole
+// vector overlapping its neighbour: the 8190 x 4095 int8 slice 2.13 -> 3.1 TB/s), and element by
+// element in rows shorter than one vector.  K = 1: the source is
+// contiguous along the rows too, one 16-byte load per vector.  K = 2, 3, 4: the source steps K
+// elements along the rows (a strided slice written out densely), each vector read as 16-byte loads
+// of its span (Span) and compacted in registers (gather_word).  All offsets first, then every load
+// of a thread, then the stores; whole vectors nontemporal (measured 5-12% faster than plain
+// accesses here; gathered loads: Span::NTM).  BUF (K = 1): the whole vectors as buffer accesses from the bases a.sbuf / a.dbuf
+// (destination vectors on the 16-byte grid: an fp32 copy at an odd element offset 6.21 -> 6.39 TB/s).
+template <int EB, int NT, int ROUNDS, bool BUF = false, int K = 1>
 __global__ void __launch_bounds__(NT) rows_unaligned_kernel(RowArgs a) {
+  static_assert(K == 1 || !BUF, "gathered rows: global accesses");
+  using S = Span<EB, K>;
   constexpr int VE = 16 / EB;
   const int t = threadIdx.x;
   const Rsrc rs = make_rsrc(BUF ? a.src + a.sbuf : a.src), rd = make_rsrc(BUF ? a.dst + a.dbuf : a.dst);
   const int64_t base = int64_t(blockIdx.x) * NT * ROUNDS;
   int64_t soff[ROUNDS], doff[ROUNDS];
   int cnt[ROUNDS];
-  uint32_t reg[ROUNDS][4];
+  uint32_t reg[ROUNDS][4 * S::NL];
 #pragma unroll
   for (int f = 0; f < ROUNDS; ++f) {
     const int64_t v = base + f * NT + t;
@@ -150,6 +206,13 @@ __global__ void __launch_bounds__(NT) rows_unaligned_kernel(RowArgs a) {
       row_offsets(a, uint32_t(v), &soff[f], &doff[f]);
       const int64_t left = a.row_elems - int64_t(k) * VE;
       cnt[f] = left < VE ? int(left) : VE;
+      if (K > 1 && cnt[f] < VE && a.row_elems >= VE) {
+        // gathered rows: a row's short last vector moves back to end at the row's end, a whole
+        // vector that overlaps its neighbour (whose bytes it writes again with the same values)
+        soff[f] -= int64_t(VE - cnt[f]) * K * EB;
+        doff[f] -= int64_t(VE - cnt[f]) * EB;
+        cnt[f] = VE;
+      }
     }
   }
 #pragma unroll
@@ -159,16 +222,37 @@ __global__ void __launch_bounds__(NT) rows_unaligned_kernel(RowArgs a) {
       const u32x4 v = bload16(rs, uint32_t(soff[f] - a.sbuf));
       reg[f][0] = v.x; reg[f][1] = v.y; reg[f][2] = v.z; reg[f][3] = v.w;
     } else {
-      gload<16, 3>(a.src + soff[f], reg[f]);
+#pragma unroll
+      for (int m = 0; m + 1 < S::NL; ++m) gload<16, S::NTM>(a.src + soff[f] + 16 * m, &reg[f][4 * m]);
+      gload<16, S::NTM>(a.src + soff[f] + S::last, &reg[f][4 * (S::NL - 1)]);
     }
   }
 #pragma unroll
   for (int f = 0; f < ROUNDS; ++f) {
     if (cnt[f] == VE) {
-      if constexpr (BUF) bstore16(rd, uint32_t(doff[f] - a.dbuf), u32x4{reg[f][0], reg[f][1], reg[f][2], reg[f][3]});
-      else gstore<16, 3>(a.dst + doff[f], reg[f]);
+      if constexpr (BUF) {
+        bstore16(rd, uint32_t(doff[f] - a.dbuf), u32x4{reg[f][0], reg[f][1], reg[f][2], reg[f][3]});
+      } else if constexpr (K == 1) {
+        gstore<16, 3>(a.dst + doff[f], reg[f]);
+      } else {
+        const uint32_t o[4] = {gather_word<EB, K, 0>(reg[f]), gather_word<EB, K, 1>(reg[f]),
+                               gather_word<EB, K, 2>(reg[f]), gather_word<EB, K, 3>(reg[f])};
+        gstore<16, 3>(a.dst + doff[f], o);
+      }
     } else if (cnt[f] > 0) {
-      copy_short(a.src + soff[f], a.dst + doff[f], cnt[f] * EB);
+      if constexpr (K == 1) {
+        copy_short(a.src + soff[f], a.dst + doff[f], cnt[f] * EB);
+      } else {
+        // rows shorter than one vector: element by element, every load issued before the stores
+        typedef typename Bytes<EB>::T E;
+        E x[VE - 1];
+#pragma unroll
+        for (int e = 0; e < VE - 1; ++e)
+          if (e < cnt[f]) x[e] = reinterpret_cast<const E*>(a.src + soff[f])[e * K];
+#pragma unroll
+        for (int e = 0; e < VE - 1; ++e)
+          if (e < cnt[f]) reinterpret_cast<E*>(a.dst + doff[f])[e] = x[e];
+      }
     }
   }
 }
@@ -430,13 +514,19 @@ void launch_rows(const Plan& p, const RowArgs& ra, int64_t wgs, hipStream_t s) {
     const dim3 grid = dim3(uint32_t(wgs)), block = dim3(kRowThreads);
     const bool buf = p.buffers && ra.sbuf != kNoBuffer;
 #define TC_RU(E, R)                                                                                          \
-  if (p.eb == E && p.row_rounds == R) {                                                                      \
+  if (p.eb == E && p.row_rounds == R && p.step == 1) {                                                       \
     if (buf) hipLaunchKernelGGL((dev::rows_unaligned_kernel<E, kRowThreads, R, true>), grid, block, 0, s, ra); \
     else hipLaunchKernelGGL((dev::rows_unaligned_kernel<E, kRowThreads, R, false>), grid, block, 0, s, ra);    \
   }
-#define TC_RU3(E) TC_RU(E, 1) TC_RU(E, 2) TC_RU(E, 4)
+#define TC_RG(E, R, K)                                                                                           \
+  if (p.eb == E && p.row_rounds == R && p.step == K)                                                             \
+    hipLaunchKernelGGL((dev::rows_unaligned_kernel<E, kRowThreads, R, false, K>), grid, block, 0, s, ra);
+#define TC_RU3(E) TC_RU(E, 1) TC_RU(E, 2) TC_RU(E, 4)                                      \
+  TC_RG(E, 1, 2) TC_RG(E, 2, 2) TC_RG(E, 4, 2) TC_RG(E, 1, 3) TC_RG(E, 2, 3) TC_RG(E, 4, 3) \
+  TC_RG(E, 1, 4) TC_RG(E, 2, 4) TC_RG(E, 4, 4)
     TC_RU3(1) TC_RU3(2) TC_RU3(4) TC_RU3(8)
 #undef TC_RU3
+#undef TC_RG
 #undef TC_RU
   } else if (p.path == TC_PATH_ROUNDTRIP) {
     if (p.vb == 16) launch_rows_t<16, kWave, true, 0>(ra, wgs, s);

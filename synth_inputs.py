@@ -139,6 +139,14 @@ def sweep_slice(dtype: str, n: int = 8192) -> Workload:
                     dtype, "bits", seed=54, src_storage=n * n)
 
 
+def sweep_slice_rows(dtype: str, n: int = 8192) -> Workload:
+    # the same source view [1:n-1:1, 0:n-2:2], written out densely in its own row order
+    rows, cols = n - 2, (n - 2 + 1) // 2
+    return Workload(f"slice_rows_{n}x{n}[1:{n-1}:1,0:{n-2}:2]_{dtype}",
+                    Side((rows, cols), (n, 2), offset=n), Side((rows, cols), (cols, 1)),
+                    dtype, "bits", seed=56, src_storage=n * n)
+
+
 def sweep_odd(dtype: str, rows: int = 8191, cols: int = 8190) -> Workload:
     return Workload(f"transpose_{rows}x{cols}_{dtype}",
                     Side((rows, cols), (cols, 1)), Side((rows, cols), (1, rows)),
@@ -149,7 +157,7 @@ def all_workloads():
     ws = [tile32_roundtrip(), sf_transpose(), transpose2d(dtype="float32"), transpose2d(dtype="bfloat16"),
           permute0213()]
     for dt in SWEEP_DTYPES:
-        ws += [sweep_dense(dt), sweep_slice(dt), sweep_odd(dt)]
+        ws += [sweep_dense(dt), sweep_slice(dt), sweep_odd(dt), sweep_slice_rows(dt)]
     return ws
 
 

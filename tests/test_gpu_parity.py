@@ -107,6 +107,15 @@ def test_cfg5_slice_8192(dtype):
 
 
 @pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
+def test_cfg5_slice_rows_8192(dtype):
+    """The same slice written out densely in its own row order: gathered rows (16-byte elements:
+    the element-wise rows, one element per access)."""
+    plan = check_workload(SI.sweep_slice_rows(dtype))
+    wide = SI.elem_bytes(dtype) == 16
+    assert plan["path_name"] == ("guarded_rows" if wide else "rows") and plan["src_step"] == (0 if wide else 2)
+
+
+@pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
 def test_cfg5_odd_8191x8190(dtype):
     plan = check_workload(SI.sweep_odd(dtype))
     assert plan["declined"] == 1 and plan["path_name"] == "transpose" and plan["unaligned"] == 1
@@ -217,6 +226,40 @@ def test_int8_stride2_pairs_not_taken_at_odd_strides():
     tile of 1-byte elements; same bytes."""
     p = _check((700, 130), (261, 2), (1, 700), 1, s_off=4, seed=77, expect="transpose")
     assert p["src_view_bytes"] == 1 and p["src_step"] == 2, p
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8])
+@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("n,m,pitch,soff", [(40, 48, 200, 0), (37, 69, 300, 3), (5, 16, 64, 1), (300, 515, 2100, 7),
+                                            (2, 3, 13, 0), (129, 1, 9, 2)])
+def test_rows_gathered_from_strided_source(eb, k, n, m, pitch, soff):
+    """A destination contiguous along rows whose source elements lie k apart (a strided slice
+    written out densely): whole 16-byte destination vectors gathered from the source bytes between
+    their first and last element, a row's short last vector element by element; ragged rows,
+    odd offsets and rows shorter than one vector."""
+    pitch = max(pitch, (m - 1) * k + 1)
+    p = _check((n, m), (pitch, k), (m, 1), eb, s_off=soff, seed=n * m + k + eb)
+    if m > 1:
+        assert p["path_name"] == "rows" and p["src_step"] == k and p["vec_bytes"] == 16, p
+
+
+@pytest.mark.parametrize("eb", [1, 2, 4, 8])
+def test_rows_gathered_batched_and_padded(eb):
+    """Gathered rows under two outer modes, a padded destination pitch and a destination offset;
+    then every other column of a matrix at full width (the 8192 x 8192 slice [1:8191, 0:8190:2]
+    written out densely, 1-byte elements only: the others at 1024 x 1024)."""
+    p = _check((3, 21, 77), (21 * 400, 400, 3), (21 * 90, 90, 1), eb, s_off=5, d_off=2, seed=eb + 100)
+    assert p["path_name"] == "rows" and p["src_step"] == 3, p
+    n = 8192 if eb == 1 else 1024
+    p = _check((n - 2, (n - 1) // 2), (n, 2), ((n - 1) // 2, 1), eb, s_off=n, src_elems=n * n, seed=eb + 200)
+    assert p["path_name"] == "rows" and p["src_step"] == 2, p
+
+
+def test_rows_gather_limits():
+    """Source strides beyond 4, and 16-byte elements, stay on the element-wise path."""
+    p = _check((50, 40), (300, 5), (40, 1), 1, seed=5, expect="guarded_rows")
+    assert p["src_step"] == 0
+    _check((50, 40), (200, 2), (40, 1), 16, seed=6, expect="guarded_rows")
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])

@@ -55,20 +55,24 @@ def test_abi_struct_layout_matches_header():
 
 def test_workload_paths_and_declines():
     expect = {"tile32x32_f32_roundtrip": "roundtrip", "sf_transpose": "shuffle", "transpose_16384": "transpose",
-              "permute0213": "rows", "transpose_8192x8192": "transpose", "slice_": "transpose",
-              "transpose_8191x8190": "transpose"}
+              "permute0213": "rows", "transpose_8192x8192": "transpose", "slice_rows_": "rows",
+              "slice_": "transpose", "transpose_8191x8190": "transpose"}
     for w in SI.all_workloads():
         p = _plan(w)
         assert p["status"] == 0, (w.name, p["error"])
         key = next(k for k in expect if w.name.startswith(k))
-        assert p["path_name"] == expect[key], (w.name, p["path_name"])
+        # 16-byte elements of the slice written out densely: one element per access already
+        wide_rows = key == "slice_rows_" and w.eb == 16
+        assert p["path_name"] == ("guarded_rows" if wide_rows else expect[key]), (w.name, p["path_name"])
         if p["path_name"] == "transpose":
             assert p["write_conflicts"] == 0 and p["read_conflicts"] == 0, w.name
         declined = w.name.startswith(("slice_", "transpose_8191x8190"))
         assert p["declined"] == int(declined), w.name
-        assert p["unaligned"] == int(declined), w.name
-        # the stride-2 slice reads every vector as two contiguous ones
-        assert p["src_step"] == (2 if w.name.startswith("slice_") else 1 if p["path_name"] == "transpose" else 0)
+        assert p["unaligned"] == int(declined and not wide_rows), w.name
+        # the stride-2 slice reads every vector as two contiguous ones (transposed), or gathers
+        # each destination vector from its source span (rows)
+        step = 0 if wide_rows else 2 if w.name.startswith("slice_") else 1 if p["path_name"] == "transpose" else 0
+        assert p["src_step"] == step, (w.name, p["src_step"])
         if declined:
             assert "not divisible by the thread count 64" in p["reason"]
             s = _plan(w, flags=L.TC_FLAG_STRICT)
@@ -629,3 +633,29 @@ def test_int8_stride2_sources_read_in_pairs():
     assert plan((n, 2), n, shape=(R, 63))[0] == 1   # columns too few for the 64-column tile
     assert plan((n, 2), n, dt=L.TC_F16)[0] == 2   # 2-byte elements: their own width
     assert plan((n, 2), n, dt=L.TC_F16)[1:3] != (512, 64)
+
+
+def test_rows_gathered_from_strided_sources():
+    """A destination contiguous along the innermost mode whose source steps 2, 3 or 4 elements
+    along it (and has no unit-stride mode) runs on the element-aligned rows path with gathered
+    vectors (src_step = the source stride); other strides, 16-byte elements, reversed rows, a
+    transposing copy and strict mode do not."""
+    def plan(shape, ss, ds, dt=L.TC_I8, flags=0, so=0):
+        return L.tc_plan((shape, ss, so), (shape, ds), dt, flags=flags)
+
+    for dt in (L.TC_I8, L.TC_F16, L.TC_F32, L.TC_F64):
+        for k in (2, 3, 4):
+            p = plan((100, 77), (1000, k), (77, 1), dt=dt, so=3)
+            assert (p["path_name"], p["src_step"], p["vec_bytes"], p["unaligned"], p["declined"]) == ("rows", k, 16, 1, 1), p
+            assert p["workgroups"] == -(-100 * -(-77 // (16 // p["elem_bytes"])) // (p["threads"] * p["load_outer"]))
+    # batched: the source strides of the outer modes may be anything
+    p = plan((3, 21, 77), (21 * 400, 400, 3), (21 * 90, 90, 1))
+    assert (p["path_name"], p["src_step"]) == ("rows", 3)
+    assert plan((100, 77), (1000, 5), (77, 1))["path_name"] == "guarded_rows"
+    assert plan((100, 77), (1000, 2), (77, 1), dt=L.TC_B128)["path_name"] == "guarded_rows"
+    assert plan((100, 77), (1000, -2), (77, 1), so=200)["path_name"] == "guarded_rows"
+    assert plan((100, 77), (1000, 2), (77, 1), flags=L.TC_FLAG_FORCE_GUARDED)["path_name"] == "guarded_rows"
+    # the source has a unit-stride mode elsewhere: a transpose
+    assert plan((100, 77), (1, 200), (77, 1))["path_name"] == "transpose"
+    with pytest.raises(L.TileCopyError):
+        plan((100, 77), (1000, 2), (77, 1), flags=L.TC_FLAG_STRICT)
