@@ -168,8 +168,9 @@ typedef struct tc_plan_info {
   int32_t unaligned;        /* 1: declined split run with 16-byte vectors at element alignment
                                (transpose kernel: element accesses at the edges of the copy; rows:
                                a row's short last vector copied in a few narrower accesses) */
-  int32_t src_step;         /* transpose: source stride of mode_c, 1 or 2 (2: each vector read as two
-                               contiguous ones and compacted); rows: source stride of the innermost
+  int32_t src_step;         /* transpose: source stride of mode_c, 1 to 4 (2: each vector read as two
+                               contiguous ones and compacted; 3, 4: read as the 16-byte loads of
+                               the bytes between its first and last element and compacted); rows: source stride of the innermost
                                mode where it is 2, 3 or 4 (gathered vectors), else 0; 0 on the
                                other paths */
   int32_t wave_local;       /* transpose: 1 if every wave reads back only LDS data it wrote itself,

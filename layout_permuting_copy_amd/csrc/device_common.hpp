@@ -171,17 +171,78 @@ __device__ __forceinline__ void pairs_up_one_byte(uint32_t* w) {
   w[3] = __builtin_amdgcn_alignbyte(w3, w2, 3);
 }
 
-// A VB-byte vector of elements S apart in memory (S = 1 or 2).  S = 2: the 2*VB contiguous bytes
+// A 16-byte vector of 16/EB elements gathered from a source that steps K elements between them
+// (a strided slice along the vector's mode): its elements lie in the L = ((VE - 1) * K + 1) * EB
+// bytes from its first element to its last, read as NL 16-byte loads at byte offsets 0, 16, ...,
+// 16 * (NL - 2) and L - 16 (the last overlapping its neighbour), so that no byte outside that span
+// is read.  K = 1 is the plain vector (L = 16, one load).  (On the rows path, loads at 16 * m up
+// to the next vector's first element, for all but a row's last vector, measured no faster.)
+template <int EB, int K>
+struct Span {
+  static constexpr int VE = 16 / EB;
+  static constexpr int L = ((VE - 1) * K + 1) * EB;
+  static constexpr int NL = (L + 15) / 16;
+  static constexpr int last = L - 16;
+  // the loaded word (of the NL * 4) and the byte in it that hold byte P of the span
+  static constexpr int word(int P) { return P < 16 * (NL - 1) ? P / 4 : 4 * (NL - 1) + (P - last) / 4; }
+  static constexpr int byte(int P) { return P < 16 * (NL - 1) ? P % 4 : (P - last) % 4; }
+  // the span byte that byte b of the gathered vector comes from
+  static constexpr int from(int b) { return b / EB * K * EB + b % EB; }
+  // rows path: nontemporal loads only for two loads of 4- or 8-byte elements (measured on
+  // 8192-row copies on MI355X: fp32 with K = 2 3.94 against 3.77 TB/s, fp64 4.00 against 3.74;
+  // 1- and 2-byte elements 2-3% slower, and K = 3 or 4 25-35% slower: int8 K = 4 1.42 against
+  // 1.96 TB/s, fp32 K = 4 1.63 against 2.15, as each line is read by K load instructions one
+  // after another)
+  static constexpr int NTM = K == 1 || (K == 2 && EB >= 4) ? 3 : 2;
+};
+
+// Word O of a gathered vector from the loaded words w: one byte permute where its four bytes come
+// from at most two words, else two (each half from at most two words, the other half zero: v_perm
+// selector 0x0c) or-ed together.  Every index and selector is a compile-time constant.
+template <int EB, int K, int O>
+__device__ __forceinline__ uint32_t gather_word(const uint32_t* w) {
+  using S = Span<EB, K>;
+  constexpr int w0 = S::word(S::from(4 * O)), w1 = S::word(S::from(4 * O + 1));
+  constexpr int w2 = S::word(S::from(4 * O + 2)), w3 = S::word(S::from(4 * O + 3));
+  constexpr int b0 = S::byte(S::from(4 * O)), b1 = S::byte(S::from(4 * O + 1));
+  constexpr int b2 = S::byte(S::from(4 * O + 2)), b3 = S::byte(S::from(4 * O + 3));
+  // a second word besides w0 among the four, if any
+  constexpr int wb = w1 != w0 ? w1 : w2 != w0 ? w2 : w3;
+  constexpr bool two = (w1 == w0 || w1 == wb) && (w2 == w0 || w2 == wb) && (w3 == w0 || w3 == wb);
+  if constexpr (two) {
+    constexpr uint32_t sel = uint32_t(b0) | uint32_t(w1 == w0 ? b1 : 4 + b1) << 8 |
+                             uint32_t(w2 == w0 ? b2 : 4 + b2) << 16 | uint32_t(w3 == w0 ? b3 : 4 + b3) << 24;
+    if constexpr (sel == 0x03020100u) return w[w0];
+    else return perm(w[wb], w[w0], sel);
+  } else {
+    constexpr uint32_t lo = uint32_t(b0) | uint32_t(w1 == w0 ? b1 : 4 + b1) << 8 | 0x0c0c0000u;
+    constexpr uint32_t hi = 0x00000c0cu | uint32_t(b2) << 16 | uint32_t(w3 == w2 ? b3 : 4 + b3) << 24;
+    return perm(w[w1], w[w0], lo) | perm(w[w3], w[w2], hi);
+  }
+}
+
+// A VB-byte vector of elements S apart in memory (S = 1 to 4).  S = 2: the 2*VB contiguous bytes
 // from p are loaded as two vectors and every other element kept (v_perm_b32 for 1- and 2-byte
 // elements, dword selection for wider ones); the caller guarantees that those bytes lie inside
-// the source allocation (they end before the row's next element).  A one-element vector is a
-// single load at any S.
+// the source allocation (they end before the row's next element).  S = 3, 4 (16-byte vectors):
+// the loads of the vector's span only (Span), compacted by gather_word.  A one-element vector is
+// a single load at any S.
 template <int EB, int VB, int S, int NTM>
 __device__ __forceinline__ void gload_step(const unsigned char* p, uint32_t* w) {
   if constexpr (S == 1 || VB == EB) {
     gload<VB, NTM>(p, w);
+  } else if constexpr (S > 2) {
+    static_assert(VB == 16 && S <= 4, "source steps 3 and 4: 16-byte vectors");
+    using Sp = Span<EB, S>;
+    uint32_t a[4 * Sp::NL];
+#pragma unroll
+    for (int m = 0; m + 1 < Sp::NL; ++m) gload<16, NTM>(p + 16 * m, a + 4 * m);
+    gload<16, NTM>(p + Sp::last, a + 4 * (Sp::NL - 1));
+    w[0] = gather_word<EB, S, 0>(a);
+    w[1] = gather_word<EB, S, 1>(a);
+    w[2] = gather_word<EB, S, 2>(a);
+    w[3] = gather_word<EB, S, 3>(a);
   } else {
-    static_assert(S == 2, "source step 1 or 2");
     uint32_t a[2 * (VB / 4)];
     gload<VB, NTM>(p, a);
     gload<VB, NTM>(p + VB, a + VB / 4);

@@ -124,55 +124,6 @@ __device__ __forceinline__ void copy_short(const unsigned char* __restrict__ p, 
   if (n & 1) q[o] = p[o];
 }
 
-// A destination vector of 16/EB elements gathered from a source that steps K elements along the
-// row: its elements lie in the L = ((VE - 1) * K + 1) * EB bytes from its first element to its
-// last, read as NL 16-byte loads at byte offsets 0, 16, ..., 16 * (NL - 2) and L - 16 (the last
-// overlapping its neighbour), so that no byte outside that span is read.  K = 1 is the plain
-// vector (L = 16, one load).  (Loads at 16 * m up to the next vector's first element, for all but
-// a row's last vector, measured no faster.)
-template <int EB, int K>
-struct Span {
-  static constexpr int VE = 16 / EB;
-  static constexpr int L = ((VE - 1) * K + 1) * EB;
-  static constexpr int NL = (L + 15) / 16;
-  static constexpr int last = L - 16;
-  // the loaded word (of the NL * 4) and the byte in it that hold byte P of the span
-  static constexpr int word(int P) { return P < 16 * (NL - 1) ? P / 4 : 4 * (NL - 1) + (P - last) / 4; }
-  static constexpr int byte(int P) { return P < 16 * (NL - 1) ? P % 4 : (P - last) % 4; }
-  // the span byte that byte b of the destination vector comes from
-  static constexpr int from(int b) { return b / EB * K * EB + b % EB; }
-  // nontemporal loads only for two loads of 4- or 8-byte elements (measured on 8192-row copies
-  // on MI355X: fp32 with K = 2 3.94 against 3.77 TB/s, fp64 4.00 against 3.74; 1- and 2-byte
-  // elements 2-3% slower, and K = 3 or 4 25-35% slower: int8 K = 4 1.42 against 1.96 TB/s, fp32
-  // K = 4 1.63 against 2.15, as each line is read by K load instructions one after another)
-  static constexpr int NTM = K == 1 || (K == 2 && EB >= 4) ? 3 : 2;
-};
-
-// Word O of a gathered vector from the loaded words w: one byte permute where its four bytes come
-// from at most two words, else two (each half from at most two words, the other half zero: v_perm
-// selector 0x0c) or-ed together.  Every index and selector is a compile-time constant.
-template <int EB, int K, int O>
-__device__ __forceinline__ uint32_t gather_word(const uint32_t* w) {
-  using S = Span<EB, K>;
-  constexpr int w0 = S::word(S::from(4 * O)), w1 = S::word(S::from(4 * O + 1));
-  constexpr int w2 = S::word(S::from(4 * O + 2)), w3 = S::word(S::from(4 * O + 3));
-  constexpr int b0 = S::byte(S::from(4 * O)), b1 = S::byte(S::from(4 * O + 1));
-  constexpr int b2 = S::byte(S::from(4 * O + 2)), b3 = S::byte(S::from(4 * O + 3));
-  // a second word besides w0 among the four, if any
-  constexpr int wb = w1 != w0 ? w1 : w2 != w0 ? w2 : w3;
-  constexpr bool two = (w1 == w0 || w1 == wb) && (w2 == w0 || w2 == wb) && (w3 == w0 || w3 == wb);
-  if constexpr (two) {
-    constexpr uint32_t sel = uint32_t(b0) | uint32_t(w1 == w0 ? b1 : 4 + b1) << 8 |
-                             uint32_t(w2 == w0 ? b2 : 4 + b2) << 16 | uint32_t(w3 == w0 ? b3 : 4 + b3) << 24;
-    if constexpr (sel == 0x03020100u) return w[w0];
-    else return perm(w[wb], w[w0], sel);
-  } else {
-    constexpr uint32_t lo = uint32_t(b0) | uint32_t(w1 == w0 ? b1 : 4 + b1) << 8 | 0x0c0c0000u;
-    constexpr uint32_t hi = 0x00000c0cu | uint32_t(b2) << 16 | uint32_t(w3 == w2 ? b3 : 4 + b3) << 24;
-    return perm(w[w1], w[w0], lo) | perm(w[w3], w[w2], hi);
-  }
-}
-
 // Element-aligned rows: 16-byte vectors at element alignment along rows of `row_elems` elements
 // (the destination contiguous along them).  A row's short last vector: K = 1, copied in the store
 // phase in at most four accesses (copy_short); K > 1, moved back to end at the row's end (a whole

@@ -869,14 +869,23 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
   }
 
   // Declined by the aligned-vector rule, but the destination has a unit-stride mode and the
-  // source a distinct mode of stride 1 or 2: the transpose kernel with 16-byte vectors at element
+  // source a distinct mode of stride 1 to 4: the transpose kernel with 16-byte vectors at element
   // alignment (gfx950 global memory takes unaligned vector accesses), whole vectors where the
   // extents allow and element accesses at the edges of the copy.  Along a stride-2 mode every
-  // vector is read as two contiguous ones (the elements in between are fetched and dropped).
+  // vector is read as two contiguous ones (the elements in between are fetched and dropped), along
+  // a stride-3 or -4 mode as the 16-byte loads of its span.
+  // Strides 3 and 4 only where the source has no unit-stride mode at all, and the elements lie at
+  // most 12 bytes apart: measured against the guarded tile on 8192-row copies on MI355X, int8
+  // stride 3 1.10 -> 1.97 TB/s, stride 4 1.11 -> 1.28, fp16 stride 3 1.90 -> 2.48, fp32 stride 3
+  // 2.14 -> 2.26; fp16 stride 4 level (1.65 / 1.67), and fp32 stride 4, fp64 and 16-byte elements
+  // 1-8% slower than the guarded tile, which they keep.  (Each lane's loads then touch a 64-byte
+  // segment apiece, so a wave's load requests, not the bytes, set the pace.)
   int c2 = c;
   if (c2 < 0 || c2 == r)
-    for (int k = 0; k < j.rank && (c2 < 0 || c2 == r); ++k)
-      if (k != r && j.m[k].s == 2) c2 = k;
+    for (int k = 0; k < j.rank; ++k) {
+      const bool strided = j.m[k].s == 2 || (c < 0 && j.m[k].s >= 3 && j.m[k].s <= 4 && j.m[k].s * p.eb <= 12);
+      if (k != r && strided && (c2 < 0 || c2 == r || j.m[k].s < j.m[c2].s)) c2 = k;
+    }
   // 1-byte elements whose column mode has source stride 2, every other source stride even, the
   // source pointer 2-byte aligned: the source is read as 2-byte pairs (a dense 2-byte transpose
   // of the pairs, on its tall tiles) and one byte of each pair is stored: the low byte where the

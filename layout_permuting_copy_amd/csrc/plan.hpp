@@ -92,8 +92,9 @@ struct TileGeom {
   int ntm = 0;                    // nontemporal global accesses: bit 0 loads, bit 1 stores
   int order = 0;                  // grid order: 0 column tiles fastest, 1 row tiles fastest,
                                   // 2 XCD super-tiles (see tile_at)
-  int step = 1;                   // source element stride along the column mode (1, or 2: every
-                                  // vector read as two contiguous ones and compacted in registers)
+  int step = 1;                   // source element stride along the column mode (1; 2: every
+                                  // vector read as two contiguous ones and compacted in registers;
+                                  // 3, 4: read as the loads of its span and compacted)
   bool wave_local = false;        // every wave reads back only LDS units it wrote itself: the
                                   // phases are ordered per wave, without a workgroup barrier
   bool edges = true;              // some tile reaches past an extent (the kernel needs its guards)
@@ -136,7 +137,8 @@ struct Plan {
   int ntm = 0;                      // rows path: nontemporal global accesses (bit 0 loads, bit 1 stores)
   bool unaligned = false;           // transpose or rows with vectors at element alignment (extents or strides
                                     // not multiples of the vector; edges element by element)
-  int step = 1;                     // source stride of the transpose's column mode (1 or 2)
+  int step = 1;                     // source stride of the transpose's column mode (1 to 4), or
+                                    // of the gathered rows' mode (2 to 4)
   int nar = 0;                      // transpose of 1-byte elements whose column mode has source
                                     // stride 2, read as 2-byte pairs (the tile planned for eb = 2,
                                     // source strides and offset halved at launch), of which the

@@ -272,6 +272,28 @@ def test_transpose_stride2_source(eb, n, m, pitch, soff):
     assert p["src_step"] == 2
 
 
+@pytest.mark.parametrize("eb,k", [(1, 3), (1, 4), (2, 3), (2, 4), (4, 3)])
+@pytest.mark.parametrize("n,m,pitch,soff", [(40, 30, 130, 0), (129, 67, 300, 3), (64, 64, 260, 0), (33, 300, 1201, 1),
+                                            (7, 5, 23, 0), (300, 257, 1030, 2)])
+def test_transpose_stride34_source(eb, k, n, m, pitch, soff):
+    """Source columns three or four elements apart (at most 12 bytes): each whole vector is read
+    as the 16-byte loads of the bytes between its first and last element and compacted; a row's
+    last vector element by element."""
+    p = _check((n, m), (pitch, k), (1, n), eb, s_off=soff, seed=n * m + eb + k, expect="transpose")
+    assert p["src_step"] == k
+
+
+def test_transpose_stride34_batched_and_limits():
+    for eb, k in ((1, 3), (1, 4), (2, 3), (2, 4), (4, 3)):
+        p = _check((3, 37, 45), (37 * 200, 200, k), (37 * 45, 1, 37), eb, seed=eb + k, expect="transpose")
+        assert p["src_step"] == k
+    # elements more than 12 bytes apart, or stride 5: the guarded tile
+    for eb, k in ((4, 4), (8, 3), (16, 3)):
+        _check((37, 45), (200, k), (1, 37), eb, seed=eb * k, expect="guarded_tile")
+    # stride 5: the guarded tile
+    _check((40, 30), (200, 5), (1, 40), 1, seed=9, expect="guarded_tile")
+
+
 def test_transpose_stride2_batched():
     for eb in (1, 2, 4, 8, 16):
         p = _check((3, 37, 45), (37 * 100, 100, 2), (37 * 45, 1, 37), eb, seed=eb, expect="transpose")

@@ -659,3 +659,24 @@ def test_rows_gathered_from_strided_sources():
     assert plan((100, 77), (1, 200), (77, 1))["path_name"] == "transpose"
     with pytest.raises(L.TileCopyError):
         plan((100, 77), (1000, 2), (77, 1), flags=L.TC_FLAG_STRICT)
+
+
+def test_transposes_from_sources_of_stride_3_and_4():
+    """A transpose whose source has no unit-stride mode but a mode of stride 3 or 4 (and no
+    stride-2 mode), its elements at most 12 bytes apart, reads 16-byte vectors along it (src_step
+    3 or 4) on the element-aligned tile; wider strides take the guarded tile."""
+    def plan(shape, ss, ds, dt=L.TC_I8):
+        return L.tc_plan((shape, ss, 0), (shape, ds), dt)
+
+    for dt in (L.TC_I8, L.TC_F16, L.TC_F32, L.TC_F64, L.TC_B128):
+        for k in (3, 4):
+            p = plan((500, 300), (2000, k), (1, 500), dt=dt)
+            if k * L.ELEM_BYTES[dt] > 12:  # elements more than 12 bytes apart: the guarded tile
+                assert p["path_name"] == "guarded_tile", p
+                continue
+            assert (p["path_name"], p["src_step"], p["vec_bytes"], p["unaligned"]) == ("transpose", k, 16, 1), p
+            assert p["write_conflicts"] == 0 and p["read_conflicts"] == 0, p
+    # the same strides without a transposition: gathered rows
+    p = plan((20, 30, 40), (3, 60 * 40, 60), (1, 20 * 40, 20))
+    assert p["path_name"] == "rows" and p["src_step"] == 3 and p["rank"] == 1, p
+    assert plan((500, 300), (2000, 5), (1, 500))["path_name"] == "guarded_tile"
