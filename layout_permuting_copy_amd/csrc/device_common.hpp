@@ -172,28 +172,33 @@ __device__ __forceinline__ void pairs_up_one_byte(uint32_t* w) {
 }
 
 // A 16-byte vector of 16/EB elements gathered from a source that steps K elements between them
-// (a strided slice along the vector's mode): its elements lie in the L = ((VE - 1) * K + 1) * EB
-// bytes from its first element to its last, read as NL 16-byte loads at byte offsets 0, 16, ...,
-// 16 * (NL - 2) and L - 16 (the last overlapping its neighbour), so that no byte outside that span
-// is read.  K = 1 is the plain vector (L = 16, one load).  (On the rows path, loads at 16 * m up
-// to the next vector's first element, for all but a row's last vector, measured no faster.)
+// (a strided slice along the vector's mode; K < 0: in reverse order, e.g. a flipped row): its
+// elements lie in the L = ((VE - 1) * |K| + 1) * EB bytes from its lowest-addressed element to its
+// highest, which start `base` bytes from its first element (0, or (VE - 1) * K * EB for K < 0).
+// They are read as NL 16-byte loads at byte offsets 0, 16, ..., 16 * (NL - 2) and L - 16 of the
+// span (the last overlapping its neighbour), so that no byte outside it is read.  K = 1 is the
+// plain vector (L = 16, one load), K = -1 one load reversed.  (On the rows path, loads at 16 * m
+// up to the next vector's first element, for all but a row's last vector, measured no faster.)
 template <int EB, int K>
 struct Span {
+  static_assert(K != 0 && K >= -4 && K <= 4, "source steps -4 to -1 and 1 to 4");
   static constexpr int VE = 16 / EB;
-  static constexpr int L = ((VE - 1) * K + 1) * EB;
+  static constexpr int AK = K < 0 ? -K : K;
+  static constexpr int L = ((VE - 1) * AK + 1) * EB;
   static constexpr int NL = (L + 15) / 16;
   static constexpr int last = L - 16;
+  static constexpr int base = K < 0 ? (VE - 1) * K * EB : 0;
   // the loaded word (of the NL * 4) and the byte in it that hold byte P of the span
   static constexpr int word(int P) { return P < 16 * (NL - 1) ? P / 4 : 4 * (NL - 1) + (P - last) / 4; }
   static constexpr int byte(int P) { return P < 16 * (NL - 1) ? P % 4 : (P - last) % 4; }
   // the span byte that byte b of the gathered vector comes from
-  static constexpr int from(int b) { return b / EB * K * EB + b % EB; }
-  // rows path: nontemporal loads only for two loads of 4- or 8-byte elements (measured on
-  // 8192-row copies on MI355X: fp32 with K = 2 3.94 against 3.77 TB/s, fp64 4.00 against 3.74;
-  // 1- and 2-byte elements 2-3% slower, and K = 3 or 4 25-35% slower: int8 K = 4 1.42 against
-  // 1.96 TB/s, fp32 K = 4 1.63 against 2.15, as each line is read by K load instructions one
-  // after another)
-  static constexpr int NTM = K == 1 || (K == 2 && EB >= 4) ? 3 : 2;
+  static constexpr int from(int b) { return (K < 0 ? VE - 1 - b / EB : b / EB) * AK * EB + b % EB; }
+  // rows path: nontemporal loads for |K| = 1, and for |K| = 2 with 4- or 8-byte elements only
+  // (measured on 8192-row copies on MI355X: fp32 with K = 2 3.94 against 3.77 TB/s, fp64 4.00
+  // against 3.74; 1- and 2-byte elements 2-3% slower, and K = 3 or 4 25-35% slower: int8 K = 4
+  // 1.42 against 1.96 TB/s, fp32 K = 4 1.63 against 2.15, as each line is read by K load
+  // instructions one after another)
+  static constexpr int NTM = AK == 1 || (AK == 2 && EB >= 4) ? 3 : 2;
 };
 
 // Word O of a gathered vector from the loaded words w: one byte permute where its four bytes come

@@ -125,15 +125,16 @@ __device__ __forceinline__ void copy_short(const unsigned char* __restrict__ p, 
 }
 
 // Element-aligned rows: 16-byte vectors at element alignment along rows of `row_elems` elements
-// (the destination contiguous along them).  A row's short last vector: K = 1, copied in the store
-// phase in at most four accesses (copy_short); K > 1, moved back to end at the row's end (a whole
-// vector overlapping its neighbour: the 8190 x 4095 int8 slice 2.13 -> 3.1 TB/s), and element by
-// element in rows shorter than one vector.  K = 1: the source is
-// contiguous along the rows too, one 16-byte load per vector.  K = 2, 3, 4: the source steps K
-// elements along the rows (a strided slice written out densely), each vector read as 16-byte loads
-// of its span (Span) and compacted in registers (gather_word).  All offsets first, then every load
-// of a thread, then the stores; whole vectors nontemporal (measured 5-12% faster than plain
-// accesses here; gathered loads: Span::NTM).  BUF (K = 1): the whole vectors as buffer accesses from the bases a.sbuf / a.dbuf
+// (the destination contiguous along them).  K = 1: the source is contiguous along the rows too,
+// one 16-byte load per vector.  K = 2, 3, 4, or -1 to -4: the source steps K elements along the
+// rows (a strided slice written out densely; a negative K reverses the order, e.g. a flipped row),
+// each vector read as 16-byte loads of its span (Span) and compacted in registers (gather_word).
+// A row's short last vector: K = 1, copied in the store phase in at most four accesses
+// (copy_short); otherwise moved back to end at the row's end (a whole vector overlapping its
+// neighbour: the 8190 x 4095 int8 slice 2.13 -> 3.1 TB/s), and element by element in rows shorter
+// than one vector.  All offsets first, then every load of a thread, then the stores; whole
+// vectors nontemporal (measured 5-12% faster than plain accesses here; gathered loads:
+// Span::NTM).  BUF (K = 1): the whole vectors as buffer accesses from the bases a.sbuf / a.dbuf
 // (destination vectors on the 16-byte grid: an fp32 copy at an odd element offset 6.21 -> 6.39 TB/s).
 template <int EB, int NT, int ROUNDS, bool BUF = false, int K = 1>
 __global__ void __launch_bounds__(NT) rows_unaligned_kernel(RowArgs a) {
@@ -157,7 +158,7 @@ __global__ void __launch_bounds__(NT) rows_unaligned_kernel(RowArgs a) {
       row_offsets(a, uint32_t(v), &soff[f], &doff[f]);
       const int64_t left = a.row_elems - int64_t(k) * VE;
       cnt[f] = left < VE ? int(left) : VE;
-      if (K > 1 && cnt[f] < VE && a.row_elems >= VE) {
+      if (K != 1 && cnt[f] < VE && a.row_elems >= VE) {
         // gathered rows: a row's short last vector moves back to end at the row's end, a whole
         // vector that overlaps its neighbour (whose bytes it writes again with the same values)
         soff[f] -= int64_t(VE - cnt[f]) * K * EB;
@@ -174,8 +175,8 @@ __global__ void __launch_bounds__(NT) rows_unaligned_kernel(RowArgs a) {
       reg[f][0] = v.x; reg[f][1] = v.y; reg[f][2] = v.z; reg[f][3] = v.w;
     } else {
 #pragma unroll
-      for (int m = 0; m + 1 < S::NL; ++m) gload<16, S::NTM>(a.src + soff[f] + 16 * m, &reg[f][4 * m]);
-      gload<16, S::NTM>(a.src + soff[f] + S::last, &reg[f][4 * (S::NL - 1)]);
+      for (int m = 0; m + 1 < S::NL; ++m) gload<16, S::NTM>(a.src + soff[f] + S::base + 16 * m, &reg[f][4 * m]);
+      gload<16, S::NTM>(a.src + soff[f] + S::base + S::last, &reg[f][4 * (S::NL - 1)]);
     }
   }
 #pragma unroll
@@ -469,12 +470,11 @@ void launch_rows(const Plan& p, const RowArgs& ra, int64_t wgs, hipStream_t s) {
     if (buf) hipLaunchKernelGGL((dev::rows_unaligned_kernel<E, kRowThreads, R, true>), grid, block, 0, s, ra); \
     else hipLaunchKernelGGL((dev::rows_unaligned_kernel<E, kRowThreads, R, false>), grid, block, 0, s, ra);    \
   }
-#define TC_RG(E, R, K)                                                                                           \
-  if (p.eb == E && p.row_rounds == R && p.step == K)                                                             \
-    hipLaunchKernelGGL((dev::rows_unaligned_kernel<E, kRowThreads, R, false, K>), grid, block, 0, s, ra);
+#define TC_RG(E, K)                                                                                              \
+  if (p.eb == E && p.step == K)                                                                                  \
+    hipLaunchKernelGGL((dev::rows_unaligned_kernel<E, kRowThreads, kRowRounds, false, K>), grid, block, 0, s, ra);
 #define TC_RU3(E) TC_RU(E, 1) TC_RU(E, 2) TC_RU(E, 4)                                      \
-  TC_RG(E, 1, 2) TC_RG(E, 2, 2) TC_RG(E, 4, 2) TC_RG(E, 1, 3) TC_RG(E, 2, 3) TC_RG(E, 4, 3) \
-  TC_RG(E, 1, 4) TC_RG(E, 2, 4) TC_RG(E, 4, 4)
+  TC_RG(E, 2) TC_RG(E, 3) TC_RG(E, 4) TC_RG(E, -1) TC_RG(E, -2) TC_RG(E, -3) TC_RG(E, -4)
     TC_RU3(1) TC_RU3(2) TC_RU3(4) TC_RU3(8)
 #undef TC_RU3
 #undef TC_RG

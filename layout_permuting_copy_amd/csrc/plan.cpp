@@ -984,12 +984,13 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
   // matrix at any offset, and copies at odd element offsets, run here instead of element-wise:
   // the 8190^2 window of an 8192^2 matrix, int8 1.01 -> 4.5 TB/s, fp16 2.04 -> 5.4, fp32 4.5 ->
   // 6.0, fp64 5.6 -> 6.3; an int8 copy at an odd offset 1.10 -> 5.8.
-  // The same rows where the source steps 2, 3 or 4 elements along them and has no unit-stride
-  // mode (a strided slice written out densely, e.g. every other column of a matrix): each
-  // destination vector is gathered from the source bytes between its first and last element
-  // (16-byte loads) and compacted in registers; 1- to 8-byte elements.
+  // The same rows where the source steps 2, 3 or 4 elements along them, or -1 to -4 (in reverse
+  // order), and has no unit-stride mode (a strided slice written out densely, e.g. every other
+  // column of a matrix; a flipped row): each destination vector is gathered from the source bytes
+  // between its first and last element (16-byte loads) and compacted in registers; 1- to 8-byte
+  // elements.
   const int64_t gstep = r >= 0 ? j.m[r].s : 0;
-  const bool gather = c_unit < 0 && p.eb <= 8 && gstep >= 2 && gstep <= 4;
+  const bool gather = c_unit < 0 && p.eb <= 8 && gstep != 0 && gstep != 1 && gstep >= -4 && gstep <= 4;
   if (!forced_guarded && r >= 0 && (r == c || gather) && r == j.rank - 1 && p.eb < 16) {
     const int64_t ve = 16 / p.eb;
     const int64_t rows = j.count / j.m[r].e;
@@ -1004,7 +1005,7 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
       const TuneCfg tc = tune_override();
       p.buffers = !gather && tc.buf != 0;
       p.row_rounds = kRowRounds;
-      if (tc.rr == 1 || tc.rr == 2 || tc.rr == 4) p.row_rounds = tc.rr;
+      if (!gather && (tc.rr == 1 || tc.rr == 2 || tc.rr == 4)) p.row_rounds = tc.rr;
     }
     p.workgroups = ceil_div(nvec, int64_t(kRowThreads) * p.row_rounds);
     p.load_outer = p.store_outer = int(std::min<int64_t>(p.row_rounds, ceil_div(nvec, p.threads)));
@@ -1063,7 +1064,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
   info->rank = p.j.rank;
   info->declined = p.declined ? 1 : 0;
   info->unaligned = p.unaligned ? 1 : 0;
-  info->src_step = p.path == TC_PATH_TRANSPOSE ? p.step : p.path == TC_PATH_ROWS && p.step > 1 ? p.step : 0;
+  info->src_step = p.path == TC_PATH_TRANSPOSE ? p.step : p.path == TC_PATH_ROWS && p.step != 1 ? p.step : 0;
   info->wave_local = p.path == TC_PATH_TRANSPOSE && p.g.wave_local ? 1 : 0;
   for (int k = 0; k < p.j.rank; ++k) {
     info->extent[k] = p.j.m[k].e;

@@ -54,6 +54,8 @@ WORKLOADS = ["sf_transpose_65536x2x1x4x32_f32", "transpose_16384x16384_float32",
              "transpose_8191x8190_float64", "transpose_8191x8190_int4vec",
              "slice_8192x8192[1:8191:1,0:8190:2]_int8", "slice_8192x8192[1:8191:1,0:8190:2]_float16",
              "slice_8192x8192[1:8191:1,0:8190:2]_float64", "slice_8192x8192[1:8191:1,0:8190:2]_int4vec",
+             "slice_rows_8192x8192[1:8191:1,0:8190:2]_int8", "slice_rows_8192x8192[1:8191:1,0:8190:2]_float16",
+             "slice_rows_8192x8192[1:8191:1,0:8190:2]_float64",
              "permute0213_32x32x2048x128_bfloat16", IDENTITY, CALIBRATION]
 
 

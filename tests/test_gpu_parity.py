@@ -229,15 +229,17 @@ def test_int8_stride2_pairs_not_taken_at_odd_strides():
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])
-@pytest.mark.parametrize("k", [2, 3, 4])
+@pytest.mark.parametrize("k", [2, 3, 4, -1, -2, -3, -4])
 @pytest.mark.parametrize("n,m,pitch,soff", [(40, 48, 200, 0), (37, 69, 300, 3), (5, 16, 64, 1), (300, 515, 2100, 7),
                                             (2, 3, 13, 0), (129, 1, 9, 2)])
 def test_rows_gathered_from_strided_source(eb, k, n, m, pitch, soff):
     """A destination contiguous along rows whose source elements lie k apart (a strided slice
-    written out densely): whole 16-byte destination vectors gathered from the source bytes between
-    their first and last element, a row's short last vector element by element; ragged rows,
-    odd offsets and rows shorter than one vector."""
-    pitch = max(pitch, (m - 1) * k + 1)
+    written out densely; k < 0: a flipped row): whole 16-byte destination vectors gathered from
+    the source bytes between their first and last element, a row's short last vector moved back
+    over its neighbour; ragged rows, odd offsets and rows shorter than one vector."""
+    pitch = max(pitch, (m - 1) * abs(k) + 1)
+    if k < 0:
+        soff += (m - 1) * -k  # each row's first element is its highest-addressed one
     p = _check((n, m), (pitch, k), (m, 1), eb, s_off=soff, seed=n * m + k + eb)
     if m > 1:
         assert p["path_name"] == "rows" and p["src_step"] == k and p["vec_bytes"] == 16, p
@@ -256,10 +258,23 @@ def test_rows_gathered_batched_and_padded(eb):
 
 
 def test_rows_gather_limits():
-    """Source strides beyond 4, and 16-byte elements, stay on the element-wise path."""
+    """Source strides beyond 4 either way, and 16-byte elements, stay on the element-wise path."""
     p = _check((50, 40), (300, 5), (40, 1), 1, seed=5, expect="guarded_rows")
     assert p["src_step"] == 0
+    _check((50, 40), (300, -5), (40, 1), 1, s_off=200, seed=7, expect="guarded_rows")
     _check((50, 40), (200, 2), (40, 1), 16, seed=6, expect="guarded_rows")
+    _check((50, 40), (200, -1), (40, 1), 16, s_off=39, seed=8, expect="guarded_rows")
+
+
+def test_rows_flipped_at_full_width():
+    """torch.flip along the last dimension of an 8192 x 8192 matrix (bytes and floats), and along
+    both dimensions."""
+    n = 8192
+    for eb in (1, 4):
+        p = _check((n, n), (n, -1), (n, 1), eb, s_off=n - 1, src_elems=n * n, seed=eb + 300)
+        assert p["path_name"] == "rows" and p["src_step"] == -1, p
+    p = _check((n, n), (-n, -1), (n, 1), 2, s_off=n * n - 1, src_elems=n * n, seed=303)
+    assert p["path_name"] == "rows" and p["src_step"] == -1, p
 
 
 @pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])

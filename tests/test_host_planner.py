@@ -637,8 +637,8 @@ def test_int8_stride2_sources_read_in_pairs():
 
 def test_rows_gathered_from_strided_sources():
     """A destination contiguous along the innermost mode whose source steps 2, 3 or 4 elements
-    along it (and has no unit-stride mode) runs on the element-aligned rows path with gathered
-    vectors (src_step = the source stride); other strides, 16-byte elements, reversed rows, a
+    along it, or -1 to -4 (reversed), and has no unit-stride mode runs on the element-aligned rows
+    path with gathered vectors (src_step = the source stride); other strides, 16-byte elements, a
     transposing copy and strict mode do not."""
     def plan(shape, ss, ds, dt=L.TC_I8, flags=0, so=0):
         return L.tc_plan((shape, ss, so), (shape, ds), dt, flags=flags)
@@ -651,9 +651,13 @@ def test_rows_gathered_from_strided_sources():
     # batched: the source strides of the outer modes may be anything
     p = plan((3, 21, 77), (21 * 400, 400, 3), (21 * 90, 90, 1))
     assert (p["path_name"], p["src_step"]) == ("rows", 3)
+    # reversed rows (a flip) and reversed strided slices: negative steps down to -4
+    for k in (-1, -2, -3, -4):
+        p = plan((100, 77), (1000, k), (77, 1), so=400)
+        assert (p["path_name"], p["src_step"], p["vec_bytes"]) == ("rows", k, 16), p
     assert plan((100, 77), (1000, 5), (77, 1))["path_name"] == "guarded_rows"
+    assert plan((100, 77), (1000, -5), (77, 1), so=400)["path_name"] == "guarded_rows"
     assert plan((100, 77), (1000, 2), (77, 1), dt=L.TC_B128)["path_name"] == "guarded_rows"
-    assert plan((100, 77), (1000, -2), (77, 1), so=200)["path_name"] == "guarded_rows"
     assert plan((100, 77), (1000, 2), (77, 1), flags=L.TC_FLAG_FORCE_GUARDED)["path_name"] == "guarded_rows"
     # the source has a unit-stride mode elsewhere: a transpose
     assert plan((100, 77), (1, 200), (77, 1))["path_name"] == "transpose"
