@@ -226,23 +226,23 @@ __device__ __forceinline__ uint32_t gather_word(const uint32_t* w) {
   }
 }
 
-// A VB-byte vector of elements S apart in memory (S = 1 to 4).  S = 2: the 2*VB contiguous bytes
-// from p are loaded as two vectors and every other element kept (v_perm_b32 for 1- and 2-byte
-// elements, dword selection for wider ones); the caller guarantees that those bytes lie inside
-// the source allocation (they end before the row's next element).  S = 3, 4 (16-byte vectors):
-// the loads of the vector's span only (Span), compacted by gather_word.  A one-element vector is
-// a single load at any S.
+// A VB-byte vector of elements S apart in memory (S = 1 to 4, or -1 to -4: elements in reverse
+// address order).  S = 2: the 2*VB contiguous bytes from p are loaded as two vectors and every
+// other element kept (v_perm_b32 for 1- and 2-byte elements, dword selection for wider ones); the
+// caller guarantees that those bytes lie inside the source allocation (they end before the row's
+// next element).  Other steps (16-byte vectors): the loads of the vector's span only (Span), from
+// p + Span::base, compacted by gather_word.  A one-element vector is a single load at any S.
 template <int EB, int VB, int S, int NTM>
 __device__ __forceinline__ void gload_step(const unsigned char* p, uint32_t* w) {
   if constexpr (S == 1 || VB == EB) {
     gload<VB, NTM>(p, w);
-  } else if constexpr (S > 2) {
-    static_assert(VB == 16 && S <= 4, "source steps 3 and 4: 16-byte vectors");
+  } else if constexpr (S != 2) {
+    static_assert(VB == 16, "source steps other than 1 and 2: 16-byte vectors");
     using Sp = Span<EB, S>;
     uint32_t a[4 * Sp::NL];
 #pragma unroll
-    for (int m = 0; m + 1 < Sp::NL; ++m) gload<16, NTM>(p + 16 * m, a + 4 * m);
-    gload<16, NTM>(p + Sp::last, a + 4 * (Sp::NL - 1));
+    for (int m = 0; m + 1 < Sp::NL; ++m) gload<16, NTM>(p + Sp::base + 16 * m, a + 4 * m);
+    gload<16, NTM>(p + Sp::base + Sp::last, a + 4 * (Sp::NL - 1));
     w[0] = gather_word<EB, S, 0>(a);
     w[1] = gather_word<EB, S, 1>(a);
     w[2] = gather_word<EB, S, 2>(a);

@@ -698,6 +698,22 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     if (j.m[k].d == 1 && r < 0) r = k;
     if (j.m[k].s == 1 && c < 0) c = k;
   }
+  // A mode that the source walks backwards with unit stride (a matrix rotated by 90 degrees, or
+  // flipped along its columns and transposed) and that is not the destination's contiguous mode:
+  // its logical index is reversed (i -> e - 1 - i: both strides negated, both offsets moved to the
+  // mode's other end), which names the same pairs of elements, so that the source reads it forwards
+  // and the ordinary transpose takes it.  (A row the source walks backwards, with the destination
+  // contiguous along it, stays as it is: gathered rows.)
+  if (c < 0)
+    for (int k = 0; k < j.rank; ++k)
+      if (k != r && j.m[k].s == -1) {
+        j.so += (j.m[k].e - 1) * j.m[k].s;
+        j.dof += (j.m[k].e - 1) * j.m[k].d;
+        j.m[k].s = -j.m[k].s;
+        j.m[k].d = -j.m[k].d;
+        c = k;
+        break;
+      }
   const int c_unit = c;
   const bool forced_guarded = flags & TC_FLAG_FORCE_GUARDED;
   if (j.count % kWave != 0)
@@ -874,17 +890,24 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
   // extents allow and element accesses at the edges of the copy.  Along a stride-2 mode every
   // vector is read as two contiguous ones (the elements in between are fetched and dropped), along
   // a stride-3 or -4 mode as the 16-byte loads of its span.
-  // Strides 3 and 4 only where the source has no unit-stride mode at all, and the elements lie at
-  // most 12 bytes apart: measured against the guarded tile on 8192-row copies on MI355X, int8
-  // stride 3 1.10 -> 1.97 TB/s, stride 4 1.11 -> 1.28, fp16 stride 3 1.90 -> 2.48, fp32 stride 3
-  // 2.14 -> 2.26; fp16 stride 4 level (1.65 / 1.67), and fp32 stride 4, fp64 and 16-byte elements
-  // 1-8% slower than the guarded tile, which they keep.  (Each lane's loads then touch a 64-byte
-  // segment apiece, so a wave's load requests, not the bytes, set the pace.)
+  // Other strides only where the source has no unit-stride mode at all: -1 and -2 (reversed
+  // columns, e.g. a rotation by 90 degrees), and strides of magnitude 3 and 4 where the elements
+  // lie at most 12 bytes apart: measured against the guarded tile on 8192-row copies on MI355X,
+  // int8 stride 3 1.10 -> 1.97 TB/s, stride 4 1.11 -> 1.28, fp16 stride 3 1.90 -> 2.48, fp32
+  // stride 3 2.14 -> 2.26; fp16 stride 4 level (1.65 / 1.67), and fp32 stride 4, fp64 and 16-byte
+  // elements 1-8% slower than the guarded tile, which they keep.  (Each lane's loads then touch a
+  // 64-byte segment apiece, so a wave's load requests, not the bytes, set the pace.)  The stride
+  // of smallest magnitude is taken, the positive one on a tie.
   int c2 = c;
   if (c2 < 0 || c2 == r)
     for (int k = 0; k < j.rank; ++k) {
-      const bool strided = j.m[k].s == 2 || (c < 0 && j.m[k].s >= 3 && j.m[k].s <= 4 && j.m[k].s * p.eb <= 12);
-      if (k != r && strided && (c2 < 0 || c2 == r || j.m[k].s < j.m[c2].s)) c2 = k;
+      const int64_t s = j.m[k].s, as = std::llabs(s);
+      const bool strided = s == 2 || (c < 0 && s != 1 && (s == -1 || s == -2 || ((as == 3 || as == 4) && as * p.eb <= 12)));
+      const auto better = [&](int q) {
+        const int64_t aq = std::llabs(j.m[q].s);
+        return as < aq || (as == aq && s > 0 && j.m[q].s < 0);
+      };
+      if (k != r && strided && (c2 < 0 || c2 == r || better(c2))) c2 = k;
     }
   // 1-byte elements whose column mode has source stride 2, every other source stride even, the
   // source pointer 2-byte aligned: the source is read as 2-byte pairs (a dense 2-byte transpose

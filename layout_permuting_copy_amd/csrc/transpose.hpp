@@ -273,8 +273,10 @@ __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
 template <int EB, int VB, int U, int TILE, int NT, int NTM, int S, bool WL = false, bool EDGE = true, int CAP = 0,
           int NAR = 0>
 bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
-  // (source steps 3 and 4 only where the elements lie at most 12 bytes apart, as planned)
-  if constexpr (Geo<EB, VB, U, TILE, NT>::valid && (S <= 2 || EB * S <= 12)) {
+  // (source steps of magnitude 3 and 4 only where the elements lie at most 12 bytes apart, as
+  // planned)
+  constexpr int AS = S < 0 ? -S : S;
+  if constexpr (Geo<EB, VB, U, TILE, NT>::valid && (AS <= 2 || EB * AS <= 12)) {
     if (ta)
       hipLaunchKernelGGL((transpose_kernel<EB, VB, U, TILE, NT, NTM, S, WL, EDGE, CAP, NAR>), dim3(uint32_t(wgs)), dim3(NT),
                          0, s, *ta);
@@ -288,8 +290,8 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 
 // Instantiation list of one element width: every (vector bytes, LDS unit, tile bytes, threads,
 // nontemporal mode, source step, phase ordering, edge code) the planner can choose.  16- and
-// 8-byte LDS units for the tall tiles; steps 2, 3 and 4 (strided sources) only in the
-// configurations of the element-aligned plans; wave-local ordering in the small batched tiles, where it occurs; the
+// 8-byte LDS units for the tall tiles; steps 2 to 4 and -1 to -4 (strided and reversed sources)
+// only in the configurations of the element-aligned plans; wave-local ordering in the small batched tiles, where it occurs; the
 // interior-only variants (EDGE = false) of the nontemporal configurations.
 #define TC_TRANSPOSE_DISPATCH(EB)                                                                           \
   bool launch_transpose_eb##EB(const TransposeCfg& c, const TransposeArgs* ta, int64_t wgs, void* stream) {   \
@@ -333,10 +335,14 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
   }
 
 #define TC_CFG_STEP2(EB, U, TILE, NT)                                                                        \
-  if (vb == 16 && tile == TILE && nt == NT && c.step >= 2 && ntm == 0 && !c.wave_local) {                    \
+  if (vb == 16 && tile == TILE && nt == NT && c.step != 1 && ntm == 0 && !c.wave_local) {                    \
     if (c.step == 2) return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, 2>(ta, wgs, s);                \
     if (c.step == 3) return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, 3>(ta, wgs, s);                \
     if (c.step == 4) return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, 4>(ta, wgs, s);                \
+    if (c.step == -1) return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, -1>(ta, wgs, s);              \
+    if (c.step == -2) return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, -2>(ta, wgs, s);              \
+    if (c.step == -3) return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, -3>(ta, wgs, s);              \
+    if (c.step == -4) return dev::launch_transpose_cfg<EB, 16, U, TILE, NT, 0, -4>(ta, wgs, s);              \
   }
 
 // Wider LDS units (UNIT/EB rows of one column): tall tiles whose store lanes run down a column

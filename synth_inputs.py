@@ -64,11 +64,14 @@ class Workload:
 
 
 def span(side: Side) -> int:
-    """Number of storage elements needed to hold every element the layout names
-    (non-negative strides only, which is all the workloads use)."""
+    """Number of storage elements needed to hold every element the layout names: one past its
+    highest offset (negative strides count from the offset down, which must stay >= 0)."""
     if any(e == 0 for e in side.shape):
         return side.offset
-    return side.offset + sum((e - 1) * s for e, s in zip(side.shape, side.stride)) + 1
+    low = side.offset + sum((e - 1) * s for e, s in zip(side.shape, side.stride) if s < 0)
+    if low < 0:
+        raise ValueError(f"layout reaches below offset 0 (lowest offset {low})")
+    return side.offset + sum((e - 1) * s for e, s in zip(side.shape, side.stride) if s > 0) + 1
 
 
 def storage_elems(w: Workload, which: str) -> int:

@@ -298,6 +298,30 @@ def test_transpose_stride34_source(eb, k, n, m, pitch, soff):
     assert p["src_step"] == k
 
 
+@pytest.mark.parametrize("eb,k", [(1, -1), (2, -1), (4, -1), (8, -1), (16, -1), (1, -2), (4, -2), (16, -2), (1, -3),
+                                  (2, -4), (4, -3)])
+@pytest.mark.parametrize("n,m,pitch", [(40, 30, 130), (129, 67, 300), (64, 64, 260), (300, 257, 1030), (7, 5, 23)])
+def test_transpose_reversed_source_columns(eb, k, n, m, pitch):
+    """Source columns in reverse order (k = -1: the column index is reversed by the planner, the
+    destination rows then run backwards; k = -2 to -4, reversed and strided: each whole vector is
+    read as the 16-byte loads of the bytes between its lowest- and highest-addressed element and
+    reordered; a row's last vector element by element)."""
+    soff = (m - 1) * -k + 2
+    p = _check((n, m), (pitch, k), (1, n), eb, s_off=soff, seed=n * m + eb - k, expect="transpose")
+    assert p["src_step"] == (1 if k == -1 else k)
+
+
+def test_rotate90_full_size():
+    """torch.rot90 of an 8192 x 8192 matrix (the transpose of the column-flipped matrix), at
+    every width: the reversed source columns become an aligned transpose into destination rows
+    that run backwards."""
+    n = 8192
+    for eb in (1, 2, 4, 8, 16):
+        m = n if eb <= 4 else n // 4
+        p = _check((m, m), (-1, m), (m, 1), eb, s_off=m - 1, src_elems=m * m, seed=eb + 400, expect="transpose")
+        assert p["src_step"] == 1 and p["unaligned"] == 0 and p["dst_stride"][0] == -m, p
+
+
 def test_transpose_stride34_batched_and_limits():
     for eb, k in ((1, 3), (1, 4), (2, 3), (2, 4), (4, 3)):
         p = _check((3, 37, 45), (37 * 200, 200, k), (37 * 45, 1, 37), eb, seed=eb + k, expect="transpose")

@@ -684,3 +684,32 @@ def test_transposes_from_sources_of_stride_3_and_4():
     p = plan((20, 30, 40), (3, 60 * 40, 60), (1, 20 * 40, 20))
     assert p["path_name"] == "rows" and p["src_step"] == 3 and p["rank"] == 1, p
     assert plan((500, 300), (2000, 5), (1, 500))["path_name"] == "guarded_tile"
+
+
+def test_transposes_from_reversed_source_columns():
+    """A transpose whose source has no unit-stride mode but a mode of stride -1 has that mode's
+    index reversed (an ordinary transpose then); one of stride -2 (or -3, -4 with elements at most
+    12 bytes apart) reads 16-byte vectors along it in reverse (src_step negative); a stride of
+    smaller magnitude wins, the positive one on a tie."""
+    def plan(shape, ss, ds, dt=L.TC_I8, so=0):
+        return L.tc_plan((shape, ss, so), (shape, ds), dt)
+
+    for dt in (L.TC_I8, L.TC_F16, L.TC_F32, L.TC_F64, L.TC_B128):
+        for k in (-1, -2, -3, -4):
+            p = plan((500, 300), (-k * 300 + 7, k), (1, 500), dt=dt, so=-k * 299)
+            if -k >= 3 and -k * L.ELEM_BYTES[dt] > 12:
+                assert p["path_name"] == "guarded_tile", p
+                continue
+            # stride -1: the column index reversed, read forwards
+            assert (p["path_name"], p["src_step"], p["unaligned"]) == ("transpose", 1 if k == -1 else k, 1), p
+            assert p["write_conflicts"] == 0 and p["read_conflicts"] == 0, p
+    # rot90, the transpose of the column-flipped matrix: the column index reversed (both strides
+    # negated, the offsets moved to its other end), then the aligned transpose
+    p = plan((256, 256), (-1, 256), (256, 1), so=255)
+    assert (p["path_name"], p["src_step"], p["declined"], p["unaligned"]) == ("transpose", 1, 0, 0), p
+    assert (p["src_stride"][:2], p["dst_stride"][:2], p["src_offset"], p["dst_offset"]) == ((1, 256), (-256, 1), 0, 255 * 256)
+    # two candidate modes: stride 2 beats stride -2 and -3
+    p = plan((30, 40, 50), (2, -3 * 30, 3 * 30 * 40 + 1), (40 * 50, 50, 1), so=3 * 30 * 39)
+    assert p["path_name"] == "transpose" and p["src_step"] == 2, p
+    p = plan((30, 40, 50), (-2, 2, 2 * 30 * 40 + 1), (40 * 50, 50, 1), so=2 * 29)
+    assert p["path_name"] == "transpose" and p["src_step"] == 2 and p["mode_c"] == 1, p
