@@ -698,22 +698,60 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     if (j.m[k].d == 1 && r < 0) r = k;
     if (j.m[k].s == 1 && c < 0) c = k;
   }
-  // A mode that the source walks backwards with unit stride (a matrix rotated by 90 degrees, or
-  // flipped along its columns and transposed) and that is not the destination's contiguous mode:
-  // its logical index is reversed (i -> e - 1 - i: both strides negated, both offsets moved to the
-  // mode's other end), which names the same pairs of elements, so that the source reads it forwards
-  // and the ordinary transpose takes it.  (A row the source walks backwards, with the destination
-  // contiguous along it, stays as it is: gathered rows.)
+  // Modes walked backwards.  Reversing a mode's logical index (i -> e - 1 - i: both strides
+  // negated, both offsets moved to the mode's other end) names the same pairs of elements, so the
+  // planner reverses: every mode both sides walk backwards; then a mode the destination walks
+  // backwards with unit stride when none is contiguous there (a copy into a flipped view); then a
+  // mode the source walks backwards with unit stride, other than the destination's contiguous
+  // one, when none is contiguous there (a matrix rotated by 90 degrees, or flipped along its
+  // columns and transposed).  Each side then reads or writes it forwards and the ordinary paths
+  // take it.  (A row the source walks backwards, with the destination contiguous along it, stays
+  // as it is: gathered rows.)
+  auto reverse_mode = [&](int k) {
+    j.so += (j.m[k].e - 1) * j.m[k].s;
+    j.dof += (j.m[k].e - 1) * j.m[k].d;
+    j.m[k].s = -j.m[k].s;
+    j.m[k].d = -j.m[k].d;
+  };
+  bool reversed = false;
+  for (int k = 0; k < j.rank; ++k)  // walked backwards on both sides: forwards on both
+    if (j.m[k].s < 0 && j.m[k].d < 0) {
+      reverse_mode(k);
+      reversed = true;
+    }
+  if (reversed) {
+    r = c = -1;
+    for (int k = 0; k < j.rank; ++k) {
+      if (j.m[k].d == 1 && r < 0) r = k;
+      if (j.m[k].s == 1 && c < 0) c = k;
+    }
+  }
+  if (r < 0)
+    for (int k = 0; k < j.rank; ++k)
+      if (j.m[k].d == -1) {
+        reverse_mode(k);
+        r = k;
+        c = -1;
+        for (int q = 0; q < j.rank && c < 0; ++q)
+          if (j.m[q].s == 1) c = q;
+        reversed = true;
+        break;
+      }
   if (c < 0)
     for (int k = 0; k < j.rank; ++k)
       if (k != r && j.m[k].s == -1) {
-        j.so += (j.m[k].e - 1) * j.m[k].s;
-        j.dof += (j.m[k].e - 1) * j.m[k].d;
-        j.m[k].s = -j.m[k].s;
-        j.m[k].d = -j.m[k].d;
-        c = k;
+        reverse_mode(k);
+        reversed = true;
         break;
       }
+  if (reversed) {  // modes that now line up merge (a copy flipped on both sides: one contiguous run)
+    canonicalize(&j);
+    r = c = -1;
+    for (int k = 0; k < j.rank; ++k) {
+      if (j.m[k].d == 1 && r < 0) r = k;
+      if (j.m[k].s == 1 && c < 0) c = k;
+    }
+  }
   const int c_unit = c;
   const bool forced_guarded = flags & TC_FLAG_FORCE_GUARDED;
   if (j.count % kWave != 0)

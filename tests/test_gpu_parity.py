@@ -322,6 +322,25 @@ def test_rotate90_full_size():
         assert p["src_step"] == 1 and p["unaligned"] == 0 and p["dst_stride"][0] == -m, p
 
 
+@pytest.mark.parametrize("eb", [1, 2, 4, 8, 16])
+def test_reversed_modes(eb):
+    """Modes walked backwards: into a row-flipped destination (the source contiguous: gathered
+    rows reversed), a destination rotated by 90 degrees (an ordinary transpose after the planner
+    reverses the mode), both sides flipped the same way (one contiguous copy), and the rows
+    reversed on both sides."""
+    n, m = 300, 257
+    p = _check((n, m), (m, 1), (m, -1), eb, d_off=m - 1, seed=eb + 500)
+    assert p["path_name"] == ("guarded_rows" if eb == 16 else "rows"), p
+    p = _check((n, m), (m, 1), (-1, n), eb, d_off=n - 1, seed=eb + 501, expect="transpose")
+    assert p["src_step"] == 1, p
+    # (16-byte elements: a count not divisible by 64 takes the element-wise rows, 16 bytes apiece)
+    rows = "guarded_rows" if eb == 16 else "rows"
+    p = _check((n, m), (m, -1), (m, -1), eb, s_off=m - 1, d_off=m - 1, seed=eb + 502, expect=rows)
+    assert p["rank"] == 1, p
+    p = _check((n, m), (-m, 1), (-m, 1), eb, s_off=(n - 1) * m, d_off=(n - 1) * m, seed=eb + 503, expect=rows)
+    assert p["rank"] == 1 and p["src_stride"][0] == 1 and p["dst_stride"][0] == 1, p
+
+
 def test_transpose_stride34_batched_and_limits():
     for eb, k in ((1, 3), (1, 4), (2, 3), (2, 4), (4, 3)):
         p = _check((3, 37, 45), (37 * 200, 200, k), (37 * 45, 1, 37), eb, seed=eb + k, expect="transpose")

@@ -713,3 +713,27 @@ def test_transposes_from_reversed_source_columns():
     assert p["path_name"] == "transpose" and p["src_step"] == 2, p
     p = plan((30, 40, 50), (-2, 2, 2 * 30 * 40 + 1), (40 * 50, 50, 1), so=2 * 29)
     assert p["path_name"] == "transpose" and p["src_step"] == 2 and p["mode_c"] == 1, p
+
+
+def test_modes_walked_backwards_are_reversed():
+    """The planner reverses modes (both strides negated, the offsets moved to the other end; the
+    same pairs of elements): those both sides walk backwards, then a destination mode of stride -1
+    where none has stride 1, then a source mode of stride -1 other than the destination's
+    contiguous one where none has stride 1.  A source row walked backwards into a contiguous
+    destination row is not reversed (gathered rows)."""
+    def plan(shape, ss, so, ds, do, dt=L.TC_F32):
+        return L.tc_plan((shape, ss, so), (shape, ds, do), dt)
+
+    n = 512
+    p = plan((n, n), (n, -1), n - 1, (n, -1), n - 1)
+    assert (p["path_name"], p["rank"], p["src_offset"], p["dst_offset"]) == ("rows", 1, 0, 0), p
+    p = plan((n, n), (-n, 1), n * (n - 1), (-n, 1), n * (n - 1))
+    assert (p["path_name"], p["rank"], p["src_stride"][0], p["dst_stride"][0]) == ("rows", 1, 1, 1), p
+    p = plan((n, n), (n, 1), 0, (n, -1), n - 1)   # into a flipped view: the source read backwards
+    assert (p["path_name"], p["src_step"], p["src_stride"][:2], p["dst_stride"][:2]) == ("rows", -1, (n, -1), (n, 1)), p
+    p = plan((n, n), (n, 1), 0, (-1, n), n - 1)   # into a rotated view: an aligned transpose
+    assert (p["path_name"], p["declined"], p["src_step"]) == ("transpose", 0, 1), p
+    p = plan((n, n), (-1, n), n - 1, (n, 1), 0)   # rot90 of the source
+    assert (p["path_name"], p["declined"], p["dst_stride"][:2]) == ("transpose", 0, (-n, 1)), p
+    p = plan((n, n), (n, -1), n - 1, (n, 1), 0)   # a flipped source row: gathered rows, not reversed
+    assert (p["path_name"], p["src_step"], p["src_offset"]) == ("rows", -1, n - 1), p
