@@ -25,7 +25,8 @@ def layouts(draw):
     rank = draw(st.integers(1, 4))
     shape = draw(st.lists(st.integers(1, 6), min_size=rank, max_size=rank))
     # destination: a permuted dense row-major layout (injective), sometimes with a zeroed or
-    # repeated stride (non-injective); source: permuted, stepped, maybe negative or zero strides
+    # repeated stride (non-injective), modes maybe walked backwards; source: permuted, stepped,
+    # maybe negative or zero strides (the planner may reverse modes: the pairs stay the same)
     perm_d = draw(st.permutations(range(rank)))
     ds, acc = [0] * rank, 1
     for k in reversed(perm_d):
@@ -34,6 +35,9 @@ def layouts(draw):
     if draw(st.integers(0, 9)) == 0:
         k = draw(st.integers(0, rank - 1))
         ds[k] = draw(st.sampled_from([0, ds[(k + 1) % rank]]))
+    # destination modes walked backwards (a flipped or rotated view)
+    flips = draw(st.lists(st.booleans(), min_size=rank, max_size=rank))
+    ds = [-d if f else d for d, f in zip(ds, flips)]
     perm_s = draw(st.permutations(range(rank)))
     steps = draw(st.lists(st.sampled_from([1, 1, 2, 3, -1]), min_size=rank, max_size=rank))
     ss, acc = [0] * rank, 1
@@ -43,7 +47,7 @@ def layouts(draw):
     if draw(st.integers(0, 9)) == 0:
         ss[draw(st.integers(0, rank - 1))] = 0  # broadcast read
     so = acc + draw(st.integers(0, 7))  # room for negative strides
-    do = draw(st.integers(0, 7))
+    do = int(np.prod(shape)) + draw(st.integers(0, 7))
     # insert extent-1 modes with arbitrary strides on either side
     if draw(st.booleans()):
         pos = draw(st.integers(0, rank))
