@@ -129,10 +129,11 @@ __device__ __forceinline__ void copy_short(const unsigned char* __restrict__ p, 
 // one 16-byte load per vector.  K = 2, 3, 4, or -1 to -4: the source steps K elements along the
 // rows (a strided slice written out densely; a negative K reverses the order, e.g. a flipped row),
 // each vector read as 16-byte loads of its span (Span) and compacted in registers (gather_word).
-// A row's short last vector: K = 1, copied in the store phase in at most four accesses
-// (copy_short); otherwise moved back to end at the row's end (a whole vector overlapping its
-// neighbour: the 8190 x 4095 int8 slice 2.13 -> 3.1 TB/s), and element by element in rows shorter
-// than one vector.  All offsets first, then every load of a thread, then the stores; whole
+// A row's short last vector moves back to end at the row's end, a whole vector overlapping its
+// neighbour (measured against copying it in a few narrower accesses: the 8190 x 4095 int8 slice
+// 2.13 -> 3.1 TB/s, the 8190^2 int8 window of an 8192^2 matrix 4.54 -> 4.96, fp32 5.94 -> 6.04);
+// rows shorter than one vector, and the BUF instances (whose stores stay on the 16-byte grid), go
+// in at most four accesses (K = 1, copy_short) or element by element.  All offsets first, then every load of a thread, then the stores; whole
 // vectors nontemporal (measured 5-12% faster than plain accesses here; gathered loads:
 // Span::NTM).  BUF (K = 1): the whole vectors as buffer accesses from the bases a.sbuf / a.dbuf
 // (destination vectors on the 16-byte grid: an fp32 copy at an odd element offset 6.21 -> 6.39 TB/s).
@@ -158,9 +159,9 @@ __global__ void __launch_bounds__(NT) rows_unaligned_kernel(RowArgs a) {
       row_offsets(a, uint32_t(v), &soff[f], &doff[f]);
       const int64_t left = a.row_elems - int64_t(k) * VE;
       cnt[f] = left < VE ? int(left) : VE;
-      if (K != 1 && cnt[f] < VE && a.row_elems >= VE) {
-        // gathered rows: a row's short last vector moves back to end at the row's end, a whole
-        // vector that overlaps its neighbour (whose bytes it writes again with the same values)
+      if (!BUF && cnt[f] < VE && a.row_elems >= VE) {
+        // a row's short last vector moves back to end at the row's end, a whole vector that
+        // overlaps its neighbour (whose bytes it writes again with the same values)
         soff[f] -= int64_t(VE - cnt[f]) * K * EB;
         doff[f] -= int64_t(VE - cnt[f]) * EB;
         cnt[f] = VE;
