@@ -304,6 +304,48 @@ def random_layouts_large(seed: int = 777, count: int = 60, max_elems: int = 3 <<
         yield tuple(shape), tuple(ss), so, tuple(ds), do, eb, span_s, span_d
 
 
+def random_layouts_steps(seed: int = 2468, count: int = 120, max_elems: int = 1 << 20):
+    """Multi-tile layout pairs whose source steps along its innermost mode by -4 to -1 or 2 to 4
+    elements (strided slices, flips), some outer source modes walked backwards, and destinations
+    dense in a random mode order with padded pitches and modes maybe walked backwards (flipped or
+    rotated views); extents up to ~1500 so that copies end in ragged tiles and rows, element
+    offsets on both sides.  Yields (shape, src_stride, src_offset, dst_stride, dst_offset,
+    elem_bytes, src_elems, dst_elems); every offset a layout reaches lies in [0, *_elems), and the
+    destination is injective."""
+    rng = np.random.default_rng(seed)
+    made = 0
+    while made < count:
+        eb = int(rng.choice([1, 2, 4, 8, 16]))
+        rank = int(rng.integers(1, 4))
+        shape = [int(rng.integers(1, 1500)) for _ in range(min(rank, 2))] + [int(rng.integers(1, 5)) for _ in range(rank - 2)]
+        if int(np.prod(shape)) > max_elems // max(1, eb // 4):
+            continue
+        order = list(rng.permutation(rank))
+        step = int(rng.choice([-4, -3, -2, -1, -1, 2, 2, 3, 4]))
+        ss = [0] * rank
+        ss[order[-1]] = step
+        acc = shape[order[-1]] * abs(step)
+        for k in reversed(order[:-1]):
+            acc += int(rng.integers(0, 20))
+            ss[k] = acc * (-1 if rng.integers(0, 4) == 0 else 1)
+            acc *= shape[k]
+        dorder = list(rng.permutation(rank))
+        ds = [0] * rank
+        ds[dorder[-1]] = 1
+        dacc = shape[dorder[-1]]
+        for k in reversed(dorder[:-1]):
+            dacc += int(rng.integers(0, 20))
+            ds[k] = dacc
+            dacc *= shape[k]
+        ds = [-d if rng.integers(0, 4) == 0 else d for d in ds]
+        so = -sum((e - 1) * st for e, st in zip(shape, ss) if st < 0) + int(rng.integers(0, 9))
+        do = -sum((e - 1) * d for e, d in zip(shape, ds) if d < 0) + int(rng.integers(0, 9))
+        span_s = so + sum((e - 1) * st for e, st in zip(shape, ss) if st > 0) + 1
+        span_d = do + sum((e - 1) * d for e, d in zip(shape, ds) if d > 0) + 1
+        made += 1
+        yield tuple(shape), tuple(ss), so, tuple(ds), do, eb, span_s, span_d
+
+
 def random_layouts_wide(seed: int = 4321, count: int = 120):
     """Like random_layouts, plus negative source strides, broadcast (stride-0) source modes,
     inserted extent-1 modes with arbitrary strides, and element offsets on both sides.  Yields

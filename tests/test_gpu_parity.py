@@ -611,6 +611,22 @@ def test_random_layouts_large():
     assert len(paths) >= 5, paths
 
 
+def test_random_layouts_steps():
+    """Multi-tile copies from sources stepping -4 to -1 or 2 to 4 elements along their innermost
+    mode, outer modes and destination modes walked backwards, padded pitches and offsets, every
+    element width (gathered rows, stride-2 to -4 and reversed transposes, reversed modes, guarded
+    paths)."""
+    paths = set()
+    for case, (shape, ss, so, ds, do, eb, ns, nd) in enumerate(SI.random_layouts_steps(2468, 120)):
+        src = _bits(ns * eb, 7000 + case)
+        sl, dl = (shape, ss, so), (shape, ds, do)
+        say(f"[gpu] steps case {case}: src={sl} dst={dl} eb={eb}")
+        got, plan = run_copy(src, sl, nd, dl, eb, dtype_code(DT_BY_EB[eb]))
+        assert_same(got, oracle_copy(src, sl, nd, dl, eb), eb, f"steps {case}")
+        paths.add((plan["path_name"], plan["src_step"]))
+    assert len(paths) >= 8, paths
+
+
 def test_adjacent_buffers_are_not_aliases():
     """A destination that starts right after the source's last byte (or ends right before its
     first) shares no byte: the copy runs."""
