@@ -133,10 +133,11 @@ __device__ __forceinline__ void copy_short(const unsigned char* __restrict__ p, 
 // neighbour (measured against copying it in a few narrower accesses: the 8190 x 4095 int8 slice
 // 2.13 -> 3.1 TB/s, the 8190^2 int8 window of an 8192^2 matrix 4.54 -> 4.96, fp32 5.94 -> 6.04);
 // rows shorter than one vector, and the BUF instances (whose stores stay on the 16-byte grid), go
-// in at most four accesses (K = 1, copy_short) or element by element.  All offsets first, then every load of a thread, then the stores; whole
-// vectors nontemporal (measured 5-12% faster than plain accesses here; gathered loads:
-// Span::NTM).  BUF (K = 1): the whole vectors as buffer accesses from the bases a.sbuf / a.dbuf
-// (destination vectors on the 16-byte grid: an fp32 copy at an odd element offset 6.21 -> 6.39 TB/s).
+// in at most four accesses (K = 1, copy_short) or element by element.  All offsets first, then
+// every load of a thread, then the stores; whole vectors nontemporal (measured 5-12% faster than
+// plain accesses here; gathered loads: Span::NTM).  BUF (K = 1): the whole vectors as buffer
+// accesses from the bases a.sbuf / a.dbuf (destination vectors on the 16-byte grid: an fp32 copy
+// at an odd element offset 6.21 -> 6.39 TB/s).
 template <int EB, int NT, int ROUNDS, bool BUF = false, int K = 1>
 __global__ void __launch_bounds__(NT) rows_unaligned_kernel(RowArgs a) {
   static_assert(K == 1 || !BUF, "gathered rows: global accesses");

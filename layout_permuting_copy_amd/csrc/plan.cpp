@@ -940,7 +940,8 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
   if (c2 < 0 || c2 == r)
     for (int k = 0; k < j.rank; ++k) {
       const int64_t s = j.m[k].s, as = std::llabs(s);
-      const bool strided = s == 2 || (c < 0 && s != 1 && (s == -1 || s == -2 || ((as == 3 || as == 4) && as * p.eb <= 12)));
+      const bool strided =
+          s == 2 || (c < 0 && s != 1 && (s == -1 || s == -2 || ((as == 3 || as == 4) && as * p.eb <= 12)));
       const auto better = [&](int q) {
         const int64_t aq = std::llabs(j.m[q].s);
         return as < aq || (as == aq && s > 0 && j.m[q].s < 0);
