@@ -444,7 +444,7 @@ def test_rows_at_element_alignment(eb, shape, pitch, soff, doff):
     lengths that are not multiples of a vector): rows of 16-byte vectors at element alignment, a
     row's short last vector moved back over its neighbour (or, in rows shorter than a vector and
     with buffer accesses, copied in narrower accesses); with the destination vectors on the
-    16-byte grid (the last two shapes, and the 1000-element copy) as buffer accesses."""
+    16-byte grid and no short last vector (the (300, 128) shape) as buffer accesses."""
     if len(shape) == 1:
         ss, ds = (1,), (1,)
     elif len(shape) == 2:
