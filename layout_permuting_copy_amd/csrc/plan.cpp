@@ -335,7 +335,17 @@ static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c)
       return true;
     case 4:
       if (eR < 256 || eC < 32) return false;
+      // 256 x 64 tiles for the large copies (16384^2), 256 x 32 below 8192 such tiles, except for
+      // destination rows of at most 2048 elements: 128 x 64 tiles there (measured on MI355X against
+      // 256 x 32, 0.25-1 GiB moved: 1024 x 4096 3.76 -> 4.63 TB/s, 2048^2 3.91 -> 4.54, 512 x 8192
+      // 4.25 -> 4.79, 1024 x 16384 4.59 -> 5.14, 1024 x 65536 5.04 -> 5.73, 512 x 131072 4.85 ->
+      // 5.71, 2048 x 32768 5.50 -> 5.78, 768 x 32768 5.38 -> 5.62, 2048 x 8192 level; with 4096
+      // elements they were 3-7% slower: 4096^2 5.11 -> 4.75).  Other shapes showed no rule: 256 x 64
+      // tiles in XCD super-tiles of 4 x 4 ran 13-19% faster on 65536 x 1024, 32768 x 2048,
+      // 16384 x 4096 and 262144 x 256, but 2-7% slower on 6144^2, 8192 x 4096, 24576 x 1536 and
+      // 131072 x 512.
       if (tiles(256, 64) >= 8192) { c->tile = 65536; c->threads = 512; c->trb = 1024; }  // 256 x 64
+      else if (eR <= 2048) { c->tile = 32768; c->threads = 512; c->trb = 512; }          // 128 x 64
       else { c->tile = 32768; c->threads = 512; c->trb = 1024; }                         // 256 x 32
       return true;
     case 2:
