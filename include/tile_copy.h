@@ -210,6 +210,32 @@ int tile_copy_ex(const void* src, const tc_layout* src_layout, void* dst, const 
                  int dtype, void* stream, int flags, tc_plan_info* info);
 
 /*
+ * tile_copy_ex that also picks the plan by measurement: the same copy (the pages' operation,
+ * dst[dst_layout(i)] = src[src_layout(i)]; TVM TIRx docs, "copy -> gmem_smem") is run on the
+ * planner's choice and on the other kernel configurations the library holds for it (transposes:
+ * conflict-free tiles of a fixed list of shapes and grid orders; the aligned rows path: vectors
+ * per lane and buffer accesses), each once to warm up and then `reps` times (0 or less: 5) between
+ * two HIP events on `stream`; the fastest becomes the cached plan of these layouts, dtype, flags
+ * and pointer alignment, which later tile_copy / tile_copy_ex calls reuse.  The tuning itself is
+ * the library's own addition (the pages plan by rule only).  Every configuration writes the same
+ * bytes, so `dst` holds the copy on return.  Blocks the calling thread until the timed launches
+ * end; `stream` must not be capturing (TC_E_ARG).  `info` (may be NULL) receives the chosen plan,
+ * `best_ms` (may be NULL) its mean time per launch in milliseconds.  Errors: those of
+ * tile_copy_ex, TC_E_ARG (capturing stream), TC_E_HIP (an event or launch failed; the cache is
+ * then unchanged).
+ */
+int tc_autotune(const void* src, const tc_layout* src_layout, void* dst, const tc_layout* dst_layout,
+                int dtype, void* stream, int flags, int reps, tc_plan_info* info, float* best_ms);
+
+/*
+ * Host only: the configurations tc_autotune would time for the copy, the planner's own first;
+ * fills out[0 .. min(count, max_out) - 1] (caller-owned) and returns the count (>= 1), or the
+ * planner's error status (out[0] then holds the failed plan when max_out > 0).
+ */
+int tc_plan_variants(const tc_layout* src_layout, const tc_layout* dst_layout, int dtype, int flags,
+                     int ptr_align, tc_plan_info* out, int max_out);
+
+/*
  * Host only: plan the copy without running it (no GPU needed).
  * `ptr_align` is the byte alignment both base pointers will have (a power of
  * two; 0 means 16).  Fills *out.  Returns the status tile_copy would return

@@ -135,6 +135,12 @@ def load_library(path: str = LIB_PATH):
     lib.tile_copy_ex.argtypes = [ctypes.c_void_p, P(TcLayout), ctypes.c_void_p, P(TcLayout), ctypes.c_int,
                                  ctypes.c_void_p, ctypes.c_int, P(TcPlanInfo)]
     lib.tile_copy_ex.restype = ctypes.c_int
+    lib.tc_autotune.argtypes = [ctypes.c_void_p, P(TcLayout), ctypes.c_void_p, P(TcLayout), ctypes.c_int,
+                                ctypes.c_void_p, ctypes.c_int, ctypes.c_int, P(TcPlanInfo), P(ctypes.c_float)]
+    lib.tc_autotune.restype = ctypes.c_int
+    lib.tc_plan_variants.argtypes = [P(TcLayout), P(TcLayout), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     P(TcPlanInfo), ctypes.c_int]
+    lib.tc_plan_variants.restype = ctypes.c_int
     lib.tc_plan.argtypes = [P(TcLayout), P(TcLayout), ctypes.c_int, ctypes.c_int, ctypes.c_int, P(TcPlanInfo)]
     lib.tc_plan.restype = ctypes.c_int
     lib.tc_last_error.argtypes = []
@@ -236,6 +242,22 @@ def tile_copy_ex(src, src_layout: LayoutLike, dst, dst_layout: LayoutLike, dtype
     return info.to_dict()
 
 
+def tc_autotune(src, src_layout: LayoutLike, dst, dst_layout: LayoutLike, dtype: int, stream=None, flags: int = 0,
+                reps: int = 5) -> dict:
+    """tile_copy_ex that times the copy on the library's candidate configurations and keeps the
+    fastest as the cached plan of these layouts; returns that plan, with its mean time per launch
+    in 'tuned_ms'.  Blocks until the timed launches end."""
+    lib = load_library()
+    s, d = _as_layout(src_layout), _as_layout(dst_layout)
+    info = TcPlanInfo()
+    ms = ctypes.c_float(0.0)
+    _check(lib.tc_autotune(_ptr(src), ctypes.byref(s), _ptr(dst), ctypes.byref(d), int(dtype), _stream(stream),
+                           int(flags), int(reps), ctypes.byref(info), ctypes.byref(ms)))
+    out = info.to_dict()
+    out["tuned_ms"] = float(ms.value)
+    return out
+
+
 def tc_plan(src_layout: LayoutLike, dst_layout: LayoutLike, dtype: int, flags: int = 0, ptr_align: int = 16,
             raise_on_error: bool = True) -> dict:
     """Host-only plan of a copy (no GPU).  With raise_on_error=False the dict carries
@@ -250,6 +272,19 @@ def tc_plan(src_layout: LayoutLike, dst_layout: LayoutLike, dtype: int, flags: i
     if rc != TC_OK and raise_on_error:
         raise TileCopyError(rc, out["error"])
     return out
+
+
+def tc_plan_variants(src_layout: LayoutLike, dst_layout: LayoutLike, dtype: int, flags: int = 0,
+                     ptr_align: int = 16, max_out: int = 64) -> list:
+    """Host-only list of the plans tc_autotune would time (the planner's own first)."""
+    lib = load_library()
+    s, d = _as_layout(src_layout), _as_layout(dst_layout)
+    arr = (TcPlanInfo * max_out)()
+    n = lib.tc_plan_variants(ctypes.byref(s), ctypes.byref(d), int(dtype), int(flags), int(ptr_align), arr,
+                             int(max_out))
+    if n < 0:
+        raise TileCopyError(n, tc_last_error())
+    return [arr[i].to_dict() for i in range(min(n, max_out))]
 
 
 def tc_set_flags(flags: int) -> int:

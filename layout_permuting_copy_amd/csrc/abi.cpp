@@ -1,4 +1,6 @@
 // C ABI of the tile-copy library: argument checks, plan cache, launch.
+#include <hip/hip_runtime_api.h>
+
 #include <cstring>
 #include <memory>
 #include <mutex>
@@ -30,11 +32,24 @@ std::string layout_key(const tc_layout& l) {
   return k;
 }
 
-std::shared_ptr<const tc::Plan> get_plan(const tc_layout& s, const tc_layout& d, int dtype, int flags, int align) {
+std::string plan_key(const tc_layout& s, const tc_layout& d, int dtype, int flags, int align) {
   std::string key = layout_key(s) + layout_key(d);
   key.append(reinterpret_cast<const char*>(&dtype), sizeof(dtype));
   key.append(reinterpret_cast<const char*>(&flags), sizeof(flags));
   key.append(reinterpret_cast<const char*>(&align), sizeof(align));
+  return key;
+}
+
+// Replaces the cached plan of `key` (tc_autotune's choice).
+void put_plan(const std::string& key, std::shared_ptr<const tc::Plan> p) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_cache) g_cache = new std::unordered_map<std::string, std::shared_ptr<const tc::Plan>>();
+  if (g_cache->size() >= kCacheMax) g_cache->clear();
+  (*g_cache)[key] = std::move(p);
+}
+
+std::shared_ptr<const tc::Plan> get_plan(const tc_layout& s, const tc_layout& d, int dtype, int flags, int align) {
+  const std::string key = plan_key(s, d, dtype, flags, align);
   {
     std::lock_guard<std::mutex> lk(g_mu);
     if (!g_cache) g_cache = new std::unordered_map<std::string, std::shared_ptr<const tc::Plan>>();
@@ -62,11 +77,12 @@ int set_last_error(int code, const std::string& why) {
 }
 }  // namespace tc
 
-extern "C" {
+namespace {
 
-int tile_copy_ex(const void* src, const tc_layout* src_layout, void* dst, const tc_layout* dst_layout, int dtype,
-                 void* stream, int flags, tc_plan_info* info) {
-  g_err.clear();
+// The argument checks of a copy and its (cached) plan: TC_OK with *plan set, or an error status
+// (with *plan set where the planner ran, for the caller's info).
+int checked_plan(const void* src, const tc_layout* src_layout, const void* dst, const tc_layout* dst_layout,
+                 int dtype, int flags, std::shared_ptr<const tc::Plan>* plan, std::string* key) {
   if (!src || !dst || !src_layout || !dst_layout) return fail(TC_E_NULL, "null pointer argument");
   const int eb = tc::elem_bytes_of(dtype);
   if (eb < 0) return fail(TC_E_DTYPE, "unknown dtype " + std::to_string(dtype));
@@ -76,21 +92,93 @@ int tile_copy_ex(const void* src, const tc_layout* src_layout, void* dst, const 
   if (ps % ealign || pd % ealign)
     return fail(TC_E_ALIGN, "base pointer not aligned to the element size (" + std::to_string(eb) + " bytes)");
   const int align = ptr_alignment(ps, pd);
-  auto plan = get_plan(*src_layout, *dst_layout, dtype, flags, align);
-  if (info) tc::plan_to_info(*plan, info);
-  if (plan->status != TC_OK) return fail(plan->status, plan->reason);
-  if (plan->path == TC_PATH_EMPTY) return TC_OK;
+  if (key) *key = plan_key(*src_layout, *dst_layout, dtype, flags, align);
+  *plan = get_plan(*src_layout, *dst_layout, dtype, flags, align);
+  const tc::Plan& p = **plan;
+  if (p.status != TC_OK) return fail(p.status, p.reason);
+  if (p.path == TC_PATH_EMPTY) return TC_OK;
   // the byte images of source and destination must not overlap (side_range gives [lo, hi) in
   // elements: hi is one past the last element)
   int64_t slo, shi, dlo, dhi;
-  tc::side_range(plan->j, true, &slo, &shi);
-  tc::side_range(plan->j, false, &dlo, &dhi);
+  tc::side_range(p.j, true, &slo, &shi);
+  tc::side_range(p.j, false, &dlo, &dhi);
   const __int128 s0 = __int128(ps) + __int128(slo) * eb, s1 = __int128(ps) + __int128(shi) * eb;
   const __int128 d0 = __int128(pd) + __int128(dlo) * eb, d1 = __int128(pd) + __int128(dhi) * eb;
   if (s0 < d1 && d0 < s1) return fail(TC_E_ALIAS, "source and destination byte ranges overlap");
+  return TC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tile_copy_ex(const void* src, const tc_layout* src_layout, void* dst, const tc_layout* dst_layout, int dtype,
+                 void* stream, int flags, tc_plan_info* info) {
+  g_err.clear();
+  std::shared_ptr<const tc::Plan> plan;
+  const int st = checked_plan(src, src_layout, dst, dst_layout, dtype, flags, &plan, nullptr);
+  if (info && plan) tc::plan_to_info(*plan, info);
+  if (st != TC_OK) return st;
+  if (plan->path == TC_PATH_EMPTY) return TC_OK;
   std::string err;
   const int rc = tc::launch_plan(*plan, src, dst, stream, &err);
   if (rc != TC_OK) return fail(rc, err);
+  return TC_OK;
+}
+
+int tc_autotune(const void* src, const tc_layout* src_layout, void* dst, const tc_layout* dst_layout, int dtype,
+                void* stream, int flags, int reps, tc_plan_info* info, float* best_ms) {
+  g_err.clear();
+  std::shared_ptr<const tc::Plan> plan;
+  std::string key;
+  const int st = checked_plan(src, src_layout, dst, dst_layout, dtype, flags, &plan, &key);
+  if (info && plan) tc::plan_to_info(*plan, info);
+  if (st != TC_OK) return st;
+  if (best_ms) *best_ms = 0.0f;
+  if (plan->path == TC_PATH_EMPTY) return TC_OK;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+    return fail(TC_E_ARG, "tc_autotune times launches and cannot run on a capturing stream");
+  if (reps <= 0) reps = 5;
+  const std::vector<tc::Plan> cands = tc::plan_variants(*plan, flags);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(TC_E_HIP, "hipEventCreate failed");
+  }
+  int best = -1;
+  float best_t = 0.0f;
+  std::string err;
+  int rc = TC_OK;
+  for (size_t i = 0; i < cands.size() && rc == TC_OK; ++i) {
+    rc = tc::launch_plan(cands[i], src, dst, stream, &err);  // warm-up (and the copy itself)
+    if (rc != TC_OK) break;
+    (void)hipEventRecord(e0, s);
+    for (int r = 0; r < reps && rc == TC_OK; ++r) rc = tc::launch_plan(cands[i], src, dst, stream, &err);
+    (void)hipEventRecord(e1, s);
+    if (rc != TC_OK || hipEventSynchronize(e1) != hipSuccess) {
+      if (rc == TC_OK) {
+        rc = TC_E_HIP;
+        err = "hipEventSynchronize failed";
+      }
+      break;
+    }
+    float ms = 0.0f;
+    (void)hipEventElapsedTime(&ms, e0, e1);
+    ms /= float(reps);
+    if (best < 0 || ms < best_t) {
+      best = int(i);
+      best_t = ms;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (rc != TC_OK) return fail(rc, err);
+  auto chosen = std::make_shared<const tc::Plan>(cands[size_t(best)]);
+  put_plan(key, chosen);
+  if (info) tc::plan_to_info(*chosen, info);
+  if (best_ms) *best_ms = best_t;
   return TC_OK;
 }
 
@@ -114,6 +202,22 @@ int tc_plan(const tc_layout* src_layout, const tc_layout* dst_layout, int dtype,
   tc::plan_to_info(p, out);
   if (p.status != TC_OK) return fail(p.status, p.reason);
   return TC_OK;
+}
+
+int tc_plan_variants(const tc_layout* src_layout, const tc_layout* dst_layout, int dtype, int flags, int ptr_align,
+                     tc_plan_info* out, int max_out) {
+  g_err.clear();
+  if (!src_layout || !dst_layout || (!out && max_out > 0)) return fail(TC_E_NULL, "null pointer argument");
+  if (ptr_align < 0 || (ptr_align & (ptr_align - 1))) return fail(TC_E_ARG, "ptr_align must be a power of two");
+  if (ptr_align == 0 || ptr_align > 16) ptr_align = 16;
+  const tc::Plan p = tc::make_plan(*src_layout, *dst_layout, dtype, flags, ptr_align);
+  if (p.status != TC_OK) {
+    if (max_out > 0) tc::plan_to_info(p, out);
+    return fail(p.status, p.reason);
+  }
+  const std::vector<tc::Plan> v = tc::plan_variants(p, flags);
+  for (int i = 0; i < max_out && i < int(v.size()); ++i) tc::plan_to_info(v[size_t(i)], out + i);
+  return int(v.size());
 }
 
 const char* tc_last_error(void) { return g_err.c_str(); }

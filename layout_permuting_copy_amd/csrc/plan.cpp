@@ -1128,6 +1128,100 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
   return p;
 }
 
+// The same copy on other kernel configurations, for tc_autotune: the plan itself first, then, for
+// a transpose (not the pair-reading one), the conflict-free tiles of a fixed list of
+// configurations the library holds kernels for (tall 16-byte-unit tiles of 32-128 KiB in both
+// row-tile-first and XCD super-tile orders, the width's default tile in both plain orders, loads
+// capped at 2 for 1- and 2-byte elements; for element-aligned plans, their small tiles in three
+// orders), and for the aligned 16-byte rows path its vectors per lane (1, 2, 4) with and without
+// buffer accesses.  Duplicates are dropped.  No configuration is better everywhere: measured on
+// MI355X, the best fp32 tile of 0.25-1 GiB transposes changed with the extents in no pattern the
+// planner's rules capture.
+std::vector<Plan> plan_variants(const Plan& p, int flags) {
+  std::vector<Plan> out{p};
+  if (p.status != TC_OK || (flags & TC_FLAG_NO_SWIZZLE)) return out;  // (a measurement of the plan's tile)
+  const Joint& j = p.j;
+  if (p.path == TC_PATH_TRANSPOSE && !p.nar) {
+    const int unit0 = p.eb < 4 ? 4 : p.eb;
+    std::vector<TuneCfg> cands;
+    auto add = [&](int tile, int threads, int trb, int unit, int nt, int order, int cap, int ssr, int ssc) {
+      TuneCfg t;
+      t.tile = tile; t.threads = threads; t.trb = trb; t.unit = unit; t.nt = nt; t.order = order; t.cap = cap;
+      t.ssr = ssr; t.ssc = ssc;
+      cands.push_back(t);
+    };
+    if (!p.unaligned && p.step == 1) {
+      const int tall[][3] = {{65536, 512, 1024}, {32768, 512, 512}, {32768, 512, 1024}, {32768, 256, 512},
+                             {65536, 512, 2048}, {131072, 1024, 1024}, {131072, 1024, 2048}, {131072, 512, 512}};
+      for (const auto& t : tall) {
+        add(t[0], t[1], t[2], 16, 3, 1, 0, 0, 0);
+        add(t[0], t[1], t[2], 16, 3, 2, 0, 4, 4);
+        if (p.eb <= 2) add(t[0], t[1], t[2], 16, 3, 1, 2, 0, 0);
+      }
+      add(65536, 512, 1024, 16, 3, 2, 0, 2, 8);
+      add(65536, 512, 1024, 16, 3, 2, 0, 8, 2);
+      if (p.eb == 1) add(131072, 512, 512, 16, 3, 2, 2, 16, 2);
+      const TuneCfg d = default_cfg(p.eb, pow2ceil(j.m[p.mode_r].e) * p.eb < 128, false);
+      add(d.tile, d.threads, 0, unit0, 3, 0, 0, 0, 0);
+      add(d.tile, d.threads, 0, unit0, 3, 1, 0, 0, 0);
+    } else {
+      const int small[][2] = {{8192, 256}, {16384, 256}, {16384, 512}};
+      for (const auto& t : small)
+        for (int order = 0; order <= 2; ++order) add(t[0], t[1], 0, unit0, 0, order, 0, 0, 0);
+    }
+    bool src_lines = (j.so * p.eb) % 128 == 0;
+    for (int k = 0; k < j.rank; ++k)
+      if (k != p.mode_c && (std::llabs(j.m[k].s) * p.eb) % 128 != 0) src_lines = false;
+    const int64_t eB = p.mode_b >= 0 ? j.m[p.mode_b].e : 1;
+    for (const TuneCfg& t : cands) {
+      TileGeom g;
+      int64_t wc, rc;
+      if (!plan_with_cfg(p, flags & ~TC_FLAG_NO_SWIZZLE, t, true, &g, &wc, &rc) || wc + rc != 0) continue;
+      g.pad_rows = g.order == 1 && !src_lines;
+      g.wave_local = false;
+      g.edges = j.m[p.mode_r].e % g.TR != 0 || j.m[p.mode_c].e % g.TC != 0 || eB % g.NB != 0 || g.step != 1 ||
+                p.eb == 16 || p.unaligned;
+      // (the interior-only kernels exist for the nontemporal configurations only)
+      if (!g.edges && !launch_transpose(g.eb, transpose_cfg(g), nullptr, 0, nullptr)) g.edges = true;
+      if (!launch_transpose(g.eb, transpose_cfg(g), nullptr, 0, nullptr)) continue;
+      Plan q = p;
+      q.g = g;
+      q.wconf = wc;
+      q.rconf = rc;
+      q.threads = g.NT;
+      q.load_outer = g.loads;
+      q.store_outer = g.stores;
+      q.lds_bytes = g.tile_bytes;
+      q.workgroups = transpose_workgroups(q, q.mode_r, q.mode_c, q.mode_b);
+      if (q.workgroups >= (int64_t(1) << 31)) continue;
+      bool dup = false;
+      for (const Plan& o : out) {
+        const TileGeom& h = o.g;
+        dup = dup || (h.TR == g.TR && h.TC == g.TC && h.NB == g.NB && h.NT == g.NT && h.U == g.U &&
+                      h.tile_bytes == g.tile_bytes && h.ntm == g.ntm && h.order == g.order && h.cap == g.cap &&
+                      h.edges == g.edges && h.wave_local == g.wave_local &&
+                      (g.order != 2 || (h.lsr == g.lsr && h.lsc == g.lsc)));
+      }
+      if (!dup) out.push_back(q);
+    }
+  } else if (p.path == TC_PATH_ROWS && p.vb == 16 && !p.unaligned) {
+    for (int rr : {1, 2, 4})
+      for (int buf = 0; buf <= 1; ++buf) {
+        Plan q = p;
+        q.row_rounds = rr;
+        q.buffers = buf != 0;
+        q.row_burst = p.row_burst;
+        const int64_t nvec = j.count / (p.vb / p.eb);
+        q.workgroups = ceil_div(nvec, int64_t(q.threads) * rr);
+        q.load_outer = q.store_outer = int(std::min<int64_t>(rr, ceil_div(nvec, q.threads)));
+        if (rr == p.row_rounds && q.buffers == p.buffers) continue;
+        if (!rows_fit(rows_grid(q), nvec)) continue;
+        out.push_back(q);
+      }
+  }
+  return out;
+}
+
 void plan_to_info(const Plan& p, tc_plan_info* info) {
   *info = tc_plan_info{};
   info->path = p.path;

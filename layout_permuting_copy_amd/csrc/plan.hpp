@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <string>
+#include <vector>
 
 #include "tile_copy.h"
 
@@ -165,6 +166,8 @@ struct Plan {
 int elem_bytes_of(int dtype);
 // Plans a copy.  ptr_align: byte alignment of both base pointers (power of two, <= 16).
 Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags, int ptr_align);
+// The plan first, then the same copy on other kernel configurations (tc_autotune).
+std::vector<Plan> plan_variants(const Plan& p, int flags);
 void plan_to_info(const Plan& p, tc_plan_info* info);
 
 // ---- kernel argument blocks (passed by value) ------------------------------------------------

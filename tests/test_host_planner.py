@@ -737,3 +737,34 @@ def test_modes_walked_backwards_are_reversed():
     assert (p["path_name"], p["declined"], p["dst_stride"][:2]) == ("transpose", 0, (-n, 1)), p
     p = plan((n, n), (n, -1), n - 1, (n, 1), 0)   # a flipped source row: gathered rows, not reversed
     assert (p["path_name"], p["src_step"], p["src_offset"]) == ("rows", -1, n - 1), p
+
+
+def test_plan_variants_for_autotune():
+    """The configurations tc_autotune times: the planner's plan first, then the same copy on other
+    tiles (transposes: conflict-free, distinct, the same path and modes) or other vector counts
+    (rows); one plan under TC_FLAG_NO_SWIZZLE; the planner's error for a copy it rejects."""
+    n = 4096
+    s, d = ((n, n), (n, 1), 0), ((n, n), (1, n), 0)
+    for dt in (L.TC_I8, L.TC_BF16, L.TC_F32, L.TC_F64, L.TC_B128):
+        v = L.tc_plan_variants(s, d, dt)
+        base = L.tc_plan(s, d, dt)
+        assert v[0] == {k: base[k] for k in v[0]}, dt
+        assert len(v) >= 3, (dt, len(v))
+        seen = set()
+        for p in v:
+            assert p["path_name"] == "transpose" and p["count"] == n * n
+            assert p["write_conflicts"] == 0 and p["read_conflicts"] == 0
+            key = (p["tile_r"], p["tile_c"], p["tile_b"], p["threads"], p["grid_order"], p["super_rows"],
+                   p["super_cols"], p["loads_in_flight"], p["nontemporal"], p["edge_tiles"], p["lds_write_bytes"],
+                   p["lds_read_bytes"])
+            assert key not in seen, key
+            seen.add(key)
+    # odd extents: the element-aligned tiles in three grid orders
+    v = L.tc_plan_variants(((8191, 8190), (8190, 1), 0), ((8191, 8190), (1, 8191), 0), L.TC_I8)
+    assert len(v) >= 3 and all(p["unaligned"] == 1 for p in v)
+    # rows: vectors per lane
+    v = L.tc_plan_variants(((1 << 24,), (1,), 0), ((1 << 24,), (1,), 0), L.TC_F32)
+    assert {p["load_outer"] for p in v} == {1, 2, 4} and all(p["path_name"] == "rows" for p in v)
+    assert len(L.tc_plan_variants(s, d, L.TC_F32, flags=L.TC_FLAG_NO_SWIZZLE)) == 1
+    with pytest.raises(L.TileCopyError):
+        L.tc_plan_variants(((8191, 8190), (8190, 1), 0), ((8191, 8190), (1, 8191), 0), L.TC_I8, flags=L.TC_FLAG_STRICT)
