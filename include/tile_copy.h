@@ -214,9 +214,14 @@ int tile_copy_ex(const void* src, const tc_layout* src_layout, void* dst, const 
  * dst[dst_layout(i)] = src[src_layout(i)]; TVM TIRx docs, "copy -> gmem_smem") is run on the
  * planner's choice and on the other kernel configurations the library holds for it (transposes:
  * conflict-free tiles of a fixed list of shapes and grid orders; the aligned rows path: vectors
- * per lane and buffer accesses), each once to warm up and then `reps` times (0 or less: 5) between
- * two HIP events on `stream`; the fastest becomes the cached plan of these layouts, dtype, flags
- * and pointer alignment, which later tile_copy / tile_copy_ex calls reuse.  The tuning itself is
+ * per lane and buffer accesses), in three rounds over the candidates, each time once to warm up
+ * and then `reps` times (0 or less: 5) between two HIP events on `stream`; the candidate with the
+ * lowest median round becomes the cached plan of these layouts, dtype, flags and pointer
+ * alignment, which later tile_copy / tile_copy_ex calls reuse -- the planner's own plan unless
+ * another is at least 3% faster (10% where source and destination span less than 512 MiB: the
+ * launches run back to back on the caller's buffers, and copies that fit the 256 MB MALL then
+ * find much of their data cached, which can rank configurations differently than copies of fresh
+ * data do).  The tuning itself is
  * the library's own addition (the pages plan by rule only).  Every configuration writes the same
  * bytes, so `dst` holds the copy on return.  Blocks the calling thread until the timed launches
  * end; `stream` must not be capturing (TC_E_ARG).  `info` (may be NULL) receives the chosen plan,

@@ -1168,6 +1168,12 @@ std::vector<Plan> plan_variants(const Plan& p, int flags) {
       const int small[][2] = {{8192, 256}, {16384, 256}, {16384, 512}};
       for (const auto& t : small)
         for (int order = 0; order <= 2; ++order) add(t[0], t[1], 0, unit0, 0, order, 0, 0, 0);
+      if (p.step == 1) {  // the tall tiles of the destination-misaligned 1- and 2-byte plans
+        add(65536, 512, 1024, 16, 0, 2, 0, 0, 0);
+        add(65536, 512, 1024, 16, 3, 2, 2, 0, 0);
+        add(131072, 512, 512, 16, 3, 2, 2, 16, 2);
+        add(131072, 512, 512, 16, 0, 2, 2, 16, 2);
+      }
     }
     bool src_lines = (j.so * p.eb) % 128 == 0;
     for (int k = 0; k < j.rank; ++k)
