@@ -303,6 +303,7 @@ def sweep_workloads():
     ws += [SI.sweep_odd(dt) for dt in SI.SWEEP_DTYPES]
     ws += [SI.sweep_slice(dt) for dt in SI.SWEEP_DTYPES]
     ws += [SI.sweep_slice_rows(dt) for dt in SI.SWEEP_DTYPES]
+    ws += [SI.a2a_pack_permute0213(), SI.a2a_unpack_permute0213()]
     return ws
 
 
@@ -392,6 +393,7 @@ def main() -> int:
         context = [SI.tile32_roundtrip(), identity_workload()]
         context += [SI.sweep_odd(dt) for dt in SI.SWEEP_DTYPES] + [SI.sweep_slice(dt) for dt in SI.SWEEP_DTYPES]
         context += [SI.sweep_slice_rows(dt) for dt in SI.SWEEP_DTYPES]
+        context += [SI.a2a_pack_permute0213(), SI.a2a_unpack_permute0213()]  # one GPU's share, 8 GPUs
         runs = [(sw, 0) for sw in context]
         runs += [(SI.sf_transpose(), L.TC_FLAG_NO_SHUFFLE), (SI.permute0213(), L.TC_FLAG_FORCE_LDS)]
         runs += [(sw, 0) for sw in target]

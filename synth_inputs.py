@@ -124,6 +124,30 @@ def permute0213(b: int = 32, h: int = 32, s: int = 2048, d: int = 128, dtype: st
                     dtype, "normal", seed=4)
 
 
+def a2a_pack_permute0213(g: int = 8, b: int = 32, h: int = 32, s: int = 2048, d: int = 128,
+                         dtype: str = "bfloat16") -> Workload:
+    """One GPU's pack before the all-to-all that turns the (0,2,1,3) permute sharded on H into
+    its output sharded on S, over g GPUs: the local shard X[b, h/g, s, d] (row-major) goes to a
+    send buffer P[g, b, s/g, h/g, d] (row-major) with P[q, i, j, k, l] = X[i, k, q*s/g + j, l]."""
+    hl, sl = h // g, s // g
+    return Workload(f"a2a_pack_permute0213_g{g}_{b}x{h}x{s}x{d}_{dtype}",
+                    Side((g, b, sl, hl, d), (sl * d, hl * s * d, d, s * d, 1)),
+                    Side((g, b, sl, hl, d), (b * sl * hl * d, sl * hl * d, hl * d, d, 1)),
+                    dtype, "bits", seed=57)
+
+
+def a2a_unpack_permute0213(g: int = 8, b: int = 32, h: int = 32, s: int = 2048, d: int = 128,
+                           dtype: str = "bfloat16") -> Workload:
+    """The receiving GPU's unpack after that all-to-all: the buffer R[g, b, s/g, h/g, d] received
+    from the g senders (row-major) into its output shard Y[b, s/g, h, d] (row-major), with
+    Y[i, j, q*h/g + k, l] = R[q, i, j, k, l]."""
+    hl, sl = h // g, s // g
+    return Workload(f"a2a_unpack_permute0213_g{g}_{b}x{h}x{s}x{d}_{dtype}",
+                    Side((g, b, sl, hl, d), (b * sl * hl * d, sl * hl * d, hl * d, d, 1)),
+                    Side((g, b, sl, hl, d), (hl * d, sl * h * d, h * d, d, 1)),
+                    dtype, "bits", seed=58)
+
+
 SWEEP_DTYPES = ("int8", "float16", "float64", "int4vec")
 SWEEP_SEEDS = {"int8": 50, "float16": 51, "float64": 52, "int4vec": 53}
 

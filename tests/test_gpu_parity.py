@@ -95,6 +95,15 @@ def test_cfg4_permute0213_full():
     check_workload(SI.permute0213(), expect_path="rows")
 
 
+@pytest.mark.parametrize("which", ["pack", "unpack"])
+def test_all_to_all_pack_unpack_full_size(which):
+    """One GPU's share of the (0,2,1,3) permute sharded over 8 GPUs (heads in, sequence out): the
+    pack into per-destination blocks before the all-to-all and the unpack after it, at their
+    per-GPU shape (32 x 4 x 2048 x 128 bf16, 64 MiB a side)."""
+    w = SI.a2a_pack_permute0213() if which == "pack" else SI.a2a_unpack_permute0213()
+    check_workload(w, expect_path="rows")
+
+
 @pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
 def test_cfg5_dense_8192(dtype):
     check_workload(SI.sweep_dense(dtype), expect_path="transpose")

@@ -768,3 +768,33 @@ def test_plan_variants_for_autotune():
     assert len(L.tc_plan_variants(s, d, L.TC_F32, flags=L.TC_FLAG_NO_SWIZZLE)) == 1
     with pytest.raises(L.TileCopyError):
         L.tc_plan_variants(((8191, 8190), (8190, 1), 0), ((8191, 8190), (1, 8191), 0), L.TC_I8, flags=L.TC_FLAG_STRICT)
+
+
+def test_all_to_all_pack_and_unpack_compose_the_sharded_permute():
+    """The (0,2,1,3) permute of X[B, H, S, D] sharded on H over G GPUs, with its output sharded on
+    S: each GPU packs its heads into per-destination blocks (a2a_pack_permute0213), an
+    all-to-all swaps the blocks, and each GPU unpacks what it received (a2a_unpack_permute0213).
+    Run with the oracle copy and a host all-to-all on a small case, every output shard equals the
+    permuted tensor's slice; both copies plan as rows (the head dimension contiguous on both
+    sides)."""
+    from oracle import ref as R
+    g, b, h, s, d = 4, 2, 8, 16, 3
+    hl, sl = h // g, s // g
+    x = np.random.default_rng(5).standard_normal((b, h, s, d)).astype(np.float32)
+    wp, wu = SI.a2a_pack_permute0213(g, b, h, s, d, "float32"), SI.a2a_unpack_permute0213(g, b, h, s, d, "float32")
+    sent = []
+    for r in range(g):
+        xr = np.ascontiguousarray(x[:, r * hl:(r + 1) * hl])
+        out = np.zeros(g * b * sl * hl * d, dtype=np.float32)
+        R.copy(xr.view(np.uint8).ravel(), (wp.src.shape, wp.src.stride, 0), out.view(np.uint8),
+               (wp.dst.shape, wp.dst.stride, 0), 4)
+        sent.append(out.reshape(g, b * sl * hl * d))
+    want = x.transpose(0, 2, 1, 3)  # [B, S, H, D]
+    for q in range(g):
+        recv = np.stack([sent[r][q] for r in range(g)]).ravel()  # from every sender, in rank order
+        y = np.zeros(b * sl * h * d, dtype=np.float32)
+        R.copy(recv.view(np.uint8), (wu.src.shape, wu.src.stride, 0), y.view(np.uint8),
+               (wu.dst.shape, wu.dst.stride, 0), 4)
+        assert np.array_equal(y.reshape(b, sl, h, d), want[:, q * sl:(q + 1) * sl]), q
+    for w in (SI.a2a_pack_permute0213(), SI.a2a_unpack_permute0213()):
+        assert _plan(w)["path_name"] == "rows", w.name
