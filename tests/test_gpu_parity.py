@@ -77,12 +77,9 @@ def test_shuffle_blocks(C, nb, pad_s, pad_d, soff, doff):
     a ragged last workgroup)."""
     shape, ss, ds = (nb, 4, C), (4 * C + pad_s, C, 1), (4 * C + pad_d, 1, 4)
     p = _check(shape, ss, ds, 4, s_off=soff, d_off=doff, seed=nb + C)
-    if (nb * 4 * C) % 64:
-        # the element count does not divide the wavefront: the aligned split is declined and the
-        # transpose kernel runs with vectors at element alignment
-        assert p["path_name"] == "transpose" and p["declined"] == 1 and p["unaligned"] == 1, p
-    else:
-        assert p["path_name"] == "shuffle"
+    # (an element count that does not divide the wavefront declines the page's split, but the
+    # vectors are whole and aligned: the butterfly still runs, its last workgroup guarded)
+    assert p["path_name"] == "shuffle" and p["declined"] == int((nb * 4 * C) % 64 != 0), p
 
 
 @pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
@@ -127,7 +124,9 @@ def test_cfg5_slice_rows_8192(dtype):
 @pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
 def test_cfg5_odd_8191x8190(dtype):
     plan = check_workload(SI.sweep_odd(dtype))
-    assert plan["declined"] == 1 and plan["path_name"] == "transpose" and plan["unaligned"] == 1
+    # (16-byte elements are whole aligned vectors: the aligned kernels, the page's reason kept)
+    wide = SI.elem_bytes(dtype) == 16
+    assert plan["declined"] == 1 and plan["path_name"] == "transpose" and plan["unaligned"] == int(not wide)
 
 
 def test_cfg5_odd_strict_declines():
@@ -158,10 +157,11 @@ def test_transpose_unaligned(eb, n, m, soff, doff, batch):
                                                           16: L.TC_B128}[eb])
     assert p["path_name"] == "transpose"
     # 65 x 64 and 64 x 65 have an aligned vector of one element from 4-byte elements up: the
-    # page's plan (strict mode) takes it; by default only 16-byte elements keep it (narrower
-    # vectors give way to 16-byte ones at element alignment)
+    # page's plan (strict mode) takes it; by default narrower vectors give way to 16-byte ones at
+    # element alignment, and 16-byte elements, always whole aligned vectors, take the aligned
+    # kernels (also where only the count rule declines)
     page_vec = eb >= 4 and (n, m) in ((65, 64), (64, 65)) and batch == 1 and soff == doff == 0
-    assert p["unaligned"] == (eb < 16 or not page_vec)
+    assert p["unaligned"] == (eb < 16)
     _check(shape, ss, ds, eb, s_off=soff, d_off=doff, seed=n + m + eb, expect="transpose")
     if page_vec and eb < 16:
         sp = _check(shape, ss, ds, eb, seed=n + m + eb, flags=L.TC_FLAG_STRICT, expect="transpose")
@@ -342,11 +342,9 @@ def test_reversed_modes(eb):
     assert p["path_name"] == ("guarded_rows" if eb == 16 else "rows"), p
     p = _check((n, m), (m, 1), (-1, n), eb, d_off=n - 1, seed=eb + 501, expect="transpose")
     assert p["src_step"] == 1, p
-    # (16-byte elements: a count not divisible by 64 takes the element-wise rows, 16 bytes apiece)
-    rows = "guarded_rows" if eb == 16 else "rows"
-    p = _check((n, m), (m, -1), (m, -1), eb, s_off=m - 1, d_off=m - 1, seed=eb + 502, expect=rows)
+    p = _check((n, m), (m, -1), (m, -1), eb, s_off=m - 1, d_off=m - 1, seed=eb + 502, expect="rows")
     assert p["rank"] == 1, p
-    p = _check((n, m), (-m, 1), (-m, 1), eb, s_off=(n - 1) * m, d_off=(n - 1) * m, seed=eb + 503, expect=rows)
+    p = _check((n, m), (-m, 1), (-m, 1), eb, s_off=(n - 1) * m, d_off=(n - 1) * m, seed=eb + 503, expect="rows")
     assert p["rank"] == 1 and p["src_stride"][0] == 1 and p["dst_stride"][0] == 1, p
 
 

@@ -68,7 +68,10 @@ def test_workload_paths_and_declines():
             assert p["write_conflicts"] == 0 and p["read_conflicts"] == 0, w.name
         declined = w.name.startswith(("slice_", "transpose_8191x8190"))
         assert p["declined"] == int(declined), w.name
-        assert p["unaligned"] == int(declined and not wide_rows), w.name
+        # (16-byte elements of the odd transpose are whole aligned vectors: the aligned kernels
+        # run it, with the page's reason kept)
+        whole = w.name.startswith("transpose_8191x8190") and w.eb == 16
+        assert p["unaligned"] == int(declined and not wide_rows and not whole), w.name
         # the stride-2 slice reads every vector as two contiguous ones (transposed), or gathers
         # each destination vector from its source span (rows)
         step = 0 if wide_rows else 2 if w.name.startswith("slice_") else 1 if p["path_name"] == "transpose" else 0
@@ -700,8 +703,10 @@ def test_transposes_from_reversed_source_columns():
             if -k >= 3 and -k * L.ELEM_BYTES[dt] > 12:
                 assert p["path_name"] == "guarded_tile", p
                 continue
-            # stride -1: the column index reversed, read forwards
-            assert (p["path_name"], p["src_step"], p["unaligned"]) == ("transpose", 1 if k == -1 else k, 1), p
+            # stride -1: the column index reversed, read forwards (16-byte elements: then whole
+            # aligned vectors, the aligned kernels)
+            unaligned = 0 if (k == -1 and L.ELEM_BYTES[dt] == 16) else 1
+            assert (p["path_name"], p["src_step"], p["unaligned"]) == ("transpose", 1 if k == -1 else k, unaligned), p
             assert p["write_conflicts"] == 0 and p["read_conflicts"] == 0, p
     # rot90, the transpose of the column-flipped matrix: the column index reversed (both strides
     # negated, the offsets moved to its other end), then the aligned transpose
@@ -798,3 +803,22 @@ def test_all_to_all_pack_and_unpack_compose_the_sharded_permute():
         assert np.array_equal(y.reshape(b, sl, h, d), want[:, q * sl:(q + 1) * sl]), q
     for w in (SI.a2a_pack_permute0213(), SI.a2a_unpack_permute0213()):
         assert _plan(w)["path_name"] == "rows", w.name
+
+
+def test_count_declines_with_whole_aligned_vectors_take_the_aligned_kernels():
+    """A copy the page's count rule declines (count not a multiple of 64) but whose 16-byte
+    vectors are whole and aligned on both sides runs the aligned kernels outside strict mode
+    (unaligned 0, the page's reason kept); with odd rows it stays on the element-aligned ones."""
+    def plan(shape, ss, ds, dt, so=0, flags=0):
+        return L.tc_plan((shape, ss, so), (shape, ds, 0), dt, flags=flags, raise_on_error=False)
+
+    p = plan((8190 * 8176,), (1,), (1,), L.TC_I8)
+    assert (p["path_name"], p["declined"], p["unaligned"], p["vec_bytes"]) == ("rows", 1, 0, 16), p
+    assert "no integer solution" in p["reason"]
+    p = plan((8191, 8184), (8184, 1), (8184, 1), L.TC_F32)   # rows of whole vectors
+    assert (p["path_name"], p["declined"], p["unaligned"]) == ("rows", 1, 0), p
+    p = plan((8184, 8191), (8191, 1), (1, 8184), L.TC_F32)   # source rows odd: element-aligned
+    assert (p["path_name"], p["declined"], p["unaligned"]) == ("transpose", 1, 1), p
+    p = plan((1000,), (1,), (1,), L.TC_F32, so=1)            # misaligned: element-aligned rows
+    assert (p["path_name"], p["unaligned"]) == ("rows", 1), p
+    assert plan((8190 * 8176,), (1,), (1,), L.TC_I8, flags=L.TC_FLAG_STRICT)["status"] == L.TC_E_DECLINED
