@@ -213,8 +213,8 @@ int tile_copy_ex(const void* src, const tc_layout* src_layout, void* dst, const 
  * tile_copy_ex that also picks the plan by measurement: the same copy (the pages' operation,
  * dst[dst_layout(i)] = src[src_layout(i)]; TVM TIRx docs, "copy -> gmem_smem") is run on the
  * planner's choice and on the other kernel configurations the library holds for it (transposes:
- * conflict-free tiles of a fixed list of shapes and grid orders; the aligned rows path: vectors
- * per lane and buffer accesses), in three rounds over the candidates, each time once to warm up
+ * conflict-free tiles of a fixed list of shapes and grid orders; the rows paths: vectors per
+ * lane, and buffer accesses on the aligned one), in three rounds over the candidates, each time once to warm up
  * and then `reps` times (0 or less: 5) between two HIP events on `stream`; the candidate with the
  * lowest median round becomes the cached plan of these layouts, dtype, flags and pointer
  * alignment, which later tile_copy / tile_copy_ex calls reuse -- the planner's own plan unless

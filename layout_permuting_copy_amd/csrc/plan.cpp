@@ -1217,6 +1217,19 @@ std::vector<Plan> plan_variants(const Plan& p, int flags) {
       }
       if (!dup) out.push_back(q);
     }
+  } else if (p.path == TC_PATH_ROWS && p.unaligned && p.step == 1) {
+    // element-aligned rows: 1, 2 or 4 vectors per lane (measured 2-4% apart either way on 64 MiB
+    // int8 copies at odd offsets, in no pattern)
+    const int64_t rows = j.count / j.m[j.rank - 1].e;
+    const int64_t nvec = rows * ceil_div(j.m[j.rank - 1].e, int64_t(16 / p.eb));
+    for (int rr : {1, 2, 4}) {
+      if (rr == p.row_rounds) continue;
+      Plan q = p;
+      q.row_rounds = rr;
+      q.workgroups = ceil_div(nvec, int64_t(q.threads) * rr);
+      q.load_outer = q.store_outer = int(std::min<int64_t>(rr, ceil_div(nvec, q.threads)));
+      out.push_back(q);
+    }
   } else if (p.path == TC_PATH_ROWS && p.vb == 16 && !p.unaligned) {
     for (int rr : {1, 2, 4})
       for (int buf = 0; buf <= 1; ++buf) {

@@ -32,6 +32,7 @@ def _key(p):
     ((777, 1029), (1030, 1), 3, (1, 777), 1),          # odd int8 transpose at element alignment
     ((300, 257), (257 * 2, 2), 0, (1, 300), 2),        # stride-2 source
     ((1 << 22,), (1,), 0, (1,), 4),                    # contiguous rows
+    ((2000, 1999), (2048, 1), 2049, (1999, 1), 1),     # a window at an odd offset (element-aligned rows)
     ((64, 96, 128), (96 * 128, 128, 1), 0, (128, 64 * 128, 1), 2),  # permuted rows
 ])
 def test_autotune_copies_and_caches(shape, ss, so, ds, eb):

@@ -767,9 +767,12 @@ def test_plan_variants_for_autotune():
     # odd extents: the element-aligned tiles in three grid orders
     v = L.tc_plan_variants(((8191, 8190), (8190, 1), 0), ((8191, 8190), (1, 8191), 0), L.TC_I8)
     assert len(v) >= 3 and all(p["unaligned"] == 1 for p in v)
-    # rows: vectors per lane
+    # rows: vectors per lane (aligned rows, and element-aligned rows such as a window at an odd
+    # offset)
     v = L.tc_plan_variants(((1 << 24,), (1,), 0), ((1 << 24,), (1,), 0), L.TC_F32)
     assert {p["load_outer"] for p in v} == {1, 2, 4} and all(p["path_name"] == "rows" for p in v)
+    v = L.tc_plan_variants(((1000, 1000), (1024, 1), 1025), ((1000, 1000), (1000, 1), 0), L.TC_I8)
+    assert [p["load_outer"] for p in v] == [4, 1, 2] and all(p["unaligned"] == 1 for p in v), v
     assert len(L.tc_plan_variants(s, d, L.TC_F32, flags=L.TC_FLAG_NO_SWIZZLE)) == 1
     with pytest.raises(L.TileCopyError):
         L.tc_plan_variants(((8191, 8190), (8190, 1), 0), ((8191, 8190), (1, 8191), 0), L.TC_I8, flags=L.TC_FLAG_STRICT)
