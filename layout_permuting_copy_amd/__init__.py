@@ -334,3 +334,17 @@ def torch_dtype_code(torch_dtype) -> int:
              torch.float32: TC_F32, torch.int32: TC_I32, torch.float64: TC_F64, torch.int64: TC_I64,
              torch.int16: TC_F16, torch.uint16: TC_F16 if hasattr(torch, "uint16") else TC_F16}
     return table[torch_dtype]
+
+
+def copy_tensor(dst, src, stream=None) -> dict:
+    """dst[...] = src[...] for two device tensors of the same shape and element width, through
+    their own strides (views: transposes, permutes, slices, expanded sources): the layouts are the
+    tensors' shape and strides from their data pointers.  Returns the plan that ran."""
+    if tuple(dst.shape) != tuple(src.shape):
+        raise ValueError(f"shapes differ: {tuple(dst.shape)} and {tuple(src.shape)}")
+    if dst.element_size() != src.element_size():
+        raise ValueError("element widths differ")
+    code = torch_dtype_code(src.dtype)
+    shape = tuple(int(e) for e in src.shape)
+    return tile_copy_ex(src, (shape, tuple(int(s) for s in src.stride()), 0), dst,
+                        (shape, tuple(int(s) for s in dst.stride()), 0), code, stream)
