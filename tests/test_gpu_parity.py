@@ -54,17 +54,17 @@ def _check(shape, s_stride, d_stride, eb, s_off=0, d_off=0, src_elems=None, dst_
 
 # --- the five workloads -----------------------------------------------------------------------
 
-def test_cfg1_tile32_roundtrip_one_wave():
+def test_tile32_roundtrip_one_wave():
     plan = check_workload(SI.tile32_roundtrip(), expect_path="roundtrip")
     assert (plan["threads"], plan["load_outer"], plan["vec_bytes"], plan["workgroups"]) == (64, 4, 16, 1)
 
 
-def test_cfg2_sf_transpose_full():
+def test_sf_transpose_full():
     plan = check_workload(SI.sf_transpose(), expect_path="shuffle")
     assert (plan["tile_r"], plan["tile_c"]) == (4, 32)
 
 
-def test_cfg2_sf_transpose_full_lds_tile():
+def test_sf_transpose_full_lds_tile():
     plan = check_workload(SI.sf_transpose(), flags=L.TC_FLAG_NO_SHUFFLE, expect_path="transpose")
     assert plan["write_conflicts"] == 0 and plan["read_conflicts"] == 0 and plan["wave_local"] == 1
 
@@ -83,12 +83,12 @@ def test_shuffle_blocks(C, nb, pad_s, pad_d, soff, doff):
 
 
 @pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
-def test_cfg3_transpose_16384(dtype):
+def test_transpose_16384(dtype):
     plan = check_workload(SI.transpose2d(dtype=dtype), expect_path="transpose")
     assert plan["write_conflicts"] == 0 and plan["read_conflicts"] == 0
 
 
-def test_cfg4_permute0213_full():
+def test_permute0213_full():
     check_workload(SI.permute0213(), expect_path="rows")
 
 
@@ -102,18 +102,18 @@ def test_all_to_all_pack_unpack_full_size(which):
 
 
 @pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
-def test_cfg5_dense_8192(dtype):
+def test_dense_transposes_8192(dtype):
     check_workload(SI.sweep_dense(dtype), expect_path="transpose")
 
 
 @pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
-def test_cfg5_slice_8192(dtype):
+def test_slice_8192(dtype):
     plan = check_workload(SI.sweep_slice(dtype))
     assert plan["declined"] == 1 and plan["path_name"] == "transpose" and plan["src_step"] == 2
 
 
 @pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
-def test_cfg5_slice_rows_8192(dtype):
+def test_slice_rows_8192(dtype):
     """The same slice written out densely in its own row order: gathered rows (16-byte elements:
     the element-wise rows, one element per access)."""
     plan = check_workload(SI.sweep_slice_rows(dtype))
@@ -122,14 +122,14 @@ def test_cfg5_slice_rows_8192(dtype):
 
 
 @pytest.mark.parametrize("dtype", SI.SWEEP_DTYPES)
-def test_cfg5_odd_8191x8190(dtype):
+def test_odd_8191x8190(dtype):
     plan = check_workload(SI.sweep_odd(dtype))
     # (16-byte elements are whole aligned vectors: the aligned kernels, the page's reason kept)
     wide = SI.elem_bytes(dtype) == 16
     assert plan["declined"] == 1 and plan["path_name"] == "transpose" and plan["unaligned"] == int(not wide)
 
 
-def test_cfg5_odd_strict_declines():
+def test_odd_strict_declines():
     import torch
     w = SI.sweep_odd("float32", 191, 190)
     src = torch.zeros(191 * 190, dtype=torch.float32, device="cuda")
