@@ -473,7 +473,9 @@ void launch_rows(const Plan& p, const RowArgs& ra, int64_t wgs, hipStream_t s) {
     else hipLaunchKernelGGL((dev::rows_unaligned_kernel<E, kRowThreads, R, false>), grid, block, 0, s, ra);    \
   }
 #define TC_RG(E, K)                                                                                              \
-  if (p.eb == E && p.step == K)                                                                                  \
+  if (p.eb == E && p.step == K && p.row_rounds == 1)                                                             \
+    hipLaunchKernelGGL((dev::rows_unaligned_kernel<E, kRowThreads, 1, false, K>), grid, block, 0, s, ra);          \
+  if (p.eb == E && p.step == K && p.row_rounds == kRowRounds && kRowRounds != 1)                                 \
     hipLaunchKernelGGL((dev::rows_unaligned_kernel<E, kRowThreads, kRowRounds, false, K>), grid, block, 0, s, ra);
 #define TC_RU3(E) TC_RU(E, 1) TC_RU(E, 2) TC_RU(E, 4)                                      \
   TC_RG(E, 2) TC_RG(E, 3) TC_RG(E, 4) TC_RG(E, -1) TC_RG(E, -2) TC_RG(E, -3) TC_RG(E, -4)

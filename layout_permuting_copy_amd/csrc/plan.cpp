@@ -1083,7 +1083,13 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     {
       const TuneCfg tc = tune_override();
       p.buffers = !gather && tc.buf != 0;
-      p.row_rounds = kRowRounds;
+      // one vector per lane for gathered rows (measured against 4 on 8192-row copies: int8 every
+      // 2nd / 3rd / 4th column 3.36 -> 3.59, 2.36 -> 2.58, 1.93 -> 2.09 TB/s, fp32 every 4th
+      // 2.16 -> 2.41, fp16 / fp32 / fp64 every 2nd +3%, the 8190 x 4095 int8 slice 3.21 -> 3.52,
+      // rows flipped: int8 5.28 -> 5.59, fp16 5.69 -> 5.9), except rows flipped with 4- and 8-byte
+      // elements (one load per vector), which keep 4 (fp32 6.26 against 5.91-5.99, fp64 6.35
+      // against 5.79-5.83)
+      p.row_rounds = gather && !(gstep == -1 && p.eb >= 4) ? 1 : kRowRounds;
       if (!gather && (tc.rr == 1 || tc.rr == 2 || tc.rr == 4)) p.row_rounds = tc.rr;
     }
     p.workgroups = ceil_div(nvec, int64_t(kRowThreads) * p.row_rounds);
