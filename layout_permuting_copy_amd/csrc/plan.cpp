@@ -310,7 +310,16 @@ static bool tall_cfg(int eb, int64_t eR, int64_t eC, int64_t others, TuneCfg* c)
   auto tiles = [&](int64_t tr, int64_t tc) { return ceil_div(eR, tr) * ceil_div(eC, tc) * others; };
   switch (eb) {
     case 1:
-      if (eR < 512 || eC < 256 || tiles(512, 256) < 512) return false;
+      if (eR < 512 || eC < 256 || tiles(512, 256) < 512) {
+        // narrower copies of at least 16 MiB (e.g. NCHW <-> NHWC with 32-128 channels): the same
+        // 128 KiB tiles with row tiles first and every load in flight (measured on MI355X against
+        // the default 16 KiB tiles: NHWC -> NCHW with 64 channels 2.42 -> 4.61 TB/s, with 32
+        // 1.82 -> 3.46, NCHW -> NHWC with 64 4.27 -> 5.14, 128 channels either way +2-6%; with 2
+        // loads in flight and 16 x 2 super-tiles 2.0-3.2)
+        if (eR < 64 || eC < 32 || eR * eC * others < (int64_t(16) << 20)) return false;
+        c->tile = 131072; c->threads = 512; c->trb = 512;
+        return true;
+      }
       c->tile = 131072; c->threads = 512; c->trb = 512; c->cap = 2;  // 512 x 256
       // XCD super-tiles of 16 row tiles by 2 column tiles: an XCD's 32 workgroups (one per CU)
       // are one super-tile, and the chip runs 16 x 16 tiles at a time, whatever the extents.
@@ -509,15 +518,24 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   // stores; below) measured faster than the tall tiles with nontemporal stores: fp64 8190 x 8192
   // 3.63 -> 5.24 TB/s and 8184 x 8184 3.71 -> 4.97, fp16 8184 x 8184 3.59 -> 4.22, int8 8176 x 8192
   // 3.34 -> 3.51.  (fp32 such copies were 4-7% slower with it, 16-byte elements equal.)
+  // 1-byte rows shorter than a line but packed one after another on a side (the channels of an
+  // NCHW <-> NHWC permute: 32 or 64 bytes per pixel) count as on the lines there: a tile spans
+  // whole rows, so its block is contiguous and shares no line with its neighbours.
+  const Mode& mR = j.m[p->mode_r];
+  const Mode& mC = j.m[p->mode_c];
+  const bool packed_dst = p->eb == 1 && !p->unaligned && mC.d == mR.e && mR.e * p->eb < 128;
+  const bool packed_src = p->eb == 1 && !p->unaligned && mR.s == mC.e && mC.e * p->eb < 128;
   bool dst_lines = (j.dof * p->eb) % 128 == 0;
   for (int k = 0; k < j.rank; ++k)
-    if (k != p->mode_r && (std::llabs(j.m[k].d) * p->eb) % 128 != 0) dst_lines = false;
+    if (k != p->mode_r && (std::llabs(j.m[k].d) * p->eb) % 128 != 0 && !(k == p->mode_c && packed_dst))
+      dst_lines = false;
   // (and whether the source rows start on 128-byte lines: for 1-byte elements either side off
   // the lines takes the element-aligned configuration, int8 8192 x 8208 3.9 -> 4.5 TB/s and
   // 8320 x 8224 3.84 -> 4.77)
   bool src_lines = (j.so * p->eb) % 128 == 0;
   for (int k = 0; k < j.rank; ++k)
-    if (k != p->mode_c && (std::llabs(j.m[k].s) * p->eb) % 128 != 0) src_lines = false;
+    if (k != p->mode_c && (std::llabs(j.m[k].s) * p->eb) % 128 != 0 && !(k == p->mode_r && packed_src))
+      src_lines = false;
   const bool line_cfg = p->unaligned || ((p->eb == 1 || p->eb == 2 || p->eb == 8) && !dst_lines) ||
                         (p->eb == 1 && !src_lines);
   TuneCfg base = default_cfg(p->eb, batched, line_cfg);
@@ -539,7 +557,9 @@ static bool plan_transpose_tile(Plan* p, int flags) {
   TuneCfg tall;
   const int64_t others = j.count / (R.e * C.e);
   // (element-aligned plans: only 16-byte elements gained, 4870 -> 5140 GB/s on 8191 x 8190)
-  if (!pinned && !batched && (!line_cfg || (p->unaligned && p->eb == 16)) && p->vb == 16 && p->step == 1 &&
+  // (1-byte rows of 64 bytes or more count as long enough for the narrow int8 tiles)
+  const bool short_rows = batched && !(p->eb == 1 && R.e >= 64);
+  if (!pinned && !short_rows && (!line_cfg || (p->unaligned && p->eb == 16)) && p->vb == 16 && p->step == 1 &&
       tall_cfg(p->eb, R.e, C.e, others, &tall))
     cands[ncand++] = tall;
   // 2-byte elements there, read with unit stride: tall 512 x 64 tiles with plain stores in the XCD

@@ -183,6 +183,22 @@ def test_transpose_xcd_super_tiles(eb, shape):
     assert (p["super_rows"], p["super_cols"]) == (8, 8), p
 
 
+@pytest.mark.parametrize("to_planes,c", [(True, 64), (False, 64), (True, 32), (False, 128)])
+def test_int8_channel_permutes_on_narrow_tall_tiles(to_planes, c):
+    """int8 NHWC <-> NCHW with 32-128 channels (rows of channels packed shorter than a line): the
+    128 KiB tiles of 16-byte LDS units with row tiles first and every load in flight."""
+    h, w = 112, 112
+    hw = h * w
+    n = -(-(16 << 20) // (hw * c))  # at least 16 Mi elements
+    if to_planes:   # logical (n, c, hw): source NHWC, destination NCHW
+        shape, ss, ds = (n, c, hw), (hw * c, 1, c), (c * hw, hw, 1)
+    else:           # logical (n, hw, c): source NCHW, destination NHWC
+        shape, ss, ds = (n, hw, c), (c * hw, 1, hw), (hw * c, c, 1)
+    p = _check(shape, ss, ds, 1, seed=c + int(to_planes), expect="transpose")
+    assert (p["lds_bytes"], p["lds_read_bytes"], p["threads"], p["grid_order"], p["loads_in_flight"]) == \
+        (131072, 16, 512, 1, 0), p
+
+
 @pytest.mark.parametrize("n,m", [(8176, 8192), (16368, 4224)])
 def test_int8_tall_tiles_destination_off_the_lines(n, m):
     """int8 transposes whose destination columns alone start off the 128-byte lines: 512 x 256
