@@ -150,13 +150,15 @@ __device__ __forceinline__ void gload_partial(const unsigned char* p, int n, uin
   }
 }
 
-// The first n (0 < n <= 8) 2-byte pairs of a 16-byte vector read as pairs of 1-byte elements (a
-// stride-2 source read in pairs), when the vector holds its row's last element: the first n - 1
-// pairs whole (in at most four accesses), then only the low byte of the last pair, so that no
-// byte past the row's last element is read; the other bytes of w are zero.
+// The first n (0 < n <= 16/EB) EB-byte groups of a 16-byte vector read as groups of 1-byte
+// elements (a stride-2 or stride-4 source read in 2-byte pairs or 4-byte words), when the vector
+// holds its row's last element: the first n - 1 groups whole (in at most four accesses), then only
+// the low byte of the last group, so that no byte past the row's last element is read; the other
+// bytes of w are zero.
+template <int EB>
 __device__ __forceinline__ void gload_pairs_last(const unsigned char* p, int n, uint32_t* w) {
-  gload_partial<2, 16>(p, n - 1, w);  // (n - 1 == 0: nothing loaded, w zeroed)
-  put_bytes<16>(w, 2 * (n - 1), uint32_t(p[2 * (n - 1)]));
+  gload_partial<EB, 16>(p, n - 1, w);  // (n - 1 == 0: nothing loaded, w zeroed)
+  put_bytes<16>(w, EB * (n - 1), uint32_t(p[EB * (n - 1)]));
 }
 
 // A vector holding its row's first element when the high bytes of the pairs are kept is read

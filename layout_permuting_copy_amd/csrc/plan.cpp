@@ -100,7 +100,7 @@ struct TuneCfg {
   int tile = 0, threads = 0, nt = -1, order = -1, trb = 0, unit = 0, wl = -1, rr = 0, buf = -1, cap = -1, so = -1;
   int xk = -1, xs = 0, xt = 0, xcs = 0, xcm = 0;
   int ssr = 0, ssc = 0;  // order 2: super-tile extents in tiles (powers of two)
-  int nar = 0;           // 1, 2: the pair-reading configuration (set by the planner, not by TC_TUNE)
+  int nar = 0;           // 1, 2: pairs, 3: words read (set by the planner, not by TC_TUNE)
 };
 
 static TuneCfg tune_override() {
@@ -495,6 +495,14 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     TuneCfg t;
     t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 3; t.order = 2; t.cap = 2;
     t.ssr = 16; t.ssc = 4; t.nar = p->nar;
+    if (p->nar == 3) {
+      // int8 with a stride-4 source read as 4-byte words: 256 x 32 tiles of 4-byte elements in
+      // row-tile-first order with 2 loads in flight.  Measured on every 4th byte of 8192 x 32768
+      // transposed, against the stride-4 tile of 1-byte elements (1.33 TB/s): 2.35-2.36 (256 x 64
+      // tiles 1.83-1.85, with all loads in flight 1.63-1.70; 128 x 64 2.18; 128 x 32 on 256 lanes
+      // 2.32; 16 x 2 or 8 x 8 super-tiles 2.18-2.23, column tiles first 1.53)
+      t.tile = 32768; t.trb = 1024; t.order = 1; t.cap = 2; t.ssr = 0; t.ssc = 0;
+    }
     // (the tuning override's tile, threads, trb, nt, order, cap and super-tile keys apply here too)
     if (ov.tile) t.tile = ov.tile;
     if (ov.nt >= 0) t.nt = ov.nt;
@@ -993,20 +1001,26 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
   // and the pair holding a row's last element is read as that one byte; with high bytes kept a
   // pair starts after the row's previous element and the pair holding a row's first element is
   // read as that one byte (the tiles holding them take the guarded code).
-  if (!forced_guarded && p.eb == 1 && r >= 0 && c2 >= 0 && r != c2 && j.m[c2].s == 2 && ptr_align >= 2 &&
+  // The same for a column-mode source stride of 4 with every source stride and the source offset
+  // multiples of 4 and the pointer 4-byte aligned: the source is read as 4-byte words (a dense
+  // 4-byte transpose) and the low byte of each is stored; the word holding a row's last element is
+  // read as that one byte.
+  const int64_t gs = c2 >= 0 ? j.m[c2].s : 0;
+  if (!forced_guarded && p.eb == 1 && r >= 0 && c2 >= 0 && r != c2 && (gs == 2 || gs == 4) && ptr_align >= gs &&
       j.m[r].e >= 512 && j.m[c2].e >= 64) {
     bool even = true;
-    for (int k = 0; k < j.rank; ++k) even = even && j.m[k].s % 2 == 0;
+    for (int k = 0; k < j.rank; ++k) even = even && j.m[k].s % gs == 0;
+    if (gs == 4) even = even && j.so % 4 == 0;
     if (even) {
-      const int sel = j.so % 2 == 0 ? 1 : 2;  // (offsets may be negative: so % 2 is then -1)
+      const int sel = gs == 4 ? 3 : j.so % 2 == 0 ? 1 : 2;  // (offsets may be negative: so % 2 is then -1)
       Plan q = p;
-      q.eb = 2;
+      q.eb = int(gs);
       q.nar = sel;
       q.vb = 16;
       q.unaligned = true;
       q.step = 1;
-      q.j.so = (sel == 1 ? j.so : j.so - 1) / 2;  // the pair holding the first element (exact)
-      for (int k = 0; k < j.rank; ++k) q.j.m[k].s = j.m[k].s / 2;
+      q.j.so = (sel == 2 ? j.so - 1 : j.so) / gs;  // the pair or word holding the first element (exact)
+      for (int k = 0; k < j.rank; ++k) q.j.m[k].s = j.m[k].s / gs;
       q.path = TC_PATH_TRANSPOSE;
       q.mode_r = r;
       q.mode_c = c2;
@@ -1024,7 +1038,7 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
         p.rconf = q.rconf;
         p.vb = 16;
         p.unaligned = true;
-        p.step = 2;
+        p.step = int(gs);
         p.mode_r = r;
         p.mode_c = c2;
         p.mode_b = b;
@@ -1330,7 +1344,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
     info->lds_read_bytes = p.g.rw;
     info->edge_tiles = p.g.edges ? 1 : 0;
     info->loads_in_flight = p.g.cap;
-    info->src_view_bytes = p.nar ? 2 : p.eb;
+    info->src_view_bytes = p.nar == 3 ? 4 : p.nar ? 2 : p.eb;
     info->super_rows = p.g.order == 2 ? 1 << p.g.lsr : 0;
     info->super_cols = p.g.order == 2 ? 1 << p.g.lsc : 0;
     info->write_conflicts = p.wconf;

@@ -103,7 +103,8 @@ struct TileGeom {
                                   // count of the grid is padded to a multiple of kXcds (tile_at)
   int cap = 0;                    // loads a lane keeps in flight in the interior load phase (0: all)
   int nar = 0;                    // 1-byte elements of a stride-2 source read in 2-byte pairs (eb is
-                                  // then the pair's 2 bytes), the low (1) or high (2) byte stored
+                                  // then the pair's 2 bytes), the low (1) or high (2) byte stored;
+                                  // of a stride-4 source read in 4-byte words, the low byte (3)
   int lsr = kSuperLog, lsc = kSuperLog;  // order 2: log2 of the super-tile extents in tiles
   int loads = 4, stores = 4;  // accesses per thread per phase
   int ww = 16, rw = 4;        // LDS write / read instruction bytes
@@ -143,7 +144,8 @@ struct Plan {
   int nar = 0;                      // transpose of 1-byte elements whose column mode has source
                                     // stride 2, read as 2-byte pairs (the tile planned for eb = 2,
                                     // source strides and offset halved at launch), of which the
-                                    // low (1: even offset) or high (2: odd offset) byte is kept
+                                    // low (1: even offset) or high (2: odd offset) byte is kept;
+                                    // 3: stride 4, read as 4-byte words (eb = 4), the low byte kept
   int shuffle_c = 0;                // shuffle path: block columns C (8, 16 or 32; 4 rows); interleave
                                     // path: the channels (2, 3, 4 or 8)
   bool to_planes = false;           // interleave path: interleaved source, planar destination
@@ -248,7 +250,7 @@ struct TransposeCfg {
   bool wave_local;
   bool edges = true;  // false: every tile lies wholly inside the copy (the interior-only kernel)
   int cap = 0;        // loads in flight per lane in the load phase (0: all of them)
-  int nar = 0;        // source read in 2-byte pairs, low (1) or high (2) bytes stored
+  int nar = 0;        // source read in 2-byte pairs, low (1) or high (2) bytes stored, or words (3)
 };
 // The kernel configuration a planned tile geometry runs with (every field of it).
 inline TransposeCfg transpose_cfg(const TileGeom& g) {

@@ -48,7 +48,8 @@ struct TileRegs {
 // last element is loaded element by element).
 //
 // NAR (EB = 2): the elements are 2-byte pairs of a 1-byte stride-2 source, of which the store
-// phase keeps the low (NAR = 1) or high (NAR = 2) bytes.  A pair must not be read whole where its
+// phase keeps the low (NAR = 1) or high (NAR = 2) bytes; NAR = 3 (EB = 4): 4-byte words of a
+// 1-byte stride-4 source, the low byte of each kept.  A pair must not be read whole where its
 // other byte lies past the row's last element (1) or before its first (2): guarded tiles read the
 // vector holding it with gload_pairs_last / gload_pairs_first, and tiles holding a row's last (1)
 // or first (2) element always take the guarded code (see transpose_kernel).
@@ -77,7 +78,7 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
 #pragma unroll
       for (int i = 0; i < G::B; ++i) {
         const bool in_row = in_b && (int64_t(ru) << G::LB) + i < t.remR && cols > 0;
-        const bool whole = S == 1 && NAR != 1 ? cols >= G::VE : cols > G::VE;
+        const bool whole = S == 1 && NAR != 1 && NAR != 3 ? cols >= G::VE : cols > G::VE;
         const int n = int(cols < G::VE ? cols : G::VE);
         // NAR = 2: the row's first vector (the first one of the first column tile) is read from
         // its first kept byte on, and moved up one byte below (pairs_up_one_byte)
@@ -85,7 +86,7 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
         if (in_row && whole) {
           gload_step<EB, VB, S, NTM>(q, r.w[f][i]);
         } else if (in_row) {
-          if constexpr (NAR == 1) gload_pairs_last(q, n, r.w[f][i]);
+          if constexpr (NAR == 1 || NAR == 3) gload_pairs_last<EB>(q, n, r.w[f][i]);
           else gload_partial<EB, VB, S>(q, n, r.w[f][i]);
         }
       }
@@ -174,7 +175,8 @@ __device__ __forceinline__ void write_lds(const TransposeArgs& a, unsigned char*
 
 // LDS -> registers (all reads first), then registers -> global.  GUARD skips stores of
 // positions outside the copy.  NAR: each 16-byte vector of 2-byte pairs is stored as its 8 low
-// (1) or high (2) bytes, the destination addressed in bytes.
+// (1) or high (2) bytes, or of 4-byte words as their 4 low bytes (3), the destination addressed
+// in bytes.
 template <int EB, int VB, int U, typename G, int NT, int NTM, bool GUARD, int NAR = 0>
 __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt& t,
                                            const unsigned char* __restrict__ lds) {
@@ -204,7 +206,21 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
     const int rv = acc & ((1 << lnRV) - 1);
     const int c = (acc >> lnRV) & (TC - 1);
     const int nb = acc >> (lnRV + a.lTC);
-    if constexpr (NAR) {
+    if constexpr (NAR == 3) {
+      static_assert(EB == 4 && VB == 16, "words of 1-byte elements in 16-byte vectors");
+      unsigned char* p = a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB)));
+      // byte 0 of words 0, 1 into bytes 0, 1 and of words 2, 3 into bytes 2, 3 (0x0c: a zero byte)
+      const uint32_t lo = perm(out[f][1], out[f][0], 0x0c0c0400u) | perm(out[f][3], out[f][2], 0x04000c0cu);
+      if constexpr (GUARD) {
+        const int64_t rows = t.remR - (int64_t(rv) << (G::LRPV + G::LB));
+        const bool ok = nb < NB && nb < t.remB && c < t.remC && rows > 0;
+        if (ok && rows >= G::VE) gstore<4, NTM>(p, &lo);
+        else if (ok) gstore_partial<1, 4>(p, int(rows), &lo);
+      } else {
+        gstore<4, NTM>(p, &lo);
+      }
+      continue;
+    } else if constexpr (NAR) {
       static_assert(EB == 2 && VB == 16, "pairs of 1-byte elements in 16-byte vectors");
       unsigned char* p = a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB)));
       constexpr uint32_t kSel = NAR == 1 ? 0x06040200u : 0x07050301u;  // bytes 0, 2 or 1, 3 of each word
@@ -255,8 +271,8 @@ __global__ void __launch_bounds__(NT) transpose_kernel(TransposeArgs a) {
   const TileAt t = tile_at(a, blockIdx.x);
   if (!t.valid) return;  // padding of the XCD super-tile order (whole workgroup, before any barrier)
   TileRegs<G> r;
-  // (tiles holding a row's last element: guarded for S = 2 and NAR = 1; its first: for NAR = 2)
-  const bool full = !EDGE || (tile_full(a, t) && ((S == 1 && NAR != 1) || t.remC > (int64_t(1) << a.lTC)) &&
+  // (tiles holding a row's last element: guarded for S = 2 and NAR = 1, 3; its first: for NAR = 2)
+  const bool full = !EDGE || (tile_full(a, t) && ((S == 1 && NAR != 1 && NAR != 3) || t.remC > (int64_t(1) << a.lTC)) &&
                               (NAR != 2 || t.remC < a.eC));
   if constexpr (!EDGE) load_tile<EB, VB, G, NT, NTM, S, false, CAP, NAR>(a, t, r);
   else if (full) load_tile<EB, VB, G, NT, NTM, S, false, CAP, NAR>(a, t, r);
@@ -372,18 +388,23 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 #define TC_CAPS_EB8
 #define TC_CAPS_EB16
 
-// 2-byte pairs of a 1-byte stride-2 source, low bytes stored (plan.cpp, make_plan): the tall
-// 512 x 64 tiles of 2-byte elements with nontemporal accesses and 2 loads in flight, with the edge
-// code (the tiles holding a row's last element always need it)
+// 2-byte pairs of a 1-byte stride-2 source, low or high bytes stored (plan.cpp, make_plan): the
+// tall 512 x 64 tiles of 2-byte elements with nontemporal accesses and 2 loads in flight; 4-byte
+// words of a 1-byte stride-4 source, low bytes stored: tall 4-byte tiles.  Always with the edge
+// code (the tiles holding a row's last element need it).
 #define TC_CFG_NAR(EB, TILE, NT, CAP)                                                                        \
   if (c.cap == CAP && c.unit == 16 && vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local &&  \
       ntm == 3 && c.edges) {                                                                                 \
-    if (c.nar == 1) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 1>(ta, wgs, s); \
-    if (c.nar == 2) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 2>(ta, wgs, s); \
+    if constexpr (EB == 4) {                                                                                 \
+      if (c.nar == 3) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 3>(ta, wgs, s); \
+    } else {                                                                                                 \
+      if (c.nar == 1) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 1>(ta, wgs, s); \
+      if (c.nar == 2) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 2>(ta, wgs, s); \
+    }                                                                                                        \
   }
 #define TC_NAR_EB1
 #define TC_NAR_EB2 TC_CFG_NAR(2, 65536, 512, 2)
-#define TC_NAR_EB4
+#define TC_NAR_EB4 TC_CFG_NAR(4, 32768, 512, 2)
 #define TC_NAR_EB8
 #define TC_NAR_EB16
 

@@ -253,6 +253,34 @@ def test_int8_stride2_pairs_not_taken_at_odd_strides():
     assert p["src_view_bytes"] == 1 and p["src_step"] == 2, p
 
 
+@pytest.mark.parametrize("shape,strides,soff", [
+    ((600, 100), (512, 4), 0),            # one column tile, ragged rows
+    ((1001, 333), (1336, 4), 1336),       # ragged both ways, the last word's upper bytes past the span
+    ((512, 64), (256, 4), 0),             # exactly one tile wide: every tile holds a row's end
+    ((2049, 2047), (8192, 4), 8192),      # the slice [1:2050, 0:8188:4] of an 8192-wide matrix
+    ((3, 700, 130), (700 * 524, 524, 4), 8),  # a batch mode
+    ((800, 90), (-368, 4), 799 * 368),    # rows in reverse order
+    ((8192, 8192), (32768, 4), 0),        # every 4th byte of an 8192 x 32768 matrix, transposed
+])
+def test_int8_stride4_source_read_in_words(shape, strides, soff):
+    """1-byte copies whose column mode has source stride 4 (every source stride and the offset
+    multiples of 4): the source is read as 4-byte words on 4-byte tiles and the low byte of each
+    stored; the word holding a row's last element is read as that byte only."""
+    n, m = shape[-2], shape[-1]
+    ds = (1, n) if len(shape) == 2 else (n * m, 1, n)
+    p = _check(shape, strides, ds, 1, s_off=soff, seed=n + m + len(shape) + 4, expect="transpose")
+    assert p["src_view_bytes"] == 4 and p["src_step"] == 4, p
+
+
+def test_int8_stride4_words_not_taken_off_word_boundaries():
+    """A source offset or a row stride that is not a multiple of 4 keeps the stride-4 tile of
+    1-byte elements; same bytes."""
+    p = _check((700, 130), (524, 4), (1, 700), 1, s_off=2, seed=78, expect="transpose")
+    assert p["src_view_bytes"] == 1 and p["src_step"] == 4, p
+    p = _check((700, 130), (522, 4), (1, 700), 1, s_off=0, seed=79, expect="transpose")
+    assert p["src_view_bytes"] == 1 and p["src_step"] == 4, p
+
+
 @pytest.mark.parametrize("eb", [1, 2, 4, 8])
 @pytest.mark.parametrize("k", [2, 3, 4, -1, -2, -3, -4])
 @pytest.mark.parametrize("n,m,pitch,soff", [(40, 48, 200, 0), (37, 69, 300, 3), (5, 16, 64, 1), (300, 515, 2100, 7),
