@@ -272,6 +272,29 @@ def test_int8_stride4_source_read_in_words(shape, strides, soff):
     assert p["src_view_bytes"] == 4 and p["src_step"] == 4, p
 
 
+@pytest.mark.parametrize("k", [2, 4])
+def test_int8_pairs_and_words_random(k):
+    """Random int8 transposes from stride-2 and stride-4 sources on the pair and word paths:
+    random extents (ragged against the tiles), row pitches and offsets (multiples of k; for
+    k = 2 odd offsets too), rows in either order, with or without a batch mode."""
+    rng = np.random.default_rng(900 + k)
+    for case in range(12):
+        n = int(rng.integers(512, 2200))
+        m = int(rng.integers(64, 600))
+        pitch = k * m + k * int(rng.integers(0, 40))
+        soff = k * int(rng.integers(0, 50)) + (int(rng.integers(0, 2)) if k == 2 else 0)
+        batch = int(rng.integers(1, 4)) if case % 3 == 2 else 0
+        if case % 4 == 3:  # rows in reverse order
+            shape, ss, ds = (n, m), (-pitch, k), (1, n)
+            soff += (n - 1) * pitch
+        elif batch:
+            shape, ss, ds = (batch, n, m), (n * pitch + k * 8, pitch, k), (n * m, 1, n)
+        else:
+            shape, ss, ds = (n, m), (pitch, k), (1, n)
+        p = _check(shape, ss, ds, 1, s_off=soff, seed=case * 7 + k, expect="transpose")
+        assert p["src_view_bytes"] == k and p["src_step"] == k, (shape, ss, soff, p)
+
+
 def test_int8_stride4_words_not_taken_off_word_boundaries():
     """A source offset or a row stride that is not a multiple of 4 keeps the stride-4 tile of
     1-byte elements; same bytes."""
