@@ -186,9 +186,10 @@ typedef struct tc_plan_info {
   int32_t src_view_bytes;   /* transpose: bytes the source elements are read as -- elem_bytes, or 2
                                for 1-byte elements of a stride-2 source read in pairs (src_step 2),
                                of which the low byte is stored where the source offset is even and
-                               the high byte where it is odd, or 4 for 1-byte elements of a stride-4
-                               source (every source stride and the offset multiples of 4) read in
-                               4-byte words, of which the low byte is stored (src_step 4) */
+                               the high byte where it is odd, or 4 x elem_bytes for 1-, 2- and
+                               4-byte elements of a stride-4 source (every source stride and the
+                               offset multiples of 4) read in groups of 4 elements, of which the
+                               first is stored (src_step 4) */
   int64_t write_conflicts, read_conflicts;       /* simulated extra LDS cycles per tile */
   char reason[192];         /* why the fast path was declined ("" if it was not) */
 } tc_plan_info;

@@ -655,11 +655,11 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
         ta.nslices = ta.tilesB.d;
         for (int k = 0; k < ta.nbatch; ++k) ta.nslices *= ta.bdiv[k].d;
       }
-      const int gw = p.nar == 3 ? 4 : 2;  // bytes per group of a source read in pairs or words
+      const int gw = p.nar == 3 ? 4 : 2;  // elements per group of a source read in pairs or groups
       if (p.nar) {
-        // the source read as 2-byte pairs or 4-byte words: its offset (of the group holding the
+        // the source read in pairs or groups of 4 elements: its offset (of the group holding the
         // first element) and strides (multiples of the group, checked by the planner) in groups;
-        // the destination stays in bytes
+        // the destination stays in its elements
         ta.src_off = (p.nar == 2 ? ta.src_off - 1 : ta.src_off) / gw;
         ta.sR /= gw;
         ta.sC /= gw;
@@ -667,7 +667,7 @@ int launch_plan(const Plan& p, const void* src, void* dst, void* stream, std::st
         for (int k = 0; k < ta.nbatch; ++k) ta.bs[k] /= gw;
       }
       const TransposeCfg cfg = transpose_cfg(p.g);
-      if (!launch_transpose(p.nar ? gw : p.eb, cfg, &ta, p.workgroups, stream)) {
+      if (!launch_transpose(p.nar ? gw * p.eb : p.eb, cfg, &ta, p.workgroups, stream)) {
         *err = "no transpose kernel instance for this element width, vector width, tile size and thread count";
         return TC_E_ARG;
       }

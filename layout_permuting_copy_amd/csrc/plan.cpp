@@ -496,12 +496,19 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 3; t.order = 2; t.cap = 2;
     t.ssr = 16; t.ssc = 4; t.nar = p->nar;
     if (p->nar == 3) {
-      // int8 with a stride-4 source read as 4-byte words: 256 x 32 tiles of 4-byte elements in
-      // row-tile-first order with 2 loads in flight.  Measured on every 4th byte of 8192 x 32768
-      // transposed, against the stride-4 tile of 1-byte elements (1.33 TB/s): 2.35-2.36 (256 x 64
+      // a stride-4 source read in groups of 4 elements: tiles of 32 groups by 1 KiB (4- and 8-byte
+      // groups: 256 x 32 and 128 x 32) or 512 bytes on 256 lanes (16-byte groups: 32 x 32) in
+      // row-tile-first order with 2 loads in flight.  Measured against the stride-4 tile of the
+      // element width: every 4th byte of 8192 x 32768 transposed 1.33 -> 2.35-2.36 TB/s (256 x 64
       // tiles 1.83-1.85, with all loads in flight 1.63-1.70; 128 x 64 2.18; 128 x 32 on 256 lanes
-      // 2.32; 16 x 2 or 8 x 8 super-tiles 2.18-2.23, column tiles first 1.53)
-      t.tile = 32768; t.trb = 1024; t.order = 1; t.cap = 2; t.ssr = 0; t.ssc = 0;
+      // 2.32; 16 x 2 or 8 x 8 super-tiles 2.18-2.23, column tiles first 1.53); every 4th fp16 of
+      // 8192 x 16384 1.75-1.76 -> 2.00-2.03 (128 x 64 1.76, 64 x 32 and 128 x 16 on 256 lanes
+      // 1.97-2.01, 16 x 2 super-tiles 2.04-2.06); every 4th fp32 of 8192 x 8192 (the guarded tile
+      // before) 1.60-1.61 -> 2.13-2.16 (64 x 32 on 512 lanes 1.98, 64 x 64 1.97-1.98, 32 x 64 2.08-2.11)
+      t.tile = p->eb == 16 ? 16384 : 32768;
+      t.threads = p->eb == 16 ? 256 : 512;
+      t.trb = p->eb == 16 ? 512 : 1024;
+      t.order = 1; t.cap = 2; t.ssr = 0; t.ssc = 0;
     }
     // (the tuning override's tile, threads, trb, nt, order, cap and super-tile keys apply here too)
     if (ov.tile) t.tile = ov.tile;
@@ -1002,31 +1009,36 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
   // pair starts after the row's previous element and the pair holding a row's first element is
   // read as that one byte (the tiles holding them take the guarded code).
   // The same for a column-mode source stride of 4 with every source stride and the source offset
-  // multiples of 4 and the pointer 4-byte aligned: the source is read as 4-byte words (a dense
-  // 4-byte transpose) and the low byte of each is stored; the word holding a row's last element is
-  // read as that one byte.
-  const int64_t gs = c2 >= 0 ? j.m[c2].s : 0;
-  if (!forced_guarded && p.eb == 1 && r >= 0 && c2 >= 0 && r != c2 && (gs == 2 || gs == 4) && ptr_align >= gs &&
-      j.m[r].e >= 512 && j.m[c2].e >= 64) {
+  // multiples of 4, for 1-, 2- and 4-byte elements: the source is read in groups of 4 elements (a
+  // dense transpose of 4-, 8- or 16-byte groups) and each group's first element is stored; the
+  // group holding a row's last element is read as that one element.  (A stride-4 mode of 4-byte
+  // elements is no candidate above, its elements lying 16 bytes apart: it is looked for here.)
+  int cg = c2;
+  if ((cg < 0 || cg == r) && c < 0 && p.eb == 4)
+    for (int k = 0; k < j.rank; ++k)
+      if (k != r && j.m[k].s == 4) cg = k;
+  const int64_t gs = cg >= 0 && cg != r ? j.m[cg].s : 0;
+  if (!forced_guarded && r >= 0 && ((gs == 2 && p.eb == 1) || (gs == 4 && p.eb <= 4)) &&
+      ptr_align >= std::min<int64_t>(16, gs * p.eb) && j.m[r].e >= 512 && j.m[cg].e >= 64) {
     bool even = true;
     for (int k = 0; k < j.rank; ++k) even = even && j.m[k].s % gs == 0;
     if (gs == 4) even = even && j.so % 4 == 0;
     if (even) {
       const int sel = gs == 4 ? 3 : j.so % 2 == 0 ? 1 : 2;  // (offsets may be negative: so % 2 is then -1)
       Plan q = p;
-      q.eb = int(gs);
+      q.eb = int(gs) * p.eb;
       q.nar = sel;
       q.vb = 16;
       q.unaligned = true;
       q.step = 1;
-      q.j.so = (sel == 2 ? j.so - 1 : j.so) / gs;  // the pair or word holding the first element (exact)
+      q.j.so = (sel == 2 ? j.so - 1 : j.so) / gs;  // the pair or group holding the first element (exact)
       for (int k = 0; k < j.rank; ++k) q.j.m[k].s = j.m[k].s / gs;
       q.path = TC_PATH_TRANSPOSE;
       q.mode_r = r;
-      q.mode_c = c2;
+      q.mode_c = cg;
       int b = -1;
       for (int k = 0; k < j.rank; ++k) {
-        if (k == r || k == c2) continue;
+        if (k == r || k == cg) continue;
         if (b < 0 || std::llabs(j.m[k].s) + std::llabs(j.m[k].d) < std::llabs(j.m[b].s) + std::llabs(j.m[b].d)) b = k;
       }
       q.mode_b = b;
@@ -1040,13 +1052,13 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
         p.unaligned = true;
         p.step = int(gs);
         p.mode_r = r;
-        p.mode_c = c2;
+        p.mode_c = cg;
         p.mode_b = b;
         p.threads = p.g.NT;
         p.load_outer = p.g.loads;
         p.store_outer = p.g.stores;
         p.lds_bytes = p.g.tile_bytes;
-        p.workgroups = transpose_workgroups(p, r, c2, b);
+        p.workgroups = transpose_workgroups(p, r, cg, b);
         if (p.workgroups >= (int64_t(1) << 31)) {
           p.status = TC_E_RANGE;
           p.reason = "more than 2^31 workgroups";
@@ -1344,7 +1356,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
     info->lds_read_bytes = p.g.rw;
     info->edge_tiles = p.g.edges ? 1 : 0;
     info->loads_in_flight = p.g.cap;
-    info->src_view_bytes = p.nar == 3 ? 4 : p.nar ? 2 : p.eb;
+    info->src_view_bytes = p.nar == 3 ? 4 * p.eb : p.nar ? 2 : p.eb;
     info->super_rows = p.g.order == 2 ? 1 << p.g.lsr : 0;
     info->super_cols = p.g.order == 2 ? 1 << p.g.lsc : 0;
     info->write_conflicts = p.wconf;

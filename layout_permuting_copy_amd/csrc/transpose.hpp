@@ -48,8 +48,8 @@ struct TileRegs {
 // last element is loaded element by element).
 //
 // NAR (EB = 2): the elements are 2-byte pairs of a 1-byte stride-2 source, of which the store
-// phase keeps the low (NAR = 1) or high (NAR = 2) bytes; NAR = 3 (EB = 4): 4-byte words of a
-// 1-byte stride-4 source, the low byte of each kept.  A pair must not be read whole where its
+// phase keeps the low (NAR = 1) or high (NAR = 2) bytes; NAR = 3 (EB = 4, 8, 16): groups of 4
+// elements of a stride-4 source of 1-, 2- or 4-byte elements, the low EB/4 bytes of each kept.  A pair must not be read whole where its
 // other byte lies past the row's last element (1) or before its first (2): guarded tiles read the
 // vector holding it with gload_pairs_last / gload_pairs_first, and tiles holding a row's last (1)
 // or first (2) element always take the guarded code (see transpose_kernel).
@@ -86,7 +86,8 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
         if (in_row && whole) {
           gload_step<EB, VB, S, NTM>(q, r.w[f][i]);
         } else if (in_row) {
-          if constexpr (NAR == 1 || NAR == 3) gload_pairs_last<EB>(q, n, r.w[f][i]);
+          if constexpr (NAR == 1) gload_pairs_last<EB>(q, n, r.w[f][i]);
+          else if constexpr (NAR == 3) gload_pairs_last<EB, EB / 4>(q, n, r.w[f][i]);
           else gload_partial<EB, VB, S>(q, n, r.w[f][i]);
         }
       }
@@ -175,8 +176,8 @@ __device__ __forceinline__ void write_lds(const TransposeArgs& a, unsigned char*
 
 // LDS -> registers (all reads first), then registers -> global.  GUARD skips stores of
 // positions outside the copy.  NAR: each 16-byte vector of 2-byte pairs is stored as its 8 low
-// (1) or high (2) bytes, or of 4-byte words as their 4 low bytes (3), the destination addressed
-// in bytes.
+// (1) or high (2) bytes, or of groups of 4 elements (3) as the 4 bytes of the groups' first
+// elements, the destination addressed in its own elements (1 byte for pairs, EB/4 for groups).
 template <int EB, int VB, int U, typename G, int NT, int NTM, bool GUARD, int NAR = 0>
 __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt& t,
                                            const unsigned char* __restrict__ lds) {
@@ -207,15 +208,21 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
     const int c = (acc >> lnRV) & (TC - 1);
     const int nb = acc >> (lnRV + a.lTC);
     if constexpr (NAR == 3) {
-      static_assert(EB == 4 && VB == 16, "words of 1-byte elements in 16-byte vectors");
-      unsigned char* p = a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB)));
-      // byte 0 of words 0, 1 into bytes 0, 1 and of words 2, 3 into bytes 2, 3 (0x0c: a zero byte)
-      const uint32_t lo = perm(out[f][1], out[f][0], 0x0c0c0400u) | perm(out[f][3], out[f][2], 0x04000c0cu);
+      static_assert((EB == 4 || EB == 8 || EB == 16) && VB == 16, "groups of 4 elements in 16-byte vectors");
+      constexpr int KB = EB / 4;  // bytes kept per group
+      unsigned char* p =
+          a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB))) * KB;
+      // the groups' first elements, packed: byte 0 of words 0-3, bytes 0-1 of words 0 and 2, or
+      // word 0 (0x0c: a zero byte)
+      uint32_t lo;
+      if constexpr (EB == 4) lo = perm(out[f][1], out[f][0], 0x0c0c0400u) | perm(out[f][3], out[f][2], 0x04000c0cu);
+      else if constexpr (EB == 8) lo = perm(out[f][2], out[f][0], 0x05040100u);
+      else lo = out[f][0];
       if constexpr (GUARD) {
         const int64_t rows = t.remR - (int64_t(rv) << (G::LRPV + G::LB));
         const bool ok = nb < NB && nb < t.remB && c < t.remC && rows > 0;
         if (ok && rows >= G::VE) gstore<4, NTM>(p, &lo);
-        else if (ok) gstore_partial<1, 4>(p, int(rows), &lo);
+        else if (ok) gstore_partial<KB, 4>(p, int(rows), &lo);
       } else {
         gstore<4, NTM>(p, &lo);
       }
@@ -390,12 +397,13 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 
 // 2-byte pairs of a 1-byte stride-2 source, low or high bytes stored (plan.cpp, make_plan): the
 // tall 512 x 64 tiles of 2-byte elements with nontemporal accesses and 2 loads in flight; 4-byte
-// words of a 1-byte stride-4 source, low bytes stored: tall 4-byte tiles.  Always with the edge
+// groups of 4 elements of a stride-4 source, the first element of each stored: 4-, 8- and
+// 16-byte tiles of 1 KiB or 512 bytes by 32 groups.  Always with the edge
 // code (the tiles holding a row's last element need it).
 #define TC_CFG_NAR(EB, TILE, NT, CAP)                                                                        \
   if (c.cap == CAP && c.unit == 16 && vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local &&  \
       ntm == 3 && c.edges) {                                                                                 \
-    if constexpr (EB == 4) {                                                                                 \
+    if constexpr (EB >= 4) {                                                                                 \
       if (c.nar == 3) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 3>(ta, wgs, s); \
     } else {                                                                                                 \
       if (c.nar == 1) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 1>(ta, wgs, s); \
@@ -405,8 +413,8 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 #define TC_NAR_EB1
 #define TC_NAR_EB2 TC_CFG_NAR(2, 65536, 512, 2)
 #define TC_NAR_EB4 TC_CFG_NAR(4, 32768, 512, 2)
-#define TC_NAR_EB8
-#define TC_NAR_EB16
+#define TC_NAR_EB8 TC_CFG_NAR(8, 32768, 512, 2)
+#define TC_NAR_EB16 TC_CFG_NAR(16, 16384, 256, 2)
 
 #define TC_CFG_WL(EB, U, TILE, NT)                                                                           \
   if (vb == 16 && tile == TILE && nt == NT && c.step == 1 && ntm == 3 && c.wave_local)                       \

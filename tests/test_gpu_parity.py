@@ -260,24 +260,33 @@ def test_int8_stride2_pairs_not_taken_at_odd_strides():
     ((2049, 2047), (8192, 4), 8192),      # the slice [1:2050, 0:8188:4] of an 8192-wide matrix
     ((3, 700, 130), (700 * 524, 524, 4), 8),  # a batch mode
     ((800, 90), (-368, 4), 799 * 368),    # rows in reverse order
-    ((8192, 8192), (32768, 4), 0),        # every 4th byte of an 8192 x 32768 matrix, transposed
 ])
-def test_int8_stride4_source_read_in_words(shape, strides, soff):
-    """1-byte copies whose column mode has source stride 4 (every source stride and the offset
-    multiples of 4): the source is read as 4-byte words on 4-byte tiles and the low byte of each
-    stored; the word holding a row's last element is read as that byte only."""
+@pytest.mark.parametrize("eb", [1, 2, 4])
+def test_stride4_source_read_in_groups(shape, strides, soff, eb):
+    """1-, 2- and 4-byte copies whose column mode has source stride 4 (every source stride and the
+    offset multiples of 4): the source is read in groups of 4 elements (4-, 8- or 16-byte groups)
+    on the tiles of that width and the first element of each stored; the group holding a row's
+    last element is read as that element only."""
     n, m = shape[-2], shape[-1]
     ds = (1, n) if len(shape) == 2 else (n * m, 1, n)
-    p = _check(shape, strides, ds, 1, s_off=soff, seed=n + m + len(shape) + 4, expect="transpose")
-    assert p["src_view_bytes"] == 4 and p["src_step"] == 4, p
+    p = _check(shape, strides, ds, eb, s_off=soff, seed=n + m + len(shape) + 4 + eb, expect="transpose")
+    assert p["src_view_bytes"] == 4 * eb and p["src_step"] == 4, p
 
 
-@pytest.mark.parametrize("k", [2, 4])
-def test_int8_pairs_and_words_random(k):
-    """Random int8 transposes from stride-2 and stride-4 sources on the pair and word paths:
-    random extents (ragged against the tiles), row pitches and offsets (multiples of k; for
-    k = 2 odd offsets too), rows in either order, with or without a batch mode."""
-    rng = np.random.default_rng(900 + k)
+@pytest.mark.parametrize("eb,n", [(1, 8192), (2, 8192), (4, 4096)])
+def test_stride4_source_read_in_groups_full_size(eb, n):
+    """Every 4th element of an n x 4n matrix, transposed (int8 and fp16 8192 x 8192 from 8192 x
+    32768, fp32 4096 x 4096 from 4096 x 16384)."""
+    p = _check((n, n), (4 * n, 4), (1, n), eb, seed=eb + 4000, expect="transpose")
+    assert p["src_view_bytes"] == 4 * eb, p
+
+
+@pytest.mark.parametrize("k,eb", [(2, 1), (4, 1), (4, 2), (4, 4)])
+def test_pairs_and_groups_random(k, eb):
+    """Random transposes from stride-2 (int8) and stride-4 (int8, fp16, fp32) sources on the pair
+    and group paths: random extents (ragged against the tiles), row pitches and offsets (multiples
+    of k; for k = 2 odd offsets too), rows in either order, with or without a batch mode."""
+    rng = np.random.default_rng(900 + k + 10 * eb)
     for case in range(12):
         n = int(rng.integers(512, 2200))
         m = int(rng.integers(64, 600))
@@ -291,8 +300,8 @@ def test_int8_pairs_and_words_random(k):
             shape, ss, ds = (batch, n, m), (n * pitch + k * 8, pitch, k), (n * m, 1, n)
         else:
             shape, ss, ds = (n, m), (pitch, k), (1, n)
-        p = _check(shape, ss, ds, 1, s_off=soff, seed=case * 7 + k, expect="transpose")
-        assert p["src_view_bytes"] == k and p["src_step"] == k, (shape, ss, soff, p)
+        p = _check(shape, ss, ds, eb, s_off=soff, seed=case * 7 + k + eb, expect="transpose")
+        assert p["src_view_bytes"] == k * eb and p["src_step"] == k, (shape, ss, soff, p)
 
 
 def test_int8_stride4_words_not_taken_off_word_boundaries():
