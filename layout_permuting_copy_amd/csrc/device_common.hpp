@@ -151,14 +151,21 @@ __device__ __forceinline__ void gload_partial(const unsigned char* p, int n, uin
 }
 
 // The first n (0 < n <= 16/EB) EB-byte groups of a 16-byte vector read as groups of KB-byte
-// elements (a stride-2 source of 1-byte elements read in 2-byte pairs, or a stride-4 source of 1-,
+// elements (a stride-2 source of 1- or 8-byte elements read in 2- or 16-byte pairs, or a stride-4 source of 1-,
 // 2- or 4-byte elements in 4-, 8- or 16-byte groups), when the vector holds its row's last
 // element: the first n - 1 groups whole (in at most four accesses), then only the low KB bytes of
 // the last group (that element), so that no byte past the row's last element is read; the other
 // bytes of w are zero.
 template <int EB, int KB = 1>
 __device__ __forceinline__ void gload_pairs_last(const unsigned char* p, int n, uint32_t* w) {
-  static_assert(KB == 1 || KB == 2 || KB == 4, "1-, 2- or 4-byte elements");
+  static_assert(KB == 1 || KB == 2 || KB == 4 || (KB == 8 && EB == 16), "1-, 2-, 4- or 8-byte elements");
+  if constexpr (KB == 8) {  // one pair of 8-byte elements per vector (n == 1): its low element
+    const uint64_t v = *reinterpret_cast<const uint64_t*>(p);
+    w[0] = uint32_t(v);
+    w[1] = uint32_t(v >> 32);
+    w[2] = w[3] = 0;
+    return;
+  }
   gload_partial<EB, 16>(p, n - 1, w);  // (n - 1 == 0: nothing loaded, w zeroed)
   const unsigned char* q = p + EB * (n - 1);
   const uint32_t v = KB == 1 ? uint32_t(*q)

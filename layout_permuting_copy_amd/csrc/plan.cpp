@@ -495,6 +495,16 @@ static bool plan_transpose_tile(Plan* p, int flags) {
     TuneCfg t;
     t.tile = 65536; t.threads = 512; t.trb = 1024; t.unit = 16; t.nt = 3; t.order = 2; t.cap = 2;
     t.ssr = 16; t.ssc = 4; t.nar = p->nar;
+    if (p->eb == 16) {
+      // fp64 with a stride-2 source read as 16-byte pairs: 64 x 8 tiles of pairs on 256 lanes in XCD
+      // super-tiles of 16 x 16 tiles, every load in flight.  Measured against the stride-2 tile of
+      // 8-byte elements (16 x 128 on 512 lanes, column tiles first): the slice [1:8191, 0:8190:2]
+      // of 8192^2 3.20-3.23 -> 3.70-3.74 TB/s, every other column of 16384 x 8192 3.40 -> 3.74-3.75,
+      // of 8192 x 16384 3.20-3.21 -> 3.95-3.96, of 4096^2 3.28 -> 4.00-4.02 (8 x 16 super-tiles
+      // 3.70 / 3.75 / 3.84-3.85 / 3.98-4.00, 16 x 8 3.34-3.97, 8 x 8 3.25-3.49, row tiles first
+      // 2.64, column tiles first 2.93-2.96; 64 x 16 tiles 2.73-3.55, 64 x 32 on 512 lanes 2.68-3.28)
+      t.tile = 8192; t.threads = 256; t.trb = 1024; t.order = 2; t.cap = 0; t.ssr = 16; t.ssc = 16;
+    }
     if (p->nar == 3) {
       // a stride-4 source read in groups of 4 elements: tiles of 32 groups by 1 KiB (4- and 8-byte
       // groups: 256 x 32 and 128 x 32) or 512 bytes on 256 lanes (16-byte groups: 32 x 32) in
@@ -1018,7 +1028,8 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     for (int k = 0; k < j.rank; ++k)
       if (k != r && j.m[k].s == 4) cg = k;
   const int64_t gs = cg >= 0 && cg != r ? j.m[cg].s : 0;
-  if (!forced_guarded && r >= 0 && ((gs == 2 && p.eb == 1) || (gs == 4 && p.eb <= 4)) &&
+  // 8-byte elements of a stride-2 source at an even offset are read as 16-byte pairs the same way.
+  if (!forced_guarded && r >= 0 && ((gs == 2 && (p.eb == 1 || (p.eb == 8 && j.so % 2 == 0))) || (gs == 4 && p.eb <= 4)) &&
       ptr_align >= std::min<int64_t>(16, gs * p.eb) && j.m[r].e >= 512 && j.m[cg].e >= 64) {
     bool even = true;
     for (int k = 0; k < j.rank; ++k) even = even && j.m[k].s % gs == 0;
@@ -1356,7 +1367,7 @@ void plan_to_info(const Plan& p, tc_plan_info* info) {
     info->lds_read_bytes = p.g.rw;
     info->edge_tiles = p.g.edges ? 1 : 0;
     info->loads_in_flight = p.g.cap;
-    info->src_view_bytes = p.nar == 3 ? 4 * p.eb : p.nar ? 2 : p.eb;
+    info->src_view_bytes = p.nar == 3 ? 4 * p.eb : p.nar ? 2 * p.eb : p.eb;
     info->super_rows = p.g.order == 2 ? 1 << p.g.lsr : 0;
     info->super_cols = p.g.order == 2 ? 1 << p.g.lsc : 0;
     info->write_conflicts = p.wconf;

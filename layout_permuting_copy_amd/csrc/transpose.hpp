@@ -48,7 +48,8 @@ struct TileRegs {
 // last element is loaded element by element).
 //
 // NAR (EB = 2): the elements are 2-byte pairs of a 1-byte stride-2 source, of which the store
-// phase keeps the low (NAR = 1) or high (NAR = 2) bytes; NAR = 3 (EB = 4, 8, 16): groups of 4
+// phase keeps the low (NAR = 1) or high (NAR = 2) bytes (EB = 16, NAR = 1: 16-byte pairs of an
+// 8-byte stride-2 source, the low halves kept); NAR = 3 (EB = 4, 8, 16): groups of 4
 // elements of a stride-4 source of 1-, 2- or 4-byte elements, the low EB/4 bytes of each kept.  A pair must not be read whole where its
 // other byte lies past the row's last element (1) or before its first (2): guarded tiles read the
 // vector holding it with gload_pairs_last / gload_pairs_first, and tiles holding a row's last (1)
@@ -86,7 +87,7 @@ __device__ __forceinline__ void load_tile(const TransposeArgs& a, const TileAt& 
         if (in_row && whole) {
           gload_step<EB, VB, S, NTM>(q, r.w[f][i]);
         } else if (in_row) {
-          if constexpr (NAR == 1) gload_pairs_last<EB>(q, n, r.w[f][i]);
+          if constexpr (NAR == 1) gload_pairs_last<EB, EB / 2>(q, n, r.w[f][i]);
           else if constexpr (NAR == 3) gload_pairs_last<EB, EB / 4>(q, n, r.w[f][i]);
           else gload_partial<EB, VB, S>(q, n, r.w[f][i]);
         }
@@ -228,15 +229,24 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
       }
       continue;
     } else if constexpr (NAR) {
-      static_assert(EB == 2 && VB == 16, "pairs of 1-byte elements in 16-byte vectors");
-      unsigned char* p = a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB)));
+      static_assert((EB == 2 || (EB == 16 && NAR == 1)) && VB == 16, "pairs of 1- or 8-byte elements in 16-byte vectors");
+      constexpr int KB = EB / 2;  // bytes kept per pair
+      unsigned char* p =
+          a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB))) * KB;
       constexpr uint32_t kSel = NAR == 1 ? 0x06040200u : 0x07050301u;  // bytes 0, 2 or 1, 3 of each word
-      const uint32_t lo[2] = {perm(out[f][1], out[f][0], kSel), perm(out[f][3], out[f][2], kSel)};
+      uint32_t lo[2];
+      if constexpr (EB == 2) {
+        lo[0] = perm(out[f][1], out[f][0], kSel);
+        lo[1] = perm(out[f][3], out[f][2], kSel);
+      } else {  // one pair of 8-byte elements: its low half
+        lo[0] = out[f][0];
+        lo[1] = out[f][1];
+      }
       if constexpr (GUARD) {
         const int64_t rows = t.remR - (int64_t(rv) << (G::LRPV + G::LB));
         const bool ok = nb < NB && nb < t.remB && c < t.remC && rows > 0;
         if (ok && rows >= G::VE) gstore<8, NTM>(p, lo);
-        else if (ok) gstore_partial<1, 8>(p, int(rows), lo);
+        else if (ok) gstore_partial<KB, 8>(p, int(rows), lo);
       } else {
         gstore<8, NTM>(p, lo);
       }
@@ -398,23 +408,27 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 // 2-byte pairs of a 1-byte stride-2 source, low or high bytes stored (plan.cpp, make_plan): the
 // tall 512 x 64 tiles of 2-byte elements with nontemporal accesses and 2 loads in flight; 4-byte
 // groups of 4 elements of a stride-4 source, the first element of each stored: 4-, 8- and
-// 16-byte tiles of 1 KiB or 512 bytes by 32 groups.  Always with the edge
+// 16-byte tiles of 1 KiB or 512 bytes by 32 groups; 16-byte pairs of an 8-byte stride-2 source:
+// 64 x 8 tiles with every load in flight.  Always with the edge
 // code (the tiles holding a row's last element need it).
 #define TC_CFG_NAR(EB, TILE, NT, CAP)                                                                        \
   if (c.cap == CAP && c.unit == 16 && vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local &&  \
       ntm == 3 && c.edges) {                                                                                 \
+    if constexpr (EB == 2 || EB == 16) {                                                                     \
+      if (c.nar == 1) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 1>(ta, wgs, s); \
+    }                                                                                                        \
+    if constexpr (EB == 2) {                                                                                 \
+      if (c.nar == 2) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 2>(ta, wgs, s); \
+    }                                                                                                        \
     if constexpr (EB >= 4) {                                                                                 \
       if (c.nar == 3) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 3>(ta, wgs, s); \
-    } else {                                                                                                 \
-      if (c.nar == 1) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 1>(ta, wgs, s); \
-      if (c.nar == 2) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 2>(ta, wgs, s); \
     }                                                                                                        \
   }
 #define TC_NAR_EB1
 #define TC_NAR_EB2 TC_CFG_NAR(2, 65536, 512, 2)
 #define TC_NAR_EB4 TC_CFG_NAR(4, 32768, 512, 2)
 #define TC_NAR_EB8 TC_CFG_NAR(8, 32768, 512, 2)
-#define TC_NAR_EB16 TC_CFG_NAR(16, 16384, 256, 2)
+#define TC_NAR_EB16 TC_CFG_NAR(16, 16384, 256, 2) TC_CFG_NAR(16, 8192, 256, 0)
 
 #define TC_CFG_WL(EB, U, TILE, NT)                                                                           \
   if (vb == 16 && tile == TILE && nt == NT && c.step == 1 && ntm == 3 && c.wave_local)                       \

@@ -246,6 +246,26 @@ def test_int8_stride2_source_read_in_pairs(shape, strides, soff):
     assert p["src_view_bytes"] == 2 and p["src_step"] == 2 and (p["tile_r"], p["tile_c"]) == (512, 64), p
 
 
+@pytest.mark.parametrize("shape,strides,soff", [
+    ((600, 100), (256, 2), 0),            # one column tile, ragged rows
+    ((1001, 333), (1000, 2), 1000),       # ragged both ways, the last pair's high half past the span
+    ((512, 64), (128, 2), 0),             # whole tiles
+    ((3, 700, 130), (700 * 262, 262, 2), 4),  # a batch mode
+    ((800, 90), (-184, 2), 799 * 184),    # rows in reverse order
+])
+def test_fp64_stride2_source_read_in_pairs(shape, strides, soff):
+    """8-byte copies whose column mode has source stride 2 (even strides and offset): the source is
+    read as 16-byte pairs on the 16-byte tiles and the low half of each pair stored; the pair
+    holding a row's last element is read as that element only.  An odd offset keeps the stride-2
+    tile of 8-byte elements."""
+    n, m = shape[-2], shape[-1]
+    ds = (1, n) if len(shape) == 2 else (n * m, 1, n)
+    p = _check(shape, strides, ds, 8, s_off=soff, seed=n + m + len(shape) + 8, expect="transpose")
+    assert p["src_view_bytes"] == 16 and p["src_step"] == 2, p
+    p = _check(shape, strides, ds, 8, s_off=soff + 1, seed=n + m + 9, expect="transpose")
+    assert p["src_view_bytes"] == 8 and p["src_step"] == 2, p
+
+
 def test_int8_stride2_pairs_not_taken_at_odd_strides():
     """An odd row stride (rows alternate between low and high bytes of the pairs) keeps the stride-2
     tile of 1-byte elements; same bytes."""
