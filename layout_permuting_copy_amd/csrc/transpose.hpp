@@ -208,6 +208,12 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
     const int rv = acc & ((1 << lnRV) - 1);
     const int c = (acc >> lnRV) & (TC - 1);
     const int nb = acc >> (lnRV + a.lTC);
+    if constexpr (NAR && EB >= 8) {
+      // only part of each 16-byte unit is stored: the compiler would narrow the LDS read to those
+      // bytes (8 or 4 at a 16-byte stride, which conflict in the banks); the empty statement keeps
+      // every word read, so the read stays the conflict-free 16-byte access the swizzle is chosen for
+      asm volatile("" : : "v"(out[f][0]), "v"(out[f][1]), "v"(out[f][2]), "v"(out[f][3]));
+    }
     if constexpr (NAR == 3) {
       static_assert((EB == 4 || EB == 8 || EB == 16) && VB == 16, "groups of 4 elements in 16-byte vectors");
       constexpr int KB = EB / 4;  // bytes kept per group
