@@ -183,10 +183,11 @@ typedef struct tc_plan_info {
                                phase (a wait after each load beyond them); 0 = all at once */
   int32_t super_rows, super_cols; /* grid_order 2: super-tile extents in row and column tiles;
                                      0 otherwise */
-  int32_t src_view_bytes;   /* transpose: bytes the source elements are read as -- elem_bytes, or 2
-                               for 1-byte elements of a stride-2 source read in pairs (src_step 2),
-                               of which the low byte is stored where the source offset is even and
-                               the high byte where it is odd, or 4 x elem_bytes for 1-, 2- and
+  int32_t src_view_bytes;   /* transpose: bytes the source elements are read as -- elem_bytes;
+                               2 x elem_bytes for a stride-2 source read in pairs (src_step 2): 1-byte
+                               elements (the low byte of each pair stored where the source offset
+                               is even, the high byte where it is odd) and 2- and 8-byte elements at
+                               even offsets (the low half stored); or 4 x elem_bytes for 1-, 2- and
                                4-byte elements of a stride-4 source (every source stride and the
                                offset multiples of 4) read in groups of 4 elements, of which the
                                first is stored (src_step 4) */

@@ -253,17 +253,18 @@ def test_int8_stride2_source_read_in_pairs(shape, strides, soff):
     ((3, 700, 130), (700 * 262, 262, 2), 4),  # a batch mode
     ((800, 90), (-184, 2), 799 * 184),    # rows in reverse order
 ])
-def test_fp64_stride2_source_read_in_pairs(shape, strides, soff):
-    """8-byte copies whose column mode has source stride 2 (even strides and offset): the source is
-    read as 16-byte pairs on the 16-byte tiles and the low half of each pair stored; the pair
-    holding a row's last element is read as that element only.  An odd offset keeps the stride-2
-    tile of 8-byte elements."""
+@pytest.mark.parametrize("eb", [2, 8])
+def test_wide_stride2_source_read_in_pairs(shape, strides, soff, eb):
+    """2- and 8-byte copies whose column mode has source stride 2 (even strides and offset): the
+    source is read as 4- or 16-byte pairs on the tiles of that width and the low half of each pair
+    stored; the pair holding a row's last element is read as that element only.  An odd offset
+    keeps the stride-2 tile of the element width."""
     n, m = shape[-2], shape[-1]
     ds = (1, n) if len(shape) == 2 else (n * m, 1, n)
-    p = _check(shape, strides, ds, 8, s_off=soff, seed=n + m + len(shape) + 8, expect="transpose")
-    assert p["src_view_bytes"] == 16 and p["src_step"] == 2, p
-    p = _check(shape, strides, ds, 8, s_off=soff + 1, seed=n + m + 9, expect="transpose")
-    assert p["src_view_bytes"] == 8 and p["src_step"] == 2, p
+    p = _check(shape, strides, ds, eb, s_off=soff, seed=n + m + len(shape) + eb, expect="transpose")
+    assert p["src_view_bytes"] == 2 * eb and p["src_step"] == 2, p
+    p = _check(shape, strides, ds, eb, s_off=soff + 1, seed=n + m + eb + 1, expect="transpose")
+    assert p["src_view_bytes"] == eb and p["src_step"] == 2, p
 
 
 def test_int8_stride2_pairs_not_taken_at_odd_strides():
