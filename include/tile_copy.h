@@ -186,8 +186,8 @@ typedef struct tc_plan_info {
   int32_t src_view_bytes;   /* transpose: bytes the source elements are read as -- elem_bytes;
                                2 x elem_bytes for a stride-2 source read in pairs (src_step 2): 1-byte
                                elements (the low byte of each pair stored where the source offset
-                               is even, the high byte where it is odd) and 2- and 8-byte elements at
-                               even offsets (the low half stored); or 4 x elem_bytes for 1-, 2- and
+                               is even, the high byte where it is odd) and 2-, 4- and 8-byte elements
+                               at even offsets (the low half stored); or 4 x elem_bytes for 1-, 2- and
                                4-byte elements of a stride-4 source (every source stride and the
                                offset multiples of 4) read in groups of 4 elements, of which the
                                first is stored (src_step 4) */

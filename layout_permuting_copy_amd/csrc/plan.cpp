@@ -505,6 +505,14 @@ static bool plan_transpose_tile(Plan* p, int flags) {
       // 2.64, column tiles first 2.93-2.96; 64 x 16 tiles 2.73-3.55, 64 x 32 on 512 lanes 2.68-3.28)
       t.tile = 8192; t.threads = 256; t.trb = 1024; t.order = 2; t.cap = 0; t.ssr = 16; t.ssc = 16;
     }
+    if (p->eb == 8 && p->nar == 1) {
+      // fp32 with a stride-2 source read as 8-byte pairs: 128 x 32 tiles of pairs on 512 lanes in
+      // 16 x 16 super-tiles, 2 loads in flight.  Against the stride-2 tile of 4-byte elements: the
+      // slice [1:8191, 0:8190:2] of 8192^2 3.35 -> 3.75-3.78 TB/s, every other column of 8192^2
+      // 3.49 -> 3.87-3.91, of 4096 x 8192 3.32-3.34 -> 3.61-3.63, of 16384 x 4096 3.40 -> 3.43-3.46
+      // (8 x 8 super-tiles 3.95 on the slice but 3.23 on 16384 x 4096; row tiles first 2.85)
+      t.tile = 32768; t.threads = 512; t.trb = 1024; t.order = 2; t.cap = 2; t.ssr = 16; t.ssc = 16;
+    }
     if (p->eb == 4 && p->nar == 1) {
       // fp16 with a stride-2 source read as 4-byte pairs: 256 x 32 tiles of pairs on 512 lanes in
       // XCD super-tiles of 16 x 16 tiles, 2 loads in flight.  Measured on the slice
@@ -1036,9 +1044,9 @@ Plan make_plan(const tc_layout& src, const tc_layout& dst, int dtype, int flags,
     for (int k = 0; k < j.rank; ++k)
       if (k != r && j.m[k].s == 4) cg = k;
   const int64_t gs = cg >= 0 && cg != r ? j.m[cg].s : 0;
-  // 2- and 8-byte elements of a stride-2 source at an even offset are read as 4- and 16-byte pairs
-  // the same way.
-  if (!forced_guarded && r >= 0 && ((gs == 2 && (p.eb == 1 || ((p.eb == 2 || p.eb == 8) && j.so % 2 == 0))) || (gs == 4 && p.eb <= 4)) &&
+  // 2-, 4- and 8-byte elements of a stride-2 source at an even offset are read as 4-, 8- and
+  // 16-byte pairs the same way.
+  if (!forced_guarded && r >= 0 && ((gs == 2 && (p.eb == 1 || (p.eb >= 2 && p.eb <= 8 && j.so % 2 == 0))) || (gs == 4 && p.eb <= 4)) &&
       ptr_align >= std::min<int64_t>(16, gs * p.eb) && j.m[r].e >= 512 && j.m[cg].e >= 64) {
     bool even = true;
     for (int k = 0; k < j.rank; ++k) even = even && j.m[k].s % gs == 0;

@@ -235,8 +235,8 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
       }
       continue;
     } else if constexpr (NAR) {
-      static_assert((EB == 2 || ((EB == 4 || EB == 16) && NAR == 1)) && VB == 16,
-                    "pairs of 1-, 2- or 8-byte elements in 16-byte vectors");
+      static_assert((EB == 2 || (EB >= 4 && NAR == 1)) && VB == 16,
+                    "pairs of 1-, 2-, 4- or 8-byte elements in 16-byte vectors");
       constexpr int KB = EB / 2;  // bytes kept per pair
       unsigned char* p =
           a.dst + (t.dbase + nb * a.dB + int64_t(c) * a.dC + (int64_t(rv) << (G::LRPV + G::LB))) * KB;
@@ -248,6 +248,9 @@ __device__ __forceinline__ void read_store(const TransposeArgs& a, const TileAt&
       } else if constexpr (EB == 4) {  // the low 2 bytes of each word
         lo[0] = perm(out[f][1], out[f][0], 0x05040100u);
         lo[1] = perm(out[f][3], out[f][2], 0x05040100u);
+      } else if constexpr (EB == 8) {  // the low word of each pair
+        lo[0] = out[f][0];
+        lo[1] = out[f][2];
       } else {  // one pair of 8-byte elements: its low half
         lo[0] = out[f][0];
         lo[1] = out[f][1];
@@ -419,13 +422,13 @@ bool launch_transpose_cfg(const TransposeArgs* ta, int64_t wgs, hipStream_t s) {
 // tall 512 x 64 tiles of 2-byte elements with nontemporal accesses and 2 loads in flight; 4-byte
 // groups of 4 elements of a stride-4 source, the first element of each stored: 4-, 8- and
 // 16-byte tiles of 1 KiB or 512 bytes by 32 groups; 16-byte pairs of an 8-byte stride-2 source:
-// 64 x 8 tiles with every load in flight; 4-byte pairs of a 2-byte stride-2 source: the 4-byte
-// group tiles.  Always with the edge
+// 64 x 8 tiles with every load in flight; 4- and 8-byte pairs of a 2- and 4-byte stride-2 source:
+// the group tiles of that width.  Always with the edge
 // code (the tiles holding a row's last element need it).
 #define TC_CFG_NAR(EB, TILE, NT, CAP)                                                                        \
   if (c.cap == CAP && c.unit == 16 && vb == 16 && tile == TILE && nt == NT && c.step == 1 && !c.wave_local &&  \
       ntm == 3 && c.edges) {                                                                                 \
-    if constexpr (EB == 2 || EB == 4 || EB == 16) {                                                         \
+    if constexpr (EB != 1) {                                                                                 \
       if (c.nar == 1) return dev::launch_transpose_cfg<EB, 16, 16, TILE, NT, 3, 1, false, true, CAP, 1>(ta, wgs, s); \
     }                                                                                                        \
     if constexpr (EB == 2) {                                                                                 \

@@ -253,10 +253,10 @@ def test_int8_stride2_source_read_in_pairs(shape, strides, soff):
     ((3, 700, 130), (700 * 262, 262, 2), 4),  # a batch mode
     ((800, 90), (-184, 2), 799 * 184),    # rows in reverse order
 ])
-@pytest.mark.parametrize("eb", [2, 8])
+@pytest.mark.parametrize("eb", [2, 4, 8])
 def test_wide_stride2_source_read_in_pairs(shape, strides, soff, eb):
-    """2- and 8-byte copies whose column mode has source stride 2 (even strides and offset): the
-    source is read as 4- or 16-byte pairs on the tiles of that width and the low half of each pair
+    """2-, 4- and 8-byte copies whose column mode has source stride 2 (even strides and offset): the
+    source is read as 4-, 8- or 16-byte pairs on the tiles of that width and the low half of each pair
     stored; the pair holding a row's last element is read as that element only.  An odd offset
     keeps the stride-2 tile of the element width."""
     n, m = shape[-2], shape[-1]

@@ -617,8 +617,8 @@ def test_int8_stride2_sources_read_in_pairs():
     """1-byte copies whose column mode has source stride 2 read the source as 2-byte pairs
     (src_view_bytes 2) where every source stride is even (the offset's parity picks the low or
     high byte), the source pointer is 2-byte aligned and the tile is at least 512 x 64; otherwise
-    the stride-2 tile of 1-byte elements (src_view_bytes 1).  2- and 8-byte elements at even offsets
-    are read as 4- and 16-byte pairs; 4-byte elements keep their stride-2 tile."""
+    the stride-2 tile of 1-byte elements (src_view_bytes 1).  2-, 4- and 8-byte elements at even
+    offsets are read as 4-, 8- and 16-byte pairs."""
     n = 8192
     R, C = n - 2, (n - 1) // 2
 
@@ -639,9 +639,10 @@ def test_int8_stride2_sources_read_in_pairs():
     # offset their own width
     assert plan((n, 2), n, dt=L.TC_F16) == (4, 256, 32, 2, 16, 16)
     assert plan((n, 2), n + 1, dt=L.TC_F16)[0] == 2
-    # 8-byte elements: 16-byte pairs on 64 x 8 tiles; 4-byte elements keep their stride-2 tile
+    # 4- and 8-byte elements: 8- and 16-byte pairs on 128 x 32 and 64 x 8 tiles
     assert plan((n, 2), n, dt=L.TC_F64) == (16, 64, 8, 2, 16, 16)
-    assert plan((n, 2), n, dt=L.TC_F32)[0] == 4
+    assert plan((n, 2), n, dt=L.TC_F32) == (8, 128, 32, 2, 16, 16)
+    assert plan((n, 2), n + 1, dt=L.TC_F32)[0] == 4
 
 
 def test_rows_gathered_from_strided_sources():
